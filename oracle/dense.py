@@ -1,0 +1,341 @@
+"""numpy fp64 oracle tiers for two-sided GPTQ.  TEST INFRASTRUCTURE ONLY.
+
+Only tests, the smoke check and the bench's CPU-baseline leg may use this
+module; the HIP library never does.  Nothing here is blocked, fused or
+reordered beyond what the cited passage states: each function is the plain
+definition, with numpy's matmul / inv / cholesky as library steps.
+
+Notation (FastKron page, section 2.1): W is m x n (outputs x inputs), A is the
+n x n input curvature, B the m x m output curvature, the Hessian of the loss
+with respect to vecop(V) is A (x) B, and vecop is the column-major
+vectorisation (WaterKron page, section 2 "Notation").  Entry (i, j) of W sits
+at vecop index p = i + m*j.
+
+U_A is the upper-triangular factor with positive diagonal and U_A^T U_A =
+A_d^{-1}; its transpose is the lower Cholesky factor L^(A) of A_d^{-1} named in
+the pith.science review of BaKron ("key_machinery").  The normalised factor
+used in the feedback is L~_A[j', j] = U_A[j, j'] / U_A[j, j] (the unit-diagonal
+LDL factor, FastKron page section 2.1 "LDL(A)").  This module stores it as
+N_A = L~_A^T, i.e. row j of U_A divided by U_A[j, j].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# Factor preparation
+# ----------------------------------------------------------------------------
+
+
+def damp(A: np.ndarray, delta: float) -> np.ndarray:
+    """A_d = A + delta * (tr A / d) * I.
+
+    The WaterKron page (section 2, "Notation") assumes PSD factors invertible and
+    adds a small damping kappa*I in practice; the reading adopted is kappa =
+    delta times the mean diagonal, applied to each Kronecker factor separately.
+    """
+    A = np.asarray(A, dtype=np.float64)
+    d = A.shape[0]
+    return A + (delta * np.trace(A) / d) * np.eye(d)
+
+
+def upper_factor_via_inverse(Ad: np.ndarray) -> np.ndarray:
+    """Route (i): U = chol(Ad^{-1})^T, so U is upper with U^T U = Ad^{-1}.
+
+    chol here is the lower Cholesky factor L with L L^T = M (WaterKron page,
+    section 2 "Notation"); L^(A) = chol(A^{-1}) is the factor of the BaKron review.
+    """
+    L = np.linalg.cholesky(np.linalg.inv(np.asarray(Ad, dtype=np.float64)))
+    return np.ascontiguousarray(L.T)
+
+
+def upper_factor_via_reverse_cholesky(Ad: np.ndarray) -> np.ndarray:
+    """Route (ii): U = RevCholesky(Ad)^{-T}, with RevCholesky(M) the lower L with
+    L^T L = M (WaterKron page, section 2 "Notation").
+
+    RevCholesky(Ad) = J C^T J where C = chol(J Ad J) and J reverses the index
+    order; hence U = J C^{-1} J.
+    """
+    Ad = np.asarray(Ad, dtype=np.float64)
+    d = Ad.shape[0]
+    J = np.eye(d)[::-1]
+    C = np.linalg.cholesky(J @ Ad @ J)
+    return np.ascontiguousarray(J @ np.linalg.inv(C) @ J)
+
+
+def normalized_factor(U: np.ndarray) -> np.ndarray:
+    """N[j, j'] = U[j, j'] / U[j, j]: row j of U divided by its diagonal entry.
+
+    N^T is the unit-diagonal LDL factor of Ad^{-1} (FastKron page section 2.1,
+    "LDL(A)": the Cholesky factor with columns normalised by their diagonal).
+    """
+    U = np.asarray(U, dtype=np.float64)
+    return U / np.diag(U)[:, None]
+
+
+# ----------------------------------------------------------------------------
+# Base quantizer
+# ----------------------------------------------------------------------------
+
+
+def grid(bits: int) -> tuple[int, int]:
+    """Symmetric b-bit integer grid [-2^(b-1), 2^(b-1)-1]."""
+    return -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+
+
+def scales(W: np.ndarray, bits: int, per_row: bool) -> np.ndarray:
+    """s_i = max_j |W_ij| / (2^(b-1) - 1) per output row, or one value per tensor.
+
+    Scales are chosen up front and handed to the algorithm (WaterKron page,
+    section 2.4).  Returns an array of length m (per row) or 1 (per tensor).
+    """
+    W = np.asarray(W)
+    _, qmax = grid(bits)
+    if per_row:
+        return np.max(np.abs(W), axis=1) / qmax
+    return np.array([np.max(np.abs(W)) / qmax])
+
+
+def row_scales(s: np.ndarray, m: int) -> np.ndarray:
+    s = np.asarray(s, dtype=np.float64).reshape(-1)
+    return np.full(m, s[0]) if s.size == 1 else s.copy()
+
+
+def quantize(x: float, s: float, qmin: int, qmax: int) -> tuple[float, float, float]:
+    """Closest grid point: z = clamp(rne(x / s)), v = s z.  Returns (z, v, y=x/s).
+
+    The FastKron page (section 2.1) replaces 'round' by a map to the closest
+    element of the alphabet; for a clipped uniform grid that is round-to-nearest
+    (ties to even) followed by a clamp.  A zero scale (an all-zero row) maps to
+    z = 0, v = 0.
+    """
+    if s == 0.0:
+        return 0.0, 0.0, 0.0
+    y = x / s
+    z = min(max(float(np.rint(y)), qmin), qmax)
+    return z, s * z, y
+
+
+# ----------------------------------------------------------------------------
+# Tier O1: literal vectorised GPTQ on the Kronecker Hessian
+# ----------------------------------------------------------------------------
+
+
+def vectorized_kron_gptq(W, Ad, Bd, s, bits, return_factor=False):
+    """Standard GPTQ on w^ = vecop(W)^T with Hessian A_d (x) B_d.
+
+    FastKron page, section 2.2: the two-sided extension is Algorithm 1 applied
+    to the vectorised weight and 'input' curvature A (x) B.  The GPTQ recurrence
+    (Frantar et al.): for p in order, q = quantize(w_p); err = (w_p - q)/U^_pp;
+    w_{p+1:} -= err * U^_{p, p+1:}, with U^ the upper Cholesky factor of the
+    inverse Hessian.  Equivalently Babai's nearest plane (BaKron / GPTQ-2D
+    abstracts).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    H = np.kron(np.asarray(Ad, dtype=np.float64), np.asarray(Bd, dtype=np.float64))
+    Uh = upper_factor_via_inverse(H)
+    w = W.reshape(-1, order="F").copy()
+    s_row = row_scales(s, m)
+    qmin, qmax = grid(bits)
+    z = np.zeros(m * n)
+    v = np.zeros(m * n)
+    y = np.zeros(m * n)
+    for p in range(m * n):
+        z[p], v[p], y[p] = quantize(w[p], s_row[p % m], qmin, qmax)
+        err = (w[p] - v[p]) / Uh[p, p]
+        w[p + 1:] -= err * Uh[p, p + 1:]
+    out = (z.reshape((m, n), order="F"), v.reshape((m, n), order="F"),
+           y.reshape((m, n), order="F"))
+    return out + (Uh,) if return_factor else out
+
+
+# ----------------------------------------------------------------------------
+# Tier O2: the two-sided loop in matrix form
+# ----------------------------------------------------------------------------
+
+
+def entry_order(m: int, n: int, order: str):
+    """Entry sequences that respect the componentwise partial order.
+
+    'column' is vecop order (j outer, i inner); 'row' is i outer; 'antidiagonal'
+    visits k = i + j ascending (FastKron page section 2.3, anti-diagonal k),
+    rows ascending within a diagonal.
+    """
+    if order == "column":
+        return [(i, j) for j in range(n) for i in range(m)]
+    if order == "row":
+        return [(i, j) for i in range(m) for j in range(n)]
+    if order == "antidiagonal":
+        return [(i, k - i) for k in range(m + n - 1)
+                for i in range(max(0, k - n + 1), min(k, m - 1) + 1)]
+    raise ValueError(order)
+
+
+def two_sided_naive(W, UA, UB, s, bits, order="column"):
+    """FastKron-naive written in matrix space (FastKron page, sections 2.2-2.4).
+
+    X := W; for each entry (i, j) in a valid order: quantize x = X[i, j], set
+    Delta = v - x and apply the outer-product feedback
+    X[i', j'] += L~_B[i', i] * Delta * L~_A[j', j] for i' >= i, j' >= j (the update
+    W <- W + L_{:,i}^(B) Delta (L_{:,j}^(A))^T of section 2.4).  Only entries to the
+    bottom-right change (section 2.3), so any order that visits (i', j') after
+    every (i, j) <= (i', j') gives the same result.
+
+    Returns (Z, V, Y, D): codes, dequantised values, pre-rounding value in grid
+    units x/s, and the errors Delta.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    NA, NB = normalized_factor(UA), normalized_factor(UB)
+    X = W.copy()
+    s_row = row_scales(s, m)
+    qmin, qmax = grid(bits)
+    Z = np.zeros((m, n)); V = np.zeros((m, n)); Y = np.zeros((m, n)); D = np.zeros((m, n))
+    for i, j in entry_order(m, n, order):
+        x = X[i, j]
+        Z[i, j], V[i, j], Y[i, j] = quantize(x, s_row[i], qmin, qmax)
+        D[i, j] = V[i, j] - x
+        X[i:, j:] += D[i, j] * np.outer(NB[i, i:], NA[j, j:])
+    return Z, V, Y, D
+
+
+def two_sided_recursive(W, UA, UB, s, bits):
+    """FastKron (Algorithm 6 reading): recursion over anti-diagonal ranges.
+
+    FastKron page section 2.5: solve the first half of the anti-diagonals, add
+    the propagated errors L~_B antidiag_{k0..mid}(Delta) L~_A^T to the second half,
+    solve the second half.  A leaf is a single anti-diagonal whose entries are
+    independent (section 2.3).  Anti-diagonals here are 0-based, k = i + j.
+    The propagation uses dense products of the full factors: it is the
+    definition of the batched update, not an efficient schedule.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    LA, LB = normalized_factor(UA).T, normalized_factor(UB).T
+    X = W.copy()
+    s_row = row_scales(s, m)
+    qmin, qmax = grid(bits)
+    Z = np.zeros((m, n)); V = np.zeros((m, n)); Y = np.zeros((m, n)); D = np.zeros((m, n))
+    kidx = np.add.outer(np.arange(m), np.arange(n))
+
+    def solve(k0, k1):
+        if k1 - k0 == 1:
+            for i in range(max(0, k0 - n + 1), min(k0, m - 1) + 1):
+                j = k0 - i
+                Z[i, j], V[i, j], Y[i, j] = quantize(X[i, j], s_row[i], qmin, qmax)
+                D[i, j] = V[i, j] - X[i, j]
+            return
+        mid = (k0 + k1) // 2
+        solve(k0, mid)
+        src = np.where((kidx >= k0) & (kidx < mid), D, 0.0)
+        upd = LB @ src @ LA.T
+        tgt = (kidx >= mid) & (kidx < k1)
+        X[tgt] += upd[tgt]
+        solve(mid, k1)
+
+    solve(0, m + n - 1)
+    return Z, V, Y, D
+
+
+def two_sided_recursive_vecop(W, UA, UB, s, bits):
+    """FastKron-recursive reading: lazy batched updates over the vecop sequence.
+
+    FastKron page section 2.4: solve the first half of the entry sequence,
+    propagate its errors to the second half with one batched update
+    L~_B Delta L~_A^T, then solve the second half; no anti-diagonal batching.
+    The sequence is vecop (column-major) order; block sizes halve recursively.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    LA, LB = normalized_factor(UA).T, normalized_factor(UB).T
+    X = W.copy()
+    s_row = row_scales(s, m)
+    qmin, qmax = grid(bits)
+    Z = np.zeros((m, n)); V = np.zeros((m, n)); Y = np.zeros((m, n)); D = np.zeros((m, n))
+    pidx = np.add.outer(np.arange(m), m * np.arange(n))
+
+    def solve(p0, p1):
+        if p1 - p0 == 1:
+            i, j = p0 % m, p0 // m
+            Z[i, j], V[i, j], Y[i, j] = quantize(X[i, j], s_row[i], qmin, qmax)
+            D[i, j] = V[i, j] - X[i, j]
+            return
+        mid = (p0 + p1) // 2
+        solve(p0, mid)
+        src = np.where((pidx >= p0) & (pidx < mid), D, 0.0)
+        upd = LB @ src @ LA.T
+        tgt = (pidx >= mid) & (pidx < p1)
+        X[tgt] += upd[tgt]
+        solve(mid, p1)
+
+    solve(0, m * n)
+    return Z, V, Y, D
+
+
+def one_sided_gptq(W, UA, s, bits):
+    """Standard one-sided GPTQ (Frantar et al.), Hessian A (x) I_m.
+
+    Columns in order: q = quantize(W[:, j]) row-wise, err = (W[:, j] - q) / U[j, j],
+    W[:, j+1:] -= err U[j, j+1:] (FastKron page section 2.2, Algorithm 1's
+    recurrence; U the upper Cholesky factor of A^{-1}).
+    """
+    Wc = np.asarray(W, dtype=np.float64).copy()
+    m, n = Wc.shape
+    s_row = row_scales(s, m)
+    qmin, qmax = grid(bits)
+    Z = np.zeros((m, n)); V = np.zeros((m, n))
+    for j in range(n):
+        for i in range(m):
+            Z[i, j], V[i, j], _ = quantize(Wc[i, j], s_row[i], qmin, qmax)
+        err = (Wc[:, j] - V[:, j]) / UA[j, j]
+        Wc[:, j + 1:] -= np.outer(err, UA[j, j + 1:])
+    return Z, V
+
+
+# ----------------------------------------------------------------------------
+# Loss, factors, scores
+# ----------------------------------------------------------------------------
+
+
+def proxy_loss(W, V, Ad, Bd) -> float:
+    """D_{A,B} = tr(B (V - W) A (V - W)^T) = ||(B^{1/2})^T (V-W) A^{1/2}||_F^2.
+
+    WaterKron page section 1 item 1 (with S S^T = M for M^{1/2}); the FastKron
+    page section 2.2 writes the same loss for symmetric roots.
+    """
+    E = np.asarray(V, dtype=np.float64) - np.asarray(W, dtype=np.float64)
+    return float(np.trace(np.asarray(Bd) @ E @ np.asarray(Ad) @ E.T))
+
+
+def loss_from_errors(D, UA, UB) -> float:
+    """sum_ij (Delta_ij / (U_B[i,i] U_A[j,j]))^2: the loss through the identity
+    V - W = L~_B Delta L~_A^T and L~ = U^T diag(U)^{-1}."""
+    dA = np.diag(np.asarray(UA, dtype=np.float64))
+    dB = np.diag(np.asarray(UB, dtype=np.float64))
+    return float(np.sum((np.asarray(D) / np.outer(dB, dA)) ** 2))
+
+
+def factor_accumulate(X, S=None, alpha=1.0, beta=0.0):
+    """S <- beta S + alpha X^T X for samples stored as rows of X.
+
+    With alpha = 1/N this is the K-FAC / 'Marginal' factor A = E[a a^T] over N
+    activation rows (FastKron page section 3.2 and section 2.6's accumulation of
+    the Hessian from the calibration data); the same for gradient rows gives B.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    G = alpha * (X.T @ X)
+    if S is None or beta == 0.0:
+        return G
+    return beta * np.asarray(S, dtype=np.float64) + G
+
+
+def sensitivity(A, B) -> float:
+    """KronQ sublayer score tr(A) * tr(B) (KronQ page, mixed-precision allocation)."""
+    return float(np.trace(A) * np.trace(B))
+
+
+def prepare(A, delta):
+    """Damped factor and its upper factor: (A_d, U) with U^T U = A_d^{-1}."""
+    Ad = damp(A, delta)
+    return Ad, upper_factor_via_inverse(Ad)
