@@ -1,0 +1,122 @@
+"""Host-only checks of the C ABI: the library loads without a GPU, exports every
+function include/kronq.h declares, sizes workspaces, and rejects bad arguments
+before anything is enqueued (no HIP call is made on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import two_sided_gptq_damped_amd as kq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "kronq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kron_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for fn in ("kron_factor_accumulate", "kron_prepare", "kron_quantize", "kron_loss"):
+        assert fn in names
+    assert set(names) == set(kq.EXPORTED)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = kq.library()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert kq.kron_abi_version() == 1
+    assert lib.kron_status_string(2) == b"factor not positive definite"
+
+
+def test_workspace_sizes():
+    lib = kq.library()
+    q32 = lib.kron_workspace_bytes(kq.KQ_OP_QUANTIZE, kq.KQ_F32, 4096, 4096)
+    q64 = lib.kron_workspace_bytes(kq.KQ_OP_QUANTIZE, kq.KQ_F64, 4096, 4096)
+    # two factors plus three m x n buffers, at least
+    assert q32 >= 5 * 4096 * 4096 * 4 and q64 >= 2 * q32 - 4096
+    assert lib.kron_workspace_bytes(kq.KQ_OP_QUANTIZE, kq.KQ_F32, 100, 70) >= 5 * 128 * 128 * 4
+    assert lib.kron_workspace_bytes(kq.KQ_OP_PREPARE, kq.KQ_F32, 4096, 0) >= 2 * 4096 * 4096 * 8
+    assert lib.kron_workspace_bytes(kq.KQ_OP_LOSS, kq.KQ_F32, 64, 64) > 0
+    assert lib.kron_workspace_bytes(kq.KQ_OP_FACTOR, kq.KQ_F32, 64, 64) == 0
+    assert lib.kron_workspace_bytes(kq.KQ_OP_QUANTIZE, 7, 64, 64) == 0
+    assert lib.kron_workspace_bytes(kq.KQ_OP_QUANTIZE, kq.KQ_F32, -1, 64) == 0
+    assert lib.kron_workspace_bytes(kq.KQ_OP_QUANTIZE, kq.KQ_F32, 1 << 17, 64) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def q(bits=3, per_row=1, scales=FAKE):
+    return ctypes.byref(kq._Quantizer(bits, per_row, scales.value if scales else None))
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=5), 1),
+    (dict(m=-1), 1),
+    (dict(W=None), 1),
+    (dict(UA=None), 1),
+    (dict(codes=None), 1),
+    (dict(V=None), 1),
+    (dict(ldw=10), 1),
+    (dict(lda=10), 1),
+    (dict(ldb=10), 1),
+    (dict(ldc=10), 1),
+    (dict(q=None), 1),
+    (dict(bits=1), 1),
+    (dict(bits=9), 1),
+    (dict(per_row=2), 1),
+    (dict(scales=None), 1),
+    (dict(ws=None), 3),
+    (dict(ws_bytes=1024), 3),
+    (dict(m=1 << 17), 1),
+])
+def test_quantize_rejects_bad_arguments(args, status):
+    lib = kq.library()
+    a = dict(dtype=kq.KQ_F32, m=64, n=64, W=FAKE, ldw=64, UA=FAKE, lda=64, UB=FAKE, ldb=64, bits=3, per_row=1,
+             scales=FAKE, codes=FAKE, ldc=64, V=FAKE, ldv=64, ws=FAKE, ws_bytes=1 << 40, q=True)
+    a.update(args)
+    qq = q(a["bits"], a["per_row"], a["scales"]) if a["q"] else None
+    rc = lib.kron_quantize(a["dtype"], a["m"], a["n"], a["W"], a["ldw"], a["UA"], a["lda"], a["UB"], a["ldb"], qq,
+                           a["codes"], a["ldc"], a["V"], a["ldv"], a["ws"], a["ws_bytes"], None)
+    assert rc == status
+    assert lib.kron_last_error() != b""
+
+
+def test_quantize_empty_is_a_no_op():
+    lib = kq.library()
+    assert lib.kron_quantize(kq.KQ_F32, 0, 64, None, 64, None, 64, None, 0, q(), None, 64, None, 64, None, 0,
+                             None) == 0
+    assert lib.kron_quantize(kq.KQ_F64, 64, 0, None, 0, None, 0, None, 64, q(), None, 0, None, 0, None, 0, None) == 0
+
+
+def test_workspace_alignment_is_checked():
+    lib = kq.library()
+    rc = lib.kron_quantize(kq.KQ_F32, 64, 64, FAKE, 64, FAKE, 64, None, 0, q(), FAKE, 64, FAKE, 64,
+                           ctypes.c_void_p(0x1008), 1 << 40, None)
+    assert rc == 3 and b"aligned" in lib.kron_last_error()
+
+
+def test_prepare_factor_loss_scales_reject_bad_arguments():
+    lib = kq.library()
+    assert lib.kron_prepare(kq.KQ_F32, 0, FAKE, 1, 0.01, FAKE, 1, None, None, None, FAKE, 1 << 40, None) == 1
+    assert lib.kron_prepare(kq.KQ_F32, 64, None, 64, 0.01, FAKE, 64, None, None, None, FAKE, 1 << 40, None) == 1
+    assert lib.kron_prepare(kq.KQ_F32, 64, FAKE, 32, 0.01, FAKE, 64, None, None, None, FAKE, 1 << 40, None) == 1
+    assert lib.kron_prepare(kq.KQ_F32, 64, FAKE, 64, -1.0, FAKE, 64, None, None, None, FAKE, 1 << 40, None) == 1
+    assert lib.kron_prepare(kq.KQ_F32, 64, FAKE, 64, float("nan"), FAKE, 64, None, None, None, FAKE, 1 << 40,
+                            None) == 1
+    assert lib.kron_prepare(kq.KQ_F32, 64, FAKE, 64, 0.01, FAKE, 64, None, None, None, FAKE, 16, None) == 3
+    assert lib.kron_factor_accumulate(kq.KQ_F32, 10, 64, None, 64, FAKE, 64, 1.0, 0.0, None) == 1
+    assert lib.kron_factor_accumulate(kq.KQ_F32, 10, 64, FAKE, 63, FAKE, 64, 1.0, 0.0, None) == 1
+    assert lib.kron_factor_accumulate(kq.KQ_F32, 10, 64, FAKE, 64, FAKE, 64, float("inf"), 0.0, None) == 1
+    assert lib.kron_factor_accumulate(kq.KQ_F32, 10, 0, None, 0, None, 0, 1.0, 0.0, None) == 0
+    assert lib.kron_loss(kq.KQ_F64, 8, 8, FAKE, 8, None, 8, FAKE, 8, None, 0, 0.0, FAKE, FAKE, 1 << 40, None) == 1
+    assert lib.kron_loss(kq.KQ_F64, 8, 8, FAKE, 8, FAKE, 8, FAKE, 8, FAKE, 4, 0.0, FAKE, FAKE, 1 << 40, None) == 1
+    assert lib.kron_loss(kq.KQ_F64, 8, 8, FAKE, 8, FAKE, 8, FAKE, 8, None, 0, 0.0, FAKE, FAKE, 8, None) == 3
+    assert lib.kron_row_scales(kq.KQ_F32, 8, 8, FAKE, 8, 1, 1, FAKE, None) == 1
+    assert lib.kron_row_scales(kq.KQ_F32, 8, 8, FAKE, 8, 4, 3, FAKE, None) == 1
+    assert lib.kron_row_scales(kq.KQ_F32, 8, 8, None, 8, 4, 1, FAKE, None) == 1

@@ -1,0 +1,254 @@
+"""GPU parity: every entry point through the C ABI against the CPU oracle.
+
+Inputs are the seeded synthetic workloads of synth/.  For kron_quantize the
+factors U_A, U_B come from the oracle's fp64 preparation and are rounded to the
+run dtype; both sides then solve the same problem:
+  fp64: codes equal, except at entries whose oracle pre-rounding value lies
+        within 1e-9 grid units of a rounding midpoint (handled by re-running the
+        oracle with the GPU's code imposed there); V equal where codes are equal.
+  fp32: code mismatch fraction <= 1e-3 and proxy-loss relative error <= 1e-3
+        against the fp64 oracle on the fp32-rounded inputs.
+The other entry points are compared with the oracle's definitions within
+tolerances derived from their arithmetic (stated per test).
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import compare, dense, o3
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import two_sided_gptq_damped_amd as kq  # noqa: E402
+from two_sided_gptq_damped_amd import pipeline  # noqa: E402
+
+DEV = "cuda"
+TORCH_DT = {np.float64: torch.float64, np.float32: torch.float32}
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def up(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a).astype(dtype))).to(DEV)
+
+
+def oracle_factors(A, B, delta=0.01):
+    Ad, UA = dense.prepare(A, delta)
+    Bd, UB = (None, None) if B is None else dense.prepare(B, delta)
+    return Ad, UA, Bd, UB
+
+
+def gpu_quantize(W, UA, UB, s, bits, per_row, dtype):
+    Wt, UAt = up(W, dtype), up(UA, dtype)
+    UBt = None if UB is None else up(UB, dtype)
+    st = up(s, dtype)
+    codes, V, _ = pipeline.quantize(Wt, UAt, UBt, bits, per_row, scales=st)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), V.cpu().numpy()
+
+
+def check_fp64(W, UA, UB, s, bits, per_row, label):
+    say(label, "fp64", W.shape)
+    Zg, Vg = gpu_quantize(W, UA, UB, s, bits, per_row, np.float64)
+    run = lambda f: o3.solve(W, UA, UB, s, bits, force=f)[0::2]
+    ok, nforced, info = compare.codes_equal_up_to_ties(Zg, run)
+    assert ok, f"{label}: {info}"
+    Zo, Vo, _, _ = o3.solve(W, UA, UB, s, bits)
+    same = Zo == Zg
+    assert np.array_equal(Vg[same], Vo[same])
+    return Zg, Vg
+
+
+def check_fp32(W, UA, UB, s, bits, per_row, Ad, Bd, label, max_mis=1e-3, max_loss=1e-3):
+    say(label, "fp32", W.shape)
+    W32, UA32 = W.astype(np.float32), UA.astype(np.float32)
+    UB32 = None if UB is None else UB.astype(np.float32)
+    s32 = np.asarray(s).astype(np.float32)
+    Zg, Vg = gpu_quantize(W32, UA32, UB32, s32, bits, per_row, np.float32)
+    Zo, Vo, _, _ = o3.solve(W32.astype(np.float64), UA32.astype(np.float64),
+                            None if UB is None else UB32.astype(np.float64), s32.astype(np.float64), bits)
+    mis = compare.mismatch_fraction(Zg, Zo)
+    Bl = np.eye(W.shape[0]) if Bd is None else Bd
+    lg = dense.proxy_loss(W32.astype(np.float64), Vg.astype(np.float64), Ad, Bl)
+    lo = dense.proxy_loss(W32.astype(np.float64), Vo, Ad, Bl)
+    rel = compare.rel_diff(lg, lo)
+    say(label, f"mismatch={mis:.3e} loss_rel={rel:.3e}")
+    assert mis <= max_mis and rel <= max_loss
+    return Zg, Vg
+
+
+# ---------------------------------------------------------------- the solver
+
+def test_tiny_fp64_matches_literal_kronecker_gptq():
+    c = synth.tiny()
+    A = dense.factor_accumulate(c["act"], alpha=1 / 256)
+    B = dense.factor_accumulate(c["grad"], alpha=1 / 256)
+    Ad, UA, Bd, UB = oracle_factors(A, B)
+    s = dense.scales(c["W"], 4, False)
+    Zg, Vg = check_fp64(c["W"], UA, UB, s, 4, False, "tiny 32x32")
+    Z1, V1, Y1 = dense.vectorized_kron_gptq(c["W"], Ad, Bd, s, 4)
+    assert np.array_equal(Zg, Z1)
+    lg = dense.proxy_loss(c["W"], Vg, Ad, Bd)
+    assert abs(lg - dense.proxy_loss(c["W"], V1, Ad, Bd)) <= 1e-12 * lg
+
+
+@pytest.fixture(scope="module")
+def spectral():
+    c = synth.spectral()
+    Ad, UA, Bd, UB = oracle_factors(c["A"], c["B"])
+    s = dense.scales(c["W"], 3, True)
+    return c, Ad, UA, Bd, UB, s
+
+
+def test_spectral_256_fp64(spectral):
+    c, Ad, UA, Bd, UB, s = spectral
+    check_fp64(c["W"], UA, UB, s, 3, True, "spectral 256")
+
+
+def test_spectral_256_fp32(spectral):
+    c, Ad, UA, Bd, UB, s = spectral
+    check_fp32(c["W"], UA, UB, s, 3, True, Ad, Bd, "spectral 256")
+
+
+def test_spectral_256_b_identity_is_one_sided_gptq(spectral):
+    c, Ad, UA, Bd, UB, s = spectral
+    say("spectral 256 B=I")
+    Zg, Vg = gpu_quantize(c["W"], UA, None, s, 3, True, np.float64)
+    Zr, Vr = dense.one_sided_gptq(c["W"], UA, s, 3)
+    Yr = o3.solve(c["W"], UA, None, s, 3)[2]
+    assert np.all((Zg == Zr) | (compare.tie_distance(Yr) < 1e-9))
+    check_fp32(c["W"], UA, None, s, 3, True, Ad, None, "spectral 256 B=I")
+
+
+@pytest.mark.parametrize("m,n", [(100, 70), (64, 130), (1, 50), (50, 1), (65, 65), (127, 129), (3, 200),
+                                 (192, 64)])
+def test_ragged_shapes_fp64(m, n):
+    c = synth.spectral(m, n, config=2)
+    _, UA, _, UB = oracle_factors(c["A"], c["B"])
+    s = dense.scales(c["W"], 4, True)
+    check_fp64(c["W"], UA, UB, s, 4, True, f"ragged {m}x{n}")
+
+
+@pytest.mark.parametrize("bits,per_row", [(2, True), (3, False), (5, True), (8, False)])
+def test_bits_and_scale_modes(bits, per_row):
+    c = synth.spectral(96, 80, config=2)
+    Ad, UA, Bd, UB = oracle_factors(c["A"], c["B"])
+    s = dense.scales(c["W"], bits, per_row)
+    check_fp64(c["W"], UA, UB, s, bits, per_row, f"bits={bits} per_row={per_row}")
+    check_fp32(c["W"], UA, UB, s, bits, per_row, Ad, Bd, f"bits={bits} per_row={per_row}")
+
+
+def test_zero_row_scale_gives_zero_codes():
+    c = synth.spectral(64, 64, config=2)
+    _, UA, _, UB = oracle_factors(c["A"], c["B"])
+    W = c["W"].copy()
+    W[5, :] = 0.0
+    s = dense.scales(W, 3, True)
+    Zg, Vg = check_fp64(W, UA, UB, s, 3, True, "zero row")
+    assert np.all(Zg[5] == 0) and np.all(Vg[5] == 0)
+
+
+def test_deterministic_replay(spectral):
+    c, Ad, UA, Bd, UB, s = spectral
+    say("replay")
+    a = gpu_quantize(c["W"], UA, UB, s, 3, True, np.float32)
+    b = gpu_quantize(c["W"], UA, UB, s, 3, True, np.float32)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# --------------------------------------------------------- other entry points
+
+@pytest.mark.parametrize("d", [1, 17, 64, 100, 256])
+def test_prepare_matches_oracle(d):
+    say("prepare", d)
+    c = synth.spectral(d, d, config=2)
+    for dtype, tol in ((np.float64, 1e-9), (np.float32, 1e-5)):
+        A = c["A"].astype(dtype)
+        U, tr, lam = pipeline.prepare(up(A, dtype), 0.01)
+        U = U.cpu().numpy().astype(np.float64)
+        _, Uo = dense.prepare(A.astype(np.float64), 0.01)
+        assert np.max(np.abs(U - Uo)) <= tol * np.max(np.abs(Uo))
+        assert np.all(np.tril(U, -1) == 0)
+        assert abs(tr.item() - np.trace(A.astype(np.float64))) <= 1e-12 * abs(np.trace(A))
+
+
+def test_prepare_detects_indefinite():
+    say("prepare indefinite")
+    A = -np.eye(32)
+    A[3, 3] = 2.0
+    At = up(A, np.float64)
+    with pytest.raises(kq.KronError) as e:
+        pipeline.prepare(At, 0.0)
+    assert e.value.status == 2
+    info = torch.zeros(1, dtype=torch.int32, device=DEV)
+    U = torch.empty_like(At)
+    ws = kq.workspace(kq.KQ_OP_PREPARE, torch.float64, 32, 0)
+    kq.kron_prepare(At, 0.0, U, ws, info=info)
+    torch.cuda.synchronize()
+    assert info.item() == 1  # the last index of A is the first pivot of the reversed factorisation
+
+
+@pytest.mark.parametrize("rows,dim", [(256, 32), (300, 100), (4096, 256), (7, 65)])
+def test_factor_accumulate(rows, dim):
+    say("factor", rows, dim)
+    X = synth.channel_scaled_rows(77, 78, rows, dim)
+    S0 = synth.gaussian(79, (dim, dim))
+    for dtype, tol in ((np.float64, 1e-12), (np.float32, 1e-5)):
+        Xt, St = up(X, dtype), up(S0, dtype)
+        kq.kron_factor_accumulate(Xt, St, 1.0 / rows, 0.5)
+        want = dense.factor_accumulate(X.astype(dtype).astype(np.float64), S0.astype(dtype), 1.0 / rows, 0.5)
+        got = St.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(got - want)) <= tol * np.max(np.abs(want))
+
+
+@pytest.mark.parametrize("m,n,bidentity", [(32, 32, False), (100, 70, False), (64, 130, True)])
+def test_loss_matches_oracle(m, n, bidentity):
+    say("loss", m, n)
+    c = synth.spectral(m, n, config=2)
+    V = c["W"] + 0.1 * synth.gaussian(91, (m, n))
+    for dtype in (np.float64, np.float32):
+        W32, V32 = c["W"].astype(dtype), V.astype(dtype)
+        B = None if bidentity else c["B"].astype(dtype)
+        got = pipeline.loss(up(W32, dtype), up(V32, dtype), up(c["A"], dtype),
+                            None if B is None else up(B, dtype), 0.01).item()
+        Ad = dense.damp(c["A"].astype(dtype).astype(np.float64), 0.01)
+        Bd = np.eye(m) if B is None else dense.damp(B.astype(np.float64), 0.01)
+        want = dense.proxy_loss(W32.astype(np.float64), V32.astype(np.float64), Ad, Bd)
+        assert abs(got - want) <= 1e-12 * abs(want)
+
+
+@pytest.mark.parametrize("per_row", [True, False])
+def test_row_scales_bit_exact(per_row):
+    say("scales", per_row)
+    W = synth.heavy_weight(5, 6, 130, 257)
+    for dtype in (np.float64, np.float32):
+        Wt = up(W, dtype)
+        s = torch.empty(130 if per_row else 1, dtype=TORCH_DT[dtype], device=DEV)
+        kq.kron_row_scales(Wt, 3, per_row, s)
+        want = dense.scales(W.astype(dtype).astype(np.float64), 3, per_row).astype(dtype)
+        assert np.array_equal(s.cpu().numpy(), want)
+
+
+def test_pipeline_tiny_all_on_gpu_fp64():
+    # Every step on the GPU (factor, prepare, scales, quantize, loss) against the
+    # oracle's own pipeline on the same samples; factors differ only by rounding.
+    say("pipeline tiny fp64")
+    c = synth.tiny()
+    out = pipeline.quantize_layer(up(c["W"], np.float64), up(c["act"], np.float64), up(c["grad"], np.float64),
+                                  bits=4, per_row=False)
+    A = dense.factor_accumulate(c["act"], alpha=1 / 256)
+    B = dense.factor_accumulate(c["grad"], alpha=1 / 256)
+    Ad, UA, Bd, UB = oracle_factors(A, B)
+    s = dense.scales(c["W"], 4, False)
+    Zo, Vo, Yo, _ = o3.solve(c["W"], UA, UB, s, 4)
+    Zg = out["codes"].cpu().numpy()
+    assert np.all((Zg == Zo) | (compare.tie_distance(Yo) < 1e-9))
+    lo = dense.proxy_loss(c["W"], Vo, Ad, Bd)
+    assert abs(out["loss"].item() - lo) <= 1e-10 * lo
+    assert abs(out["trace_A"].item() * out["trace_B"].item() - dense.sensitivity(A, B)) <= 1e-12 * dense.sensitivity(A, B)

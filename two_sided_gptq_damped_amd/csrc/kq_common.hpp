@@ -1,0 +1,265 @@
+// Shared device and host helpers of the kronq HIP library (gfx950 only).
+//
+// The matrix-core tile used by every dense contraction in the library is a
+// 64 x 64 output block computed by one 256-thread workgroup (four wave64s in a
+// 2 x 2 arrangement, 32 x 32 outputs per wave), K consumed 16 at a time through
+// double-buffered LDS.  fp32 uses v_mfma_f32_32x32x2f32, fp64 uses
+// v_mfma_f64_16x16x4f64 (four 16 x 16 blocks per wave).  Operand lane layouts
+// (measured on gfx950):
+//   f32 32x32x2 : A[i=l%32][k=l/32], B[k=l/32][j=l%32],
+//                 D reg r -> row 8*(r/4) + 4*(l/32) + r%4, col l%32
+//   f64 16x16x4 : A[i=l%16][k=l/16], B[k=l/16][j=l%16],
+//                 D reg r -> row l/16 + 4*r, col l%16
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/kronq.h"
+
+namespace kq {
+
+constexpr int TILE = 64;     // solver / GEMM tile edge
+constexpr int KSTEP = 16;    // K slice staged in LDS per iteration
+constexpr int GEMM_THREADS = 256;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ host side
+
+void set_error(const std::string& msg);
+kq_status hip_fail(hipError_t e, const char* what);
+
+#define KQ_HIP(expr)                                                   \
+    do {                                                               \
+        hipError_t kq_e_ = (expr);                                     \
+        if (kq_e_ != hipSuccess) return ::kq::hip_fail(kq_e_, #expr);  \
+    } while (0)
+
+#define KQ_LAUNCHED(name)                                              \
+    do {                                                               \
+        hipError_t kq_e_ = hipGetLastError();                          \
+        if (kq_e_ != hipSuccess) return ::kq::hip_fail(kq_e_, name);   \
+    } while (0)
+
+inline int64_t round_up(int64_t x, int64_t q) { return (x + q - 1) / q * q; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Simple bump allocator over the caller's workspace.
+struct Carve {
+    char* base;
+    size_t used = 0;
+    explicit Carve(void* p) : base(static_cast<char*>(p)) {}
+    template <typename T>
+    T* take(size_t count) {
+        T* p = reinterpret_cast<T*>(base ? base + used : nullptr);
+        used += align256(count * sizeof(T));
+        return p;
+    }
+};
+
+// ---------------------------------------------------------------- device side
+
+// Base quantizer: z = clamp(rne(x / s)), v = s * z.  IEEE division (HIP's default
+// correctly rounded divide), rint = round half to even.  s == 0 gives z = v = 0.
+template <typename T>
+__device__ __forceinline__ void quantize(T x, T s, T qmin, T qmax, T& z, T& v) {
+    if (s == T(0)) {
+        z = T(0);
+        v = T(0);
+        return;
+    }
+    T r = __builtin_rint(x / s);
+    r = r < qmin ? qmin : r;
+    r = r > qmax ? qmax : r;
+    z = r;
+    v = s * r;
+}
+
+template <typename T>
+struct LdsStride;
+template <>
+struct LdsStride<float> {
+    static constexpr int value = 68;  // 16-byte aligned rows, spreads banks
+};
+template <>
+struct LdsStride<double> {
+    static constexpr int value = 66;
+};
+
+// Per-wave accumulator of a 32 x 32 block of the 64 x 64 tile.
+template <typename T>
+struct WaveAcc;
+
+template <>
+struct WaveAcc<float> {
+    f32x16 c;
+    __device__ void zero() {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[r] = 0.f;
+    }
+    // As/Bs: one 16-deep K slice, element (k, idx) at [k * S + idx].
+    __device__ void mma(const float* As, const float* Bs, int wy, int wx, int lane) {
+        constexpr int S = LdsStride<float>::value;
+        const int kr = lane >> 5, ix = lane & 31;
+#pragma unroll
+        for (int kk = 0; kk < KSTEP; kk += 2) {
+            float a = As[(kk + kr) * S + wy * 32 + ix];
+            float b = Bs[(kk + kr) * S + wx * 32 + ix];
+            c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+        }
+    }
+    static constexpr int NREG = 16;
+    __device__ float get(int r) const { return c[r]; }
+    // Position of register r inside the wave's 32 x 32 block.
+    static __device__ __forceinline__ int row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+    static __device__ __forceinline__ int col(int r, int lane) { return lane & 31; }
+};
+
+template <>
+struct WaveAcc<double> {
+    f64x4 c[2][2];
+    __device__ void zero() {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) c[i][j][r] = 0.0;
+    }
+    __device__ void mma(const double* As, const double* Bs, int wy, int wx, int lane) {
+        constexpr int S = LdsStride<double>::value;
+        const int kr = lane >> 4, ix = lane & 15;
+#pragma unroll
+        for (int kk = 0; kk < KSTEP; kk += 4) {
+            double a0 = As[(kk + kr) * S + wy * 32 + ix];
+            double a1 = As[(kk + kr) * S + wy * 32 + 16 + ix];
+            double b0 = Bs[(kk + kr) * S + wx * 32 + ix];
+            double b1 = Bs[(kk + kr) * S + wx * 32 + 16 + ix];
+            c[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, c[0][0], 0, 0, 0);
+            c[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, c[0][1], 0, 0, 0);
+            c[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, c[1][0], 0, 0, 0);
+            c[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, c[1][1], 0, 0, 0);
+        }
+    }
+    static constexpr int NREG = 16;
+    __device__ double get(int r) const { return c[r >> 3][(r >> 2) & 1][r & 3]; }
+    static __device__ __forceinline__ int row(int r, int lane) { return 16 * (r >> 3) + (lane >> 4) + 4 * (r & 3); }
+    static __device__ __forceinline__ int col(int r, int lane) { return 16 * ((r >> 2) & 1) + (lane & 15); }
+};
+
+// Operand access patterns.  Element (r, k) of the M x K operand A and element
+// (k, c) of the K x N operand B.
+//   A_KMAJ == false : A(r, k) = A[r * lda + k]   (row-major A)
+//   A_KMAJ == true  : A(r, k) = A[k * lda + r]   (A stored transposed)
+//   B_KMAJ == false : B(k, c) = B[k * ldb + c]   (row-major B)
+//   B_KMAJ == true  : B(k, c) = B[c * ldb + k]   (B stored transposed)
+// CHECK: rows >= mv, columns >= nv and k >= kv read as zero (any alignment);
+// otherwise all reads are in range and 4-element vector aligned.
+template <typename T, typename TIn, bool A_KMAJ, bool B_KMAJ, bool CHECK>
+struct TileLoader {
+    T ra[4], rb[4];
+    __device__ __forceinline__ void fetch(const TIn* __restrict__ A, int64_t lda, const TIn* __restrict__ B,
+                                          int64_t ldb, int k0, int mv, int nv, int kv, int t) {
+        // A tile 64 x 16
+        if (!A_KMAJ) {
+            const int r = t >> 2, kq = (t & 3) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int k = k0 + kq + e;
+                ra[e] = (!CHECK || (r < mv && k < kv)) ? T(A[int64_t(r) * lda + k]) : T(0);
+            }
+        } else {
+            const int k = t >> 4, rq = (t & 15) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = rq + e;
+                ra[e] = (!CHECK || (r < mv && k0 + k < kv)) ? T(A[int64_t(k0 + k) * lda + r]) : T(0);
+            }
+        }
+        if (!B_KMAJ) {
+            const int k = t >> 4, cq = (t & 15) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = cq + e;
+                rb[e] = (!CHECK || (c < nv && k0 + k < kv)) ? T(B[int64_t(k0 + k) * ldb + c]) : T(0);
+            }
+        } else {
+            const int c = t >> 2, kq = (t & 3) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int k = k0 + kq + e;
+                rb[e] = (!CHECK || (c < nv && k < kv)) ? T(B[int64_t(c) * ldb + k]) : T(0);
+            }
+        }
+    }
+    __device__ __forceinline__ void stash(T* As, T* Bs, int t) const {
+        constexpr int S = LdsStride<T>::value;
+        if (!A_KMAJ) {
+            const int r = t >> 2, kq = (t & 3) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) As[(kq + e) * S + r] = ra[e];
+        } else {
+            const int k = t >> 4, rq = (t & 15) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) As[k * S + rq + e] = ra[e];
+        }
+        if (!B_KMAJ) {
+            const int k = t >> 4, cq = (t & 15) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Bs[k * S + cq + e] = rb[e];
+        } else {
+            const int c = t >> 2, kq = (t & 3) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Bs[(kq + e) * S + c] = rb[e];
+        }
+    }
+};
+
+template <typename T>
+struct GemmSmem {
+    T a[2][KSTEP * LdsStride<T>::value];
+    T b[2][KSTEP * LdsStride<T>::value];
+};
+
+// acc += A(64 x K) * B(K x 64) for one 64 x 64 output tile.  All 256 threads of
+// the workgroup must call it (it contains barriers).  K is the number of K
+// elements; without CHECK it must be a multiple of 16.
+template <typename T, typename TIn, bool A_KMAJ, bool B_KMAJ, bool CHECK>
+__device__ void tile_gemm(const TIn* __restrict__ A, int64_t lda, const TIn* __restrict__ B, int64_t ldb,
+                          int mv, int nv, int K, GemmSmem<T>& sm, WaveAcc<T>& acc) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int wy = w >> 1, wx = w & 1;
+    TileLoader<T, TIn, A_KMAJ, B_KMAJ, CHECK> ld;
+    const int nk = (K + KSTEP - 1) / KSTEP;
+    if (nk == 0) return;
+    ld.fetch(A, lda, B, ldb, 0, mv, nv, K, t);
+    __syncthreads();  // previous users of sm are done
+    ld.stash(sm.a[0], sm.b[0], t);
+    __syncthreads();
+    for (int s = 0; s < nk; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < nk) ld.fetch(A, lda, B, ldb, (s + 1) * KSTEP, mv, nv, K, t);
+        acc.mma(sm.a[cur], sm.b[cur], wy, wx, lane);
+        if (s + 1 < nk) {
+            ld.stash(sm.a[cur ^ 1], sm.b[cur ^ 1], t);
+            __syncthreads();
+        }
+    }
+}
+
+// Visit the 16 accumulator registers of this thread with their tile coordinates.
+template <typename T, typename F>
+__device__ __forceinline__ void for_each_acc(const WaveAcc<T>& acc, F&& f) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int r0 = (w >> 1) * 32, c0 = (w & 1) * 32;
+#pragma unroll
+    for (int r = 0; r < WaveAcc<T>::NREG; ++r)
+        f(r0 + WaveAcc<T>::row(r, lane), c0 + WaveAcc<T>::col(r, lane), acc.get(r));
+}
+
+}  // namespace kq

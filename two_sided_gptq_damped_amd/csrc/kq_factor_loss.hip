@@ -1,0 +1,297 @@
+// K-FAC factor accumulation, proxy loss and scale helper for gfx950.
+#include "kq_common.hpp"
+
+namespace kq {
+
+// ------------------------------------------------------- factor accumulation
+// S <- beta S + alpha X^T X (FastKron page, section 3.2 'Marginal' factors and
+// section 2.6's accumulation over the calibration set).  One workgroup per
+// 64 x 64 tile of the lower triangle (I >= J); the tile and its mirror are both
+// written, so the full symmetric matrix is produced.  The diagonal tile writes
+// each element once.
+template <typename T>
+__global__ __launch_bounds__(GEMM_THREADS) void syrk_kernel(const T* __restrict__ X, int64_t ldx, int rows, int dim,
+                                                            T* __restrict__ S, int64_t lds, T alpha, T beta) {
+    const int I = blockIdx.y, J = blockIdx.x;
+    if (J > I) return;
+    __shared__ GemmSmem<T> sm;
+    WaveAcc<T> acc;
+    acc.zero();
+    const int mv = dim - I * TILE, nv = dim - J * TILE;
+    // A(r, k) = X[k][I*64 + r]; B(k, c) = X[k][J*64 + c]
+    tile_gemm<T, T, true, false, true>(X + I * TILE, ldx, X + J * TILE, ldx, mv, nv, rows, sm, acc);
+    for_each_acc(acc, [&](int r, int c, T v) {
+        if (r >= mv || c >= nv) return;
+        const int64_t gi = int64_t(I) * TILE + r, gj = int64_t(J) * TILE + c;
+        T* p = S + gi * lds + gj;
+        *p = beta == T(0) ? alpha * v : beta * *p + alpha * v;
+        if (I != J) {
+            T* q = S + gj * lds + gi;
+            *q = beta == T(0) ? alpha * v : beta * *q + alpha * v;
+        }
+    });
+}
+
+kq_status factor_dispatch(kq_dtype dtype, int64_t rows, int64_t dim, const void* X, int64_t ldx, void* S, int64_t lds,
+                          double alpha, double beta, hipStream_t st) {
+    const int tiles = int((dim + TILE - 1) / TILE);
+    if (dtype == KQ_F64)
+        hipLaunchKernelGGL(syrk_kernel<double>, dim3(tiles, tiles), dim3(GEMM_THREADS), 0, st,
+                           static_cast<const double*>(X), ldx, int(rows), int(dim), static_cast<double*>(S), lds, alpha,
+                           beta);
+    else
+        hipLaunchKernelGGL(syrk_kernel<float>, dim3(tiles, tiles), dim3(GEMM_THREADS), 0, st,
+                           static_cast<const float*>(X), ldx, int(rows), int(dim), static_cast<float*>(S), lds,
+                           float(alpha), float(beta));
+    KQ_LAUNCHED("syrk_kernel");
+    return KQ_OK;
+}
+
+// ------------------------------------------------------------------ the loss
+// tr(B_d E A_d E^T) = sum_ij (B_d E)_ij (E A_d)_ij with E = V - W (A_d, B_d
+// symmetric), and B_d E = B E + lam_B E, E A_d = E A + lam_A E.  Products in fp64
+// on matrix cores over zero-padded fp64 copies; a two-pass fixed-order reduction.
+
+template <typename TIn>
+__global__ void diag_trace_kernel(const TIn* __restrict__ A, int64_t lda, int d, double* __restrict__ out) {
+    __shared__ double red[1024];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) s += double(A[int64_t(i) * lda + i]);
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+        if (int(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = red[0];
+}
+
+// dst (rp x cp, fp64) = src (rows x cols) zero-padded; with sub != nullptr, dst = src - sub.
+template <typename TIn>
+__global__ void pad_copy_kernel(const TIn* __restrict__ src, int64_t lds, const TIn* __restrict__ sub, int64_t ldsub,
+                                int rows, int cols, int rp, int cp, double* __restrict__ dst) {
+    const int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
+    if (idx >= int64_t(rp) * cp) return;
+    const int r = int(idx / cp), c = int(idx % cp);
+    double v = 0.0;
+    if (r < rows && c < cols) {
+        v = double(src[int64_t(r) * lds + c]);
+        if (sub) v -= double(sub[int64_t(r) * ldsub + c]);
+    }
+    dst[idx] = v;
+}
+
+// C = A B for padded row-major fp64 operands (M x K times K x N), 64 x 64 tiles.
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_nn_f64_kernel(const double* __restrict__ A, int lda,
+                                                                   const double* __restrict__ B, int ldb,
+                                                                   double* __restrict__ C, int ldc, int K) {
+    __shared__ GemmSmem<double> sm;
+    const int I = blockIdx.y, J = blockIdx.x;
+    WaveAcc<double> acc;
+    acc.zero();
+    tile_gemm<double, double, false, false, false>(A + int64_t(I) * TILE * lda, lda, B + int64_t(J) * TILE, ldb, TILE,
+                                                   TILE, K, sm, acc);
+    double* out = C + int64_t(I) * TILE * ldc + int64_t(J) * TILE;
+    for_each_acc(acc, [&](int r, int c, double v) { out[int64_t(r) * ldc + c] = v; });
+}
+
+// Partial sums of (P + lamB E)(Q + lamA E), one per block, in a fixed order.
+__global__ void loss_partial_kernel(const double* __restrict__ P, const double* __restrict__ Q,
+                                    const double* __restrict__ E, int64_t count, const double* __restrict__ trA, int n,
+                                    const double* __restrict__ trB, int m, double damp_rel, int b_identity,
+                                    double* __restrict__ partial) {
+    __shared__ double red[256];
+    const double lamA = damp_rel * (*trA) / n;
+    const double lamB = b_identity ? 0.0 : damp_rel * (*trB) / m;
+    double s = 0.0;
+    for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < count; i += int64_t(gridDim.x) * blockDim.x) {
+        const double e = E[i];
+        const double p = b_identity ? e : P[i] + lamB * e;
+        s += p * (Q[i] + lamA * e);
+    }
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+        if (int(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
+__global__ void loss_final_kernel(const double* __restrict__ partial, int count, double* __restrict__ out) {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < count; i += blockDim.x) s += partial[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+        if (int(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = red[0];
+}
+
+constexpr int LOSS_BLOCKS = 1024;
+
+struct LossLayout {
+    int64_t mp, np;
+    size_t off_E, off_P, off_Q, off_A, off_B, off_scal, bytes;
+};
+
+LossLayout loss_layout(int64_t m, int64_t n) {
+    LossLayout L;
+    L.mp = round_up(m, TILE);
+    L.np = round_up(n, TILE);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    L.off_E = take(size_t(L.mp) * L.np * 8);
+    L.off_P = take(size_t(L.mp) * L.np * 8);
+    L.off_Q = take(size_t(L.mp) * L.np * 8);
+    L.off_A = take(size_t(L.np) * L.np * 8);
+    L.off_B = take(size_t(L.mp) * L.mp * 8);
+    L.off_scal = take((LOSS_BLOCKS + 8) * 8);
+    L.bytes = off;
+    return L;
+}
+
+size_t loss_workspace_bytes(int64_t m, int64_t n) { return loss_layout(m, n).bytes; }
+
+template <typename T>
+kq_status loss_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T* V, int64_t ldv, const T* A, int64_t lda,
+                     const T* B, int64_t ldb, double damp_rel, double* loss_dev, void* ws, hipStream_t st) {
+    const LossLayout L = loss_layout(m, n);
+    char* base = static_cast<char*>(ws);
+    double* E = reinterpret_cast<double*>(base + L.off_E);
+    double* P = reinterpret_cast<double*>(base + L.off_P);
+    double* Q = reinterpret_cast<double*>(base + L.off_Q);
+    double* Ap = reinterpret_cast<double*>(base + L.off_A);
+    double* Bp = reinterpret_cast<double*>(base + L.off_B);
+    double* scal = reinterpret_cast<double*>(base + L.off_scal);
+    double *trA = scal, *trB = scal + 1, *partial = scal + 8;
+    const int mp = int(L.mp), np = int(L.np);
+    auto blocks = [](int64_t count) { return dim3(unsigned((count + 255) / 256)); };
+
+    hipLaunchKernelGGL(pad_copy_kernel<T>, blocks(int64_t(mp) * np), dim3(256), 0, st, V, ldv, W, ldw, int(m), int(n),
+                       mp, np, E);
+    KQ_LAUNCHED("pad_copy_kernel");
+    hipLaunchKernelGGL(pad_copy_kernel<T>, blocks(int64_t(np) * np), dim3(256), 0, st, A, lda, (const T*)nullptr,
+                       int64_t(0), int(n), int(n), np, np, Ap);
+    KQ_LAUNCHED("pad_copy_kernel");
+    hipLaunchKernelGGL(diag_trace_kernel<T>, dim3(1), dim3(1024), 0, st, A, lda, int(n), trA);
+    KQ_LAUNCHED("diag_trace_kernel");
+    if (B) {
+        hipLaunchKernelGGL(pad_copy_kernel<T>, blocks(int64_t(mp) * mp), dim3(256), 0, st, B, ldb, (const T*)nullptr,
+                           int64_t(0), int(m), int(m), mp, mp, Bp);
+        KQ_LAUNCHED("pad_copy_kernel");
+        hipLaunchKernelGGL(diag_trace_kernel<T>, dim3(1), dim3(1024), 0, st, B, ldb, int(m), trB);
+        KQ_LAUNCHED("diag_trace_kernel");
+        hipLaunchKernelGGL(gemm_nn_f64_kernel, dim3(np / TILE, mp / TILE), dim3(GEMM_THREADS), 0, st, Bp, mp, E, np, P,
+                           np, mp);
+        KQ_LAUNCHED("gemm_nn_f64_kernel");
+    }
+    hipLaunchKernelGGL(gemm_nn_f64_kernel, dim3(np / TILE, mp / TILE), dim3(GEMM_THREADS), 0, st, E, np, Ap, np, Q, np,
+                       np);
+    KQ_LAUNCHED("gemm_nn_f64_kernel");
+    hipLaunchKernelGGL(loss_partial_kernel, dim3(LOSS_BLOCKS), dim3(256), 0, st, P, Q, E, int64_t(mp) * np, trA,
+                       int(n), trB, int(m), damp_rel, B ? 0 : 1, partial);
+    KQ_LAUNCHED("loss_partial_kernel");
+    hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(256), 0, st, partial, LOSS_BLOCKS, loss_dev);
+    KQ_LAUNCHED("loss_final_kernel");
+    return KQ_OK;
+}
+
+kq_status loss_dispatch(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* V, int64_t ldv,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, double damp_rel, double* loss_dev,
+                        void* ws, hipStream_t st) {
+    if (dtype == KQ_F64)
+        return loss_typed<double>(m, n, static_cast<const double*>(W), ldw, static_cast<const double*>(V), ldv,
+                                  static_cast<const double*>(A), lda, static_cast<const double*>(B), ldb, damp_rel,
+                                  loss_dev, ws, st);
+    return loss_typed<float>(m, n, static_cast<const float*>(W), ldw, static_cast<const float*>(V), ldv,
+                             static_cast<const float*>(A), lda, static_cast<const float*>(B), ldb, damp_rel, loss_dev,
+                             ws, st);
+}
+
+// ------------------------------------------------------------------- scales
+// s_i = max_j |W_ij| / (2^(bits-1) - 1) per row, or over the whole tensor.
+
+template <typename T>
+struct Bits;
+template <>
+struct Bits<float> {
+    typedef unsigned int U;
+    static __device__ U to(float x) { return __float_as_uint(x); }
+    static __device__ float from(U u) { return __uint_as_float(u); }
+};
+template <>
+struct Bits<double> {
+    typedef unsigned long long U;
+    static __device__ U to(double x) { return (U)__double_as_longlong(x); }
+    static __device__ double from(U u) { return __longlong_as_double((long long)u); }
+};
+
+template <typename T>
+__global__ void clear_scalar_kernel(T* p) {
+    if (threadIdx.x == 0) *p = T(0);
+}
+
+// One block per row.  Non-negative floats order like their bit patterns, so the
+// tensor-wide maximum is an integer atomic max on the bits.
+template <typename T>
+__global__ void row_absmax_kernel(const T* __restrict__ W, int64_t ldw, int n, int per_row, T qmax,
+                                  T* __restrict__ scales) {
+    __shared__ T red[256];
+    const int r = blockIdx.x;
+    T mx = T(0);
+    for (int c = threadIdx.x; c < n; c += blockDim.x) {
+        const T a = fabs(W[int64_t(r) * ldw + c]);
+        mx = a > mx ? a : mx;
+    }
+    red[threadIdx.x] = mx;
+    __syncthreads();
+    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+        if (int(threadIdx.x) < w) red[threadIdx.x] = red[threadIdx.x] > red[threadIdx.x + w] ? red[threadIdx.x] : red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        if (per_row)
+            scales[r] = red[0] / qmax;
+        else
+            atomicMax(reinterpret_cast<typename Bits<T>::U*>(scales), Bits<T>::to(red[0]));
+    }
+}
+
+template <typename T>
+__global__ void divide_scalar_kernel(T* p, T q) {
+    if (threadIdx.x == 0) *p = *p / q;
+}
+
+template <typename T>
+kq_status scales_typed(int64_t m, int64_t n, const T* W, int64_t ldw, int bits, int per_row, T* scales, hipStream_t st) {
+    const T qmax = T((1 << (bits - 1)) - 1);
+    if (!per_row) {
+        hipLaunchKernelGGL(clear_scalar_kernel<T>, dim3(1), dim3(64), 0, st, scales);
+        KQ_LAUNCHED("clear_scalar_kernel");
+    }
+    hipLaunchKernelGGL(row_absmax_kernel<T>, dim3(unsigned(m)), dim3(256), 0, st, W, ldw, int(n), per_row, qmax, scales);
+    KQ_LAUNCHED("row_absmax_kernel");
+    if (!per_row) {
+        hipLaunchKernelGGL(divide_scalar_kernel<T>, dim3(1), dim3(64), 0, st, scales, qmax);
+        KQ_LAUNCHED("divide_scalar_kernel");
+    }
+    return KQ_OK;
+}
+
+kq_status scales_dispatch(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, int bits, int per_row,
+                          void* scales, hipStream_t st) {
+    if (dtype == KQ_F64)
+        return scales_typed<double>(m, n, static_cast<const double*>(W), ldw, bits, per_row, static_cast<double*>(scales),
+                                    st);
+    return scales_typed<float>(m, n, static_cast<const float*>(W), ldw, bits, per_row, static_cast<float*>(scales), st);
+}
+
+}  // namespace kq

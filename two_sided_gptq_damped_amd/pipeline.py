@@ -1,0 +1,69 @@
+"""One layer through the whole path on the GPU: factor accumulation, damped
+factors, scales, two-sided GPTQ and the proxy loss.  Every step is a call into
+libkronq; this module only allocates device tensors and chains the calls.
+
+Order of the steps (FastKron page, section 2.6: accumulate the Hessian factors
+from the calibration data, factor them, run the core algorithm):
+    A = E[a a^T] = X_a^T X_a / N,  B = E[g g^T] = X_g^T X_g / N
+    U_A, U_B with U^T U = (factor + damp_rel tr/d I)^{-1}
+    s = max |W_row| / (2^(bits-1) - 1)
+    codes, V = two-sided GPTQ(W, U_A, U_B, s)
+    loss = tr(B_d (V - W) A_d (V - W)^T)
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (KQ_OP_LOSS, KQ_OP_PREPARE, KQ_OP_QUANTIZE, kron_factor_accumulate, kron_loss, kron_prepare,
+               kron_quantize, kron_row_scales, workspace)
+
+
+def factor(X: torch.Tensor) -> torch.Tensor:
+    """E[x x^T] over the rows of X."""
+    S = torch.empty(X.shape[1], X.shape[1], dtype=X.dtype, device=X.device)
+    return kron_factor_accumulate(X, S, 1.0 / X.shape[0], 0.0)
+
+
+def prepare(A: torch.Tensor, damp_rel: float):
+    """(U, trace, lambda) for the damped factor; raises KronError if not PD."""
+    d = A.shape[0]
+    U = torch.empty_like(A)
+    tr = torch.empty(1, dtype=torch.float64, device=A.device)
+    lam = torch.empty(1, dtype=torch.float64, device=A.device)
+    ws = workspace(KQ_OP_PREPARE, A.dtype, d, 0, A.device)
+    kron_prepare(A, damp_rel, U, ws, trace_out=tr, lambda_out=lam)
+    return U, tr, lam
+
+
+def quantize(W, U_A, U_B, bits, per_row, scales=None, ws=None):
+    m, n = W.shape
+    if scales is None:
+        scales = torch.empty(m if per_row else 1, dtype=W.dtype, device=W.device)
+        kron_row_scales(W, bits, per_row, scales)
+    codes = torch.empty(m, n, dtype=torch.int8, device=W.device)
+    V = torch.empty_like(W)
+    if ws is None:
+        ws = workspace(KQ_OP_QUANTIZE, W.dtype, m, n, W.device)
+    kron_quantize(W, U_A, U_B, bits, per_row, scales, codes, V, ws)
+    return codes, V, scales
+
+
+def loss(W, V, A, B, damp_rel):
+    m, n = W.shape
+    out = torch.empty(1, dtype=torch.float64, device=W.device)
+    ws = workspace(KQ_OP_LOSS, W.dtype, m, n, W.device)
+    kron_loss(W, V, A, B, damp_rel, out, ws)
+    return out
+
+
+def quantize_layer(W, act, grad, bits, per_row=True, damp_rel=0.01, two_sided=True):
+    """Run the whole path for one layer.  act: N x n activation rows, grad: N x m gradient rows."""
+    A = factor(act)
+    U_A, trA, _ = prepare(A, damp_rel)
+    B = U_B = trB = None
+    if two_sided:
+        B = factor(grad)
+        U_B, trB, _ = prepare(B, damp_rel)
+    codes, V, scales = quantize(W, U_A, U_B, bits, per_row)
+    return dict(A=A, B=B, U_A=U_A, U_B=U_B, trace_A=trA, trace_B=trB, codes=codes, V=V, scales=scales,
+                loss=loss(W, V, A, B, damp_rel))
