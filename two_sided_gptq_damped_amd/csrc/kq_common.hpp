@@ -64,6 +64,15 @@ struct Carve {
 
 // ---------------------------------------------------------------- device side
 
+// Precision-preserving scalar helpers (the plain __builtin_fma / rint / fmin
+// are the double-precision builtins and would promote float arguments).
+__device__ __forceinline__ float kfma(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double kfma(double a, double b, double c) { return __builtin_fma(a, b, c); }
+__device__ __forceinline__ float krint(float x) { return __builtin_rintf(x); }
+__device__ __forceinline__ double krint(double x) { return __builtin_rint(x); }
+__device__ __forceinline__ float kclamp(float x, float lo, float hi) { return __builtin_fminf(__builtin_fmaxf(x, lo), hi); }
+__device__ __forceinline__ double kclamp(double x, double lo, double hi) { return __builtin_fmin(__builtin_fmax(x, lo), hi); }
+
 // Base quantizer: z = clamp(rne(x / s)), v = s * z.  IEEE division (HIP's default
 // correctly rounded divide), rint = round half to even.  s == 0 gives z = v = 0.
 template <typename T>
@@ -73,9 +82,7 @@ __device__ __forceinline__ void quantize(T x, T s, T qmin, T qmax, T& z, T& v) {
         v = T(0);
         return;
     }
-    T r = __builtin_rint(x / s);
-    r = r < qmin ? qmin : r;
-    r = r > qmax ? qmax : r;
+    const T r = kclamp(krint(x / s), qmin, qmax);
     z = r;
     v = s * r;
 }
@@ -244,6 +251,65 @@ __device__ void tile_gemm(const TIn* __restrict__ A, int64_t lda, const TIn* __r
     for (int s = 0; s < nk; ++s) {
         const int cur = s & 1;
         if (s + 1 < nk) ld.fetch(A, lda, B, ldb, (s + 1) * KSTEP, mv, nv, K, t);
+        acc.mma(sm.a[cur], sm.b[cur], wy, wx, lane);
+        if (s + 1 < nk) {
+            ld.stash(sm.a[cur ^ 1], sm.b[cur ^ 1], t);
+            __syncthreads();
+        }
+    }
+}
+
+// Masked variant over padded, in-range operands: element (r, k) of A is used
+// only where ma(r, k) holds and element (k, c) of B only where mb(k, c) holds;
+// elsewhere the operand reads as zero (a select, so non-finite stale values
+// never reach the sum).  K must be a multiple of 16.
+struct NoMask {
+    __device__ __forceinline__ bool operator()(int, int) const { return true; }
+};
+
+template <typename T, bool A_KMAJ, bool B_KMAJ, typename MA, typename MB>
+__device__ void tile_gemm_masked(const T* __restrict__ A, int64_t lda, const T* __restrict__ B, int64_t ldb, int K,
+                                 GemmSmem<T>& sm, WaveAcc<T>& acc, MA ma, MB mb) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int wy = w >> 1, wx = w & 1;
+    TileLoader<T, T, A_KMAJ, B_KMAJ, false> ld;
+    const int nk = K / KSTEP;
+    if (nk == 0) return;
+    auto apply = [&](int k0) {
+        if (!A_KMAJ) {
+            const int r = t >> 2, kq = (t & 3) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!ma(r, k0 + kq + e)) ld.ra[e] = T(0);
+        } else {
+            const int k = t >> 4, rq = (t & 15) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!ma(rq + e, k0 + k)) ld.ra[e] = T(0);
+        }
+        if (!B_KMAJ) {
+            const int k = t >> 4, cq = (t & 15) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!mb(k0 + k, cq + e)) ld.rb[e] = T(0);
+        } else {
+            const int c = t >> 2, kq = (t & 3) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!mb(k0 + kq + e, c)) ld.rb[e] = T(0);
+        }
+    };
+    ld.fetch(A, lda, B, ldb, 0, TILE, TILE, K, t);
+    apply(0);
+    __syncthreads();
+    ld.stash(sm.a[0], sm.b[0], t);
+    __syncthreads();
+    for (int s = 0; s < nk; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < nk) {
+            ld.fetch(A, lda, B, ldb, (s + 1) * KSTEP, TILE, TILE, K, t);
+            apply((s + 1) * KSTEP);
+        }
         acc.mma(sm.a[cur], sm.b[cur], wy, wx, lane);
         if (s + 1 < nk) {
             ld.stash(sm.a[cur ^ 1], sm.b[cur ^ 1], t);

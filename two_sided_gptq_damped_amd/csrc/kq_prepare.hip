@@ -13,8 +13,8 @@
 //   2. right-looking blocked Cholesky: diagonal-block factor + its inverse,
 //      panel (C_ik <- C_ik L_kk^{-T}) and trailing update (C_ij -= C_ik C_jk^T),
 //      the last two on fp64 matrix cores
-//   3. blocked lower-triangular inverse, one block row at a time:
-//      Li_ik = -L_ii^{-1} sum_{k<=j<i} L_ij Li_jk
+//   3. lower-triangular inverse by recursive halving of the block range,
+//      one pair of matrix-core launches per recursion level
 //   4. U[r][c] = Li[d-1-r][d-1-c] for c >= r, 0 below the diagonal.
 #include "kq_common.hpp"
 
@@ -68,50 +68,59 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ C,
     constexpr int P = TILE + 1;
     __shared__ double L[TILE * P];
     __shared__ double X[TILE * P];
-    __shared__ int failed;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, ti = t >> 4, tc = t & 15;
     double* blk = C + int64_t(k) * TILE * dp + int64_t(k) * TILE;
-    for (int e = t; e < TILE * TILE; e += 256) L[(e >> 6) * P + (e & 63)] = blk[int64_t(e >> 6) * dp + (e & 63)];
-    if (t == 0) failed = 0;
+    for (int e = t; e < TILE * TILE; e += 256) {
+        const int r = e >> 6, c = e & 63;
+        L[r * P + c] = blk[int64_t(r) * dp + c];
+        X[r * P + c] = r == c ? 1.0 : 0.0;
+    }
     __syncthreads();
+    bool failed = false;  // uniform: every thread sees the same pivots
     for (int j = 0; j < TILE; ++j) {
-        if (t == 0) {
-            double p = L[j * P + j];
-            if (!(p > 0.0)) {
-                if (!failed && *info == 0) *info = k * TILE + j + 1;
-                failed = 1;
-                p = 1.0;
-            }
-            L[j * P + j] = sqrt(p);
+        double p = L[j * P + j];
+        if (!(p > 0.0)) {
+            if (t == 0 && !failed && *info == 0) *info = k * TILE + j + 1;
+            failed = true;
+            p = 1.0;
         }
+        const double piv = sqrt(p);
+        if (t > j && t < TILE) L[t * P + j] /= piv;
         __syncthreads();
-        const double piv = L[j * P + j];
-        for (int i = j + 1 + t; i < TILE; i += 256) L[i * P + j] /= piv;
-        __syncthreads();
+        if (t == 0) L[j * P + j] = piv;
         // trailing lower triangle: rows i > j, columns c in (j, i]
-        const int rem = TILE - 1 - j;
-        for (int e = t; e < rem * rem; e += 256) {
-            const int i = j + 1 + e / rem, c = j + 1 + e % rem;
-            if (c <= i) L[i * P + c] -= L[i * P + j] * L[c * P + j];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int i = j + 1 + ti + 16 * a;
+            if (i < TILE) {
+                const double lij = L[i * P + j];
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int c = j + 1 + tc + 16 * bb;
+                    if (c <= i) L[i * P + c] -= lij * L[c * P + j];
+                }
+            }
         }
         __syncthreads();
     }
-    // inverse of the lower factor, one column per thread
-    if (t < TILE) {
-        const int c = t;
-        for (int i = 0; i < TILE; ++i) {
-            double x;
-            if (i < c) {
-                x = 0.0;
-            } else {
-                double s = (i == c) ? 1.0 : 0.0;
-                for (int j = c; j < i; ++j) s -= L[i * P + j] * X[j * P + c];
-                x = s / L[i * P + i];
+    // inverse of the lower factor: right-looking forward substitution of L X = I
+    for (int j = 0; j < TILE; ++j) {
+        if (t <= j) X[j * P + t] /= L[j * P + j];
+        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int i = j + 1 + ti + 16 * a;
+            if (i < TILE) {
+                const double lij = L[i * P + j];
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int c = tc + 16 * bb;
+                    if (c <= j) X[i * P + c] -= lij * X[j * P + c];
+                }
             }
-            X[i * P + c] = x;
         }
+        __syncthreads();
     }
-    __syncthreads();
     double* dinv = Dinv + int64_t(k) * TILE * TILE;
     for (int e = t; e < TILE * TILE; e += 256) {
         const int r = e >> 6, c = e & 63;
@@ -149,38 +158,52 @@ __global__ __launch_bounds__(GEMM_THREADS) void potrf_trailing_kernel(double* __
     for_each_acc(acc, [&](int r, int c, double v) { out[int64_t(r) * dp + c] -= v; });
 }
 
-// Block row i of the inverse, first part: Li[i][k] = sum_{k<=j<i} L[i][j] Li[j][k]
-// for k < i (grid.x = i), plus Li[i][i] = Dinv[i] (block grid.x == i).
-__global__ __launch_bounds__(GEMM_THREADS) void trtri_row_kernel(const double* __restrict__ C, double* __restrict__ Li,
-                                                                 int dp, int i, const double* __restrict__ Dinv) {
+// Lower-triangular inverse by recursive halving over block ranges:
+// inv([[L11, 0], [L21, L22]]) = [[X11, 0], [-X22 L21 X11, X22]].  Diagonal blocks
+// come from the factorisation (Dinv); each recursion level is two launches
+// covering all nodes of the level (nodes of one level are disjoint):
+//   stage a: Tm[i][j] = sum_{j <= k < mid} L[i][k] Li[k][j]        (L21 X11)
+//   stage b: Li[i][j] = -sum_{mid <= k <= i} Li[i][k] Tm[k][j]     (-X22 (L21 X11))
+// for i in [mid, hi), j in [lo, mid) with lo = node * 2h, mid = lo + h.
+__global__ void trtri_diag_kernel(double* __restrict__ Li, int dp, const double* __restrict__ Dinv) {
     const int k = blockIdx.x;
-    double* out = Li + int64_t(i) * TILE * dp + int64_t(k) * TILE;
-    if (k == i) {
-        const double* src = Dinv + int64_t(i) * TILE * TILE;
-        for (int e = threadIdx.x; e < TILE * TILE; e += GEMM_THREADS) out[int64_t(e >> 6) * dp + (e & 63)] = src[e];
-        return;
-    }
+    double* out = Li + int64_t(k) * TILE * dp + int64_t(k) * TILE;
+    const double* src = Dinv + int64_t(k) * TILE * TILE;
+    for (int e = threadIdx.x; e < TILE * TILE; e += blockDim.x) out[int64_t(e >> 6) * dp + (e & 63)] = src[e];
+}
+
+__global__ __launch_bounds__(GEMM_THREADS) void trtri_level_a_kernel(const double* __restrict__ C,
+                                                                     const double* __restrict__ Li,
+                                                                     double* __restrict__ Tm, int dp, int nt, int h) {
+    const int lo = blockIdx.z * 2 * h, mid = lo + h;
+    const int hi = lo + 2 * h < nt ? lo + 2 * h : nt;
+    const int i = mid + blockIdx.y, j = lo + blockIdx.x;
+    if (i >= hi) return;
     __shared__ GemmSmem<double> sm;
     WaveAcc<double> acc;
     acc.zero();
-    const double* A = C + int64_t(i) * TILE * dp + int64_t(k) * TILE;   // L[i][k..i-1]
-    const double* B = Li + int64_t(k) * TILE * dp + int64_t(k) * TILE;  // Li[k..i-1][k]
-    tile_gemm<double, double, false, false, false>(A, dp, B, dp, TILE, TILE, (i - k) * TILE, sm, acc);
+    const double* A = C + int64_t(i) * TILE * dp + int64_t(j) * TILE;
+    const double* B = Li + int64_t(j) * TILE * dp + int64_t(j) * TILE;
+    tile_gemm<double, double, false, false, false>(A, dp, B, dp, TILE, TILE, (mid - j) * TILE, sm, acc);
+    double* out = Tm + int64_t(i) * TILE * dp + int64_t(j) * TILE;
     for_each_acc(acc, [&](int r, int c, double v) { out[int64_t(r) * dp + c] = v; });
 }
 
-// Second part: Li[i][k] <- -Dinv[i] Li[i][k] for k < i.
-__global__ __launch_bounds__(GEMM_THREADS) void trtri_scale_kernel(double* __restrict__ Li, int dp, int i,
-                                                                   const double* __restrict__ Dinv) {
-    const int k = blockIdx.x;
-    double* blk = Li + int64_t(i) * TILE * dp + int64_t(k) * TILE;
+__global__ __launch_bounds__(GEMM_THREADS) void trtri_level_b_kernel(double* __restrict__ Li,
+                                                                     const double* __restrict__ Tm, int dp, int nt,
+                                                                     int h) {
+    const int lo = blockIdx.z * 2 * h, mid = lo + h;
+    const int hi = lo + 2 * h < nt ? lo + 2 * h : nt;
+    const int i = mid + blockIdx.y, j = lo + blockIdx.x;
+    if (i >= hi) return;
     __shared__ GemmSmem<double> sm;
     WaveAcc<double> acc;
     acc.zero();
-    tile_gemm<double, double, false, false, false>(Dinv + int64_t(i) * TILE * TILE, TILE, blk, dp, TILE, TILE, TILE,
-                                                   sm, acc);
-    __syncthreads();
-    for_each_acc(acc, [&](int r, int c, double v) { blk[int64_t(r) * dp + c] = -v; });
+    const double* A = Li + int64_t(i) * TILE * dp + int64_t(mid) * TILE;
+    const double* B = Tm + int64_t(mid) * TILE * dp + int64_t(j) * TILE;
+    tile_gemm<double, double, false, false, false>(A, dp, B, dp, TILE, TILE, (i - mid + 1) * TILE, sm, acc);
+    double* out = Li + int64_t(i) * TILE * dp + int64_t(j) * TILE;
+    for_each_acc(acc, [&](int r, int c, double v) { out[int64_t(r) * dp + c] = -v; });
 }
 
 template <typename TOut>
@@ -195,7 +218,7 @@ __global__ void flip_kernel(const double* __restrict__ Li, int dp, int d, TOut* 
 
 struct PrepareLayout {
     int64_t dp, nt;
-    size_t off_C, off_Li, off_Dinv, off_scal, bytes;
+    size_t off_C, off_Li, off_Tm, off_Dinv, off_scal, bytes;
 };
 
 PrepareLayout prepare_layout(int64_t d) {
@@ -210,6 +233,7 @@ PrepareLayout prepare_layout(int64_t d) {
     };
     L.off_C = take(size_t(L.dp) * L.dp * 8);
     L.off_Li = take(size_t(L.dp) * L.dp * 8);
+    L.off_Tm = take(size_t(L.dp) * L.dp * 8);
     L.off_Dinv = take(size_t(L.nt) * TILE * TILE * 8);
     L.off_scal = take(64);
     L.bytes = off;
@@ -225,6 +249,7 @@ kq_status prepare_typed(int64_t d, const T* A, int64_t lda, double damp_rel, T* 
     char* base = static_cast<char*>(ws);
     double* C = reinterpret_cast<double*>(base + L.off_C);
     double* Li = reinterpret_cast<double*>(base + L.off_Li);
+    double* Tm = reinterpret_cast<double*>(base + L.off_Tm);
     double* Dinv = reinterpret_cast<double*>(base + L.off_Dinv);
     double* trace = reinterpret_cast<double*>(base + L.off_scal);
     int32_t* info_ws = reinterpret_cast<int32_t*>(base + L.off_scal + 16);
@@ -250,13 +275,14 @@ kq_status prepare_typed(int64_t d, const T* A, int64_t lda, double damp_rel, T* 
             KQ_LAUNCHED("potrf_trailing_kernel");
         }
     }
-    for (int i = 0; i < nt; ++i) {
-        hipLaunchKernelGGL(trtri_row_kernel, dim3(i + 1), dim3(GEMM_THREADS), 0, st, C, Li, dp, i, Dinv);
-        KQ_LAUNCHED("trtri_row_kernel");
-        if (i > 0) {
-            hipLaunchKernelGGL(trtri_scale_kernel, dim3(i), dim3(GEMM_THREADS), 0, st, Li, dp, i, Dinv);
-            KQ_LAUNCHED("trtri_scale_kernel");
-        }
+    hipLaunchKernelGGL(trtri_diag_kernel, dim3(nt), dim3(256), 0, st, Li, dp, Dinv);
+    KQ_LAUNCHED("trtri_diag_kernel");
+    for (int h = 1; h < nt; h *= 2) {
+        const int nodes = (nt + 2 * h - 1) / (2 * h);
+        hipLaunchKernelGGL(trtri_level_a_kernel, dim3(h, h, nodes), dim3(GEMM_THREADS), 0, st, C, Li, Tm, dp, nt, h);
+        KQ_LAUNCHED("trtri_level_a_kernel");
+        hipLaunchKernelGGL(trtri_level_b_kernel, dim3(h, h, nodes), dim3(GEMM_THREADS), 0, st, Li, Tm, dp, nt, h);
+        KQ_LAUNCHED("trtri_level_b_kernel");
     }
     const int64_t ucnt = d * d;
     hipLaunchKernelGGL(flip_kernel<T>, dim3(unsigned((ucnt + 255) / 256)), dim3(256), 0, st, Li, dp, int(d), U, ldu);

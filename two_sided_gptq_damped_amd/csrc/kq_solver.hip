@@ -8,15 +8,19 @@
 // Updates flow only to the bottom-right (section 2.3), so entries on one
 // anti-diagonal i + j = k are independent.
 //
-// Schedule.  The matrix is cut into 64 x 64 tiles; tiles with I + J = K form
-// tile-diagonal K, and tiles of one tile-diagonal are independent for the same
-// reason.  solve(K0, K1) over tile-diagonal ranges follows section 2.5's
-// recursion: solve(K0, mid), add the errors of the first half to the second half
-// with two batched products (stage 1: T1 = Delta_band N_A restricted to the tiles
-// it can reach; stage 2: X += N_B^T T1 on the tiles of diagonals [mid, K1)), then
-// solve(mid, K1).  A leaf is one tile-diagonal: every tile on it runs the
-// element-level anti-diagonal sweep of its 64 x 64 entries (127 steps) with the
-// in-tile feedback, one workgroup per tile.
+// Schedule.  The matrix is cut into 32 x 32 scheduling tiles; tiles with
+// I + J = K form tile-diagonal K and are independent for the same reason.
+// solve(K0, K1) over tile-diagonal ranges follows section 2.5's recursion:
+// solve(K0, mid); add the errors of the first half to the second half with two
+// batched products; solve(mid, K1):
+//   stage 1  T1[I', J] = sum_{J' : K0 <= I'+J' < mid} Delta[I', J'] N_A[J', J]
+//            for the tiles (I', J) a target can read (K0 <= I'+J < K1, I' < mid)
+//   stage 2  X[I, J] += sum_{I'} N_B[I', I]^T T1[I', J] for mid <= I+J < K1.
+// Both stages run on 64 x 64 matrix-core output blocks (2 x 2 scheduling tiles)
+// and mask at 32-tile granularity: source tiles outside the band and T1 tiles not
+// written by this node read as zero, targets outside the band are not written.
+// A leaf is one tile-diagonal: each 32 x 32 tile runs the element-level
+// anti-diagonal sweep (63 steps) with the in-tile feedback, one workgroup per tile.
 //
 // Workspace layout (row-major, padded to multiples of 64 with zero weights,
 // unit scales and identity factors, so padding never reaches a real entry):
@@ -29,6 +33,8 @@
 #include "kq_common.hpp"
 
 namespace kq {
+
+constexpr int ST = 32;  // scheduling tile edge
 
 // N[r][c] = U[r][c] / U[r][r] for c >= r inside d x d; identity in the padding.
 template <typename T>
@@ -60,26 +66,51 @@ __global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, 
     }
 }
 
-// Leaf: one tile-diagonal K.  Workgroup = one 64 x 64 tile, 1024 threads; thread
-// (w, l) owns column l and rows w, w+16, w+32, w+48.  Right-looking in-tile
-// feedback: after the entries of element anti-diagonal d are rounded, every
-// later entry of the tile adds the contribution of the entry to its left in the
-// same row (Delta * L~_A) and of the entry above it in the same column
-// (L~_B * R, R = row-accumulated error); only the tile's own diagonal blocks of
-// the factors are needed, everything from earlier tiles is already in X.
+// Leaf: the tiles of one tile-diagonal K, one 256-thread workgroup per 32 x 32
+// tile.  Thread (w, l) owns column b = l % 32 and rows r0..r0+3 with
+// r0 = 8w + 4(l / 32).  Right-looking in-tile feedback: after the entries of
+// element anti-diagonal d are rounded, each later entry adds the contribution of
+// the rounded entry in its row (Delta * L~_A) and of the one in its column
+// (L~_B * R, R the row-accumulated error).  Everything from earlier tiles is
+// already in X.  One barrier per step (double-buffered exchange arrays).
+//
+// The tile's diagonal factor blocks sit in LDS with their unit diagonal
+// replaced by 0 and an extra all-zero row / column; a source that does not exist
+// (off the tile) is mapped to that zero line.  Because N is upper triangular,
+// every update whose source is not strictly to the left / above its target then
+// multiplies by an exact zero, so the updates need no predicates (finished
+// entries only ever receive +0).  The exchange arrays start at zero so the
+// multiplied values are always finite.
+//
+// The quotient x / s is formed as q = x * (1/s) with one Markstein correction
+// q + (x - q s) (1/s): within an ulp of the IEEE quotient, so it can change a
+// rounding decision only for values that sit within ~1e-15 grid units of a
+// midpoint.
 template <typename T>
-__global__ __launch_bounds__(1024) void leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
-                                                    const T* __restrict__ NA, const T* __restrict__ NB,
-                                                    const T* __restrict__ S, int np, int mp, int Mt,
-                                                    int Nt, int K, int m, int n, int qmin, int qmax,
-                                                    int8_t* __restrict__ Z, int64_t ldz,
-                                                    T* __restrict__ V, int64_t ldv) {
-    constexpr int P = TILE + 1;
-    __shared__ T sNA[TILE * P];  // sNA[b'][b] = N_A[J*64+b'][J*64+b]
-    __shared__ T sNB[TILE * P];  // sNB[a'][a] = N_B[I*64+a'][I*64+a]
-    __shared__ T dD[2][TILE];    // errors of the current element diagonal, by row
-    __shared__ T dR[2][TILE];    // row-accumulated errors of the diagonal, by column
-    __shared__ T sS[TILE];
+__device__ __forceinline__ void quantize_fast(T x, T s, T rs, T qmin, T qmax, T& z, T& v) {
+    const T q = x * rs;
+    const T y = kfma(kfma(-q, s, x), rs, q);
+    const T r = kclamp(krint(y), qmin, qmax);
+    z = s == T(0) ? T(0) : r;
+    v = s * z;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
+                                                   const T* __restrict__ NA, const T* __restrict__ NB,
+                                                   const T* __restrict__ S, int np, int mp, int Mt, int Nt,
+                                                   int K, int m, int n, int qmin, int qmax,
+                                                   int8_t* __restrict__ Z, int64_t ldz, T* __restrict__ V,
+                                                   int64_t ldv) {
+    constexpr int PB = ST + 4;  // 16-byte aligned rows for the vector reads
+    constexpr int PA = ST + 1;  // column ST is the zero sentinel
+    constexpr int PO = ST + 1;
+    __shared__ __attribute__((aligned(16))) T sNB[(ST + 1) * PB];  // sNB[as][a] = N_B[..as][..a], row ST = 0
+    __shared__ T sNAt[ST * PA];                                    // sNAt[b][bs] = N_A[..bs][..b], col ST = 0
+    __shared__ __attribute__((aligned(16))) T dD[2][ST];           // errors of the current diagonal, by row
+    __shared__ T dR[2][ST];                                        // row-accumulated errors, by column
+    __shared__ T oD[ST * PO];                                      // finished errors
+    __shared__ T oZ[ST * PO];                                      // finished codes
 
     const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
     const int I = ilo + blockIdx.x;
@@ -87,126 +118,171 @@ __global__ __launch_bounds__(1024) void leaf_kernel(const T* __restrict__ X, T* 
     if (I > ihi) return;
     const int J = K - I;
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int b = l & 31, r0 = 8 * w + 4 * (l >> 5);
 
-    for (int e = t; e < TILE * TILE; e += 1024) {
-        const int r = e >> 6, c = e & 63;
-        sNA[r * P + c] = NA[int64_t(J * TILE + r) * np + J * TILE + c];
-        sNB[r * P + c] = NB ? NB[int64_t(I * TILE + r) * mp + I * TILE + c] : T(r == c);
+    for (int e = t; e < ST * ST; e += 256) {
+        const int r = e >> 5, c = e & 31;
+        const T nb = NB ? NB[int64_t(I * ST + r) * mp + I * ST + c] : T(0);
+        sNB[r * PB + c] = r == c ? T(0) : nb;
+        const T na = NA[int64_t(J * ST + r) * np + J * ST + c];
+        sNAt[c * PA + r] = r == c ? T(0) : na;
     }
-    if (t < TILE) sS[t] = S[I * TILE + t];
+    if (t < ST) {
+        sNB[ST * PB + t] = T(0);
+        sNAt[t * PA + ST] = T(0);
+        dD[0][t] = dD[1][t] = T(0);
+        dR[0][t] = dR[1][t] = T(0);
+    }
 
-    T acc[4], rp[4];
+    T acc[4], rp[4], sc[4], rs[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        acc[i] = X[int64_t(I * TILE + w + 16 * i) * np + J * TILE + l];
+        acc[i] = X[int64_t(I * ST + r0 + i) * np + J * ST + b];
         rp[i] = T(0);
+        sc[i] = S[I * ST + r0 + i];
+        rs[i] = sc[i] == T(0) ? T(0) : T(1) / sc[i];
     }
     __syncthreads();
 
     const T tqmin = T(qmin), tqmax = T(qmax);
-    for (int d = 0; d < 2 * TILE - 1; ++d) {
+    for (int d = 0; d < 2 * ST - 1; ++d) {
         const int buf = d & 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int a = w + 16 * i;
-            if (a + l == d) {
-                T z, v;
-                quantize(acc[i], sS[a], tqmin, tqmax, z, v);
-                const T delta = v - acc[i];
-                dD[buf][a] = delta;
-                dR[buf][l] = rp[i] + delta;
-                const int64_t gi = int64_t(I) * TILE + a, gj = int64_t(J) * TILE + l;
-                D[gi * np + gj] = delta;
-                if (gi < m && gj < n) {
-                    Z[gi * ldz + gj] = int8_t(z);
-                    V[gi * ldv + gj] = v;
-                }
-            }
+        const int own = d - b - r0;  // index of my entry on diagonal d, if any
+        if (own >= 0 && own < 4) {
+            // explicit selects keep the accumulators in registers
+            const bool hi = own & 2, od = own & 1;
+            const T x = hi ? (od ? acc[3] : acc[2]) : (od ? acc[1] : acc[0]);
+            const T r = hi ? (od ? rp[3] : rp[2]) : (od ? rp[1] : rp[0]);
+            const T sa = hi ? (od ? sc[3] : sc[2]) : (od ? sc[1] : sc[0]);
+            const T ra = hi ? (od ? rs[3] : rs[2]) : (od ? rs[1] : rs[0]);
+            T z, v;
+            quantize_fast(x, sa, ra, tqmin, tqmax, z, v);
+            const T delta = v - x;
+            const int a = r0 + own;
+            dD[buf][a] = delta;
+            dR[buf][b] = r + delta;
+            oD[a * PO + b] = delta;
+            oZ[a * PO + b] = z;
         }
         __syncthreads();
+        // all LDS operands first, then unconditional updates
+        const int as = d - b;        // column source (as, b)
+        const int asc = unsigned(as) > unsigned(ST - 1) ? ST : as;
+        const T rv = dR[buf][b];
+        const int bs0 = d - r0;      // row source (r0 + i, bs0 - i)
+        T nbv[4], ddv[4], nav[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int a = w + 16 * i;
-            if (a + l > d) {
-                const int bs = d - a;  // row source (a, bs) on diagonal d
-                if (bs >= 0 && bs < l) {
-                    const T c = dD[buf][a] * sNA[bs * P + l];
-                    acc[i] += c;
-                    rp[i] += c;
-                }
-                const int as = d - l;  // column source (as, l) on diagonal d
-                if (as >= 0 && as < a) acc[i] += sNB[as * P + a] * dR[buf][l];
-            }
+            nbv[i] = sNB[asc * PB + r0 + i];
+            ddv[i] = dD[buf][r0 + i];
+            const int bs = bs0 - i;
+            nav[i] = sNAt[b * PA + (unsigned(bs) > unsigned(ST - 1) ? ST : bs)];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const T cr = ddv[i] * nav[i];
+            acc[i] = kfma(nbv[i], rv, acc[i]) + cr;
+            rp[i] += cr;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int a = r0 + i;
+        const int64_t gi = int64_t(I) * ST + a, gj = int64_t(J) * ST + b;
+        const T z = oZ[a * PO + b];
+        D[gi * np + gj] = oD[a * PO + b];
+        if (gi < m && gj < n) {
+            Z[gi * ldz + gj] = int8_t(z);
+            V[gi * ldv + gj] = sc[i] * z;
         }
     }
 }
 
-// Stage 1 of the band propagation at node [K0, K1) with split mid:
-// T1[I', J] = sum_{J' in source band, J' <= J} Delta[I', J'] N_A[J', J]
-// for every tile (I', J) that a target tile (I >= I', J) of diagonals [mid, K1)
-// reads.  Grid: x = column offset within the row's window, y = source row.
+// Stage 1 at node [K0, K1) with split mid, on 64-row block P and 64-column block Q.
 template <typename T>
 __global__ __launch_bounds__(GEMM_THREADS) void band_stage1_kernel(const T* __restrict__ D,
                                                                    const T* __restrict__ NA,
-                                                                   T* __restrict__ T1, int np, int Nt,
-                                                                   int K0, int mid, int K1, int row0) {
+                                                                   T* __restrict__ T1, int np, int Nt, int K0,
+                                                                   int mid, int K1, int P0) {
     __shared__ GemmSmem<T> sm;
-    const int Ip = row0 + blockIdx.y;
-    const int jlo = K0 - Ip > 0 ? K0 - Ip : 0;
-    const int J = jlo + blockIdx.x;
-    const int jend = K1 - Ip < Nt ? K1 - Ip : Nt;
-    if (J >= jend) return;
-    const int khi = J < mid - 1 - Ip ? J : mid - 1 - Ip;  // inclusive
+    const int P = P0 + blockIdx.y;
+    const int I0 = 2 * P;  // first 32-row tile of the block
+    const int jlo = K0 - I0 - 1 > 0 ? K0 - I0 - 1 : 0;
+    const int jend = K1 - I0 < Nt ? K1 - I0 : Nt;  // exclusive, over both rows
+    const int Q = (jlo >> 1) + blockIdx.x;
+    if (2 * Q >= jend) return;
+    const int kl = jlo;
+    int kh = 2 * Q + 1;
+    if (mid - 1 - I0 < kh) kh = mid - 1 - I0;
+    if (Nt - 1 < kh) kh = Nt - 1;
     WaveAcc<T> acc;
     acc.zero();
-    if (khi >= jlo) {
-        const T* A = D + int64_t(Ip) * TILE * np + int64_t(jlo) * TILE;
-        const T* B = NA + int64_t(jlo) * TILE * np + int64_t(J) * TILE;
-        tile_gemm<T, T, false, false, false>(A, np, B, np, TILE, TILE, (khi - jlo + 1) * TILE, sm, acc);
+    if (kh >= kl) {
+        const T* A = D + int64_t(I0) * ST * np + int64_t(kl) * ST;
+        const T* B = NA + int64_t(kl) * ST * np + int64_t(Q) * TILE;
+        auto ma = [=](int r, int k) {
+            const int s = I0 + (r >> 5) + kl + (k >> 5);  // tile-diagonal of the source tile
+            return s >= K0 && s < mid;
+        };
+        tile_gemm_masked<T, false, false>(A, np, B, np, (kh - kl + 1) * ST, sm, acc, ma, NoMask());
     }
-    T* out = T1 + int64_t(Ip) * TILE * np + int64_t(J) * TILE;
+    T* out = T1 + int64_t(I0) * ST * np + int64_t(Q) * TILE;
     for_each_acc(acc, [&](int r, int c, T v) { out[int64_t(r) * np + c] = v; });
 }
 
-// Stage 2: X[I, J] += sum_{I'} N_B[I', I]^T T1[I', J] for the tiles of
-// diagonals [mid, K1).  With B = I only the I' = I term exists (N_B = identity).
+// Stage 2: X[I, J] += sum_{I'} N_B[I', I]^T T1[I', J] for the tiles of diagonals
+// [mid, K1), on 64 x 64 target block (P, Q) of block-diagonal sig = P + Q.
 template <typename T>
 __global__ __launch_bounds__(GEMM_THREADS) void band_stage2_kernel(const T* __restrict__ T1,
                                                                    const T* __restrict__ NB,
-                                                                   T* __restrict__ X, int np, int mp,
-                                                                   int Mt, int Nt, int K0, int mid) {
+                                                                   T* __restrict__ X, int np, int mp, int Mt,
+                                                                   int Nt, int K0, int mid, int K1, int sig0) {
     __shared__ GemmSmem<T> sm;
-    const int K = mid + blockIdx.y;
-    const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
-    const int I = ilo + blockIdx.x;
-    const int ihi = K < Mt - 1 ? K : Mt - 1;
-    if (I > ihi) return;
-    const int J = K - I;
-    const int klo = K0 - J > 0 ? K0 - J : 0;
-    const int khi = I < mid - 1 ? I : mid - 1;
-    if (klo > khi) return;
-    T* out = X + int64_t(I) * TILE * np + int64_t(J) * TILE;
+    const int sig = sig0 + blockIdx.y;
+    const int Mb = Mt >> 1, Nb = Nt >> 1;
+    const int plo = sig - Nb + 1 > 0 ? sig - Nb + 1 : 0;
+    const int P = plo + blockIdx.x;
+    const int phi = sig < Mb - 1 ? sig : Mb - 1;
+    if (P > phi) return;
+    const int Q = sig - P;
+    const int I0 = 2 * P, J0 = 2 * Q;
+    auto in_band = [=](int r, int c) {
+        const int k = I0 + (r >> 5) + J0 + (c >> 5);
+        return k >= mid && k < K1;
+    };
+    auto t1_valid = [=](int ip, int j) {  // T1 tile written by this node's stage 1
+        const int k = ip + j;
+        return ip < mid && k >= K0 && k < K1;
+    };
+    T* out = X + int64_t(I0) * ST * np + int64_t(J0) * ST;
     if (!NB) {
-        if (I < klo || I > khi) return;
-        const T* src = T1 + int64_t(I) * TILE * np + int64_t(J) * TILE;
+        const T* src = T1 + int64_t(I0) * ST * np + int64_t(J0) * ST;
         for (int e = threadIdx.x; e < TILE * TILE; e += GEMM_THREADS) {
             const int r = e >> 6, c = e & 63;
-            out[int64_t(r) * np + c] += src[int64_t(r) * np + c];
+            if (in_band(r, c) && t1_valid(I0 + (r >> 5), J0 + (c >> 5)))
+                out[int64_t(r) * np + c] += src[int64_t(r) * np + c];
         }
         return;
     }
+    const int kl = K0 - J0 - 1 > 0 ? K0 - J0 - 1 : 0;
+    const int kh = I0 + 1 < mid - 1 ? I0 + 1 : mid - 1;
+    if (kl > kh) return;
     WaveAcc<T> acc;
     acc.zero();
-    const T* A = NB + int64_t(klo) * TILE * mp + int64_t(I) * TILE;  // A(r, k) = NB[k][r]
-    const T* B = T1 + int64_t(klo) * TILE * np + int64_t(J) * TILE;
-    tile_gemm<T, T, true, false, false>(A, mp, B, np, TILE, TILE, (khi - klo + 1) * TILE, sm, acc);
-    for_each_acc(acc, [&](int r, int c, T v) { out[int64_t(r) * np + c] += v; });
+    const T* A = NB + int64_t(kl) * ST * mp + int64_t(I0) * ST;  // A(r, k) = NB[k][r]
+    const T* B = T1 + int64_t(kl) * ST * np + int64_t(J0) * ST;
+    auto mb = [=](int k, int c) { return t1_valid(kl + (k >> 5), J0 + (c >> 5)); };
+    tile_gemm_masked<T, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
+    for_each_acc(acc, [&](int r, int c, T v) {
+        if (in_band(r, c)) out[int64_t(r) * np + c] += v;
+    });
 }
 
 // ------------------------------------------------------------------- host side
 
 struct SolverLayout {
-    int64_t mp, np, Mt, Nt;
+    int64_t mp, np, Mt, Nt;  // padded extents; tile counts in 32-tiles
     size_t bytes;
     size_t off_NA, off_NB, off_X, off_D, off_T1, off_S;
 };
@@ -216,8 +292,8 @@ SolverLayout solver_layout(kq_dtype dtype, int64_t m, int64_t n) {
     const size_t es = dtype == KQ_F64 ? 8 : 4;
     L.mp = round_up(m, TILE);
     L.np = round_up(n, TILE);
-    L.Mt = L.mp / TILE;
-    L.Nt = L.np / TILE;
+    L.Mt = L.mp / ST;
+    L.Nt = L.np / ST;
     size_t off = 0;
     auto take = [&](size_t count) {
         size_t o = off;
@@ -246,28 +322,37 @@ struct SolverRun {
     hipStream_t st;
 
     kq_status leaf(int K) {
-        const int ilo = K - int(L.Nt) + 1 > 0 ? K - int(L.Nt) + 1 : 0;
-        const int ihi = K < int(L.Mt) - 1 ? K : int(L.Mt) - 1;
-        hipLaunchKernelGGL(leaf_kernel<T>, dim3(ihi - ilo + 1), dim3(1024), 0, st, X, D, NA, NB, S,
-                           int(L.np), int(L.mp), int(L.Mt), int(L.Nt), K, m, n, qmin, qmax, Z, ldz, V, ldv);
+        const int Mt = int(L.Mt), Nt = int(L.Nt);
+        const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
+        const int ihi = K < Mt - 1 ? K : Mt - 1;
+        hipLaunchKernelGGL(leaf_kernel<T>, dim3(ihi - ilo + 1), dim3(256), 0, st, X, D, NA, NB, S, int(L.np),
+                           int(L.mp), Mt, Nt, K, m, n, qmin, qmax, Z, ldz, V, ldv);
         KQ_LAUNCHED("leaf_kernel");
         return KQ_OK;
     }
 
     kq_status propagate(int K0, int mid, int K1) {
         const int Mt = int(L.Mt), Nt = int(L.Nt);
-        // stage 1 rows: I' with a source tile in [K0, mid): K0 - Nt < I' < mid
+        // stage 1 rows I' with a source tile in [K0, mid): K0 - Nt < I' < mid
         const int row0 = K0 - Nt + 1 > 0 ? K0 - Nt + 1 : 0;
         const int row1 = mid < Mt ? mid : Mt;  // exclusive
         if (row1 > row0) {
-            hipLaunchKernelGGL(band_stage1_kernel<T>, dim3(K1 - K0, row1 - row0), dim3(GEMM_THREADS), 0, st,
-                               D, NA, T1, int(L.np), Nt, K0, mid, K1, row0);
+            const int P0 = row0 >> 1, P1 = (row1 - 1) >> 1;
+            hipLaunchKernelGGL(band_stage1_kernel<T>, dim3((K1 - K0) / 2 + 2, P1 - P0 + 1), dim3(GEMM_THREADS), 0,
+                               st, D, NA, T1, int(L.np), Nt, K0, mid, K1, P0);
             KQ_LAUNCHED("band_stage1_kernel");
         }
-        const int width = Mt < Nt ? Mt : Nt;
-        hipLaunchKernelGGL(band_stage2_kernel<T>, dim3(width, K1 - mid), dim3(GEMM_THREADS), 0, st, T1, NB, X,
-                           int(L.np), int(L.mp), Mt, Nt, K0, mid);
-        KQ_LAUNCHED("band_stage2_kernel");
+        // stage 2 target block-diagonals sig with [2 sig, 2 sig + 2] meeting [mid, K1)
+        const int sig0 = (mid - 1) >> 1 > 0 ? (mid - 1) >> 1 : 0;
+        int sig1 = (K1 - 1) >> 1;
+        const int sigmax = int(L.Mt / 2 + L.Nt / 2 - 2);
+        if (sig1 > sigmax) sig1 = sigmax;
+        if (sig1 >= sig0) {
+            const int width = Mt < Nt ? Mt / 2 : Nt / 2;
+            hipLaunchKernelGGL(band_stage2_kernel<T>, dim3(width, sig1 - sig0 + 1), dim3(GEMM_THREADS), 0, st, T1,
+                               NB, X, int(L.np), int(L.mp), Mt, Nt, K0, mid, K1, sig0);
+            KQ_LAUNCHED("band_stage2_kernel");
+        }
         return KQ_OK;
     }
 
