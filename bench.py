@@ -49,13 +49,18 @@ def main() -> int:
     ap.add_argument("--n", type=int, default=4096)
     ap.add_argument("--bits", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(the per-matrix solver does not shard; see DESIGN.md for how it would)"}))
+                          "(the per-matrix solver is not sharded across GPUs)"}))
         return 2
 
     import torch
+
+    if args.copy_probe:
+        return copy_probe(torch, args.copy_probe)
 
     import synth
     import two_sided_gptq_damped_amd as kq
@@ -184,6 +189,19 @@ def main() -> int:
         print("[bench] cpu baseline (oracle pipeline)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(c, bits)
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def copy_probe(torch, nbytes):
+    """A plain copy of a known byte count: the reference reading for the HBM
+    byte counters (each copy reads and writes ``nbytes`` once)."""
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "copies": 3}), flush=True)
     return 0
 
 

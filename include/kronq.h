@@ -23,8 +23,7 @@
  *    returns KQ_ERR_HIP; kron_last_error() then holds the HIP message.
  *  - Floating-point type of every real array is `dtype` (fp32 or fp64).  The
  *    factor preparation always computes in fp64.
- *  - Calls are re-entrant; the only library state is a thread-local error string
- *    and a per-device cache of launch properties.
+ *  - Calls are re-entrant; the only library state is a thread-local error string.
  */
 #ifndef KRONQ_H
 #define KRONQ_H

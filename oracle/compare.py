@@ -9,7 +9,14 @@ different summation orders can agree, as the BaKron review notes for the
 equivalence theorem).
 
 fp32 rule: the fraction of differing codes and the relative difference of the
-proxy loss are reported and compared against the caller's bounds.
+proxy loss are reported and compared against the caller's bounds.  In single
+precision one near-tie decision that goes the other way changes every later
+entry it feeds (the oracle's own fp32 loop differs from its fp64 loop on a few
+percent of a 4096 x 4096 layer that way), so large fp32 runs are also checked
+along their own trajectory: the oracle is run with every code imposed from the
+candidate, which gives the exact pre-rounding values that the candidate's
+earlier decisions imply, and each candidate code must be the rounding of its
+value except where that value lies within ``tie_tol`` of a boundary.
 """
 from __future__ import annotations
 
@@ -55,6 +62,23 @@ def codes_equal_up_to_ties(Z_cand, run_oracle, tie_tol=1e-9, max_forced=64):
             force = np.full(Z_cand.shape, NOT_FORCED, np.int32)
         force[i, j] = Z_cand[i, j]
         n_forced += 1
+
+
+def trajectory_violations(Z_cand, Y_forced, bits, tie_tol):
+    """Entries where the candidate's code is not clamp(rne(y)) of the pre-rounding
+    value y that the oracle computed with every code imposed from the candidate.
+
+    Returns (violations, near_ties): violations are such entries with y farther
+    than ``tie_tol`` from a rounding boundary; near_ties are the ones within it.
+    Non-finite y (a zero scale) expects code 0.
+    """
+    qmin, qmax = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    Y = np.asarray(Y_forced, dtype=np.float64)
+    finite = np.isfinite(Y)
+    own = np.where(finite, np.clip(np.rint(np.where(finite, Y, 0.0)), qmin, qmax), 0.0)
+    differ = own != np.asarray(Z_cand).astype(np.float64)
+    near = differ & finite & (tie_distance(np.where(finite, Y, 0.0)) < tie_tol)
+    return int((differ & ~near).sum()), int(near.sum())
 
 
 def mismatch_fraction(Z_a, Z_b) -> float:

@@ -329,6 +329,32 @@ def test_comparator_accepts_forced_tie_and_rejects_real_mismatch():
     assert not ok and "(5, 7)" in info
 
 
+def test_trajectory_check_accepts_near_tie_branch_and_rejects_wrong_code():
+    # A candidate that took the other branch at one near-tie entry, and followed
+    # its own trajectory afterwards, is valid; a code changed anywhere else is not.
+    c = synth.spectral()
+    _, UA = dense.prepare(c["A"], 0.01)
+    _, UB = dense.prepare(c["B"], 0.01)
+    s = dense.scales(c["W"], 3, True)
+    Z, _, Y, _ = o3.solve(c["W"], UA, UB, s, 3)
+    Yf = o3.solve(c["W"], UA, UB, s, 3, force=Z.astype(np.int32))[2]
+    assert compare.trajectory_violations(Z, Yf, 3, 1e-4) == (0, 0)
+    td = compare.tie_distance(Y)
+    i, j = np.unravel_index(np.argmin(np.where(np.abs(Y) < 3.0, td, 1.0)), Y.shape)
+    force = np.full(Z.shape, compare.NOT_FORCED, np.int32)
+    force[i, j] = Z[i, j] + (1 if Y[i, j] > Z[i, j] else -1)  # the other side of the boundary
+    Zb = o3.solve(c["W"], UA, UB, s, 3, force=force)[0]
+    Yb = o3.solve(c["W"], UA, UB, s, 3, force=Zb.astype(np.int32))[2]
+    viol, near = compare.trajectory_violations(Zb, Yb, 3, max(2 * td[i, j], 1e-12))
+    assert viol == 0 and near == 1
+    bad = Z.copy()
+    k = np.unravel_index(np.argmax(np.where(Z == 0, td, -1.0)), Z.shape)  # far from a boundary
+    bad[k] = 1
+    Ybad = o3.solve(c["W"], UA, UB, s, 3, force=bad.astype(np.int32))[2]
+    viol, _ = compare.trajectory_violations(bad, Ybad, 3, 1e-4)
+    assert viol >= 1
+
+
 # ------------------------------------------------------------ mutation tests
 
 def test_pins_catch_planted_mistakes(tiny):

@@ -28,6 +28,7 @@ constexpr int GEMM_THREADS = 256;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ host side
 
@@ -306,12 +307,10 @@ __device__ void tile_gemm_masked(const T* __restrict__ A, int64_t lda, const T* 
     __syncthreads();
     for (int s = 0; s < nk; ++s) {
         const int cur = s & 1;
-        if (s + 1 < nk) {
-            ld.fetch(A, lda, B, ldb, (s + 1) * KSTEP, TILE, TILE, K, t);
-            apply((s + 1) * KSTEP);
-        }
+        if (s + 1 < nk) ld.fetch(A, lda, B, ldb, (s + 1) * KSTEP, TILE, TILE, K, t);
         acc.mma(sm.a[cur], sm.b[cur], wy, wx, lane);
         if (s + 1 < nk) {
+            apply((s + 1) * KSTEP);  // after the products, so the loads overlap them
             ld.stash(sm.a[cur ^ 1], sm.b[cur ^ 1], t);
             __syncthreads();
         }

@@ -34,7 +34,8 @@
 
 namespace kq {
 
-constexpr int ST = 32;  // scheduling tile edge
+constexpr int ST = 32;    // scheduling tile edge
+constexpr int CHUNK = 8;  // tile-diagonals per recursion leaf (chunk)
 
 // N[r][c] = U[r][c] / U[r][r] for c >= r inside d x d; identity in the padding.
 template <typename T>
@@ -66,13 +67,38 @@ __global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, 
     }
 }
 
+// Four consecutive elements (16-byte aligned), from global memory or LDS.
+template <typename T>
+struct Vec4;
+template <>
+struct Vec4<float> {
+    f32x4 v;
+    __device__ void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
+    __device__ void store(float* p) const { *reinterpret_cast<f32x4*>(p) = v; }
+    __device__ float operator[](int j) const { return v[j]; }
+};
+template <>
+struct Vec4<double> {
+    f64x2 lo, hi;
+    __device__ void load(const double* p) {
+        lo = reinterpret_cast<const f64x2*>(p)[0];
+        hi = reinterpret_cast<const f64x2*>(p)[1];
+    }
+    __device__ void store(double* p) const {
+        reinterpret_cast<f64x2*>(p)[0] = lo;
+        reinterpret_cast<f64x2*>(p)[1] = hi;
+    }
+    __device__ double operator[](int j) const { return j < 2 ? lo[j] : hi[j - 2]; }
+};
+
 // Leaf: the tiles of one tile-diagonal K, one 256-thread workgroup per 32 x 32
 // tile.  Thread (w, l) owns column b = l % 32 and rows r0..r0+3 with
 // r0 = 8w + 4(l / 32).  Right-looking in-tile feedback: after the entries of
 // element anti-diagonal d are rounded, each later entry adds the contribution of
 // the rounded entry in its row (Delta * L~_A) and of the one in its column
-// (L~_B * R, R the row-accumulated error).  Everything from earlier tiles is
-// already in X.  One barrier per step (double-buffered exchange arrays).
+// (L~_B * R, R the row-accumulated error).  One barrier per step
+// (double-buffered exchange arrays); finished errors and codes stay in the
+// owning thread's registers.
 //
 // The tile's diagonal factor blocks sit in LDS with their unit diagonal
 // replaced by 0 and an extra all-zero row / column; a source that does not exist
@@ -81,6 +107,20 @@ __global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, 
 // multiplies by an exact zero, so the updates need no predicates (finished
 // entries only ever receive +0).  The exchange arrays start at zero so the
 // multiplied values are always finite.
+//
+// Chunks.  The recursion stops at chunks of consecutive tile-diagonals
+// [c0, c1); inside a chunk the feedback between tiles is pulled by each leaf
+// (left-looking, the per-entry form of section 2.4 at tile granularity).  For
+// tile (I, J) on diagonal K of the chunk, with the chunk-local row-propagated
+// errors
+//   T1c[I', J] = sum_{J' <= J, I' + J' >= c0} Delta[I', J'] N_A[J', J]
+// (written by tile (I', J)'s own leaf), the chunk's contribution is
+//   rowpart = sum_{c0 - I <= J' < J} Delta[I, J'] N_A[J', J]
+//   X[I, J] += N_B[I, I]^T rowpart + sum_{c0 - J <= I' < I} N_B[I', I]^T T1c[I', J]
+// and after the sweep the leaf writes T1c[I, J] = rowpart + Delta[I, J] N_A[J, J]
+// for the later diagonals of its chunk.  With B = I only rowpart is added.  The
+// 32 x 32 x 32 products are few and small; each thread computes its own four
+// entries with FMAs on operands staged k-major in LDS.
 //
 // The quotient x / s is formed as q = x * (1/s) with one Markstein correction
 // q + (x - q s) (1/s): within an ulp of the IEEE quotient, so it can change a
@@ -98,19 +138,23 @@ __device__ __forceinline__ void quantize_fast(T x, T s, T rs, T qmin, T qmax, T&
 template <typename T>
 __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
                                                    const T* __restrict__ NA, const T* __restrict__ NB,
-                                                   const T* __restrict__ S, int np, int mp, int Mt, int Nt,
-                                                   int K, int m, int n, int qmin, int qmax,
-                                                   int8_t* __restrict__ Z, int64_t ldz, T* __restrict__ V,
-                                                   int64_t ldv) {
+                                                   const T* __restrict__ S, T* __restrict__ T1c, int np, int mp,
+                                                   int Mt, int Nt, int K, int c0, int c1, int m, int n, int qmin,
+                                                   int qmax, int8_t* __restrict__ Z, int64_t ldz,
+                                                   T* __restrict__ V, int64_t ldv) {
     constexpr int PB = ST + 4;  // 16-byte aligned rows for the vector reads
     constexpr int PA = ST + 1;  // column ST is the zero sentinel
-    constexpr int PO = ST + 1;
+    constexpr int PK = ST + 4;  // k-major staging rows, 16-byte aligned
     __shared__ __attribute__((aligned(16))) T sNB[(ST + 1) * PB];  // sNB[as][a] = N_B[..as][..a], row ST = 0
     __shared__ T sNAt[ST * PA];                                    // sNAt[b][bs] = N_A[..bs][..b], col ST = 0
     __shared__ __attribute__((aligned(16))) T dD[2][ST];           // errors of the current diagonal, by row
     __shared__ T dR[2][ST];                                        // row-accumulated errors, by column
-    __shared__ T oD[ST * PO];                                      // finished errors
-    __shared__ T oZ[ST * PO];                                      // finished codes
+    // chunk operands of up to BATCH slices: A(r, k) at [k][r], B(k, c) at [k][c]
+    constexpr int MAXS = 2 * (CHUNK - 1);                  // most slices a leaf needs
+    constexpr int BATCH = sizeof(T) == 4 ? MAXS : MAXS / 2;  // staged together (LDS budget)
+    __shared__ __attribute__((aligned(16))) T stg[BATCH][2][ST * PK];
+    T* const bufA = stg[0][0];
+    T* const bufB = stg[0][1];
 
     const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
     const int I = ilo + blockIdx.x;
@@ -119,6 +163,30 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
     const int J = K - I;
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int b = l & 31, r0 = 8 * w + 4 * (l >> 5);
+    const int q8 = t >> 3, c4 = 4 * (t & 7);  // this thread's share of a 32 x 32 staging load
+
+    // chunk sources: row tiles J' in [jl, J), column tiles I' in [il, I)
+    const int jl = c0 - I > 0 ? c0 - I : 0;
+    const int il = c0 - J > 0 ? c0 - J : 0;
+    const int n1 = J - jl;
+    const int n2 = NB ? I - il : 0;
+    const int ns = n1 + n2;
+    Vec4<T> pa[BATCH], pb[BATCH];
+    auto fetch = [&](int sl, Vec4<T>& va, Vec4<T>& vb) {
+        if (sl < n1) {
+            const int jp = jl + sl;
+            va.load(D + int64_t(I * ST + q8) * np + jp * ST + c4);   // A(r = q8, k = c4 + j)
+            vb.load(NA + int64_t(jp * ST + q8) * np + J * ST + c4);  // B(k = q8, c = c4 + j)
+        } else {
+            const int ip = il + sl - n1;
+            va.load(NB + int64_t(ip * ST + q8) * mp + I * ST + c4);  // A(r = c4 + j, k = q8)
+            vb.load(T1c + int64_t(ip * ST + q8) * np + J * ST + c4); // B(k = q8, c = c4 + j)
+        }
+    };
+    // every load of the first batch is in flight before anything waits on one
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u)
+        if (u < ns) fetch(u, pa[u], pb[u]);
 
     for (int e = t; e < ST * ST; e += 256) {
         const int r = e >> 5, c = e & 31;
@@ -134,17 +202,83 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
         dR[0][t] = dR[1][t] = T(0);
     }
 
-    T acc[4], rp[4], sc[4], rs[4];
+    T acc[4], rp[4], sc[4], rs[4], crow[4], ccol[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         acc[i] = X[int64_t(I * ST + r0 + i) * np + J * ST + b];
         rp[i] = T(0);
         sc[i] = S[I * ST + r0 + i];
         rs[i] = sc[i] == T(0) ? T(0) : T(1) / sc[i];
+        crow[i] = T(0);
+        ccol[i] = T(0);
     }
     __syncthreads();
 
+    // ---- chunk prologue: rowpart (crow) and the column feedback (ccol)
+    if (ns > 0) {
+        for (int sb = 0; sb < ns; sb += BATCH) {
+            if (sb > 0) {
+                __syncthreads();  // the previous batch is consumed
+#pragma unroll
+                for (int u = 0; u < BATCH; ++u)
+                    if (sb + u < ns) fetch(sb + u, pa[u], pb[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                if (sb + u < ns) {
+                    if (sb + u < n1) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) stg[u][0][(c4 + j) * PK + q8] = pa[u][j];
+                    } else {
+                        pa[u].store(stg[u][0] + q8 * PK + c4);
+                    }
+                    pb[u].store(stg[u][1] + q8 * PK + c4);
+                }
+            }
+            __syncthreads();
+            const int nbat = ns - sb < BATCH ? ns - sb : BATCH;
+            for (int u = 0; u < nbat; ++u) {
+                const T* sa = stg[u][0];
+                const T* sbm = stg[u][1];
+                T o[4] = {T(0), T(0), T(0), T(0)};
+#pragma unroll 8
+                for (int k = 0; k < ST; ++k) {
+                    Vec4<T> a4;
+                    a4.load(sa + k * PK + r0);
+                    const T bk = sbm[k * PK + b];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[i] = kfma(a4[i], bk, o[i]);
+                }
+                if (sb + u < n1) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) crow[i] += o[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ccol[i] += o[i];
+                }
+            }
+        }
+        __syncthreads();  // staged operands consumed before bufA is reused
+        if (NB && n1 > 0) {
+            // column feedback of rowpart inside the tile: strict(N_B[I, I])^T rowpart
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bufA[(r0 + i) * PK + b] = crow[i];
+            __syncthreads();
+#pragma unroll 8
+            for (int k = 0; k < ST; ++k) {
+                Vec4<T> nb4;
+                nb4.load(sNB + k * PB + r0);
+                const T rk = bufA[k * PK + b];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ccol[i] = kfma(nb4[i], rk, ccol[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += crow[i] + ccol[i];
+    }
+
     const T tqmin = T(qmin), tqmax = T(qmax);
+    T dfin[4] = {T(0), T(0), T(0), T(0)}, zfin[4] = {T(0), T(0), T(0), T(0)};
     for (int d = 0; d < 2 * ST - 1; ++d) {
         const int buf = d & 1;
         const int own = d - b - r0;  // index of my entry on diagonal d, if any
@@ -158,11 +292,13 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
             T z, v;
             quantize_fast(x, sa, ra, tqmin, tqmax, z, v);
             const T delta = v - x;
-            const int a = r0 + own;
-            dD[buf][a] = delta;
+            dD[buf][r0 + own] = delta;
             dR[buf][b] = r + delta;
-            oD[a * PO + b] = delta;
-            oZ[a * PO + b] = z;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dfin[i] = own == i ? delta : dfin[i];
+                zfin[i] = own == i ? z : zfin[i];
+            }
         }
         __syncthreads();
         // all LDS operands first, then unconditional updates
@@ -185,17 +321,33 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
             rp[i] += cr;
         }
     }
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int a = r0 + i;
-        const int64_t gi = int64_t(I) * ST + a, gj = int64_t(J) * ST + b;
-        const T z = oZ[a * PO + b];
-        D[gi * np + gj] = oD[a * PO + b];
+        const int64_t gi = int64_t(I) * ST + r0 + i, gj = int64_t(J) * ST + b;
+        D[gi * np + gj] = dfin[i];
         if (gi < m && gj < n) {
-            Z[gi * ldz + gj] = int8_t(z);
-            V[gi * ldv + gj] = sc[i] * z;
+            Z[gi * ldz + gj] = int8_t(zfin[i]);
+            V[gi * ldv + gj] = sc[i] * zfin[i];
         }
+    }
+    // ---- chunk epilogue: T1c[I, J] = rowpart + Delta + Delta strict(N_A[J, J])
+    if (NB && K + 1 < c1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bufB[b * PK + r0 + i] = dfin[i];  // Delta(r, k) at [k][r]
+        __syncthreads();
+        T o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = crow[i] + dfin[i];
+#pragma unroll 8
+        for (int k = 0; k < ST; ++k) {
+            Vec4<T> d4;
+            d4.load(bufB + k * PK + r0);
+            const T nak = sNAt[b * PA + k];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = kfma(d4[i], nak, o[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) T1c[int64_t(I * ST + r0 + i) * np + J * ST + b] = o[i];
     }
 }
 
@@ -321,12 +473,12 @@ struct SolverRun {
     int64_t ldv;
     hipStream_t st;
 
-    kq_status leaf(int K) {
+    kq_status leaf(int K, int c0, int c1) {
         const int Mt = int(L.Mt), Nt = int(L.Nt);
         const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
         const int ihi = K < Mt - 1 ? K : Mt - 1;
-        hipLaunchKernelGGL(leaf_kernel<T>, dim3(ihi - ilo + 1), dim3(256), 0, st, X, D, NA, NB, S, int(L.np),
-                           int(L.mp), Mt, Nt, K, m, n, qmin, qmax, Z, ldz, V, ldv);
+        hipLaunchKernelGGL(leaf_kernel<T>, dim3(ihi - ilo + 1), dim3(256), 0, st, X, D, NA, NB, S, T1, int(L.np),
+                           int(L.mp), Mt, Nt, K, c0, c1, m, n, qmin, qmax, Z, ldz, V, ldv);
         KQ_LAUNCHED("leaf_kernel");
         return KQ_OK;
     }
@@ -357,8 +509,15 @@ struct SolverRun {
     }
 
     kq_status solve(int K0, int K1) {
-        if (K1 - K0 == 1) return leaf(K0);
-        const int mid = (K0 + K1) / 2;
+        if (K1 - K0 <= CHUNK) {
+            for (int K = K0; K < K1; ++K) {
+                const kq_status s = leaf(K, K0, K1);
+                if (s != KQ_OK) return s;
+            }
+            return KQ_OK;
+        }
+        const int chunks = (K1 - K0 + CHUNK - 1) / CHUNK;
+        const int mid = K0 + CHUNK * (chunks / 2);
         kq_status s = solve(K0, mid);
         if (s != KQ_OK) return s;
         s = propagate(K0, mid, K1);
