@@ -40,6 +40,33 @@ def solver_flops(m: int, n: int) -> float:
     return float(m) * n * (m + n - 2)
 
 
+COUNTERS = os.path.join(ROOT, "profiles", "solver_llm4096x4096_fp32_hbm_counters.txt")
+SOLVER_SOURCES = ("two_sided_gptq_damped_amd/csrc/kq_solver.hip", "two_sided_gptq_damped_amd/csrc/kq_common.hpp")
+
+
+def solver_traffic(m: int, n: int):
+    """Calibrated HBM bytes per kron_quantize call from the committed counter
+    summary, or None when the summary is for another shape or the solver sources
+    changed after the counters were taken."""
+    import hashlib
+    if (m, n) != (4096, 4096) or not os.path.exists(COUNTERS):
+        return None
+    h = hashlib.sha256()
+    for f in SOLVER_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    fields = {}
+    with open(COUNTERS) as fh:
+        for line in fh:
+            if line.startswith("traffic_bytes_per_call:"):
+                fields["traffic"] = float(line.split(":", 1)[1])
+            elif line.startswith("source_sha256"):
+                fields["sha"] = line.rsplit(":", 1)[1].strip()
+    if fields.get("sha") != h.hexdigest():
+        return None
+    return fields.get("traffic")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,7 +207,8 @@ def main() -> int:
             "peak": PEAK_FP32_MFMA / 1e12,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_MFMA,
-            "traffic": None,
+            "traffic": solver_traffic(m, n),
+            "traffic_unit": "bytes per kron_quantize call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "work_per_launch": f"F = m n (m + n - 2) = {F:.4e} flops",
         },
     }
