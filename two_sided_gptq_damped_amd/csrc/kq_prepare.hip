@@ -58,66 +58,124 @@ __global__ void build_reversed_kernel(const TIn* __restrict__ A, int64_t lda, in
     C[idx] = v;
 }
 
-// Cholesky of the diagonal block C[k][k] in LDS (unblocked, right-looking), and
-// the inverse of the factor by forward substitution.  Writes L (zero above the
-// diagonal) back into C and L^{-1} into Dinv[k].  A pivot that is not > 0
-// records its 1-based position in *info (first failure only) and continues
-// with a unit pivot so the remaining kernels stay finite.
+// Lane l's copy of another lane's double (the lane index must be uniform).
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const unsigned lo = unsigned(__builtin_amdgcn_readlane(int(b & 0xffffffffll), l));
+    const unsigned hi = unsigned(__builtin_amdgcn_readlane(int(b >> 32), l));
+    return __longlong_as_double((long long)((unsigned long long)hi << 32 | lo));
+}
+
+// Cholesky of the diagonal block C[k][k] and the inverse of its factor.
+//
+// Factor: left-looking over four 16-column panels.  For panel p (columns c0..c0+15)
+// all 256 threads first subtract the contribution of the finished columns
+// (L[r][c] -= sum_{q < c0} L[r][q] L[c][q]); then one wave factors the panel in
+// registers, lane i holding row c0 + i: per column, the pivot and the column
+// entries of the other panel rows are broadcast with readlane, so a column costs
+// no LDS round trip and no workgroup barrier.
+// Inverse: the four 16 x 16 diagonal blocks are inverted by forward substitution,
+// one wave each (lane = column); then the blocks below the diagonal follow by
+// distance d = 1..3: T = sum_{q=j}^{i-1} L_iq X_qj, X_ij = -X_ii T.
+// Writes L (zero above the diagonal) back into C and L^{-1} into Dinv[k].  A pivot
+// that is not > 0 records its 1-based position in *info (first failure only) and
+// continues with a unit pivot so the remaining kernels stay finite.
 __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ C, int dp, int k,
                                                          double* __restrict__ Dinv, int32_t* __restrict__ info) {
     constexpr int P = TILE + 1;
+    constexpr int PW = 16;  // panel width
     __shared__ double L[TILE * P];
     __shared__ double X[TILE * P];
-    const int t = threadIdx.x, ti = t >> 4, tc = t & 15;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     double* blk = C + int64_t(k) * TILE * dp + int64_t(k) * TILE;
     for (int e = t; e < TILE * TILE; e += 256) {
         const int r = e >> 6, c = e & 63;
         L[r * P + c] = blk[int64_t(r) * dp + c];
-        X[r * P + c] = r == c ? 1.0 : 0.0;
+        X[r * P + c] = 0.0;
     }
     __syncthreads();
-    bool failed = false;  // uniform: every thread sees the same pivots
-    for (int j = 0; j < TILE; ++j) {
-        double p = L[j * P + j];
-        if (!(p > 0.0)) {
-            if (t == 0 && !failed && *info == 0) *info = k * TILE + j + 1;
-            failed = true;
-            p = 1.0;
-        }
-        const double piv = sqrt(p);
-        if (t > j && t < TILE) L[t * P + j] /= piv;
-        __syncthreads();
-        if (t == 0) L[j * P + j] = piv;
-        // trailing lower triangle: rows i > j, columns c in (j, i]
+    bool failed = false;  // uniform in wave 0, the only writer of *info
+    for (int p = 0; p < TILE / PW; ++p) {
+        const int c0 = PW * p;
+        if (p > 0) {
+            for (int e = t; e < (TILE - c0) * PW; e += 256) {
+                const int r = c0 + (e >> 4), c = c0 + (e & 15);
+                if (c <= r) {
+                    double acc[4] = {0.0, 0.0, 0.0, 0.0};  // independent chains
+                    for (int q = 0; q < c0; q += 4) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int i = j + 1 + ti + 16 * a;
-            if (i < TILE) {
-                const double lij = L[i * P + j];
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb) {
-                    const int c = j + 1 + tc + 16 * bb;
-                    if (c <= i) L[i * P + c] -= lij * L[c * P + j];
+                        for (int u = 0; u < 4; ++u)
+                            acc[u] = __builtin_fma(L[r * P + q + u], L[c * P + q + u], acc[u]);
+                    }
+                    L[r * P + c] -= (acc[0] + acc[1]) + (acc[2] + acc[3]);
                 }
+            }
+            __syncthreads();
+        }
+        if (w == 0) {
+            const int r = c0 + lane;
+            const bool live = r < TILE;
+            double a[PW];
+#pragma unroll
+            for (int j = 0; j < PW; ++j) a[j] = (live && c0 + j <= r) ? L[r * P + c0 + j] : 0.0;
+#pragma unroll
+            for (int j = 0; j < PW; ++j) {
+                double d = readlane_f64(a[j], j);
+                if (!(d > 0.0)) {
+                    if (lane == 0 && !failed && *info == 0) *info = k * TILE + c0 + j + 1;
+                    failed = true;
+                    d = 1.0;
+                }
+                const double piv = __builtin_sqrt(d), inv = 1.0 / piv;
+                a[j] = lane > j ? a[j] * inv : (lane == j ? piv : a[j]);
+#pragma unroll
+                for (int c = j + 1; c < PW; ++c) a[c] = __builtin_fma(-a[j], readlane_f64(a[j], c), a[c]);
+            }
+            if (live) {
+#pragma unroll
+                for (int j = 0; j < PW; ++j)
+                    if (c0 + j <= r) L[r * P + c0 + j] = a[j];
             }
         }
         __syncthreads();
     }
-    // inverse of the lower factor: right-looking forward substitution of L X = I
-    for (int j = 0; j < TILE; ++j) {
-        if (t <= j) X[j * P + t] /= L[j * P + j];
-        __syncthreads();
+    // diagonal 16 x 16 blocks of the inverse: wave w, block w, lane = column
+    if (lane < PW) {
+        const int i0 = PW * w, c = lane;
+        double x[PW];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int i = j + 1 + ti + 16 * a;
-            if (i < TILE) {
-                const double lij = L[i * P + j];
+        for (int r = 0; r < PW; ++r) {
+            double s = r == c ? 1.0 : 0.0;
 #pragma unroll
-                for (int bb = 0; bb < 4; ++bb) {
-                    const int c = tc + 16 * bb;
-                    if (c <= j) X[i * P + c] -= lij * X[j * P + c];
-                }
+            for (int q = 0; q < r; ++q) s = __builtin_fma(-L[(i0 + r) * P + i0 + q], x[q], s);
+            x[r] = s / L[(i0 + r) * P + i0 + r];
+        }
+#pragma unroll
+        for (int r = 0; r < PW; ++r) X[(i0 + r) * P + i0 + c] = x[r];
+    }
+    __syncthreads();
+    // blocks below the diagonal; T_ij is kept in the (unused) upper triangle of L
+    for (int d = 1; d < TILE / PW; ++d) {
+        const int nblk = TILE / PW - d;
+        for (int e = t; e < nblk * PW * PW; e += 256) {
+            const int jb = e >> 8, ib = jb + d, rr = (e >> 4) & 15, cc = e & 15;
+            const int row = PW * ib + rr, col = PW * jb + cc;
+            double acc[4] = {0.0, 0.0, 0.0, 0.0};
+            for (int q = PW * jb; q < PW * ib; q += 4) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[u] = __builtin_fma(L[row * P + q + u], X[(q + u) * P + col], acc[u]);
             }
+            L[(PW * jb + rr) * P + PW * ib + cc] = (acc[0] + acc[1]) + (acc[2] + acc[3]);  // T_ij at the mirrored block
+        }
+        __syncthreads();
+        for (int e = t; e < nblk * PW * PW; e += 256) {
+            const int jb = e >> 8, ib = jb + d, rr = (e >> 4) & 15, cc = e & 15;
+            double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int q = 0; q < PW; ++q)
+                acc[q & 3] = __builtin_fma(X[(PW * ib + rr) * P + PW * ib + q], L[(PW * jb + q) * P + PW * ib + cc],
+                                           acc[q & 3]);
+            X[(PW * ib + rr) * P + PW * jb + cc] = -((acc[0] + acc[1]) + (acc[2] + acc[3]));
         }
         __syncthreads();
     }
