@@ -92,8 +92,9 @@ struct Vec4<double> {
 };
 
 // Leaf: the tiles of one tile-diagonal K, one 256-thread workgroup per 32 x 32
-// tile.  Thread (w, l) owns column b = l % 32 and rows r0..r0+3 with
-// r0 = 8w + 4(l / 32).  Right-looking in-tile feedback: after the entries of
+// tile.  Thread t owns four entries of column b = t % 32 (in the sweep, rows
+// (4g - b + i) mod 32 with g = t / 32, see the layouts below).  Right-looking
+// in-tile feedback: after the entries of
 // element anti-diagonal d are rounded, each later entry adds the contribution of
 // the rounded entry in its row (Delta * L~_A) and of the one in its column
 // (L~_B * R, R the row-accumulated error).  One barrier per step
@@ -202,13 +203,24 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
         dR[0][t] = dR[1][t] = T(0);
     }
 
-    T acc[4], rp[4], sc[4], rs[4], crow[4], ccol[4];
+    // Two layouts of the tile over the threads, both with column b:
+    //   block layout  rows r0 + i = 4g + i (g = t / 32): vector LDS reads, coalesced
+    //                 global access, the chunk products;
+    //   sweep layout  rows ar[i] = (4g - b + i) mod 32: entry i of every thread lies
+    //                 on an element diagonal congruent to i mod 4, so the entry to
+    //                 round at step d sits in slot d % 4 of every thread.
+    const int g = t >> 5;
+    int ar[4], dg[4];
+    T acc[4], crow[4], ccol[4], sblk[4], x[4], rp[4], sc[4], rs[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        ar[i] = (4 * g - b + i) & (ST - 1);
+        dg[i] = b + ar[i];
         acc[i] = X[int64_t(I * ST + r0 + i) * np + J * ST + b];
-        rp[i] = T(0);
-        sc[i] = S[I * ST + r0 + i];
+        sblk[i] = S[I * ST + r0 + i];
+        sc[i] = S[I * ST + ar[i]];
         rs[i] = sc[i] == T(0) ? T(0) : T(1) / sc[i];
+        rp[i] = T(0);
         crow[i] = T(0);
         ccol[i] = T(0);
     }
@@ -277,67 +289,83 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
         for (int i = 0; i < 4; ++i) acc[i] += crow[i] + ccol[i];
     }
 
+    // ---- to the sweep layout through LDS
+    __syncthreads();  // the prologue's reads of bufA are done
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bufA[(r0 + i) * PK + b] = acc[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = bufA[ar[i] * PK + b];
+
+    // ---- the sweep: 2 ST - 1 element anti-diagonals, one barrier each
     const T tqmin = T(qmin), tqmax = T(qmax);
     T dfin[4] = {T(0), T(0), T(0), T(0)}, zfin[4] = {T(0), T(0), T(0), T(0)};
-    for (int d = 0; d < 2 * ST - 1; ++d) {
-        const int buf = d & 1;
-        const int own = d - b - r0;  // index of my entry on diagonal d, if any
-        if (own >= 0 && own < 4) {
-            // explicit selects keep the accumulators in registers
-            const bool hi = own & 2, od = own & 1;
-            const T x = hi ? (od ? acc[3] : acc[2]) : (od ? acc[1] : acc[0]);
-            const T r = hi ? (od ? rp[3] : rp[2]) : (od ? rp[1] : rp[0]);
-            const T sa = hi ? (od ? sc[3] : sc[2]) : (od ? sc[1] : sc[0]);
-            const T ra = hi ? (od ? rs[3] : rs[2]) : (od ? rs[1] : rs[0]);
-            T z, v;
-            quantize_fast(x, sa, ra, tqmin, tqmax, z, v);
-            const T delta = v - x;
-            dD[buf][r0 + own] = delta;
-            dR[buf][b] = r + delta;
+    for (int dq = 0; dq < (2 * ST + 2) / 4; ++dq) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dfin[i] = own == i ? delta : dfin[i];
-                zfin[i] = own == i ? z : zfin[i];
+        for (int i = 0; i < 4; ++i) {
+            const int d = 4 * dq + i;
+            if (d < 2 * ST - 1) {
+                const int buf = d & 1;
+                {
+                    // slot i holds this thread's entry on diagonal d, if it has one
+                    T z, v;
+                    quantize_fast(x[i], sc[i], rs[i], tqmin, tqmax, z, v);
+                    const T delta = v - x[i];
+                    if (dg[i] == d) {
+                        dD[buf][ar[i]] = delta;
+                        dR[buf][b] = rp[i] + delta;
+                        dfin[i] = delta;
+                        zfin[i] = z;
+                    }
+                }
+                __syncthreads();
+                // all LDS operands first, then unconditional updates
+                const int as = d - b;  // column source (as, b)
+                const int asc = unsigned(as) > unsigned(ST - 1) ? ST : as;
+                const T rv = dR[buf][b];
+                T nbv[4], ddv[4], nav[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    nbv[j] = sNB[asc * PB + ar[j]];
+                    ddv[j] = dD[buf][ar[j]];
+                    const int bs = d - ar[j];  // row source (ar[j], bs)
+                    nav[j] = sNAt[b * PA + (unsigned(bs) > unsigned(ST - 1) ? ST : bs)];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const T cr = ddv[j] * nav[j];
+                    x[j] = kfma(nbv[j], rv, x[j]) + cr;
+                    rp[j] += cr;
+                }
             }
         }
-        __syncthreads();
-        // all LDS operands first, then unconditional updates
-        const int as = d - b;        // column source (as, b)
-        const int asc = unsigned(as) > unsigned(ST - 1) ? ST : as;
-        const T rv = dR[buf][b];
-        const int bs0 = d - r0;      // row source (r0 + i, bs0 - i)
-        T nbv[4], ddv[4], nav[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            nbv[i] = sNB[asc * PB + r0 + i];
-            ddv[i] = dD[buf][r0 + i];
-            const int bs = bs0 - i;
-            nav[i] = sNAt[b * PA + (unsigned(bs) > unsigned(ST - 1) ? ST : bs)];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const T cr = ddv[i] * nav[i];
-            acc[i] = kfma(nbv[i], rv, acc[i]) + cr;
-            rp[i] += cr;
-        }
     }
+
+    // ---- back to the block layout: errors k-major in bufB (for the epilogue), codes in bufA
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bufB[b * PK + ar[i]] = dfin[i];
+        bufA[ar[i] * PK + b] = zfin[i];
+    }
+    __syncthreads();
+    T dblk[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t gi = int64_t(I) * ST + r0 + i, gj = int64_t(J) * ST + b;
-        D[gi * np + gj] = dfin[i];
+        dblk[i] = bufB[b * PK + r0 + i];
+        const T z = bufA[(r0 + i) * PK + b];
+        D[gi * np + gj] = dblk[i];
         if (gi < m && gj < n) {
-            Z[gi * ldz + gj] = int8_t(zfin[i]);
-            V[gi * ldv + gj] = sc[i] * zfin[i];
+            Z[gi * ldz + gj] = int8_t(z);
+            V[gi * ldv + gj] = sblk[i] * z;
         }
     }
     // ---- chunk epilogue: T1c[I, J] = rowpart + Delta + Delta strict(N_A[J, J])
     if (NB && K + 1 < c1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bufB[b * PK + r0 + i] = dfin[i];  // Delta(r, k) at [k][r]
-        __syncthreads();
         T o[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = crow[i] + dfin[i];
+        for (int i = 0; i < 4; ++i) o[i] = crow[i] + dblk[i];
 #pragma unroll 8
         for (int k = 0; k < ST; ++k) {
             Vec4<T> d4;
