@@ -123,6 +123,7 @@ struct WaveAcc<float> {
     }
     static constexpr int NREG = 16;
     __device__ float get(int r) const { return c[r]; }
+    __device__ void add(int r, float v) { c[r] += v; }
     // Position of register r inside the wave's 32 x 32 block.
     static __device__ __forceinline__ int row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
     static __device__ __forceinline__ int col(int r, int lane) { return lane & 31; }
@@ -156,6 +157,7 @@ struct WaveAcc<double> {
     }
     static constexpr int NREG = 16;
     __device__ double get(int r) const { return c[r >> 3][(r >> 2) & 1][r & 3]; }
+    __device__ void add(int r, double v) { c[r >> 3][(r >> 2) & 1][r & 3] += v; }
     static __device__ __forceinline__ int row(int r, int lane) { return 16 * (r >> 3) + (lane >> 4) + 4 * (r & 3); }
     static __device__ __forceinline__ int col(int r, int lane) { return 16 * ((r >> 2) & 1) + (lane & 15); }
 };
@@ -317,10 +319,94 @@ __device__ void tile_gemm_masked(const T* __restrict__ A, int64_t lda, const T* 
     }
 }
 
+// Split-K variant for launch shapes with few blocks and long K ranges: G groups of
+// four waves (blockDim = 256 G) share one 64 x 64 output.  Group g takes the
+// K slices s = g, g + G, ... with its own double-buffered LDS stage, all groups
+// step together (one workgroup barrier per step), and at the end groups 1..G-1
+// hand their partial sums to group 0 through LDS, which adds them in group
+// order, so the result does not depend on timing.  Only group 0's acc holds
+// the product afterwards.
+template <typename T, int G>
+struct SplitSmem {
+    GemmSmem<T> st[G];
+};
+
+template <typename T, int G, bool A_KMAJ, bool B_KMAJ, typename MA, typename MB>
+__device__ void tile_gemm_masked_splitk(const T* __restrict__ A, int64_t lda, const T* __restrict__ B,
+                                        int64_t ldb, int K, SplitSmem<T, G>& sm, WaveAcc<T>& acc, MA ma, MB mb) {
+    const int tg = threadIdx.x, grp = tg >> 8, t = tg & 255, lane = t & 63, w = t >> 6;
+    const int wy = w >> 1, wx = w & 1;
+    TileLoader<T, T, A_KMAJ, B_KMAJ, false> ld;
+    GemmSmem<T>& my = sm.st[grp];
+    const int nk = K / KSTEP;
+    const int iters = (nk + G - 1) / G;
+    auto apply = [&](int k0) {
+        if (!A_KMAJ) {
+            const int r = t >> 2, kq = (t & 3) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!ma(r, k0 + kq + e)) ld.ra[e] = T(0);
+        } else {
+            const int k = t >> 4, rq = (t & 15) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!ma(rq + e, k0 + k)) ld.ra[e] = T(0);
+        }
+        if (!B_KMAJ) {
+            const int k = t >> 4, cq = (t & 15) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!mb(k0 + k, cq + e)) ld.rb[e] = T(0);
+        } else {
+            const int c = t >> 2, kq = (t & 3) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!mb(k0 + kq + e, c)) ld.rb[e] = T(0);
+        }
+    };
+    if (iters > 0) {
+        int s = grp;
+        if (s < nk) {
+            ld.fetch(A, lda, B, ldb, s * KSTEP, TILE, TILE, K, t);
+            apply(s * KSTEP);
+            ld.stash(my.a[0], my.b[0], t);
+        }
+        __syncthreads();
+        for (int it = 0; it < iters; ++it) {
+            const int cur = it & 1;
+            const int sn = s + G;  // this group's next slice
+            if (sn < nk) ld.fetch(A, lda, B, ldb, sn * KSTEP, TILE, TILE, K, t);
+            if (s < nk) acc.mma(my.a[cur], my.b[cur], wy, wx, lane);
+            if (sn < nk) {
+                apply(sn * KSTEP);
+                ld.stash(my.a[cur ^ 1], my.b[cur ^ 1], t);
+            }
+            __syncthreads();
+            s = sn;
+        }
+    }
+    // reduction: group g > 0 parks its partials in its own stage buffers
+    constexpr int NR = WaveAcc<T>::NREG;
+    static_assert(sizeof(GemmSmem<T>) >= sizeof(T) * NR * 256, "stage buffer too small for the partials");
+    if (grp > 0) {
+        T* park = reinterpret_cast<T*>(&sm.st[grp]);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) park[r * 256 + t] = acc.get(r);
+    }
+    __syncthreads();
+    if (grp == 0) {
+        for (int g = 1; g < G; ++g) {
+            const T* park = reinterpret_cast<const T*>(&sm.st[g]);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc.add(r, park[r * 256 + t]);
+        }
+    }
+}
+
 // Visit the 16 accumulator registers of this thread with their tile coordinates.
 template <typename T, typename F>
 __device__ __forceinline__ void for_each_acc(const WaveAcc<T>& acc, F&& f) {
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int t = threadIdx.x & 255, lane = t & 63, w = t >> 6;
     const int r0 = (w >> 1) * 32, c0 = (w & 1) * 32;
 #pragma unroll
     for (int r = 0; r < WaveAcc<T>::NREG; ++r)

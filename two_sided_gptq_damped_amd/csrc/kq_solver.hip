@@ -380,12 +380,24 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
 }
 
 // Stage 1 at node [K0, K1) with split mid, on 64-row block P and 64-column block Q.
+// Band GEMMs run split-K inside the workgroup: their launches have few blocks
+// with long K ranges in the lower recursion levels, so each block gets BAND_G
+// groups of four waves (deterministic reduction, see tile_gemm_masked_splitk).
 template <typename T>
-__global__ __launch_bounds__(GEMM_THREADS) void band_stage1_kernel(const T* __restrict__ D,
-                                                                   const T* __restrict__ NA,
-                                                                   T* __restrict__ T1, int np, int Nt, int K0,
-                                                                   int mid, int K1, int P0) {
-    __shared__ GemmSmem<T> sm;
+struct Band {
+    static constexpr int G = sizeof(T) == 4 ? 4 : 2;  // stage 1: groups per block
+    static constexpr int THREADS = 256 * G;
+    // Stage 2 has half the blocks of stage 1 at the top node with twice the K
+    // each; there four-wave blocks at full occupancy balance better than split K.
+    static constexpr int THREADS2 = GEMM_THREADS;
+};
+
+template <typename T>
+__global__ __launch_bounds__(Band<T>::THREADS) void band_stage1_kernel(const T* __restrict__ D,
+                                                                       const T* __restrict__ NA,
+                                                                       T* __restrict__ T1, int np, int Nt, int K0,
+                                                                       int mid, int K1, int P0) {
+    __shared__ SplitSmem<T, Band<T>::G> sm;
     const int P = P0 + blockIdx.y;
     const int I0 = 2 * P;  // first 32-row tile of the block
     const int jlo = K0 - I0 - 1 > 0 ? K0 - I0 - 1 : 0;
@@ -405,8 +417,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void band_stage1_kernel(const T* __re
             const int s = I0 + (r >> 5) + kl + (k >> 5);  // tile-diagonal of the source tile
             return s >= K0 && s < mid;
         };
-        tile_gemm_masked<T, false, false>(A, np, B, np, (kh - kl + 1) * ST, sm, acc, ma, NoMask());
+        tile_gemm_masked_splitk<T, Band<T>::G, false, false>(A, np, B, np, (kh - kl + 1) * ST, sm, acc, ma,
+                                                             NoMask());
     }
+    if (threadIdx.x >= 256) return;  // group 0 holds the product
     T* out = T1 + int64_t(I0) * ST * np + int64_t(Q) * TILE;
     for_each_acc(acc, [&](int r, int c, T v) { out[int64_t(r) * np + c] = v; });
 }
@@ -414,10 +428,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void band_stage1_kernel(const T* __re
 // Stage 2: X[I, J] += sum_{I'} N_B[I', I]^T T1[I', J] for the tiles of diagonals
 // [mid, K1), on 64 x 64 target block (P, Q) of block-diagonal sig = P + Q.
 template <typename T>
-__global__ __launch_bounds__(GEMM_THREADS) void band_stage2_kernel(const T* __restrict__ T1,
-                                                                   const T* __restrict__ NB,
-                                                                   T* __restrict__ X, int np, int mp, int Mt,
-                                                                   int Nt, int K0, int mid, int K1, int sig0) {
+__global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T* __restrict__ T1,
+                                                                        const T* __restrict__ NB,
+                                                                        T* __restrict__ X, int np, int mp, int Mt,
+                                                                        int Nt, int K0, int mid, int K1, int sig0) {
     __shared__ GemmSmem<T> sm;
     const int sig = sig0 + blockIdx.y;
     const int Mb = Mt >> 1, Nb = Nt >> 1;
@@ -438,7 +452,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void band_stage2_kernel(const T* __re
     T* out = X + int64_t(I0) * ST * np + int64_t(J0) * ST;
     if (!NB) {
         const T* src = T1 + int64_t(I0) * ST * np + int64_t(J0) * ST;
-        for (int e = threadIdx.x; e < TILE * TILE; e += GEMM_THREADS) {
+        for (int e = threadIdx.x; e < TILE * TILE; e += Band<T>::THREADS2) {
             const int r = e >> 6, c = e & 63;
             if (in_band(r, c) && t1_valid(I0 + (r >> 5), J0 + (c >> 5)))
                 out[int64_t(r) * np + c] += src[int64_t(r) * np + c];
@@ -518,7 +532,7 @@ struct SolverRun {
         const int row1 = mid < Mt ? mid : Mt;  // exclusive
         if (row1 > row0) {
             const int P0 = row0 >> 1, P1 = (row1 - 1) >> 1;
-            hipLaunchKernelGGL(band_stage1_kernel<T>, dim3((K1 - K0) / 2 + 2, P1 - P0 + 1), dim3(GEMM_THREADS), 0,
+            hipLaunchKernelGGL(band_stage1_kernel<T>, dim3((K1 - K0) / 2 + 2, P1 - P0 + 1), dim3(Band<T>::THREADS), 0,
                                st, D, NA, T1, int(L.np), Nt, K0, mid, K1, P0);
             KQ_LAUNCHED("band_stage1_kernel");
         }
@@ -529,7 +543,7 @@ struct SolverRun {
         if (sig1 > sigmax) sig1 = sigmax;
         if (sig1 >= sig0) {
             const int width = Mt < Nt ? Mt / 2 : Nt / 2;
-            hipLaunchKernelGGL(band_stage2_kernel<T>, dim3(width, sig1 - sig0 + 1), dim3(GEMM_THREADS), 0, st, T1,
+            hipLaunchKernelGGL(band_stage2_kernel<T>, dim3(width, sig1 - sig0 + 1), dim3(Band<T>::THREADS2), 0, st, T1,
                                NB, X, int(L.np), int(L.mp), Mt, Nt, K0, mid, K1, sig0);
             KQ_LAUNCHED("band_stage2_kernel");
         }
