@@ -136,8 +136,11 @@ __device__ __forceinline__ void quantize_fast(T x, T s, T rs, T qmin, T qmax, T&
     v = s * z;
 }
 
+constexpr int LEAF_THREADS = 512;  // the sweep: two entries per thread
+constexpr int LEAF_E = ST * ST / LEAF_THREADS;
+
 template <typename T>
-__global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
+__global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
                                                    const T* __restrict__ NA, const T* __restrict__ NB,
                                                    const T* __restrict__ S, T* __restrict__ T1c, int np, int mp,
                                                    int Mt, int Nt, int K, int c0, int c1, int m, int n, int qmin,
@@ -162,9 +165,13 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
     const int ihi = K < Mt - 1 ? K : Mt - 1;
     if (I > ihi) return;
     const int J = K - I;
-    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    // threads t < 256 also work in the block layout (four rows each); all
+    // LEAF_THREADS threads take part in the sweep
+    const int t = threadIdx.x, tb = t & 255, w = tb >> 6, l = tb & 63;
+    const bool blk = t < 256;
     const int b = l & 31, r0 = 8 * w + 4 * (l >> 5);
-    const int q8 = t >> 3, c4 = 4 * (t & 7);  // this thread's share of a 32 x 32 staging load
+    const int fgrp = t >> 8;                    // staging loads: slices rotate over the 256-thread groups
+    const int q8 = tb >> 3, c4 = 4 * (tb & 7);  // this thread's share of a 32 x 32 staging load
 
     // chunk sources: row tiles J' in [jl, J), column tiles I' in [il, I)
     const int jl = c0 - I > 0 ? c0 - I : 0;
@@ -172,7 +179,9 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
     const int n1 = J - jl;
     const int n2 = NB ? I - il : 0;
     const int ns = n1 + n2;
-    Vec4<T> pa[BATCH], pb[BATCH];
+    constexpr int NFG = LEAF_THREADS / 256;
+    constexpr int SLOTS = (BATCH + NFG - 1) / NFG;  // slices of a batch held by one thread
+    Vec4<T> pa[SLOTS], pb[SLOTS];
     auto fetch = [&](int sl, Vec4<T>& va, Vec4<T>& vb) {
         if (sl < n1) {
             const int jp = jl + sl;
@@ -186,10 +195,12 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
     };
     // every load of the first batch is in flight before anything waits on one
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u)
-        if (u < ns) fetch(u, pa[u], pb[u]);
+    for (int v = 0; v < SLOTS; ++v) {
+        const int u = NFG * v + fgrp;
+        if (u < BATCH && u < ns) fetch(u, pa[v], pb[v]);
+    }
 
-    for (int e = t; e < ST * ST; e += 256) {
+    for (int e = t; e < ST * ST; e += LEAF_THREADS) {
         const int r = e >> 5, c = e & 31;
         const T nb = NB ? NB[int64_t(I * ST + r) * mp + I * ST + c] : T(0);
         sNB[r * PB + c] = r == c ? T(0) : nb;
@@ -203,86 +214,101 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
         dR[0][t] = dR[1][t] = T(0);
     }
 
-    // Two layouts of the tile over the threads, both with column b:
-    //   block layout  rows r0 + i = 4g + i (g = t / 32): vector LDS reads, coalesced
-    //                 global access, the chunk products;
-    //   sweep layout  rows ar[i] = (4g - b + i) mod 32: entry i of every thread lies
-    //                 on an element diagonal congruent to i mod 4, so the entry to
-    //                 round at step d sits in slot d % 4 of every thread.
-    const int g = t >> 5;
-    int ar[4], dg[4];
-    T acc[4], crow[4], ccol[4], sblk[4], x[4], rp[4], sc[4], rs[4];
+    // Two layouts of the tile over the threads, both with column b = t % 32:
+    //   block layout  threads t < 256, rows r0 + i (four each): vector LDS reads,
+    //                 coalesced global access, the chunk products;
+    //   sweep layout  all threads, rows ar[i] = (E g - b + i) mod 32 with g = t / 32
+    //                 and E = LEAF_E entries each: entry i of every thread lies on
+    //                 an element diagonal congruent to i mod E, so the entry to
+    //                 round at step d sits in slot d % E of every thread.
+    constexpr int E = LEAF_E;
+    const int g = t >> 5;  // sweep layout: column b, rows (E g - b + i) mod 32
+    int ar[E], dg[E];
+    T x[E], rp[E], sc[E], rs[E];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ar[i] = (4 * g - b + i) & (ST - 1);
+    for (int i = 0; i < E; ++i) {
+        ar[i] = (E * g - b + i) & (ST - 1);
         dg[i] = b + ar[i];
-        acc[i] = X[int64_t(I * ST + r0 + i) * np + J * ST + b];
-        sblk[i] = S[I * ST + r0 + i];
         sc[i] = S[I * ST + ar[i]];
         rs[i] = sc[i] == T(0) ? T(0) : T(1) / sc[i];
         rp[i] = T(0);
+    }
+    T acc[4], crow[4], ccol[4], sblk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[i] = blk ? X[int64_t(I * ST + r0 + i) * np + J * ST + b] : T(0);
+        sblk[i] = blk ? S[I * ST + r0 + i] : T(0);
         crow[i] = T(0);
         ccol[i] = T(0);
     }
     __syncthreads();
 
-    // ---- chunk prologue: rowpart (crow) and the column feedback (ccol)
+    // ---- chunk prologue: rowpart (crow) and the column feedback (ccol), block layout
     if (ns > 0) {
         for (int sb = 0; sb < ns; sb += BATCH) {
             if (sb > 0) {
                 __syncthreads();  // the previous batch is consumed
 #pragma unroll
-                for (int u = 0; u < BATCH; ++u)
-                    if (sb + u < ns) fetch(sb + u, pa[u], pb[u]);
+                for (int v = 0; v < SLOTS; ++v) {
+                    const int u = NFG * v + fgrp;
+                    if (u < BATCH && sb + u < ns) fetch(sb + u, pa[v], pb[v]);
+                }
             }
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-                if (sb + u < ns) {
+            for (int v = 0; v < SLOTS; ++v) {
+                const int u = NFG * v + fgrp;
+                if (u < BATCH && sb + u < ns) {
                     if (sb + u < n1) {
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) stg[u][0][(c4 + j) * PK + q8] = pa[u][j];
+                        for (int j = 0; j < 4; ++j) stg[u][0][(c4 + j) * PK + q8] = pa[v][j];
                     } else {
-                        pa[u].store(stg[u][0] + q8 * PK + c4);
+                        pa[v].store(stg[u][0] + q8 * PK + c4);
                     }
-                    pb[u].store(stg[u][1] + q8 * PK + c4);
+                    pb[v].store(stg[u][1] + q8 * PK + c4);
                 }
             }
             __syncthreads();
             const int nbat = ns - sb < BATCH ? ns - sb : BATCH;
-            for (int u = 0; u < nbat; ++u) {
-                const T* sa = stg[u][0];
-                const T* sbm = stg[u][1];
-                T o[4] = {T(0), T(0), T(0), T(0)};
+            if (blk) {
+                for (int u = 0; u < nbat; ++u) {
+                    const T* sa = stg[u][0];
+                    const T* sbm = stg[u][1];
+                    T o[4] = {T(0), T(0), T(0), T(0)};
 #pragma unroll 8
-                for (int k = 0; k < ST; ++k) {
-                    Vec4<T> a4;
-                    a4.load(sa + k * PK + r0);
-                    const T bk = sbm[k * PK + b];
+                    for (int k = 0; k < ST; ++k) {
+                        Vec4<T> a4;
+                        a4.load(sa + k * PK + r0);
+                        const T bk = sbm[k * PK + b];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i] = kfma(a4[i], bk, o[i]);
-                }
-                if (sb + u < n1) {
+                        for (int i = 0; i < 4; ++i) o[i] = kfma(a4[i], bk, o[i]);
+                    }
+                    if (sb + u < n1) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) crow[i] += o[i];
-                } else {
+                        for (int i = 0; i < 4; ++i) crow[i] += o[i];
+                    } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) ccol[i] += o[i];
+                        for (int i = 0; i < 4; ++i) ccol[i] += o[i];
+                    }
                 }
             }
         }
         __syncthreads();  // staged operands consumed before bufA is reused
         if (NB && n1 > 0) {
             // column feedback of rowpart inside the tile: strict(N_B[I, I])^T rowpart
+            if (blk) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bufA[(r0 + i) * PK + b] = crow[i];
+                for (int i = 0; i < 4; ++i) bufA[(r0 + i) * PK + b] = crow[i];
+            }
             __syncthreads();
+            if (blk) {
 #pragma unroll 8
-            for (int k = 0; k < ST; ++k) {
-                Vec4<T> nb4;
-                nb4.load(sNB + k * PB + r0);
-                const T rk = bufA[k * PK + b];
+                for (int k = 0; k < ST; ++k) {
+                    Vec4<T> nb4;
+                    nb4.load(sNB + k * PB + r0);
+                    const T rk = bufA[k * PK + b];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ccol[i] = kfma(nb4[i], rk, ccol[i]);
+                    for (int i = 0; i < 4; ++i) ccol[i] = kfma(nb4[i], rk, ccol[i]);
+                }
             }
         }
 #pragma unroll
@@ -291,19 +317,23 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
 
     // ---- to the sweep layout through LDS
     __syncthreads();  // the prologue's reads of bufA are done
+    if (blk) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bufA[(r0 + i) * PK + b] = acc[i];
+        for (int i = 0; i < 4; ++i) bufA[(r0 + i) * PK + b] = acc[i];
+    }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = bufA[ar[i] * PK + b];
+    for (int i = 0; i < E; ++i) x[i] = bufA[ar[i] * PK + b];
 
     // ---- the sweep: 2 ST - 1 element anti-diagonals, one barrier each
     const T tqmin = T(qmin), tqmax = T(qmax);
-    T dfin[4] = {T(0), T(0), T(0), T(0)}, zfin[4] = {T(0), T(0), T(0), T(0)};
-    for (int dq = 0; dq < (2 * ST + 2) / 4; ++dq) {
+    T dfin[E], zfin[E];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d = 4 * dq + i;
+    for (int i = 0; i < E; ++i) dfin[i] = zfin[i] = T(0);
+    for (int dq = 0; dq < (2 * ST - 2 + E) / E; ++dq) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            const int d = E * dq + i;
             if (d < 2 * ST - 1) {
                 const int buf = d & 1;
                 {
@@ -323,16 +353,16 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
                 const int as = d - b;  // column source (as, b)
                 const int asc = unsigned(as) > unsigned(ST - 1) ? ST : as;
                 const T rv = dR[buf][b];
-                T nbv[4], ddv[4], nav[4];
+                T nbv[E], ddv[E], nav[E];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < E; ++j) {
                     nbv[j] = sNB[asc * PB + ar[j]];
                     ddv[j] = dD[buf][ar[j]];
                     const int bs = d - ar[j];  // row source (ar[j], bs)
                     nav[j] = sNAt[b * PA + (unsigned(bs) > unsigned(ST - 1) ? ST : bs)];
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < E; ++j) {
                     const T cr = ddv[j] * nav[j];
                     x[j] = kfma(nbv[j], rv, x[j]) + cr;
                     rp[j] += cr;
@@ -344,11 +374,12 @@ __global__ __launch_bounds__(256) void leaf_kernel(const T* __restrict__ X, T* _
     // ---- back to the block layout: errors k-major in bufB (for the epilogue), codes in bufA
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < E; ++i) {
         bufB[b * PK + ar[i]] = dfin[i];
         bufA[ar[i] * PK + b] = zfin[i];
     }
     __syncthreads();
+    if (!blk) return;  // no barriers follow
     T dblk[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -519,7 +550,7 @@ struct SolverRun {
         const int Mt = int(L.Mt), Nt = int(L.Nt);
         const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
         const int ihi = K < Mt - 1 ? K : Mt - 1;
-        hipLaunchKernelGGL(leaf_kernel<T>, dim3(ihi - ilo + 1), dim3(256), 0, st, X, D, NA, NB, S, T1, int(L.np),
+        hipLaunchKernelGGL(leaf_kernel<T>, dim3(ihi - ilo + 1), dim3(LEAF_THREADS), 0, st, X, D, NA, NB, S, T1, int(L.np),
                            int(L.mp), Mt, Nt, K, c0, c1, m, n, qmin, qmax, Z, ldz, V, ldv);
         KQ_LAUNCHED("leaf_kernel");
         return KQ_OK;
