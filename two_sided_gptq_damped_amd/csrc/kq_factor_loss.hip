@@ -9,7 +9,9 @@ namespace kq {
 // 64 x 64 tile of the lower triangle (I >= J); the tile and its mirror are both
 // written, so the full symmetric matrix is produced.  The diagonal tile writes
 // each element once.
-template <typename T>
+// EXACT: dim is a multiple of 64, rows of 16 and ldx of 4, so every operand load
+// is in range and vector aligned and the bounds checks are dropped.
+template <typename T, bool EXACT>
 __global__ __launch_bounds__(GEMM_THREADS) void syrk_kernel(const T* __restrict__ X, int64_t ldx, int rows, int dim,
                                                             T* __restrict__ S, int64_t lds, T alpha, T beta) {
     const int I = blockIdx.y, J = blockIdx.x;
@@ -19,7 +21,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void syrk_kernel(const T* __restrict_
     acc.zero();
     const int mv = dim - I * TILE, nv = dim - J * TILE;
     // A(r, k) = X[k][I*64 + r]; B(k, c) = X[k][J*64 + c]
-    tile_gemm<T, T, true, false, true>(X + I * TILE, ldx, X + J * TILE, ldx, mv, nv, rows, sm, acc);
+    tile_gemm<T, T, true, false, !EXACT>(X + I * TILE, ldx, X + J * TILE, ldx, mv, nv, rows, sm, acc);
     for_each_acc(acc, [&](int r, int c, T v) {
         if (r >= mv || c >= nv) return;
         const int64_t gi = int64_t(I) * TILE + r, gj = int64_t(J) * TILE + c;
@@ -35,14 +37,19 @@ __global__ __launch_bounds__(GEMM_THREADS) void syrk_kernel(const T* __restrict_
 kq_status factor_dispatch(kq_dtype dtype, int64_t rows, int64_t dim, const void* X, int64_t ldx, void* S, int64_t lds,
                           double alpha, double beta, hipStream_t st) {
     const int tiles = int((dim + TILE - 1) / TILE);
-    if (dtype == KQ_F64)
-        hipLaunchKernelGGL(syrk_kernel<double>, dim3(tiles, tiles), dim3(GEMM_THREADS), 0, st,
-                           static_cast<const double*>(X), ldx, int(rows), int(dim), static_cast<double*>(S), lds, alpha,
-                           beta);
-    else
-        hipLaunchKernelGGL(syrk_kernel<float>, dim3(tiles, tiles), dim3(GEMM_THREADS), 0, st,
-                           static_cast<const float*>(X), ldx, int(rows), int(dim), static_cast<float*>(S), lds,
-                           float(alpha), float(beta));
+    const size_t es = dtype == KQ_F64 ? 8 : 4;
+    const bool exact = dim % TILE == 0 && rows % KSTEP == 0 && ldx % 4 == 0 &&
+                       reinterpret_cast<uintptr_t>(X) % (4 * es) == 0;
+    const dim3 grid(tiles, tiles), block(GEMM_THREADS);
+    if (dtype == KQ_F64) {
+        auto k = exact ? syrk_kernel<double, true> : syrk_kernel<double, false>;
+        hipLaunchKernelGGL(k, grid, block, 0, st, static_cast<const double*>(X), ldx, int(rows), int(dim),
+                           static_cast<double*>(S), lds, alpha, beta);
+    } else {
+        auto k = exact ? syrk_kernel<float, true> : syrk_kernel<float, false>;
+        hipLaunchKernelGGL(k, grid, block, 0, st, static_cast<const float*>(X), ldx, int(rows), int(dim),
+                           static_cast<float*>(S), lds, float(alpha), float(beta));
+    }
     KQ_LAUNCHED("syrk_kernel");
     return KQ_OK;
 }

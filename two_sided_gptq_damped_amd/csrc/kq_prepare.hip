@@ -86,6 +86,8 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ C,
     constexpr int PW = 16;  // panel width
     __shared__ double L[TILE * P];
     __shared__ double X[TILE * P];
+    __shared__ double rdiag[TILE];  // 1 / L[j][j]
+    __shared__ double colj[64];     // the panel column being eliminated, one entry per lane
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     double* blk = C + int64_t(k) * TILE * dp + int64_t(k) * TILE;
     for (int e = t; e < TILE * TILE; e += 256) {
@@ -118,19 +120,30 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ C,
             double a[PW];
 #pragma unroll
             for (int j = 0; j < PW; ++j) a[j] = (live && c0 + j <= r) ? L[r * P + c0 + j] : 0.0;
+            int fail_col = -1;  // first non-positive pivot of this panel (uniform)
 #pragma unroll
             for (int j = 0; j < PW; ++j) {
                 double d = readlane_f64(a[j], j);
                 if (!(d > 0.0)) {
-                    if (lane == 0 && !failed && *info == 0) *info = k * TILE + c0 + j + 1;
-                    failed = true;
+                    fail_col = fail_col < 0 ? j : fail_col;
                     d = 1.0;
                 }
-                const double piv = __builtin_sqrt(d), inv = 1.0 / piv;
+                // 1/sqrt(d) from the hardware estimate and two Newton steps (each
+                // squares the relative error; the result is within a few ulps)
+                double inv = __builtin_amdgcn_rsq(d);
+                inv = inv * __builtin_fma(-0.5 * d * inv, inv, 1.5);
+                inv = inv * __builtin_fma(-0.5 * d * inv, inv, 1.5);
+                const double piv = d * inv;
+                if (lane == 0) rdiag[c0 + j] = inv;
                 a[j] = lane > j ? a[j] * inv : (lane == j ? piv : a[j]);
+                // column j of the panel rows to every lane through LDS (one wave:
+                // its LDS accesses complete in order, no barrier needed)
+                colj[lane] = a[j];
 #pragma unroll
-                for (int c = j + 1; c < PW; ++c) a[c] = __builtin_fma(-a[j], readlane_f64(a[j], c), a[c]);
+                for (int c = j + 1; c < PW; ++c) a[c] = __builtin_fma(-a[j], colj[c], a[c]);
             }
+            if (fail_col >= 0 && lane == 0 && !failed && *info == 0) *info = k * TILE + c0 + fail_col + 1;
+            failed = failed || fail_col >= 0;
             if (live) {
 #pragma unroll
                 for (int j = 0; j < PW; ++j)
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ C,
             double s = r == c ? 1.0 : 0.0;
 #pragma unroll
             for (int q = 0; q < r; ++q) s = __builtin_fma(-L[(i0 + r) * P + i0 + q], x[q], s);
-            x[r] = s / L[(i0 + r) * P + i0 + r];
+            x[r] = s * rdiag[i0 + r];
         }
 #pragma unroll
         for (int r = 0; r < PW; ++r) X[(i0 + r) * P + i0 + c] = x[r];
