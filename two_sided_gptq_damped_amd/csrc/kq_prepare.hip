@@ -80,21 +80,27 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 // Writes L (zero above the diagonal) back into C and L^{-1} into Dinv[k].  A pivot
 // that is not > 0 records its 1-based position in *info (first failure only) and
 // continues with a unit pivot so the remaining kernels stay finite.
-__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ C, int dp, int k,
-                                                         double* __restrict__ Dinv, int32_t* __restrict__ info) {
-    constexpr int P = TILE + 1;
+constexpr int DP = TILE + 1;  // row stride of the diagonal-block arrays
+struct DiagSmem {
+    double L[TILE * DP];
+    double X[TILE * DP];
+    double rdiag[TILE];  // 1 / L[j][j]
+    double colj[64];     // the panel column being eliminated, one entry per lane
+};
+
+// Factor the diagonal block k held in sm.L (full 64 x 64, lower part used) by
+// the 256 threads of the workgroup; writes L into C and L^{-1} into Dinv[k].
+__device__ __forceinline__ void diag_factor(double* __restrict__ C, int dp, int k, double* __restrict__ Dinv,
+                            int32_t* __restrict__ info, DiagSmem& sm) {
+    constexpr int P = DP;
     constexpr int PW = 16;  // panel width
-    __shared__ double L[TILE * P];
-    __shared__ double X[TILE * P];
-    __shared__ double rdiag[TILE];  // 1 / L[j][j]
-    __shared__ double colj[64];     // the panel column being eliminated, one entry per lane
+    double* const L = sm.L;
+    double* const X = sm.X;
+    double* const rdiag = sm.rdiag;
+    double* const colj = sm.colj;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     double* blk = C + int64_t(k) * TILE * dp + int64_t(k) * TILE;
-    for (int e = t; e < TILE * TILE; e += 256) {
-        const int r = e >> 6, c = e & 63;
-        L[r * P + c] = blk[int64_t(r) * dp + c];
-        X[r * P + c] = 0.0;
-    }
+    for (int e = t; e < TILE * TILE; e += 256) X[(e >> 6) * P + (e & 63)] = 0.0;
     __syncthreads();
     bool failed = false;  // uniform in wave 0, the only writer of *info
     for (int p = 0; p < TILE / PW; ++p) {
@@ -200,6 +206,16 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ C,
     }
 }
 
+// The first diagonal block (the others are factored inside the trailing update
+// of the step before, see potrf_trailing_kernel).
+__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ C, int dp, int k,
+                                                         double* __restrict__ Dinv, int32_t* __restrict__ info) {
+    __shared__ DiagSmem sm;
+    const double* blk = C + int64_t(k) * TILE * dp + int64_t(k) * TILE;
+    for (int e = threadIdx.x; e < TILE * TILE; e += 256) sm.L[(e >> 6) * DP + (e & 63)] = blk[int64_t(e >> 6) * dp + (e & 63)];
+    diag_factor(C, dp, k, Dinv, info, sm);
+}
+
 // C[i][k] <- C[i][k] * Dinv[k]^T for the block rows i > k.
 __global__ __launch_bounds__(GEMM_THREADS) void potrf_panel_kernel(double* __restrict__ C, int dp, int k,
                                                                    const double* __restrict__ Dinv) {
@@ -216,16 +232,30 @@ __global__ __launch_bounds__(GEMM_THREADS) void potrf_panel_kernel(double* __res
 }
 
 // C[i][j] -= C[i][k] C[j][k]^T for k < j <= i.
-__global__ __launch_bounds__(GEMM_THREADS) void potrf_trailing_kernel(double* __restrict__ C, int dp, int k) {
+// C[i][j] -= C[i][k] C[j][k]^T for k < j <= i.  Block (k+1, k+1) instead updates
+// into LDS and goes on to factor it (diag_factor), so the next step's diagonal
+// factorisation runs while the rest of the trailing matrix is updated.
+__global__ __launch_bounds__(GEMM_THREADS) void potrf_trailing_kernel(double* __restrict__ C, int dp, int k,
+                                                                      double* __restrict__ Dinv,
+                                                                      int32_t* __restrict__ info) {
     const int i = k + 1 + blockIdx.y, j = k + 1 + blockIdx.x;
     if (j > i) return;
-    __shared__ GemmSmem<double> sm;
+    __shared__ union {
+        GemmSmem<double> g;
+        DiagSmem d;
+    } sm;
     WaveAcc<double> acc;
     acc.zero();
     const double* A = C + int64_t(i) * TILE * dp + int64_t(k) * TILE;
     const double* B = C + int64_t(j) * TILE * dp + int64_t(k) * TILE;  // B(kk, c) = C[j*64+c][k*64+kk]
-    tile_gemm<double, double, false, true, false>(A, dp, B, dp, TILE, TILE, TILE, sm, acc);
+    tile_gemm<double, double, false, true, false>(A, dp, B, dp, TILE, TILE, TILE, sm.g, acc);
     double* out = C + int64_t(i) * TILE * dp + int64_t(j) * TILE;
+    if (i == k + 1 && j == k + 1) {
+        __syncthreads();  // the product's LDS reads are done before L overwrites them
+        for_each_acc(acc, [&](int r, int c, double v) { sm.d.L[r * DP + c] = out[int64_t(r) * dp + c] - v; });
+        diag_factor(C, dp, k + 1, Dinv, info, sm.d);
+        return;
+    }
     for_each_acc(acc, [&](int r, int c, double v) { out[int64_t(r) * dp + c] -= v; });
 }
 
@@ -335,16 +365,14 @@ kq_status prepare_typed(int64_t d, const T* A, int64_t lda, double damp_rel, T* 
     hipLaunchKernelGGL(build_reversed_kernel<T>, dim3(unsigned((cnt + 255) / 256)), dim3(256), 0, st, A, lda, int(d),
                        dp, trace, damp_rel, C, trace_out, lambda_out);
     KQ_LAUNCHED("build_reversed_kernel");
-    for (int k = 0; k < nt; ++k) {
-        hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, st, C, dp, k, Dinv, info);
-        KQ_LAUNCHED("potrf_diag_kernel");
+    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, st, C, dp, 0, Dinv, info);
+    KQ_LAUNCHED("potrf_diag_kernel");
+    for (int k = 0; k + 1 < nt; ++k) {
         const int rest = nt - k - 1;
-        if (rest > 0) {
-            hipLaunchKernelGGL(potrf_panel_kernel, dim3(rest), dim3(GEMM_THREADS), 0, st, C, dp, k, Dinv);
-            KQ_LAUNCHED("potrf_panel_kernel");
-            hipLaunchKernelGGL(potrf_trailing_kernel, dim3(rest, rest), dim3(GEMM_THREADS), 0, st, C, dp, k);
-            KQ_LAUNCHED("potrf_trailing_kernel");
-        }
+        hipLaunchKernelGGL(potrf_panel_kernel, dim3(rest), dim3(GEMM_THREADS), 0, st, C, dp, k, Dinv);
+        KQ_LAUNCHED("potrf_panel_kernel");
+        hipLaunchKernelGGL(potrf_trailing_kernel, dim3(rest, rest), dim3(GEMM_THREADS), 0, st, C, dp, k, Dinv, info);
+        KQ_LAUNCHED("potrf_trailing_kernel");
     }
     hipLaunchKernelGGL(trtri_diag_kernel, dim3(nt), dim3(256), 0, st, Li, dp, Dinv);
     KQ_LAUNCHED("trtri_diag_kernel");
