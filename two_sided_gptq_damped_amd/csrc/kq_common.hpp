@@ -319,6 +319,89 @@ __device__ void tile_gemm_masked(const T* __restrict__ A, int64_t lda, const T* 
     }
 }
 
+// K-slice depth as a parameter: KS = 16 R deep slices, each thread moving R
+// groups of the 16-deep loader pattern.  Deeper slices carry more matrix-core
+// work per global round trip, which matters when few blocks share a CU and the
+// loads of the next slice are the only latency hiding.
+template <typename T, bool A_KMAJ, bool B_KMAJ, int KS>
+struct LoaderK {
+    static constexpr int R = KS / KSTEP;
+    TileLoader<T, T, A_KMAJ, B_KMAJ, false> g[R];
+    __device__ __forceinline__ void fetch(const T* __restrict__ A, int64_t lda, const T* __restrict__ B, int64_t ldb,
+                                          int k0, int t) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) g[q].fetch(A, lda, B, ldb, k0 + KSTEP * q, TILE, TILE, 0, t);
+    }
+    __device__ __forceinline__ void stash(T* As, T* Bs, int t) const {
+        constexpr int S = LdsStride<T>::value;
+#pragma unroll
+        for (int q = 0; q < R; ++q) g[q].stash(As + KSTEP * q * S, Bs + KSTEP * q * S, t);
+    }
+    template <typename MA, typename MB>
+    __device__ __forceinline__ void apply(int k0, int t, MA ma, MB mb) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const int kq0 = k0 + KSTEP * q;
+            if (!A_KMAJ) {
+                const int r = t >> 2, kq = (t & 3) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!ma(r, kq0 + kq + e)) g[q].ra[e] = T(0);
+            } else {
+                const int k = t >> 4, rq = (t & 15) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!ma(rq + e, kq0 + k)) g[q].ra[e] = T(0);
+            }
+            if (!B_KMAJ) {
+                const int k = t >> 4, cq = (t & 15) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!mb(kq0 + k, cq + e)) g[q].rb[e] = T(0);
+            } else {
+                const int c = t >> 2, kq = (t & 3) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!mb(kq0 + kq + e, c)) g[q].rb[e] = T(0);
+            }
+        }
+    }
+};
+
+template <typename T, int KS>
+struct GemmSmemK {
+    T a[2][KS * LdsStride<T>::value];
+    T b[2][KS * LdsStride<T>::value];
+};
+
+// tile_gemm_masked with KS-deep slices; K must be a multiple of KS.
+template <typename T, int KS, bool A_KMAJ, bool B_KMAJ, typename MA, typename MB>
+__device__ void tile_gemm_masked_k(const T* __restrict__ A, int64_t lda, const T* __restrict__ B, int64_t ldb, int K,
+                                   GemmSmemK<T, KS>& sm, WaveAcc<T>& acc, MA ma, MB mb) {
+    constexpr int S = LdsStride<T>::value;
+    const int t = threadIdx.x & 255, lane = t & 63, w = t >> 6;
+    const int wy = w >> 1, wx = w & 1;
+    LoaderK<T, A_KMAJ, B_KMAJ, KS> ld;
+    const int nk = K / KS;
+    if (nk == 0) return;
+    ld.fetch(A, lda, B, ldb, 0, t);
+    ld.apply(0, t, ma, mb);
+    __syncthreads();
+    ld.stash(sm.a[0], sm.b[0], t);
+    __syncthreads();
+    for (int s = 0; s < nk; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < nk) ld.fetch(A, lda, B, ldb, (s + 1) * KS, t);
+#pragma unroll
+        for (int q = 0; q < KS / KSTEP; ++q) acc.mma(sm.a[cur] + KSTEP * q * S, sm.b[cur] + KSTEP * q * S, wy, wx, lane);
+        if (s + 1 < nk) {
+            ld.apply((s + 1) * KS, t, ma, mb);  // after the products, so the loads overlap them
+            ld.stash(sm.a[cur ^ 1], sm.b[cur ^ 1], t);
+            __syncthreads();
+        }
+    }
+}
+
 // Split-K variant for launch shapes with few blocks and long K ranges: G groups of
 // four waves (blockDim = 256 G) share one 64 x 64 output.  Group g takes the
 // K slices s = g, g + G, ... with its own double-buffered LDS stage, all groups

@@ -458,12 +458,14 @@ __global__ __launch_bounds__(Band<T>::THREADS) void band_stage1_kernel(const T* 
 
 // Stage 2: X[I, J] += sum_{I'} N_B[I', I]^T T1[I', J] for the tiles of diagonals
 // [mid, K1), on 64 x 64 target block (P, Q) of block-diagonal sig = P + Q.
-template <typename T>
+// KS: K-slice depth of the product (16 at the top node, where many blocks share
+// each CU; 32 below, where a block's loads are its only latency hiding).
+template <typename T, int KS>
 __global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T* __restrict__ T1,
                                                                         const T* __restrict__ NB,
                                                                         T* __restrict__ X, int np, int mp, int Mt,
                                                                         int Nt, int K0, int mid, int K1, int sig0) {
-    __shared__ GemmSmem<T> sm;
+    __shared__ GemmSmemK<T, KS> sm;
     const int sig = sig0 + blockIdx.y;
     const int Mb = Mt >> 1, Nb = Nt >> 1;
     const int plo = sig - Nb + 1 > 0 ? sig - Nb + 1 : 0;
@@ -498,7 +500,7 @@ __global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T*
     const T* A = NB + int64_t(kl) * ST * mp + int64_t(I0) * ST;  // A(r, k) = NB[k][r]
     const T* B = T1 + int64_t(kl) * ST * np + int64_t(J0) * ST;
     auto mb = [=](int k, int c) { return t1_valid(kl + (k >> 5), J0 + (c >> 5)); };
-    tile_gemm_masked<T, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
+    tile_gemm_masked_k<T, KS, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
     for_each_acc(acc, [&](int r, int c, T v) {
         if (in_band(r, c)) out[int64_t(r) * np + c] += v;
     });
@@ -574,7 +576,9 @@ struct SolverRun {
         if (sig1 > sigmax) sig1 = sigmax;
         if (sig1 >= sig0) {
             const int width = Mt < Nt ? Mt / 2 : Nt / 2;
-            hipLaunchKernelGGL(band_stage2_kernel<T>, dim3(width, sig1 - sig0 + 1), dim3(Band<T>::THREADS2), 0, st, T1,
+            const bool top = K0 == 0 && K1 == int(L.Mt + L.Nt - 1);
+            auto kern = top ? band_stage2_kernel<T, KSTEP> : band_stage2_kernel<T, 2 * KSTEP>;
+            hipLaunchKernelGGL(kern, dim3(width, sig1 - sig0 + 1), dim3(Band<T>::THREADS2), 0, st, T1,
                                NB, X, int(L.np), int(L.mp), Mt, Nt, K0, mid, K1, sig0);
             KQ_LAUNCHED("band_stage2_kernel");
         }
