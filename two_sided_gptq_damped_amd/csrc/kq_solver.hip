@@ -268,31 +268,54 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
                 }
             }
             __syncthreads();
+            // every thread of the block layout has a twin in the other half of
+            // the workgroup; the pair splits each product's K range in two
             const int nbat = ns - sb < BATCH ? ns - sb : BATCH;
-            if (blk) {
-                for (int u = 0; u < nbat; ++u) {
-                    const T* sa = stg[u][0];
-                    const T* sbm = stg[u][1];
-                    T o[4] = {T(0), T(0), T(0), T(0)};
+            const int kb = (ST / NFG) * fgrp;
+            for (int u = 0; u < nbat; ++u) {
+                const T* sa = stg[u][0];
+                const T* sbm = stg[u][1];
+                T o[4] = {T(0), T(0), T(0), T(0)};
 #pragma unroll 8
-                    for (int k = 0; k < ST; ++k) {
-                        Vec4<T> a4;
-                        a4.load(sa + k * PK + r0);
-                        const T bk = sbm[k * PK + b];
+                for (int k = kb; k < kb + ST / NFG; ++k) {
+                    Vec4<T> a4;
+                    a4.load(sa + k * PK + r0);
+                    const T bk = sbm[k * PK + b];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) o[i] = kfma(a4[i], bk, o[i]);
-                    }
-                    if (sb + u < n1) {
+                    for (int i = 0; i < 4; ++i) o[i] = kfma(a4[i], bk, o[i]);
+                }
+                if (sb + u < n1) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) crow[i] += o[i];
-                    } else {
+                    for (int i = 0; i < 4; ++i) crow[i] += o[i];
+                } else {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) ccol[i] += o[i];
-                    }
+                    for (int i = 0; i < 4; ++i) ccol[i] += o[i];
                 }
             }
         }
-        __syncthreads();  // staged operands consumed before bufA is reused
+        __syncthreads();  // staged operands consumed
+        // the second half's partial sums join the first half's (fixed order)
+        {
+            T* park = reinterpret_cast<T*>(stg);  // 2 x 256 x 4 values: one slice's staging area
+            static_assert(NFG == 2, "two halves");
+            static_assert(2 * ST * PK * sizeof(T) >= 8 * 256 * sizeof(T), "staging area too small");
+            if (!blk) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    park[i * 256 + tb] = crow[i];
+                    park[(4 + i) * 256 + tb] = ccol[i];
+                }
+            }
+            __syncthreads();
+            if (blk) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    crow[i] += park[i * 256 + tb];
+                    ccol[i] += park[(4 + i) * 256 + tb];
+                }
+            }
+            __syncthreads();  // partials read before bufA is reused
+        }
         if (NB && n1 > 0) {
             // column feedback of rowpart inside the tile: strict(N_B[I, I])^T rowpart
             if (blk) {
