@@ -174,20 +174,27 @@ __device__ __forceinline__ void diag_factor(double* __restrict__ C, int dp, int 
     }
     __syncthreads();
     // blocks below the diagonal; T_ij is kept in the (unused) upper triangle of L
+#pragma unroll
     for (int d = 1; d < TILE / PW; ++d) {
         const int nblk = TILE / PW - d;
-        for (int e = t; e < nblk * PW * PW; e += 256) {
+#pragma unroll
+        for (int e0 = 0; e0 < nblk * PW * PW; e0 += 256) {
+            const int e = e0 + t;
             const int jb = e >> 8, ib = jb + d, rr = (e >> 4) & 15, cc = e & 15;
             const int row = PW * ib + rr, col = PW * jb + cc;
             double acc[4] = {0.0, 0.0, 0.0, 0.0};
-            for (int q = PW * jb; q < PW * ib; q += 4) {
+#pragma unroll
+            for (int q4 = 0; q4 < PW * d; q4 += 4) {
+                const int q = PW * jb + q4;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc[u] = __builtin_fma(L[row * P + q + u], X[(q + u) * P + col], acc[u]);
             }
             L[(PW * jb + rr) * P + PW * ib + cc] = (acc[0] + acc[1]) + (acc[2] + acc[3]);  // T_ij at the mirrored block
         }
         __syncthreads();
-        for (int e = t; e < nblk * PW * PW; e += 256) {
+#pragma unroll
+        for (int e0 = 0; e0 < nblk * PW * PW; e0 += 256) {
+            const int e = e0 + t;
             const int jb = e >> 8, ib = jb + d, rr = (e >> 4) & 15, cc = e & 15;
             double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -212,7 +219,17 @@ __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ C,
                                                          double* __restrict__ Dinv, int32_t* __restrict__ info) {
     __shared__ DiagSmem sm;
     const double* blk = C + int64_t(k) * TILE * dp + int64_t(k) * TILE;
-    for (int e = threadIdx.x; e < TILE * TILE; e += 256) sm.L[(e >> 6) * DP + (e & 63)] = blk[int64_t(e >> 6) * dp + (e & 63)];
+    double v[TILE * TILE / 256];  // all loads in flight before the LDS stores wait on them
+#pragma unroll
+    for (int q = 0; q < TILE * TILE / 256; ++q) {
+        const int e = threadIdx.x + 256 * q;
+        v[q] = blk[int64_t(e >> 6) * dp + (e & 63)];
+    }
+#pragma unroll
+    for (int q = 0; q < TILE * TILE / 256; ++q) {
+        const int e = threadIdx.x + 256 * q;
+        sm.L[(e >> 6) * DP + (e & 63)] = v[q];
+    }
     diag_factor(C, dp, k, Dinv, info, sm);
 }
 
@@ -248,11 +265,24 @@ __global__ __launch_bounds__(GEMM_THREADS) void potrf_trailing_kernel(double* __
     acc.zero();
     const double* A = C + int64_t(i) * TILE * dp + int64_t(k) * TILE;
     const double* B = C + int64_t(j) * TILE * dp + int64_t(k) * TILE;  // B(kk, c) = C[j*64+c][k*64+kk]
-    tile_gemm<double, double, false, true, false>(A, dp, B, dp, TILE, TILE, TILE, sm.g, acc);
     double* out = C + int64_t(i) * TILE * dp + int64_t(j) * TILE;
-    if (i == k + 1 && j == k + 1) {
+    const bool diag = i == k + 1 && j == k + 1;
+    double pre[WaveAcc<double>::NREG];  // the diagonal block, loaded while the product runs
+    if (diag) {
+        const int t = threadIdx.x & 255, lane = t & 63, w = t >> 6;
+#pragma unroll
+        for (int r = 0; r < WaveAcc<double>::NREG; ++r)
+            pre[r] = out[int64_t((w >> 1) * 32 + WaveAcc<double>::row(r, lane)) * dp + (w & 1) * 32 +
+                         WaveAcc<double>::col(r, lane)];
+    }
+    tile_gemm<double, double, false, true, false>(A, dp, B, dp, TILE, TILE, TILE, sm.g, acc);
+    if (diag) {
         __syncthreads();  // the product's LDS reads are done before L overwrites them
-        for_each_acc(acc, [&](int r, int c, double v) { sm.d.L[r * DP + c] = out[int64_t(r) * dp + c] - v; });
+        const int t = threadIdx.x & 255, lane = t & 63, w = t >> 6;
+#pragma unroll
+        for (int r = 0; r < WaveAcc<double>::NREG; ++r)
+            sm.d.L[((w >> 1) * 32 + WaveAcc<double>::row(r, lane)) * DP + (w & 1) * 32 + WaveAcc<double>::col(r, lane)] =
+                pre[r] - acc.get(r);
         diag_factor(C, dp, k + 1, Dinv, info, sm.d);
         return;
     }
