@@ -3,7 +3,9 @@
 One step = one pass of the whole path over one layer of synthetic input that
 is already resident in HBM: K-FAC factor accumulation for A (4096 activation
 rows) and B (4096 gradient rows), damped factor preparation of both, per-row
-scales, two-sided GPTQ (2-bit grid) and the proxy loss.  ``value`` is weights
+scales, two-sided GPTQ (2-bit grid) and the proxy loss.  The B factor chain runs
+on a second stream beside the A chain; ``serial_breakdown_ms`` times the same
+calls one after another on one stream.  ``value`` is weights
 per second of the whole step (m n / step time).  The core solver alone
 (kron_quantize with factors and scales resident, the pages' "core algorithm"
 timing) is reported under ``core``.
@@ -118,27 +120,50 @@ def main() -> int:
     loss = torch.empty(1, dtype=torch.float64, device=dev)
     names = ["factor", "prepare", "scales", "quantize", "loss"]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()  # default priority
+    a_done = torch.cuda.Event()
 
     def step(record=False):
+        """One layer.  The B chain (its product, then its prepare) runs on a
+        second stream once the A product is done, beside the A chain; the solver
+        waits for both.  Step k + 1's B chain starts after step k's loss, since
+        it waits on an event recorded later on the in-order main stream."""
         if record:
             ev[0].record()
         kq.kron_factor_accumulate(act, A, 1.0 / rows, 0.0)
-        kq.kron_factor_accumulate(grad, B, 1.0 / rows, 0.0)
+        a_done.record(main)
+        side.wait_event(a_done)
+        with torch.cuda.stream(side):
+            kq.kron_factor_accumulate(grad, B, 1.0 / rows, 0.0)
+            kq.kron_prepare(B, damp, UB, ws_pb, trace_out=trB, lambda_out=lamB, info=infoB)
+        kq.kron_prepare(A, damp, UA, ws_pa, trace_out=trA, lambda_out=lamA, info=infoA)
+        kq.kron_row_scales(W, bits, True, scales)
+        main.wait_stream(side)
         if record:
             ev[1].record()
-        kq.kron_prepare(A, damp, UA, ws_pa, trace_out=trA, lambda_out=lamA, info=infoA)
-        kq.kron_prepare(B, damp, UB, ws_pb, trace_out=trB, lambda_out=lamB, info=infoB)
-        if record:
-            ev[2].record()
-        kq.kron_row_scales(W, bits, True, scales)
-        if record:
-            ev[3].record()
         kq.kron_quantize(W, UA, UB, bits, True, scales, codes, V, ws_q)
         if record:
-            ev[4].record()
+            ev[2].record()
         kq.kron_loss(W, V, A, B, damp, loss, ws_l)
         if record:
-            ev[5].record()
+            ev[3].record()
+
+    def serial_step():
+        """The same calls one after another on one stream, timed per phase."""
+        ev[0].record()
+        kq.kron_factor_accumulate(act, A, 1.0 / rows, 0.0)
+        kq.kron_factor_accumulate(grad, B, 1.0 / rows, 0.0)
+        ev[1].record()
+        kq.kron_prepare(A, damp, UA, ws_pa, trace_out=trA, lambda_out=lamA, info=infoA)
+        kq.kron_prepare(B, damp, UB, ws_pb, trace_out=trB, lambda_out=lamB, info=infoB)
+        ev[2].record()
+        kq.kron_row_scales(W, bits, True, scales)
+        ev[3].record()
+        kq.kron_quantize(W, UA, UB, bits, True, scales, codes, V, ws_q)
+        ev[4].record()
+        kq.kron_loss(W, V, A, B, damp, loss, ws_l)
+        ev[5].record()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -147,16 +172,22 @@ def main() -> int:
     assert infoA.item() == 0 and infoB.item() == 0, "factor not positive definite"
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    phase = {k: [] for k in names}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(record=True)  # events are re-recorded each step; the last step's remain
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for i, k in enumerate(names):
-        phase[k].append(ev[i].elapsed_time(ev[i + 1]))
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    overlapped = {"factors_prepares_scales": ev[0].elapsed_time(ev[1]),
+                  "quantize": ev[1].elapsed_time(ev[2]), "loss": ev[2].elapsed_time(ev[3])}
+
+    serial = {k: [] for k in names}
+    for _ in range(3):
+        serial_step()
+        torch.cuda.synchronize()
+        for i, k in enumerate(names):
+            serial[k].append(ev[i].elapsed_time(ev[i + 1]))
 
     # core solver timing: kron_quantize alone, repeated, events on torch's stream
     qs, qe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -189,10 +220,11 @@ def main() -> int:
                         f"A, B from {rows} activation / gradient rows with lognormal channel scales; "
                         f"damping 0.01; {bits}-bit grid, per-row scales",
             "m": m, "n": n, "bits": bits, "calibration_rows": rows,
-            "step": "factor_accumulate(A), factor_accumulate(B), prepare(A), prepare(B), row_scales, "
-                    "quantize, loss",
+            "step": "[factor_accumulate(A), prepare(A), row_scales] beside [factor_accumulate(B), prepare(B)] "
+                    "on a second stream, then quantize, loss",
         },
-        "breakdown_ms": {k: float(np.median(v)) for k, v in phase.items()},
+        "breakdown_ms": overlapped,
+        "serial_breakdown_ms": {k: float(np.median(v)) for k, v in serial.items()},
         "core": {
             "what": "kron_quantize only, factors and scales resident (median of repeats)",
             "ms": core_ms,

@@ -207,7 +207,10 @@ def test_factor_accumulate(rows, dim):
         assert np.max(np.abs(got - want)) <= tol * np.max(np.abs(want))
 
 
-@pytest.mark.parametrize("m,n,bidentity", [(32, 32, False), (100, 70, False), (64, 130, True)])
+# (n <= m: the m x m form E A_d E^T; n > m: the n x n form E^T B_d E; several
+# tiles of the symmetric product with ragged edges; B = I)
+@pytest.mark.parametrize("m,n,bidentity", [(32, 32, False), (100, 70, False), (200, 130, False), (130, 300, False),
+                                           (256, 256, False), (64, 130, True), (300, 90, True)])
 def test_loss_matches_oracle(m, n, bidentity):
     say("loss", m, n)
     c = synth.spectral(m, n, config=2)

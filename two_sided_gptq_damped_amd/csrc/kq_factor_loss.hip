@@ -1,4 +1,6 @@
 // K-FAC factor accumulation, proxy loss and scale helper for gfx950.
+#include <algorithm>
+
 #include "kq_common.hpp"
 
 namespace kq {
@@ -55,9 +57,17 @@ kq_status factor_dispatch(kq_dtype dtype, int64_t rows, int64_t dim, const void*
 }
 
 // ------------------------------------------------------------------ the loss
-// tr(B_d E A_d E^T) = sum_ij (B_d E)_ij (E A_d)_ij with E = V - W (A_d, B_d
-// symmetric), and B_d E = B E + lam_B E, E A_d = E A + lam_A E.  Products in fp64
-// on matrix cores over zero-padded fp64 copies; a two-pass fixed-order reduction.
+// tr(B_d E A_d E^T) with E = V - W, A_d = A + lam_A I, B_d = B + lam_B I, in fp64
+// on matrix cores over zero-padded fp64 copies (the damping folded into the
+// copies' diagonals).  A_d and B_d are symmetric, so with G = E A_d E^T (m x m)
+// and H = E^T B_d E (n x n), both symmetric,
+//   tr(B_d E A_d E^T) = sum_ij (B_d)_ij G_ij = sum_ij (A_d)_ij H_ij.
+// The cheaper form is taken: one full product (E A_d, or B_d E) and the upper
+// triangle of tiles of the symmetric one, each tile's weighted sum formed as it
+// leaves the matrix cores (off-diagonal tiles count twice).  Flops
+// m n (2 n + m) for G when n <= m, m n (2 m + n) for H otherwise, against
+// 2 m n (m + n) for the two full products B_d E and E A_d.  B = I needs only
+// sum_ij E_ij (E A_d)_ij.  Partial sums per tile, then one fixed-order pass.
 
 template <typename TIn>
 __global__ void diag_trace_kernel(const TIn* __restrict__ A, int64_t lda, int d, double* __restrict__ out) {
@@ -73,10 +83,13 @@ __global__ void diag_trace_kernel(const TIn* __restrict__ A, int64_t lda, int d,
     if (threadIdx.x == 0) *out = red[0];
 }
 
-// dst (rp x cp, fp64) = src (rows x cols) zero-padded; with sub != nullptr, dst = src - sub.
+// dst (rp x cp, fp64) = src (rows x cols) zero-padded; with sub != nullptr,
+// dst = src - sub; with trace != nullptr, damp_rel * trace / rows is added on the
+// diagonal of the square src.
 template <typename TIn>
 __global__ void pad_copy_kernel(const TIn* __restrict__ src, int64_t lds, const TIn* __restrict__ sub, int64_t ldsub,
-                                int rows, int cols, int rp, int cp, double* __restrict__ dst) {
+                                int rows, int cols, int rp, int cp, const double* __restrict__ trace, double damp_rel,
+                                double* __restrict__ dst) {
     const int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
     if (idx >= int64_t(rp) * cp) return;
     const int r = int(idx / cp), c = int(idx % cp);
@@ -84,6 +97,7 @@ __global__ void pad_copy_kernel(const TIn* __restrict__ src, int64_t lds, const 
     if (r < rows && c < cols) {
         v = double(src[int64_t(r) * lds + c]);
         if (sub) v -= double(sub[int64_t(r) * ldsub + c]);
+        if (trace && r == c) v += damp_rel * (*trace) / rows;
     }
     dst[idx] = v;
 }
@@ -102,53 +116,85 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_nn_f64_kernel(const double*
     for_each_acc(acc, [&](int r, int c, double v) { out[int64_t(r) * ldc + c] = v; });
 }
 
-// Partial sums of (P + lamB E)(Q + lamA E), one per block, in a fixed order.
-__global__ void loss_partial_kernel(const double* __restrict__ P, const double* __restrict__ Q,
-                                    const double* __restrict__ E, int64_t count, const double* __restrict__ trA, int n,
-                                    const double* __restrict__ trB, int m, double damp_rel, int b_identity,
-                                    double* __restrict__ partial) {
-    __shared__ double red[256];
-    const double lamA = damp_rel * (*trA) / n;
-    const double lamB = b_identity ? 0.0 : damp_rel * (*trB) / m;
-    double s = 0.0;
-    for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < count; i += int64_t(gridDim.x) * blockDim.x) {
-        const double e = E[i];
-        const double p = b_identity ? e : P[i] + lamB * e;
-        s += p * (Q[i] + lamA * e);
-    }
+// Fixed-order sum of the 256 per-thread values of a workgroup.
+__device__ __forceinline__ double block_sum_256(double s, double* red) {
     red[threadIdx.x] = s;
     __syncthreads();
-    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    for (int w = 128; w > 0; w >>= 1) {
         if (int(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
-    if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+    return red[0];
+}
+
+// One tile (I <= J) of the symmetric product S = X^T-or-X times E, weighted by
+// the damped factor F:  partial[tile] = w sum_rc F[I r][J c] S_IJ[r][c], w = 1 on
+// the diagonal and 2 above it.
+//   ROWS (G = Q E^T, Q = E A_d):   S_IJ(r, c) = sum_k Q[I r][k] E[J c][k],  K = np
+//   !ROWS (H = P^T E, P = B_d E):  S_IJ(r, c) = sum_k P[k][I r] E[k][J c],  K = mp
+// Tiles are numbered J (J + 1) / 2 + I over the upper triangle.
+template <bool ROWS>
+__global__ __launch_bounds__(GEMM_THREADS) void loss_sym_kernel(const double* __restrict__ X,
+                                                                const double* __restrict__ E, int ld, int K,
+                                                                const double* __restrict__ F, int ldf,
+                                                                double* __restrict__ partial) {
+    __shared__ GemmSmem<double> sm;
+    __shared__ double red[GEMM_THREADS];
+    const int b = blockIdx.x;
+    int J = int((sqrt(8.0 * b + 1.0) - 1.0) * 0.5);
+    while (J * (J + 1) / 2 > b) --J;
+    while ((J + 1) * (J + 2) / 2 <= b) ++J;
+    const int I = b - J * (J + 1) / 2;
+    WaveAcc<double> acc;
+    acc.zero();
+    if (ROWS)
+        tile_gemm<double, double, false, true, false>(X + int64_t(I) * TILE * ld, ld, E + int64_t(J) * TILE * ld, ld,
+                                                      TILE, TILE, K, sm, acc);
+    else
+        tile_gemm<double, double, true, false, false>(X + int64_t(I) * TILE, ld, E + int64_t(J) * TILE, ld, TILE, TILE,
+                                                      K, sm, acc);
+    const double* f = F + int64_t(I) * TILE * ldf + int64_t(J) * TILE;
+    double s = 0.0;
+    for_each_acc(acc, [&](int r, int c, double v) { s = __builtin_fma(f[int64_t(r) * ldf + c], v, s); });
+    const double tot = block_sum_256(s, red);
+    if (threadIdx.x == 0) partial[b] = I == J ? tot : 2.0 * tot;
+}
+
+// B = I: partial sums of E * Q (Q = E A_d), one per block, in a fixed order.
+__global__ void loss_partial_kernel(const double* __restrict__ Q, const double* __restrict__ E, int64_t count,
+                                    double* __restrict__ partial) {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < count; i += int64_t(gridDim.x) * blockDim.x)
+        s = __builtin_fma(E[i], Q[i], s);
+    const double tot = block_sum_256(s, red);
+    if (threadIdx.x == 0) partial[blockIdx.x] = tot;
 }
 
 __global__ void loss_final_kernel(const double* __restrict__ partial, int count, double* __restrict__ out) {
     __shared__ double red[256];
     double s = 0.0;
     for (int i = threadIdx.x; i < count; i += blockDim.x) s += partial[i];
-    red[threadIdx.x] = s;
-    __syncthreads();
-    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-        if (int(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) *out = red[0];
+    const double tot = block_sum_256(s, red);
+    if (threadIdx.x == 0) *out = tot;
 }
 
 constexpr int LOSS_BLOCKS = 1024;
 
 struct LossLayout {
     int64_t mp, np;
-    size_t off_E, off_P, off_Q, off_A, off_B, off_scal, bytes;
+    int npart;  // partial sums: tiles of the symmetric product, or LOSS_BLOCKS
+    bool rows;  // G = E A_d E^T (m x m) rather than H = E^T B_d E (n x n)
+    size_t off_E, off_Q, off_A, off_B, off_scal, bytes;
 };
 
 LossLayout loss_layout(int64_t m, int64_t n) {
     LossLayout L;
     L.mp = round_up(m, TILE);
     L.np = round_up(n, TILE);
+    L.rows = n <= m;
+    const int64_t t = (L.rows ? L.mp : L.np) / TILE;
+    L.npart = int(std::max<int64_t>(LOSS_BLOCKS, t * (t + 1) / 2));
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -156,11 +202,10 @@ LossLayout loss_layout(int64_t m, int64_t n) {
         return o;
     };
     L.off_E = take(size_t(L.mp) * L.np * 8);
-    L.off_P = take(size_t(L.mp) * L.np * 8);
     L.off_Q = take(size_t(L.mp) * L.np * 8);
     L.off_A = take(size_t(L.np) * L.np * 8);
     L.off_B = take(size_t(L.mp) * L.mp * 8);
-    L.off_scal = take((LOSS_BLOCKS + 8) * 8);
+    L.off_scal = take((size_t(L.npart) + 8) * 8);
     L.bytes = off;
     return L;
 }
@@ -173,7 +218,6 @@ kq_status loss_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T* V, 
     const LossLayout L = loss_layout(m, n);
     char* base = static_cast<char*>(ws);
     double* E = reinterpret_cast<double*>(base + L.off_E);
-    double* P = reinterpret_cast<double*>(base + L.off_P);
     double* Q = reinterpret_cast<double*>(base + L.off_Q);
     double* Ap = reinterpret_cast<double*>(base + L.off_A);
     double* Bp = reinterpret_cast<double*>(base + L.off_B);
@@ -183,30 +227,46 @@ kq_status loss_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T* V, 
     auto blocks = [](int64_t count) { return dim3(unsigned((count + 255) / 256)); };
 
     hipLaunchKernelGGL(pad_copy_kernel<T>, blocks(int64_t(mp) * np), dim3(256), 0, st, V, ldv, W, ldw, int(m), int(n),
-                       mp, np, E);
-    KQ_LAUNCHED("pad_copy_kernel");
-    hipLaunchKernelGGL(pad_copy_kernel<T>, blocks(int64_t(np) * np), dim3(256), 0, st, A, lda, (const T*)nullptr,
-                       int64_t(0), int(n), int(n), np, np, Ap);
+                       mp, np, (const double*)nullptr, 0.0, E);
     KQ_LAUNCHED("pad_copy_kernel");
     hipLaunchKernelGGL(diag_trace_kernel<T>, dim3(1), dim3(1024), 0, st, A, lda, int(n), trA);
     KQ_LAUNCHED("diag_trace_kernel");
-    if (B) {
-        hipLaunchKernelGGL(pad_copy_kernel<T>, blocks(int64_t(mp) * mp), dim3(256), 0, st, B, ldb, (const T*)nullptr,
-                           int64_t(0), int(m), int(m), mp, mp, Bp);
-        KQ_LAUNCHED("pad_copy_kernel");
+    hipLaunchKernelGGL(pad_copy_kernel<T>, blocks(int64_t(np) * np), dim3(256), 0, st, A, lda, (const T*)nullptr,
+                       int64_t(0), int(n), int(n), np, np, trA, damp_rel, Ap);
+    KQ_LAUNCHED("pad_copy_kernel");
+    int nparts = LOSS_BLOCKS;
+    if (!B) {
+        hipLaunchKernelGGL(gemm_nn_f64_kernel, dim3(np / TILE, mp / TILE), dim3(GEMM_THREADS), 0, st, E, np, Ap, np, Q,
+                           np, np);
+        KQ_LAUNCHED("gemm_nn_f64_kernel");
+        hipLaunchKernelGGL(loss_partial_kernel, dim3(LOSS_BLOCKS), dim3(256), 0, st, Q, E, int64_t(mp) * np, partial);
+        KQ_LAUNCHED("loss_partial_kernel");
+    } else {
         hipLaunchKernelGGL(diag_trace_kernel<T>, dim3(1), dim3(1024), 0, st, B, ldb, int(m), trB);
         KQ_LAUNCHED("diag_trace_kernel");
-        hipLaunchKernelGGL(gemm_nn_f64_kernel, dim3(np / TILE, mp / TILE), dim3(GEMM_THREADS), 0, st, Bp, mp, E, np, P,
-                           np, mp);
-        KQ_LAUNCHED("gemm_nn_f64_kernel");
+        hipLaunchKernelGGL(pad_copy_kernel<T>, blocks(int64_t(mp) * mp), dim3(256), 0, st, B, ldb, (const T*)nullptr,
+                           int64_t(0), int(m), int(m), mp, mp, trB, damp_rel, Bp);
+        KQ_LAUNCHED("pad_copy_kernel");
+        if (L.rows) {  // Q = E A_d, then G = Q E^T weighted by B_d
+            hipLaunchKernelGGL(gemm_nn_f64_kernel, dim3(np / TILE, mp / TILE), dim3(GEMM_THREADS), 0, st, E, np, Ap,
+                               np, Q, np, np);
+            KQ_LAUNCHED("gemm_nn_f64_kernel");
+            const int t = mp / TILE;
+            nparts = t * (t + 1) / 2;
+            hipLaunchKernelGGL(loss_sym_kernel<true>, dim3(nparts), dim3(GEMM_THREADS), 0, st, Q, E, np, np, Bp, mp,
+                               partial);
+        } else {  // Q = B_d E, then H = Q^T E weighted by A_d
+            hipLaunchKernelGGL(gemm_nn_f64_kernel, dim3(np / TILE, mp / TILE), dim3(GEMM_THREADS), 0, st, Bp, mp, E,
+                               np, Q, np, mp);
+            KQ_LAUNCHED("gemm_nn_f64_kernel");
+            const int t = np / TILE;
+            nparts = t * (t + 1) / 2;
+            hipLaunchKernelGGL(loss_sym_kernel<false>, dim3(nparts), dim3(GEMM_THREADS), 0, st, Q, E, np, mp, Ap, np,
+                               partial);
+        }
+        KQ_LAUNCHED("loss_sym_kernel");
     }
-    hipLaunchKernelGGL(gemm_nn_f64_kernel, dim3(np / TILE, mp / TILE), dim3(GEMM_THREADS), 0, st, E, np, Ap, np, Q, np,
-                       np);
-    KQ_LAUNCHED("gemm_nn_f64_kernel");
-    hipLaunchKernelGGL(loss_partial_kernel, dim3(LOSS_BLOCKS), dim3(256), 0, st, P, Q, E, int64_t(mp) * np, trA,
-                       int(n), trB, int(m), damp_rel, B ? 0 : 1, partial);
-    KQ_LAUNCHED("loss_partial_kernel");
-    hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(256), 0, st, partial, LOSS_BLOCKS, loss_dev);
+    hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(256), 0, st, partial, nparts, loss_dev);
     KQ_LAUNCHED("loss_final_kernel");
     return KQ_OK;
 }

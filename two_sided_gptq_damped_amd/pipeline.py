@@ -9,13 +9,19 @@ from the calibration data, factor them, run the core algorithm):
     s = max |W_row| / (2^(bits-1) - 1)
     codes, V = two-sided GPTQ(W, U_A, U_B, s)
     loss = tr(B_d (V - W) A_d (V - W)^T)
+
+The two factor chains (accumulate, then prepare) are independent until the
+solver needs both, and a prepare is a long chain of small dependent launches
+(one diagonal block per step).  quantize_layer therefore runs the B chain on a
+second stream, started once the A product is done, so that it fills the device
+beside the A chain; the solver waits for both.
 """
 from __future__ import annotations
 
 import torch
 
-from . import (KQ_OP_LOSS, KQ_OP_PREPARE, KQ_OP_QUANTIZE, kron_factor_accumulate, kron_loss, kron_prepare,
-               kron_quantize, kron_row_scales, workspace)
+from . import (KQ_OP_LOSS, KQ_OP_PREPARE, KQ_OP_QUANTIZE, KronError, kron_factor_accumulate, kron_loss,
+               kron_prepare, kron_quantize, kron_row_scales, workspace)
 
 
 def factor(X: torch.Tensor) -> torch.Tensor:
@@ -24,15 +30,17 @@ def factor(X: torch.Tensor) -> torch.Tensor:
     return kron_factor_accumulate(X, S, 1.0 / X.shape[0], 0.0)
 
 
-def prepare(A: torch.Tensor, damp_rel: float):
-    """(U, trace, lambda) for the damped factor; raises KronError if not PD."""
+def prepare(A: torch.Tensor, damp_rel: float, info: torch.Tensor | None = None):
+    """(U, trace, lambda) for the damped factor.  With info=None the call waits
+    and raises KronError if the damped factor is not PD; otherwise it stays
+    asynchronous and info[0] receives 0 or the failing pivot (1-based)."""
     d = A.shape[0]
     U = torch.empty_like(A)
     tr = torch.empty(1, dtype=torch.float64, device=A.device)
     lam = torch.empty(1, dtype=torch.float64, device=A.device)
     ws = workspace(KQ_OP_PREPARE, A.dtype, d, 0, A.device)
-    kron_prepare(A, damp_rel, U, ws, trace_out=tr, lambda_out=lam)
-    return U, tr, lam
+    kron_prepare(A, damp_rel, U, ws, trace_out=tr, lambda_out=lam, info=info)
+    return U, tr, lam  # ws goes back to this stream's pool: stream-ordered reuse
 
 
 def quantize(W, U_A, U_B, bits, per_row, scales=None, ws=None):
@@ -57,13 +65,30 @@ def loss(W, V, A, B, damp_rel):
 
 
 def quantize_layer(W, act, grad, bits, per_row=True, damp_rel=0.01, two_sided=True):
-    """Run the whole path for one layer.  act: N x n activation rows, grad: N x m gradient rows."""
+    """Run the whole path for one layer.  act: N x n activation rows, grad: N x m gradient rows.
+    Raises KronError if a damped factor is not positive definite."""
+    main = torch.cuda.current_stream(W.device)
+    info = torch.zeros(2, dtype=torch.int32, device=W.device)
     A = factor(act)
-    U_A, trA, _ = prepare(A, damp_rel)
     B = U_B = trB = None
     if two_sided:
-        B = factor(grad)
-        U_B, trB, _ = prepare(B, damp_rel)
+        side = torch.cuda.Stream(W.device)
+        side.wait_stream(main)  # the A product (and every input) is ready
+        with torch.cuda.stream(side):
+            B = factor(grad)
+            U_B, trB, _ = prepare(B, damp_rel, info[1:])
+        # blocks shared by the two streams are not reused before both are done with them
+        for t in (grad, info):
+            t.record_stream(side)
+        for t in (B, U_B, trB):
+            t.record_stream(main)
+    U_A, trA, _ = prepare(A, damp_rel, info[:1])
+    if two_sided:
+        main.wait_stream(side)
+    bad = info.cpu()
+    for name, k in (("A", int(bad[0])), ("B", int(bad[1]))):
+        if k != 0:
+            raise KronError(2, f"kron_prepare: damped factor {name} is not positive definite (pivot step {k})")
     codes, V, scales = quantize(W, U_A, U_B, bits, per_row)
     return dict(A=A, B=B, U_A=U_A, U_B=U_B, trace_A=trA, trace_B=trB, codes=codes, V=V, scales=scales,
                 loss=loss(W, V, A, B, damp_rel))
