@@ -68,6 +68,15 @@ kq_status factor_dispatch(kq_dtype dtype, int64_t rows, int64_t dim, const void*
 // m n (2 n + m) for G when n <= m, m n (2 m + n) for H otherwise, against
 // 2 m n (m + n) for the two full products B_d E and E A_d.  B = I needs only
 // sum_ij E_ij (E A_d)_ij.  Partial sums per tile, then one fixed-order pass.
+//
+// Every product reads its left operand k-major (E through its transpose E^T,
+// B_d as itself, being symmetric) and its right operand row-major, so both
+// tiles arrive in LDS in the order the matrix cores read them.  The full
+// product uses 128 x 128 output blocks: half the operand traffic per flop of a
+// 64 x 64 block, which is what an fp64 product of this size is short of.  (The
+// symmetric product keeps 64 x 64 tiles: its triangle of 128 x 128 tiles is too
+// few to spread evenly over the CUs, and splitting their K ranges to even it out
+// scatters the blocks over the operands and loses the shared cache lines.)
 
 template <typename TIn>
 __global__ void diag_trace_kernel(const TIn* __restrict__ A, int64_t lda, int d, double* __restrict__ out) {
@@ -102,22 +111,138 @@ __global__ void pad_copy_kernel(const TIn* __restrict__ src, int64_t lds, const 
     dst[idx] = v;
 }
 
-// C = A B for padded row-major fp64 operands (M x K times K x N), 64 x 64 tiles.
-__global__ __launch_bounds__(GEMM_THREADS) void gemm_nn_f64_kernel(const double* __restrict__ A, int lda,
-                                                                   const double* __restrict__ B, int ldb,
-                                                                   double* __restrict__ C, int ldc, int K) {
-    __shared__ GemmSmem<double> sm;
+// dstT (cp x rp, fp64) = (src - sub)^T zero-padded, through a 32 x 32 LDS tile
+// so that reads and writes are both row-contiguous.  Block (32, 8), grid
+// (cp / 32, rp / 32).
+template <typename TIn>
+__global__ void pad_diff_transpose_kernel(const TIn* __restrict__ src, int64_t lds, const TIn* __restrict__ sub,
+                                          int64_t ldsub, int rows, int cols, int rp, double* __restrict__ dstT) {
+    __shared__ double tile[32][33];
+    const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32, tx = threadIdx.x, ty = threadIdx.y;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = r0 + ty + 8 * q, c = c0 + tx;
+        double v = 0.0;
+        if (r < rows && c < cols) v = double(src[int64_t(r) * lds + c]) - double(sub[int64_t(r) * ldsub + c]);
+        tile[ty + 8 * q][tx] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = c0 + ty + 8 * q;
+        dstT[int64_t(c) * rp + r0 + tx] = tile[tx][ty + 8 * q];
+    }
+}
+
+// C (M x N) = At^T B with At K x M and B K x N row-major fp64, M, N multiples of
+// 128 and K of 16.  One 256-thread workgroup per 128 x 128 block, each wave a
+// 64 x 64 quarter (4 x 4 v_mfma_f64_16x16x4 blocks), K in 16-deep slices through
+// double-buffered LDS, both operands stored k-major.
+constexpr int BIG = 128;
+constexpr int BIG_S = BIG + 16;  // LDS row stride: rows k and k + 1 start 32 banks apart
+
+struct __attribute__((aligned(16))) BigSmem {
+    double a[2][KSTEP * BIG_S];
+    double b[2][KSTEP * BIG_S];
+};
+
+// acc += At[k0:k1, a-cols]^T B[k0:k1, b-cols] for one 128 x 128 block; At and B
+// point at the block's first column, rows k are ld apart.  All 256 threads call
+// it (it contains barriers); k1 - k0 is a multiple of 16.
+__device__ __forceinline__ void big_mma(const double* __restrict__ a0, int lda, const double* __restrict__ b0,
+                                        int ldb, int k0, int k1, BigSmem& sm, f64x4 (&acc)[4][4]) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int wy = w >> 1, wx = w & 1;
+    const int lk = t >> 4, lq = (t & 15) * 8;  // loader: slice row lk, 8 consecutive columns from lq
+    f64x2 ra[4], rb[4];
+    auto fetch = [&](int k) {
+        const f64x2* pa = reinterpret_cast<const f64x2*>(a0 + int64_t(k + lk) * lda + lq);
+        const f64x2* pb = reinterpret_cast<const f64x2*>(b0 + int64_t(k + lk) * ldb + lq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ra[e] = pa[e];
+            rb[e] = pb[e];
+        }
+    };
+    auto stash = [&](int buf) {
+        f64x2* sa = reinterpret_cast<f64x2*>(sm.a[buf] + lk * BIG_S + lq);
+        f64x2* sb = reinterpret_cast<f64x2*>(sm.b[buf] + lk * BIG_S + lq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sa[e] = ra[e];
+            sb[e] = rb[e];
+        }
+    };
+    const int nk = (k1 - k0) / KSTEP;
+    fetch(k0);
+    __syncthreads();  // earlier readers of sm are done
+    stash(0);
+    __syncthreads();
+    const int kr = lane >> 4, ix = lane & 15;
+    for (int s = 0; s < nk; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < nk) fetch(k0 + (s + 1) * KSTEP);
+        const double* As = sm.a[cur];
+        const double* Bs = sm.b[cur];
+#pragma unroll
+        for (int kk = 0; kk < KSTEP; kk += 4) {
+            double av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                av[i] = As[(kk + kr) * BIG_S + wy * 64 + 16 * i + ix];
+                bv[i] = Bs[(kk + kr) * BIG_S + wx * 64 + 16 * i + ix];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+        if (s + 1 < nk) {
+            stash(cur ^ 1);
+            __syncthreads();
+        }
+    }
+}
+
+__device__ __forceinline__ void big_zero(f64x4 (&acc)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0;
+}
+
+// Visit the accumulators with their block coordinates: D register r of a 16 x 16
+// block sits at row lane / 16 + 4 r, column lane % 16.
+template <typename Fn>
+__device__ __forceinline__ void big_for_each(const f64x4 (&acc)[4][4], Fn&& fn) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wy = w >> 1, wx = w & 1, kr = lane >> 4, ix = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) fn(wy * 64 + 16 * i + kr + 4 * r, wx * 64 + 16 * j + ix, acc[i][j][r]);
+}
+
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_tn_f64_big_kernel(const double* __restrict__ At, int lda,
+                                                                       const double* __restrict__ B, int ldb,
+                                                                       double* __restrict__ C, int ldc, int K) {
+    __shared__ BigSmem sm;
     const int I = blockIdx.y, J = blockIdx.x;
-    WaveAcc<double> acc;
-    acc.zero();
-    tile_gemm<double, double, false, false, false>(A + int64_t(I) * TILE * lda, lda, B + int64_t(J) * TILE, ldb, TILE,
-                                                   TILE, K, sm, acc);
-    double* out = C + int64_t(I) * TILE * ldc + int64_t(J) * TILE;
-    for_each_acc(acc, [&](int r, int c, double v) { out[int64_t(r) * ldc + c] = v; });
+    f64x4 acc[4][4];
+    big_zero(acc);
+    big_mma(At + int64_t(I) * BIG, lda, B + int64_t(J) * BIG, ldb, 0, K, sm, acc);
+    double* out = C + int64_t(I) * BIG * ldc + int64_t(J) * BIG;
+    big_for_each(acc, [&](int r, int c, double v) { out[int64_t(r) * ldc + c] = v; });
 }
 
 // Fixed-order sum of the 256 per-thread values of a workgroup.
 __device__ __forceinline__ double block_sum_256(double s, double* red) {
+    __syncthreads();  // earlier readers of red are done
     red[threadIdx.x] = s;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
@@ -127,15 +252,14 @@ __device__ __forceinline__ double block_sum_256(double s, double* red) {
     return red[0];
 }
 
-// One tile (I <= J) of the symmetric product S = X^T-or-X times E, weighted by
-// the damped factor F:  partial[tile] = w sum_rc F[I r][J c] S_IJ[r][c], w = 1 on
-// the diagonal and 2 above it.
-//   ROWS (G = Q E^T, Q = E A_d):   S_IJ(r, c) = sum_k Q[I r][k] E[J c][k],  K = np
-//   !ROWS (H = P^T E, P = B_d E):  S_IJ(r, c) = sum_k P[k][I r] E[k][J c],  K = mp
-// Tiles are numbered J (J + 1) / 2 + I over the upper triangle.
-template <bool ROWS>
+// One 64 x 64 tile (I <= J) of a symmetric product S = X^T Y (X, Y: K x W
+// row-major), weighted by the damped factor F:
+//   partial[tile] = w sum_rc F[I r][J c] S_IJ[r][c],  w = 1 on the diagonal, 2 above.
+// Tiles are numbered J (J + 1) / 2 + I over the upper triangle.  64 x 64 tiles
+// rather than 128 x 128: the triangle then has enough tiles to spread evenly
+// over the CUs.
 __global__ __launch_bounds__(GEMM_THREADS) void loss_sym_kernel(const double* __restrict__ X,
-                                                                const double* __restrict__ E, int ld, int K,
+                                                                const double* __restrict__ Y, int ld, int K,
                                                                 const double* __restrict__ F, int ldf,
                                                                 double* __restrict__ partial) {
     __shared__ GemmSmem<double> sm;
@@ -147,12 +271,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void loss_sym_kernel(const double* __
     const int I = b - J * (J + 1) / 2;
     WaveAcc<double> acc;
     acc.zero();
-    if (ROWS)
-        tile_gemm<double, double, false, true, false>(X + int64_t(I) * TILE * ld, ld, E + int64_t(J) * TILE * ld, ld,
-                                                      TILE, TILE, K, sm, acc);
-    else
-        tile_gemm<double, double, true, false, false>(X + int64_t(I) * TILE, ld, E + int64_t(J) * TILE, ld, TILE, TILE,
-                                                      K, sm, acc);
+    // A(r, k) = X[k][I*64 + r], B(k, c) = Y[k][J*64 + c]
+    tile_gemm<double, double, true, false, false>(X + int64_t(I) * TILE, ld, Y + int64_t(J) * TILE, ld, TILE, TILE, K,
+                                                  sm, acc);
     const double* f = F + int64_t(I) * TILE * ldf + int64_t(J) * TILE;
     double s = 0.0;
     for_each_acc(acc, [&](int r, int c, double v) { s = __builtin_fma(f[int64_t(r) * ldf + c], v, s); });
@@ -180,18 +301,17 @@ __global__ void loss_final_kernel(const double* __restrict__ partial, int count,
 }
 
 constexpr int LOSS_BLOCKS = 1024;
-
 struct LossLayout {
-    int64_t mp, np;
-    int npart;  // partial sums: tiles of the symmetric product, or LOSS_BLOCKS
-    bool rows;  // G = E A_d E^T (m x m) rather than H = E^T B_d E (n x n)
-    size_t off_E, off_Q, off_A, off_B, off_scal, bytes;
+    int64_t mp, np;  // padded to 128
+    int npart;       // partial sums
+    bool rows;       // G = E A_d E^T (m x m) rather than H = E^T B_d E (n x n)
+    size_t off_E, off_Et, off_Q, off_A, off_B, off_scal, bytes;
 };
 
 LossLayout loss_layout(int64_t m, int64_t n) {
     LossLayout L;
-    L.mp = round_up(m, TILE);
-    L.np = round_up(n, TILE);
+    L.mp = round_up(m, BIG);
+    L.np = round_up(n, BIG);
     L.rows = n <= m;
     const int64_t t = (L.rows ? L.mp : L.np) / TILE;
     L.npart = int(std::max<int64_t>(LOSS_BLOCKS, t * (t + 1) / 2));
@@ -202,6 +322,7 @@ LossLayout loss_layout(int64_t m, int64_t n) {
         return o;
     };
     L.off_E = take(size_t(L.mp) * L.np * 8);
+    L.off_Et = L.off_E;  // a path reads E or E^T, never both
     L.off_Q = take(size_t(L.mp) * L.np * 8);
     L.off_A = take(size_t(L.np) * L.np * 8);
     L.off_B = take(size_t(L.mp) * L.mp * 8);
@@ -218,6 +339,7 @@ kq_status loss_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T* V, 
     const LossLayout L = loss_layout(m, n);
     char* base = static_cast<char*>(ws);
     double* E = reinterpret_cast<double*>(base + L.off_E);
+    double* Et = reinterpret_cast<double*>(base + L.off_Et);
     double* Q = reinterpret_cast<double*>(base + L.off_Q);
     double* Ap = reinterpret_cast<double*>(base + L.off_A);
     double* Bp = reinterpret_cast<double*>(base + L.off_B);
@@ -226,20 +348,26 @@ kq_status loss_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T* V, 
     const int mp = int(L.mp), np = int(L.np);
     auto blocks = [](int64_t count) { return dim3(unsigned((count + 255) / 256)); };
 
-    hipLaunchKernelGGL(pad_copy_kernel<T>, blocks(int64_t(mp) * np), dim3(256), 0, st, V, ldv, W, ldw, int(m), int(n),
-                       mp, np, (const double*)nullptr, 0.0, E);
-    KQ_LAUNCHED("pad_copy_kernel");
+    if (!B || L.rows) {  // the products read E only through E^T
+        hipLaunchKernelGGL(pad_diff_transpose_kernel<T>, dim3(np / 32, mp / 32), dim3(32, 8), 0, st, V, ldv, W, ldw,
+                           int(m), int(n), mp, Et);
+        KQ_LAUNCHED("pad_diff_transpose_kernel");
+    } else {
+        hipLaunchKernelGGL(pad_copy_kernel<T>, blocks(int64_t(mp) * np), dim3(256), 0, st, V, ldv, W, ldw, int(m),
+                           int(n), mp, np, (const double*)nullptr, 0.0, E);
+        KQ_LAUNCHED("pad_copy_kernel");
+    }
     hipLaunchKernelGGL(diag_trace_kernel<T>, dim3(1), dim3(1024), 0, st, A, lda, int(n), trA);
     KQ_LAUNCHED("diag_trace_kernel");
     hipLaunchKernelGGL(pad_copy_kernel<T>, blocks(int64_t(np) * np), dim3(256), 0, st, A, lda, (const T*)nullptr,
                        int64_t(0), int(n), int(n), np, np, trA, damp_rel, Ap);
     KQ_LAUNCHED("pad_copy_kernel");
     int nparts = LOSS_BLOCKS;
-    if (!B) {
-        hipLaunchKernelGGL(gemm_nn_f64_kernel, dim3(np / TILE, mp / TILE), dim3(GEMM_THREADS), 0, st, E, np, Ap, np, Q,
-                           np, np);
-        KQ_LAUNCHED("gemm_nn_f64_kernel");
-        hipLaunchKernelGGL(loss_partial_kernel, dim3(LOSS_BLOCKS), dim3(256), 0, st, Q, E, int64_t(mp) * np, partial);
+    if (!B) {  // Q^T = A_d E^T (A_d symmetric: its own transpose), then sum E^T * Q^T
+        hipLaunchKernelGGL(gemm_tn_f64_big_kernel, dim3(mp / BIG, np / BIG), dim3(GEMM_THREADS), 0, st, Ap, np, Et,
+                           mp, Q, mp, np);
+        KQ_LAUNCHED("gemm_tn_f64_big_kernel");
+        hipLaunchKernelGGL(loss_partial_kernel, dim3(LOSS_BLOCKS), dim3(256), 0, st, Q, Et, int64_t(mp) * np, partial);
         KQ_LAUNCHED("loss_partial_kernel");
     } else {
         hipLaunchKernelGGL(diag_trace_kernel<T>, dim3(1), dim3(1024), 0, st, B, ldb, int(m), trB);
@@ -247,21 +375,21 @@ kq_status loss_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T* V, 
         hipLaunchKernelGGL(pad_copy_kernel<T>, blocks(int64_t(mp) * mp), dim3(256), 0, st, B, ldb, (const T*)nullptr,
                            int64_t(0), int(m), int(m), mp, mp, trB, damp_rel, Bp);
         KQ_LAUNCHED("pad_copy_kernel");
-        if (L.rows) {  // Q = E A_d, then G = Q E^T weighted by B_d
-            hipLaunchKernelGGL(gemm_nn_f64_kernel, dim3(np / TILE, mp / TILE), dim3(GEMM_THREADS), 0, st, E, np, Ap,
-                               np, Q, np, np);
-            KQ_LAUNCHED("gemm_nn_f64_kernel");
+        if (L.rows) {  // Q^T = A_d E^T; G = Q E^T = (Q^T)^T E^T weighted by B_d
+            hipLaunchKernelGGL(gemm_tn_f64_big_kernel, dim3(mp / BIG, np / BIG), dim3(GEMM_THREADS), 0, st, Ap, np,
+                               Et, mp, Q, mp, np);
+            KQ_LAUNCHED("gemm_tn_f64_big_kernel");
             const int t = mp / TILE;
             nparts = t * (t + 1) / 2;
-            hipLaunchKernelGGL(loss_sym_kernel<true>, dim3(nparts), dim3(GEMM_THREADS), 0, st, Q, E, np, np, Bp, mp,
+            hipLaunchKernelGGL(loss_sym_kernel, dim3(nparts), dim3(GEMM_THREADS), 0, st, Q, Et, mp, np, Bp, mp,
                                partial);
-        } else {  // Q = B_d E, then H = Q^T E weighted by A_d
-            hipLaunchKernelGGL(gemm_nn_f64_kernel, dim3(np / TILE, mp / TILE), dim3(GEMM_THREADS), 0, st, Bp, mp, E,
+        } else {  // P = B_d E (B_d its own transpose); H = P^T E weighted by A_d
+            hipLaunchKernelGGL(gemm_tn_f64_big_kernel, dim3(np / BIG, mp / BIG), dim3(GEMM_THREADS), 0, st, Bp, mp, E,
                                np, Q, np, mp);
-            KQ_LAUNCHED("gemm_nn_f64_kernel");
+            KQ_LAUNCHED("gemm_tn_f64_big_kernel");
             const int t = np / TILE;
             nparts = t * (t + 1) / 2;
-            hipLaunchKernelGGL(loss_sym_kernel<false>, dim3(nparts), dim3(GEMM_THREADS), 0, st, Q, E, np, mp, Ap, np,
+            hipLaunchKernelGGL(loss_sym_kernel, dim3(nparts), dim3(GEMM_THREADS), 0, st, Q, E, np, mp, Ap, np,
                                partial);
         }
         KQ_LAUNCHED("loss_sym_kernel");
