@@ -303,21 +303,30 @@ __global__ void trtri_diag_kernel(double* __restrict__ Li, int dp, const double*
     for (int e = threadIdx.x; e < TILE * TILE; e += blockDim.x) out[int64_t(e >> 6) * dp + (e & 63)] = src[e];
 }
 
+// The K range of output tile (i, j) is triangular in j (stage a: mid - j tiles)
+// or in i (stage b: i - mid + 1 tiles), so one workgroup takes a pair of tiles
+// whose ranges add up to the same length: j and lo + h - 1 - (j - lo) in stage a,
+// i and hi - 1 - (i - mid) in stage b.  Every workgroup of a level then does the
+// same work.
 __global__ __launch_bounds__(GEMM_THREADS) void trtri_level_a_kernel(const double* __restrict__ C,
                                                                      const double* __restrict__ Li,
                                                                      double* __restrict__ Tm, int dp, int nt, int h) {
     const int lo = blockIdx.z * 2 * h, mid = lo + h;
     const int hi = lo + 2 * h < nt ? lo + 2 * h : nt;
-    const int i = mid + blockIdx.y, j = lo + blockIdx.x;
+    const int i = mid + blockIdx.y;
     if (i >= hi) return;
     __shared__ GemmSmem<double> sm;
-    WaveAcc<double> acc;
-    acc.zero();
-    const double* A = C + int64_t(i) * TILE * dp + int64_t(j) * TILE;
-    const double* B = Li + int64_t(j) * TILE * dp + int64_t(j) * TILE;
-    tile_gemm<double, double, false, false, false>(A, dp, B, dp, TILE, TILE, (mid - j) * TILE, sm, acc);
-    double* out = Tm + int64_t(i) * TILE * dp + int64_t(j) * TILE;
-    for_each_acc(acc, [&](int r, int c, double v) { out[int64_t(r) * dp + c] = v; });
+    const int jpair[2] = {lo + int(blockIdx.x), lo + h - 1 - int(blockIdx.x)};
+    for (int q = 0; q < (jpair[0] == jpair[1] ? 1 : 2); ++q) {
+        const int j = jpair[q];
+        WaveAcc<double> acc;
+        acc.zero();
+        const double* A = C + int64_t(i) * TILE * dp + int64_t(j) * TILE;
+        const double* B = Li + int64_t(j) * TILE * dp + int64_t(j) * TILE;
+        tile_gemm<double, double, false, false, false>(A, dp, B, dp, TILE, TILE, (mid - j) * TILE, sm, acc);
+        double* out = Tm + int64_t(i) * TILE * dp + int64_t(j) * TILE;
+        for_each_acc(acc, [&](int r, int c, double v) { out[int64_t(r) * dp + c] = v; });
+    }
 }
 
 __global__ __launch_bounds__(GEMM_THREADS) void trtri_level_b_kernel(double* __restrict__ Li,
@@ -325,16 +334,20 @@ __global__ __launch_bounds__(GEMM_THREADS) void trtri_level_b_kernel(double* __r
                                                                      int h) {
     const int lo = blockIdx.z * 2 * h, mid = lo + h;
     const int hi = lo + 2 * h < nt ? lo + 2 * h : nt;
-    const int i = mid + blockIdx.y, j = lo + blockIdx.x;
-    if (i >= hi) return;
+    const int ipair[2] = {mid + int(blockIdx.y), hi - 1 - int(blockIdx.y)};
+    if (ipair[0] > ipair[1]) return;
+    const int j = lo + blockIdx.x;
     __shared__ GemmSmem<double> sm;
-    WaveAcc<double> acc;
-    acc.zero();
-    const double* A = Li + int64_t(i) * TILE * dp + int64_t(mid) * TILE;
-    const double* B = Tm + int64_t(mid) * TILE * dp + int64_t(j) * TILE;
-    tile_gemm<double, double, false, false, false>(A, dp, B, dp, TILE, TILE, (i - mid + 1) * TILE, sm, acc);
-    double* out = Li + int64_t(i) * TILE * dp + int64_t(j) * TILE;
-    for_each_acc(acc, [&](int r, int c, double v) { out[int64_t(r) * dp + c] = -v; });
+    for (int q = 0; q < (ipair[0] == ipair[1] ? 1 : 2); ++q) {
+        const int i = ipair[q];
+        WaveAcc<double> acc;
+        acc.zero();
+        const double* A = Li + int64_t(i) * TILE * dp + int64_t(mid) * TILE;
+        const double* B = Tm + int64_t(mid) * TILE * dp + int64_t(j) * TILE;
+        tile_gemm<double, double, false, false, false>(A, dp, B, dp, TILE, TILE, (i - mid + 1) * TILE, sm, acc);
+        double* out = Li + int64_t(i) * TILE * dp + int64_t(j) * TILE;
+        for_each_acc(acc, [&](int r, int c, double v) { out[int64_t(r) * dp + c] = -v; });
+    }
 }
 
 template <typename TOut>
@@ -408,9 +421,11 @@ kq_status prepare_typed(int64_t d, const T* A, int64_t lda, double damp_rel, T* 
     KQ_LAUNCHED("trtri_diag_kernel");
     for (int h = 1; h < nt; h *= 2) {
         const int nodes = (nt + 2 * h - 1) / (2 * h);
-        hipLaunchKernelGGL(trtri_level_a_kernel, dim3(h, h, nodes), dim3(GEMM_THREADS), 0, st, C, Li, Tm, dp, nt, h);
+        const int half = (h + 1) / 2;  // tile pairs per row (stage a) or column (stage b)
+        hipLaunchKernelGGL(trtri_level_a_kernel, dim3(half, h, nodes), dim3(GEMM_THREADS), 0, st, C, Li, Tm, dp, nt,
+                           h);
         KQ_LAUNCHED("trtri_level_a_kernel");
-        hipLaunchKernelGGL(trtri_level_b_kernel, dim3(h, h, nodes), dim3(GEMM_THREADS), 0, st, Li, Tm, dp, nt, h);
+        hipLaunchKernelGGL(trtri_level_b_kernel, dim3(h, half, nodes), dim3(GEMM_THREADS), 0, st, Li, Tm, dp, nt, h);
         KQ_LAUNCHED("trtri_level_b_kernel");
     }
     const int64_t ucnt = d * d;
