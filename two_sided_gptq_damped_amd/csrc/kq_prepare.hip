@@ -69,17 +69,25 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 // Cholesky of the diagonal block C[k][k] and the inverse of its factor.
 //
 // Factor: left-looking over four 16-column panels.  For panel p (columns c0..c0+15)
-// all 256 threads first subtract the contribution of the finished columns
-// (L[r][c] -= sum_{q < c0} L[r][q] L[c][q]); then one wave factors the panel in
+// the waves first subtract the contribution of the finished columns
+// (L[r][c] -= sum_{q < c0} L[r][q] L[c][q], one 16-row block per wave on the
+// matrix cores); then one wave factors the panel in
 // registers, lane i holding row c0 + i: per column, the pivot and the column
 // entries of the other panel rows are broadcast with readlane, so a column costs
 // no LDS round trip and no workgroup barrier.
 // Inverse: the four 16 x 16 diagonal blocks are inverted by forward substitution,
 // one wave each (lane = column); then the blocks below the diagonal follow by
-// distance d = 1..3: T = sum_{q=j}^{i-1} L_iq X_qj, X_ij = -X_ii T.
-// Writes L (zero above the diagonal) back into C and L^{-1} into Dinv[k].  A pivot
+// distance d = 1..3 on the matrix cores: T = sum_{q=j}^{i-1} L_iq X_qj,
+// X_ij = -X_ii T.
+// Writes L^{-1} into Dinv[k] (the block of L itself is used only through it).  A pivot
 // that is not > 0 records its 1-based position in *info (first failure only) and
 // continues with a unit pivot so the remaining kernels stay finite.
+// One v_mfma_f64_16x16x4 step: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; register r of the result holds row l / 16 + 4 r, column l % 16.
+__device__ __forceinline__ f64x4 mma16(double a, double b, f64x4 c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
 constexpr int DP = TILE + 1;  // row stride of the diagonal-block arrays
 struct DiagSmem {
     double L[TILE * DP];
@@ -99,24 +107,21 @@ __device__ __forceinline__ void diag_factor(double* __restrict__ C, int dp, int 
     double* const rdiag = sm.rdiag;
     double* const colj = sm.colj;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-    double* blk = C + int64_t(k) * TILE * dp + int64_t(k) * TILE;
-    for (int e = t; e < TILE * TILE; e += 256) X[(e >> 6) * P + (e & 63)] = 0.0;
-    __syncthreads();
+    const int ix = lane & 15, kr = lane >> 4;  // 16 x 16 x 4 operand position: row / column ix, k kr
     bool failed = false;  // uniform in wave 0, the only writer of *info
     for (int p = 0; p < TILE / PW; ++p) {
         const int c0 = PW * p;
         if (p > 0) {
-            for (int e = t; e < (TILE - c0) * PW; e += 256) {
-                const int r = c0 + (e >> 4), c = c0 + (e & 15);
-                if (c <= r) {
-                    double acc[4] = {0.0, 0.0, 0.0, 0.0};  // independent chains
-                    for (int q = 0; q < c0; q += 4) {
+            // row block rb = p + w of the panel: L[rb][p] -= L[rb][0:p] L[p][0:p]^T
+            // (whole 16 x 16 blocks; the upper triangle of the diagonal block is
+            // never read)
+            if (w < TILE / PW - p) {
+                const int rb = p + w;
+                f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+                for (int q = 0; q < c0; q += 4)
+                    acc = mma16(L[(PW * rb + ix) * P + q + kr], L[(c0 + ix) * P + q + kr], acc);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            acc[u] = __builtin_fma(L[r * P + q + u], L[c * P + q + u], acc[u]);
-                    }
-                    L[r * P + c] -= (acc[0] + acc[1]) + (acc[2] + acc[3]);
-                }
+                for (int r = 0; r < 4; ++r) L[(PW * rb + kr + 4 * r) * P + c0 + ix] -= acc[r];
             }
             __syncthreads();
         }
@@ -127,26 +132,34 @@ __device__ __forceinline__ void diag_factor(double* __restrict__ C, int dp, int 
 #pragma unroll
             for (int j = 0; j < PW; ++j) a[j] = (live && c0 + j <= r) ? L[r * P + c0 + j] : 0.0;
             int fail_col = -1;  // first non-positive pivot of this panel (uniform)
+            double dnext = readlane_f64(a[0], 0);
 #pragma unroll
             for (int j = 0; j < PW; ++j) {
-                double d = readlane_f64(a[j], j);
+                double d = dnext;
                 if (!(d > 0.0)) {
                     fail_col = fail_col < 0 ? j : fail_col;
                     d = 1.0;
                 }
-                // 1/sqrt(d) from the hardware estimate and two Newton steps (each
-                // squares the relative error; the result is within a few ulps)
+                // 1/sqrt(d) from the hardware estimate and one Newton step (it
+                // squares the estimate's relative error)
                 double inv = __builtin_amdgcn_rsq(d);
-                inv = inv * __builtin_fma(-0.5 * d * inv, inv, 1.5);
                 inv = inv * __builtin_fma(-0.5 * d * inv, inv, 1.5);
                 const double piv = d * inv;
                 if (lane == 0) rdiag[c0 + j] = inv;
                 a[j] = lane > j ? a[j] * inv : (lane == j ? piv : a[j]);
-                // column j of the panel rows to every lane through LDS (one wave:
-                // its LDS accesses complete in order, no barrier needed)
-                colj[lane] = a[j];
+                // Column j + 1, which the next pivot needs, is updated with a
+                // register broadcast (lane j + 1's a[j]); the later columns get their
+                // multipliers through LDS (one wave: its LDS accesses complete in
+                // order, no barrier needed), off the chain of pivots.
+                if (j + 1 < PW) {
+                    a[j + 1] = __builtin_fma(-a[j], readlane_f64(a[j], j + 1), a[j + 1]);
+                    dnext = readlane_f64(a[j + 1], j + 1);
+                }
+                if (j + 2 < PW) {
+                    colj[lane] = a[j];
 #pragma unroll
-                for (int c = j + 1; c < PW; ++c) a[c] = __builtin_fma(-a[j], colj[c], a[c]);
+                    for (int c = j + 2; c < PW; ++c) a[c] = __builtin_fma(-a[j], colj[c], a[c]);
+                }
             }
             if (fail_col >= 0 && lane == 0 && !failed && *info == 0) *info = k * TILE + c0 + fail_col + 1;
             failed = failed || fail_col >= 0;
@@ -173,43 +186,34 @@ __device__ __forceinline__ void diag_factor(double* __restrict__ C, int dp, int 
         for (int r = 0; r < PW; ++r) X[(i0 + r) * P + i0 + c] = x[r];
     }
     __syncthreads();
-    // blocks below the diagonal; T_ij is kept in the (unused) upper triangle of L
+    // blocks below the diagonal, by distance d = ib - jb, one wave per block:
+    // T = sum_{q=jb}^{ib-1} L[ib][q] X[q][jb], then X[ib][jb] = -X[ib][ib] T.  The
+    // 16 x 16 x 4 product leaves rows kr + 4 r of T in register r, which is how
+    // the k-group r of the second product's right operand is laid out, so T
+    // never leaves the registers.
 #pragma unroll
     for (int d = 1; d < TILE / PW; ++d) {
-        const int nblk = TILE / PW - d;
+        if (w < TILE / PW - d) {
+            const int jb = w, ib = w + d;
+            f64x4 tacc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int e0 = 0; e0 < nblk * PW * PW; e0 += 256) {
-            const int e = e0 + t;
-            const int jb = e >> 8, ib = jb + d, rr = (e >> 4) & 15, cc = e & 15;
-            const int row = PW * ib + rr, col = PW * jb + cc;
-            double acc[4] = {0.0, 0.0, 0.0, 0.0};
+            for (int q = PW * jb; q < PW * ib; q += 4)
+                tacc = mma16(L[(PW * ib + ix) * P + q + kr], X[(q + kr) * P + PW * jb + ix], tacc);
+            f64x4 xacc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-            for (int q4 = 0; q4 < PW * d; q4 += 4) {
-                const int q = PW * jb + q4;
+            for (int g = 0; g < 4; ++g) xacc = mma16(X[(PW * ib + ix) * P + PW * ib + 4 * g + kr], tacc[g], xacc);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[u] = __builtin_fma(L[row * P + q + u], X[(q + u) * P + col], acc[u]);
-            }
-            L[(PW * jb + rr) * P + PW * ib + cc] = (acc[0] + acc[1]) + (acc[2] + acc[3]);  // T_ij at the mirrored block
-        }
-        __syncthreads();
-#pragma unroll
-        for (int e0 = 0; e0 < nblk * PW * PW; e0 += 256) {
-            const int e = e0 + t;
-            const int jb = e >> 8, ib = jb + d, rr = (e >> 4) & 15, cc = e & 15;
-            double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-            for (int q = 0; q < PW; ++q)
-                acc[q & 3] = __builtin_fma(X[(PW * ib + rr) * P + PW * ib + q], L[(PW * jb + q) * P + PW * ib + cc],
-                                           acc[q & 3]);
-            X[(PW * ib + rr) * P + PW * jb + cc] = -((acc[0] + acc[1]) + (acc[2] + acc[3]));
+            for (int r = 0; r < 4; ++r) X[(PW * ib + kr + 4 * r) * P + PW * jb + ix] = -xacc[r];
         }
         __syncthreads();
     }
+    // L^{-1} to Dinv (blocks above the 16 x 16 block diagonal were never written:
+    // zeros).  L[k][k] itself is not stored: every later step reads the diagonal
+    // block only through its inverse.
     double* dinv = Dinv + int64_t(k) * TILE * TILE;
     for (int e = t; e < TILE * TILE; e += 256) {
         const int r = e >> 6, c = e & 63;
-        blk[int64_t(r) * dp + c] = c <= r ? L[r * P + c] : 0.0;
-        dinv[e] = X[r * P + c];
+        dinv[e] = (c >> 4) > (r >> 4) ? 0.0 : X[r * P + c];
     }
 }
 
