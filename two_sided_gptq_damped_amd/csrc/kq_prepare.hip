@@ -171,16 +171,20 @@ __device__ __forceinline__ void diag_factor(double* __restrict__ C, int dp, int 
         }
         __syncthreads();
     }
-    // diagonal 16 x 16 blocks of the inverse: wave w, block w, lane = column
+    // diagonal 16 x 16 blocks of the inverse: wave w, block w, lane = column.
+    // Forward substitution, column-oriented: once x[q] is known it is taken out
+    // of every later row, so the dependent chain is 16 steps long; each row
+    // still receives its terms in order q = 0, 1, ...
     if (lane < PW) {
         const int i0 = PW * w, c = lane;
         double x[PW];
 #pragma unroll
-        for (int r = 0; r < PW; ++r) {
-            double s = r == c ? 1.0 : 0.0;
+        for (int r = 0; r < PW; ++r) x[r] = r == c ? 1.0 : 0.0;
 #pragma unroll
-            for (int q = 0; q < r; ++q) s = __builtin_fma(-L[(i0 + r) * P + i0 + q], x[q], s);
-            x[r] = s * rdiag[i0 + r];
+        for (int q = 0; q < PW; ++q) {
+            x[q] *= rdiag[i0 + q];
+#pragma unroll
+            for (int r = q + 1; r < PW; ++r) x[r] = __builtin_fma(-L[(i0 + r) * P + i0 + q], x[q], x[r]);
         }
 #pragma unroll
         for (int r = 0; r < PW; ++r) X[(i0 + r) * P + i0 + c] = x[r];
