@@ -108,6 +108,7 @@ __device__ __forceinline__ void diag_factor(double* __restrict__ C, int dp, int 
     double* const colj = sm.colj;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     const int ix = lane & 15, kr = lane >> 4;  // 16 x 16 x 4 operand position: row / column ix, k kr
+    __syncthreads();  // the block the caller's threads wrote into L is complete
     bool failed = false;  // uniform in wave 0, the only writer of *info
     for (int p = 0; p < TILE / PW; ++p) {
         const int c0 = PW * p;

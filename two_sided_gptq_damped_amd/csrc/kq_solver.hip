@@ -76,6 +76,7 @@ struct Vec4<float> {
     __device__ void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
     __device__ void store(float* p) const { *reinterpret_cast<f32x4*>(p) = v; }
     __device__ float operator[](int j) const { return v[j]; }
+    __device__ void set(int j, float x) { v[j] = x; }
 };
 template <>
 struct Vec4<double> {
@@ -89,7 +90,30 @@ struct Vec4<double> {
         reinterpret_cast<f64x2*>(p)[1] = hi;
     }
     __device__ double operator[](int j) const { return j < 2 ? lo[j] : hi[j - 2]; }
+    __device__ void set(int j, double x) {
+        if (j < 2)
+            lo[j] = x;
+        else
+            hi[j - 2] = x;
+    }
 };
+
+// o[i][j] += sum_k A(rr + i, k) B(k, cc + j) over a staged 32-deep slice (A at
+// [k][r], B at [k][c], rows PK apart).
+template <typename T, int PK>
+__device__ __forceinline__ void mac4x4_impl(const T* __restrict__ sa, const T* __restrict__ sb, int rr, int cc,
+                                            T (&o)[4][4]) {
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+        Vec4<T> a4, b4;
+        a4.load(sa + k * PK + rr);
+        b4.load(sb + k * PK + cc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[i][j] = kfma(a4[i], b4[j], o[i][j]);
+    }
+}
 
 // Leaf: the tiles of one tile-diagonal K, one 256-thread workgroup per 32 x 32
 // tile.  Thread t owns four entries of column b = t % 32 (in the sweep, rows
@@ -159,6 +183,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     __shared__ __attribute__((aligned(16))) T stg[BATCH][2][ST * PK];
     T* const bufA = stg[0][0];
     T* const bufB = stg[0][1];
+    auto mac4x4 = [](const T* a, const T* bm, int r, int c, T (&o)[4][4]) { mac4x4_impl<T, PK>(a, bm, r, c, o); };
 
     const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
     const int I = ilo + blockIdx.x;
@@ -171,6 +196,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     const bool blk = t < 256;
     const int b = l & 31, r0 = 8 * w + 4 * (l >> 5);
     const int fgrp = t >> 8;                    // staging loads: slices rotate over the 256-thread groups
+    const int wv = t >> 6, rr = 4 * ((t & 63) >> 3), cc = 4 * (t & 7);  // chunk products: wave, 4 x 4 block
     const int q8 = tb >> 3, c4 = 4 * (tb & 7);  // this thread's share of a 32 x 32 staging load
 
     // chunk sources: row tiles J' in [jl, J), column tiles I' in [il, I)
@@ -245,6 +271,11 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
 
     // ---- chunk prologue: rowpart (crow) and the column feedback (ccol), block layout
     if (ns > 0) {
+        T pr[4][4], pc[4][4];  // this wave's sums of row-part and column-part slices
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pr[i][j] = pc[i][j] = T(0);
         for (int sb = 0; sb < ns; sb += BATCH) {
             if (sb > 0) {
                 __syncthreads();  // the previous batch is consumed
@@ -268,54 +299,50 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
                 }
             }
             __syncthreads();
-            // every thread of the block layout has a twin in the other half of
-            // the workgroup; the pair splits each product's K range in two
+            // one wave per slice (slices u = wave, wave + 8, ...), each lane a 4 x 4
+            // block of the 32 x 32 product: two 16-byte LDS reads feed 16 FMAs
             const int nbat = ns - sb < BATCH ? ns - sb : BATCH;
-            const int kb = (ST / NFG) * fgrp;
-            for (int u = 0; u < nbat; ++u) {
+            for (int u = wv; u < nbat; u += LEAF_THREADS / 64) {
                 const T* sa = stg[u][0];
                 const T* sbm = stg[u][1];
-                T o[4] = {T(0), T(0), T(0), T(0)};
-#pragma unroll 8
-                for (int k = kb; k < kb + ST / NFG; ++k) {
-                    Vec4<T> a4;
-                    a4.load(sa + k * PK + r0);
-                    const T bk = sbm[k * PK + b];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i] = kfma(a4[i], bk, o[i]);
-                }
-                if (sb + u < n1) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) crow[i] += o[i];
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ccol[i] += o[i];
-                }
+                if (sb + u < n1)
+                    mac4x4(sa, sbm, rr, cc, pr);
+                else
+                    mac4x4(sa, sbm, rr, cc, pc);
             }
         }
-        __syncthreads();  // staged operands consumed
-        // the second half's partial sums join the first half's (fixed order)
-        {
-            T* park = reinterpret_cast<T*>(stg);  // 2 x 256 x 4 values: one slice's staging area
-            static_assert(NFG == 2, "two halves");
-            static_assert(2 * ST * PK * sizeof(T) >= 8 * 256 * sizeof(T), "staging area too small");
-            if (!blk) {
+        // the waves' partial sums, added in wave order into the block layout: the
+        // row parts, then the column parts, through the staging area
+        const int nw = ns < LEAF_THREADS / 64 ? ns : LEAF_THREADS / 64;  // waves that had a slice
+        T* park = reinterpret_cast<T*>(stg);                            // [wave][32 x 32]
+        static_assert(sizeof(stg) >= (LEAF_THREADS / 64) * ST * ST * sizeof(T), "staging area too small");
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+            __syncthreads();  // staged operands (or the previous part) consumed
+            if (wv < nw) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    park[i * 256 + tb] = crow[i];
-                    park[(4 + i) * 256 + tb] = ccol[i];
+                    Vec4<T> v4;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v4.set(j, part == 0 ? pr[i][j] : pc[i][j]);
+                    v4.store(park + wv * ST * ST + (rr + i) * ST + cc);
                 }
             }
             __syncthreads();
             if (blk) {
+                for (int v = 0; v < nw; ++v) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    crow[i] += park[i * 256 + tb];
-                    ccol[i] += park[(4 + i) * 256 + tb];
+                    for (int i = 0; i < 4; ++i) {
+                        const T x = park[v * ST * ST + (r0 + i) * ST + b];
+                        if (part == 0)
+                            crow[i] += x;
+                        else
+                            ccol[i] += x;
+                    }
                 }
             }
-            __syncthreads();  // partials read before bufA is reused
         }
+        __syncthreads();  // partials read before bufA is reused
         if (NB && n1 > 0) {
             // column feedback of rowpart inside the tile: strict(N_B[I, I])^T rowpart
             if (blk) {
