@@ -311,54 +311,59 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
                     mac4x4(sa, sbm, rr, cc, pc);
             }
         }
-        // the waves' partial sums, added in wave order into the block layout: the
-        // row parts, then the column parts, through the staging area
+        // The waves' partial sums reach the block layout through the staging
+        // area, added in wave order: first the row parts (rowpart, kept in LDS
+        // as the right operand of the next product), then the column parts,
+        // to which every wave has added its share of strict(N_B[I, I])^T rowpart
+        // (K split eight ways, 4 x 4 register blocks).
         const int nw = ns < LEAF_THREADS / 64 ? ns : LEAF_THREADS / 64;  // waves that had a slice
-        T* park = reinterpret_cast<T*>(stg);                            // [wave][32 x 32]
-        static_assert(sizeof(stg) >= (LEAF_THREADS / 64) * ST * ST * sizeof(T), "staging area too small");
+        const bool nbs = NB && n1 > 0;                                    // the in-tile column feedback
+        T* park = reinterpret_cast<T*>(stg);                             // [wave][32 x 32]
+        T* rowp = park + (LEAF_THREADS / 64) * ST * ST;                  // rowpart, [k][c]
+        static_assert(sizeof(stg) >= (LEAF_THREADS / 64 + 1) * ST * ST * sizeof(T), "staging area too small");
+        auto park_wave = [&](const T (&o)[4][4]) {
 #pragma unroll
-        for (int part = 0; part < 2; ++part) {
-            __syncthreads();  // staged operands (or the previous part) consumed
-            if (wv < nw) {
+            for (int i = 0; i < 4; ++i) {
+                Vec4<T> v4;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    Vec4<T> v4;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) v4.set(j, part == 0 ? pr[i][j] : pc[i][j]);
-                    v4.store(park + wv * ST * ST + (rr + i) * ST + cc);
-                }
+                for (int j = 0; j < 4; ++j) v4.set(j, o[i][j]);
+                v4.store(park + wv * ST * ST + (rr + i) * ST + cc);
             }
-            __syncthreads();
-            if (blk) {
-                for (int v = 0; v < nw; ++v) {
+        };
+        __syncthreads();  // staged operands consumed
+        if (wv < nw) park_wave(pr);
+        __syncthreads();
+        if (blk) {
+            for (int v = 0; v < nw; ++v) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const T x = park[v * ST * ST + (r0 + i) * ST + b];
-                        if (part == 0)
-                            crow[i] += x;
-                        else
-                            ccol[i] += x;
-                    }
-                }
+                for (int i = 0; i < 4; ++i) crow[i] += park[v * ST * ST + (r0 + i) * ST + b];
+            }
+            if (nbs) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rowp[(r0 + i) * ST + b] = crow[i];
             }
         }
-        __syncthreads();  // partials read before bufA is reused
-        if (NB && n1 > 0) {
-            // column feedback of rowpart inside the tile: strict(N_B[I, I])^T rowpart
-            if (blk) {
+        __syncthreads();  // rowpart complete; the row partials are read
+        if (nbs) {
+            const int k0 = 4 * wv;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) bufA[(r0 + i) * PK + b] = crow[i];
+            for (int k = k0; k < k0 + 4; ++k) {
+                Vec4<T> a4, b4;
+                a4.load(sNB + k * PB + rr);  // strict(N_B[I, I])^T (r, k) = N_B[k][r]
+                b4.load(rowp + k * ST + cc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) pc[i][j] = kfma(a4[i], b4[j], pc[i][j]);
             }
-            __syncthreads();
-            if (blk) {
-#pragma unroll 8
-                for (int k = 0; k < ST; ++k) {
-                    Vec4<T> nb4;
-                    nb4.load(sNB + k * PB + r0);
-                    const T rk = bufA[k * PK + b];
+        }
+        const int nw2 = nbs ? LEAF_THREADS / 64 : nw;
+        if (wv < nw2) park_wave(pc);
+        __syncthreads();
+        if (blk) {
+            for (int v = 0; v < nw2; ++v) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) ccol[i] = kfma(nb4[i], rk, ccol[i]);
-                }
+                for (int i = 0; i < 4; ++i) ccol[i] += park[v * ST * ST + (r0 + i) * ST + b];
             }
         }
 #pragma unroll
