@@ -402,6 +402,49 @@ __device__ void tile_gemm_masked_k(const T* __restrict__ A, int64_t lda, const T
     }
 }
 
+// tile_gemm_masked_k with two slices in flight: while the matrix cores work on
+// slice s from LDS, the loads of slices s + 1 and s + 2 are both outstanding (two
+// register sets used in turn), so a block whose K loop is bound by the latency of
+// its own loads waits half as often.  K must be a multiple of KS.
+template <typename T, int KS, bool A_KMAJ, bool B_KMAJ, typename MA, typename MB>
+__device__ void tile_gemm_masked_k2(const T* __restrict__ A, int64_t lda, const T* __restrict__ B, int64_t ldb, int K,
+                                    GemmSmemK<T, KS>& sm, WaveAcc<T>& acc, MA ma, MB mb) {
+    constexpr int S = LdsStride<T>::value;
+    const int t = threadIdx.x & 255, lane = t & 63, w = t >> 6;
+    const int wy = w >> 1, wx = w & 1;
+    LoaderK<T, A_KMAJ, B_KMAJ, KS> la, lb;
+    const int nk = K / KS;
+    if (nk == 0) return;
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < KS / KSTEP; ++q) acc.mma(sm.a[buf] + KSTEP * q * S, sm.b[buf] + KSTEP * q * S, wy, wx, lane);
+    };
+    la.fetch(A, lda, B, ldb, 0, t);
+    if (nk > 1) lb.fetch(A, lda, B, ldb, KS, t);
+    la.apply(0, t, ma, mb);
+    __syncthreads();
+    la.stash(sm.a[0], sm.b[0], t);
+    __syncthreads();
+    for (int s = 0; s < nk; s += 2) {
+        // LDS stage 0 holds slice s, lb carries slice s + 1
+        if (s + 2 < nk) la.fetch(A, lda, B, ldb, (s + 2) * KS, t);
+        mma(0);
+        if (s + 1 < nk) {
+            lb.apply((s + 1) * KS, t, ma, mb);
+            lb.stash(sm.a[1], sm.b[1], t);
+            __syncthreads();
+            // LDS stage 1 holds slice s + 1, la carries slice s + 2
+            if (s + 3 < nk) lb.fetch(A, lda, B, ldb, (s + 3) * KS, t);
+            mma(1);
+            if (s + 2 < nk) {
+                la.apply((s + 2) * KS, t, ma, mb);
+                la.stash(sm.a[0], sm.b[0], t);
+                __syncthreads();
+            }
+        }
+    }
+}
+
 // Split-K variant for launch shapes with few blocks and long K ranges: G groups of
 // four waves (blockDim = 256 G) share one 64 x 64 output.  Group g takes the
 // K slices s = g, g + G, ... with its own double-buffered LDS stage, all groups

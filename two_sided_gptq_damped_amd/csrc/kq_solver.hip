@@ -555,7 +555,10 @@ __global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T*
     const T* A = NB + int64_t(kl) * ST * mp + int64_t(I0) * ST;  // A(r, k) = NB[k][r]
     const T* B = T1 + int64_t(kl) * ST * np + int64_t(J0) * ST;
     auto mb = [=](int k, int c) { return t1_valid(kl + (k >> 5), J0 + (c >> 5)); };
-    tile_gemm_masked_k<T, KS, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
+    if (KS == KSTEP)  // the top node: many blocks per CU hide the loads
+        tile_gemm_masked_k<T, KS, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
+    else
+        tile_gemm_masked_k2<T, KS, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
     for_each_acc(acc, [&](int r, int c, T v) {
         if (in_band(r, c)) out[int64_t(r) * np + c] += v;
     });
