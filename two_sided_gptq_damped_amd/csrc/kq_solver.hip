@@ -144,19 +144,17 @@ __device__ __forceinline__ void mac4x4_impl(const T* __restrict__ sa, const T* _
 //   X[I, J] += N_B[I, I]^T rowpart + sum_{c0 - J <= I' < I} N_B[I', I]^T T1c[I', J]
 // and after the sweep the leaf writes T1c[I, J] = rowpart + Delta[I, J] N_A[J, J]
 // for the later diagonals of its chunk.  With B = I only rowpart is added.  The
-// 32 x 32 x 32 products are few and small; each thread computes its own four
-// entries with FMAs on operands staged k-major in LDS.
+// 32 x 32 x 32 products are few and small: their operands are staged k-major in
+// LDS and each wave takes whole slices, every lane a 4 x 4 block of the product.
 //
-// The quotient x / s is formed as q = x * (1/s) with one Markstein correction
-// q + (x - q s) (1/s): within an ulp of the IEEE quotient, so it can change a
-// rounding decision only for values that sit within ~1e-15 grid units of a
-// midpoint.
+// The quotient x / s is formed as x * (1/s) (1/s rounded once per row): within
+// two ulps of the IEEE quotient, so it can change a rounding decision only for
+// values that sit within ~1e-15 (fp64) or ~1e-7 (fp32) grid units of a
+// midpoint.  A zero scale has 1/s = 0, so q = 0 and the code is 0 with no test
+// (for finite x).
 template <typename T>
 __device__ __forceinline__ void quantize_fast(T x, T s, T rs, T qmin, T qmax, T& z, T& v) {
-    const T q = x * rs;
-    const T y = kfma(kfma(-q, s, x), rs, q);
-    const T r = kclamp(krint(y), qmin, qmax);
-    z = s == T(0) ? T(0) : r;
+    z = kclamp(krint(x * rs), qmin, qmax);
     v = s * z;
 }
 
