@@ -257,28 +257,35 @@ __device__ __forceinline__ double block_sum_256(double s, double* red) {
 //   partial[tile] = w sum_rc F[I r][J c] S_IJ[r][c],  w = 1 on the diagonal, 2 above.
 // Tiles are numbered J (J + 1) / 2 + I over the upper triangle.  64 x 64 tiles
 // rather than 128 x 128: the triangle then has enough tiles to spread evenly
-// over the CUs.
+// over the CUs.  The K range of each tile is cut into SYM_KSPLIT parts, one
+// workgroup each (part-major, so workgroups running together read the same rows
+// of X and Y): the triangle's tile count is rarely a multiple of the resident
+// workgroups, and quarter-size pieces shrink the last, partly filled round.
+constexpr int SYM_KSPLIT = 4;
+
 __global__ __launch_bounds__(GEMM_THREADS) void loss_sym_kernel(const double* __restrict__ X,
                                                                 const double* __restrict__ Y, int ld, int K,
-                                                                const double* __restrict__ F, int ldf,
+                                                                const double* __restrict__ F, int ldf, int ntiles,
                                                                 double* __restrict__ partial) {
     __shared__ GemmSmem<double> sm;
     __shared__ double red[GEMM_THREADS];
-    const int b = blockIdx.x;
+    const int kpart = blockIdx.x / ntiles, b = blockIdx.x - kpart * ntiles;
+    const int kl = K / SYM_KSPLIT;
     int J = int((sqrt(8.0 * b + 1.0) - 1.0) * 0.5);
     while (J * (J + 1) / 2 > b) --J;
     while ((J + 1) * (J + 2) / 2 <= b) ++J;
     const int I = b - J * (J + 1) / 2;
     WaveAcc<double> acc;
     acc.zero();
-    // A(r, k) = X[k][I*64 + r], B(k, c) = Y[k][J*64 + c]
-    tile_gemm<double, double, true, false, false>(X + int64_t(I) * TILE, ld, Y + int64_t(J) * TILE, ld, TILE, TILE, K,
-                                                  sm, acc);
+    // A(r, k) = X[k][I*64 + r], B(k, c) = Y[k][J*64 + c] over this part's rows k
+    const int64_t k0 = int64_t(kpart) * kl * ld;
+    tile_gemm<double, double, true, false, false>(X + k0 + int64_t(I) * TILE, ld, Y + k0 + int64_t(J) * TILE, ld, TILE,
+                                                  TILE, kl, sm, acc);
     const double* f = F + int64_t(I) * TILE * ldf + int64_t(J) * TILE;
     double s = 0.0;
     for_each_acc(acc, [&](int r, int c, double v) { s = __builtin_fma(f[int64_t(r) * ldf + c], v, s); });
     const double tot = block_sum_256(s, red);
-    if (threadIdx.x == 0) partial[b] = I == J ? tot : 2.0 * tot;
+    if (threadIdx.x == 0) partial[blockIdx.x] = I == J ? tot : 2.0 * tot;
 }
 
 // B = I: partial sums of E * Q (Q = E A_d), one per block, in a fixed order.
@@ -314,7 +321,7 @@ LossLayout loss_layout(int64_t m, int64_t n) {
     L.np = round_up(n, BIG);
     L.rows = n <= m;
     const int64_t t = (L.rows ? L.mp : L.np) / TILE;
-    L.npart = int(std::max<int64_t>(LOSS_BLOCKS, t * (t + 1) / 2));
+    L.npart = int(std::max<int64_t>(LOSS_BLOCKS, t * (t + 1) / 2 * SYM_KSPLIT));
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -380,17 +387,17 @@ kq_status loss_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T* V, 
                                Et, mp, Q, mp, np);
             KQ_LAUNCHED("gemm_tn_f64_big_kernel");
             const int t = mp / TILE;
-            nparts = t * (t + 1) / 2;
+            nparts = t * (t + 1) / 2 * SYM_KSPLIT;
             hipLaunchKernelGGL(loss_sym_kernel, dim3(nparts), dim3(GEMM_THREADS), 0, st, Q, Et, mp, np, Bp, mp,
-                               partial);
+                               t * (t + 1) / 2, partial);
         } else {  // P = B_d E (B_d its own transpose); H = P^T E weighted by A_d
             hipLaunchKernelGGL(gemm_tn_f64_big_kernel, dim3(np / BIG, mp / BIG), dim3(GEMM_THREADS), 0, st, Bp, mp, E,
                                np, Q, np, mp);
             KQ_LAUNCHED("gemm_tn_f64_big_kernel");
             const int t = np / TILE;
-            nparts = t * (t + 1) / 2;
+            nparts = t * (t + 1) / 2 * SYM_KSPLIT;
             hipLaunchKernelGGL(loss_sym_kernel, dim3(nparts), dim3(GEMM_THREADS), 0, st, Q, E, np, mp, Ap, np,
-                               partial);
+                               t * (t + 1) / 2, partial);
         }
         KQ_LAUNCHED("loss_sym_kernel");
     }
