@@ -146,10 +146,13 @@ kq_status kron_quantize(kq_dtype dtype, int64_t m, int64_t n, const void* W, int
 
 /*
  * Proxy loss D_{A,B} = tr(B_d (V - W) A_d (V - W)^T) (WaterKron page section 1,
- * item 1; FastKron page section 2.2), accumulated in fp64:
- * sum_ij ((B_d E)_ij * (E A_d)_ij) with E = V - W, A_d = A + damp_rel tr(A)/n I,
- * B_d likewise.  damp_rel = 0 gives the undamped loss.
- *   A  n x n, B  m x m (symmetric); B = NULL means B = I
+ * item 1; FastKron page section 2.2) with E = V - W, A_d = A + damp_rel tr(A)/n I,
+ * B_d likewise; damp_rel = 0 gives the undamped loss.  Computed in fp64 as
+ * sum_ij (B_d)_ij (E A_d E^T)_ij when n <= m, else sum_ij (A_d)_ij (E^T B_d E)_ij
+ * (the same value for symmetric factors, at 3/4 of the flops of forming both
+ * B_d E and E A_d when m = n); B = I gives sum_ij E_ij (E A_d)_ij.
+ *   A  n x n, B  m x m, both symmetric (each is read as its own transpose);
+ *      B = NULL means B = I
  *   loss_dev  device double output
  *   ws  workspace of kron_workspace_bytes(KQ_OP_LOSS, dtype, m, n)
  */
