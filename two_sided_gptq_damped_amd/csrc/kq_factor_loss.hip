@@ -7,18 +7,20 @@ namespace kq {
 
 // ------------------------------------------------------- factor accumulation
 // S <- beta S + alpha X^T X (FastKron page, section 3.2 'Marginal' factors and
-// section 2.6's accumulation over the calibration set).  One workgroup per
-// 64 x 64 tile of the lower triangle (I >= J); the tile and its mirror are both
-// written, so the full symmetric matrix is produced.  The diagonal tile writes
-// each element once.
+// section 2.6's accumulation over the calibration set), on the 64 x 64 tiles of
+// the lower triangle (I >= J); each tile and its mirror are written, so the full
+// symmetric matrix is produced, and a diagonal tile writes each element once.
+// Work items: the T (T - 1) / 2 tiles below the diagonal, one workgroup each,
+// and the T diagonal tiles in pairs.  At T = 64 that is 2048 workgroups, a
+// whole number of the 8-per-CU rounds, where one workgroup per tile would leave
+// 32 tiles to a second round; the 32 pair items come first so that they start
+// in the first wave of dispatches.
 // EXACT: dim is a multiple of 64, rows of 16 and ldx of 4, so every operand load
 // is in range and vector aligned and the bounds checks are dropped.
 template <typename T, bool EXACT>
-__global__ __launch_bounds__(GEMM_THREADS) void syrk_kernel(const T* __restrict__ X, int64_t ldx, int rows, int dim,
-                                                            T* __restrict__ S, int64_t lds, T alpha, T beta) {
-    const int I = blockIdx.y, J = blockIdx.x;
-    if (J > I) return;
-    __shared__ GemmSmem<T> sm;
+__device__ __forceinline__ void syrk_tile(const T* __restrict__ X, int64_t ldx, int rows, int dim,
+                                          T* __restrict__ S, int64_t lds, T alpha, T beta, int I, int J,
+                                          GemmSmem<T>& sm) {
     WaveAcc<T> acc;
     acc.zero();
     const int mv = dim - I * TILE, nv = dim - J * TILE;
@@ -36,21 +38,42 @@ __global__ __launch_bounds__(GEMM_THREADS) void syrk_kernel(const T* __restrict_
     });
 }
 
+template <typename T, bool EXACT>
+__global__ __launch_bounds__(GEMM_THREADS) void syrk_kernel(const T* __restrict__ X, int64_t ldx, int rows, int dim,
+                                                            T* __restrict__ S, int64_t lds, T alpha, T beta,
+                                                            int tiles) {
+    __shared__ GemmSmem<T> sm;
+    const int npairs = (tiles + 1) / 2;
+    const int item = blockIdx.x;
+    if (item < npairs) {  // diagonal tiles 2 item and 2 item + 1
+        syrk_tile<T, EXACT>(X, ldx, rows, dim, S, lds, alpha, beta, 2 * item, 2 * item, sm);
+        if (2 * item + 1 < tiles)
+            syrk_tile<T, EXACT>(X, ldx, rows, dim, S, lds, alpha, beta, 2 * item + 1, 2 * item + 1, sm);
+        return;
+    }
+    // below the diagonal: o = I (I - 1) / 2 + J with J < I
+    const int o = item - npairs;
+    int I = int((1.0 + sqrt(1.0 + 8.0 * o)) * 0.5);
+    while (I * (I - 1) / 2 > o) --I;
+    while ((I + 1) * I / 2 <= o) ++I;
+    syrk_tile<T, EXACT>(X, ldx, rows, dim, S, lds, alpha, beta, I, o - I * (I - 1) / 2, sm);
+}
+
 kq_status factor_dispatch(kq_dtype dtype, int64_t rows, int64_t dim, const void* X, int64_t ldx, void* S, int64_t lds,
                           double alpha, double beta, hipStream_t st) {
     const int tiles = int((dim + TILE - 1) / TILE);
     const size_t es = dtype == KQ_F64 ? 8 : 4;
     const bool exact = dim % TILE == 0 && rows % KSTEP == 0 && ldx % 4 == 0 &&
                        reinterpret_cast<uintptr_t>(X) % (4 * es) == 0;
-    const dim3 grid(tiles, tiles), block(GEMM_THREADS);
+    const dim3 grid(unsigned((tiles + 1) / 2 + tiles * (tiles - 1) / 2)), block(GEMM_THREADS);
     if (dtype == KQ_F64) {
         auto k = exact ? syrk_kernel<double, true> : syrk_kernel<double, false>;
         hipLaunchKernelGGL(k, grid, block, 0, st, static_cast<const double*>(X), ldx, int(rows), int(dim),
-                           static_cast<double*>(S), lds, alpha, beta);
+                           static_cast<double*>(S), lds, alpha, beta, tiles);
     } else {
         auto k = exact ? syrk_kernel<float, true> : syrk_kernel<float, false>;
         hipLaunchKernelGGL(k, grid, block, 0, st, static_cast<const float*>(X), ldx, int(rows), int(dim),
-                           static_cast<float*>(S), lds, float(alpha), float(beta));
+                           static_cast<float*>(S), lds, float(alpha), float(beta), tiles);
     }
     KQ_LAUNCHED("syrk_kernel");
     return KQ_OK;
