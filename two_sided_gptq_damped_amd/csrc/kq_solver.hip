@@ -513,18 +513,42 @@ __global__ __launch_bounds__(Band<T>::THREADS) void band_stage1_kernel(const T* 
 // [mid, K1), on 64 x 64 target block (P, Q) of block-diagonal sig = P + Q.
 // KS: K-slice depth of the product (16 at the top node, where many blocks share
 // each CU; 32 below, where a block's loads are its only latency hiding).
+// Block order: with byrow, a 1-D grid walks the target blocks by block row P
+// from the last to the first (sig ascending within a row).  At the top node the
+// K range of block (P, Q) is 2 P + 2 tiles, so the longest blocks are
+// dispatched first and the short ones fill in behind them; otherwise grid
+// (x, y) = (P - first P of the diagonal, sig - sig0).
 template <typename T, int KS>
 __global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T* __restrict__ T1,
                                                                         const T* __restrict__ NB,
                                                                         T* __restrict__ X, int np, int mp, int Mt,
-                                                                        int Nt, int K0, int mid, int K1, int sig0) {
+                                                                        int Nt, int K0, int mid, int K1, int sig0,
+                                                                        int sig1, int byrow) {
     __shared__ GemmSmemK<T, KS> sm;
-    const int sig = sig0 + blockIdx.y;
     const int Mb = Mt >> 1, Nb = Nt >> 1;
-    const int plo = sig - Nb + 1 > 0 ? sig - Nb + 1 : 0;
-    const int P = plo + blockIdx.x;
-    const int phi = sig < Mb - 1 ? sig : Mb - 1;
-    if (P > phi) return;
+    int sig, P;
+    if (byrow) {
+        int b = blockIdx.x;
+        P = -1;
+        sig = 0;
+        for (int p = Mb - 1; p >= 0; --p) {
+            const int lo = sig0 > p ? sig0 : p, hi = sig1 < p + Nb - 1 ? sig1 : p + Nb - 1;
+            const int cnt = hi >= lo ? hi - lo + 1 : 0;
+            if (b < cnt) {
+                P = p;
+                sig = lo + b;
+                break;
+            }
+            b -= cnt;
+        }
+        if (P < 0) return;
+    } else {
+        sig = sig0 + blockIdx.y;
+        const int plo = sig - Nb + 1 > 0 ? sig - Nb + 1 : 0;
+        P = plo + blockIdx.x;
+        const int phi = sig < Mb - 1 ? sig : Mb - 1;
+        if (P > phi) return;
+    }
     const int Q = sig - P;
     const int I0 = 2 * P, J0 = 2 * Q;
     auto in_band = [=](int r, int c) {
@@ -634,8 +658,17 @@ struct SolverRun {
             const int width = Mt < Nt ? Mt / 2 : Nt / 2;
             const bool top = K0 == 0 && K1 == int(L.Mt + L.Nt - 1);
             auto kern = top ? band_stage2_kernel<T, KSTEP> : band_stage2_kernel<T, 2 * KSTEP>;
-            hipLaunchKernelGGL(kern, dim3(width, sig1 - sig0 + 1), dim3(Band<T>::THREADS2), 0, st, T1,
-                               NB, X, int(L.np), int(L.mp), Mt, Nt, K0, mid, K1, sig0);
+            dim3 grid(width, sig1 - sig0 + 1);
+            if (top) {  // one block per target block, longest K ranges first
+                int total = 0;
+                for (int p = 0; p < Mt / 2; ++p) {
+                    const int lo = sig0 > p ? sig0 : p, hi = sig1 < p + Nt / 2 - 1 ? sig1 : p + Nt / 2 - 1;
+                    total += hi >= lo ? hi - lo + 1 : 0;
+                }
+                grid = dim3(total);
+            }
+            hipLaunchKernelGGL(kern, grid, dim3(Band<T>::THREADS2), 0, st, T1, NB, X, int(L.np), int(L.mp), Mt, Nt,
+                               K0, mid, K1, sig0, sig1, top ? 1 : 0);
             KQ_LAUNCHED("band_stage2_kernel");
         }
         return KQ_OK;
