@@ -513,42 +513,31 @@ __global__ __launch_bounds__(Band<T>::THREADS) void band_stage1_kernel(const T* 
 // [mid, K1), on 64 x 64 target block (P, Q) of block-diagonal sig = P + Q.
 // KS: K-slice depth of the product (16 at the top node, where many blocks share
 // each CU; 32 below, where a block's loads are its only latency hiding).
-// Block order: with byrow, a 1-D grid walks the target blocks by block row P
-// from the last to the first (sig ascending within a row).  At the top node the
-// K range of block (P, Q) is 2 P + 2 tiles, so the longest blocks are
-// dispatched first and the short ones fill in behind them; otherwise grid
-// (x, y) = (P - first P of the diagonal, sig - sig0).
+// Block order: a 1-D grid walks the target blocks by block row P from the last
+// to the first (sig ascending within a row).  The K range of block (P, Q) grows
+// with P (at the top node it is 2 P + 2 tiles), so the long blocks are
+// dispatched first and the short ones fill in behind them, and no workgroup is
+// spent on an empty position.
 template <typename T, int KS>
 __global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T* __restrict__ T1,
                                                                         const T* __restrict__ NB,
                                                                         T* __restrict__ X, int np, int mp, int Mt,
                                                                         int Nt, int K0, int mid, int K1, int sig0,
-                                                                        int sig1, int byrow) {
+                                                                        int sig1) {
     __shared__ GemmSmemK<T, KS> sm;
     const int Mb = Mt >> 1, Nb = Nt >> 1;
-    int sig, P;
-    if (byrow) {
-        int b = blockIdx.x;
-        P = -1;
-        sig = 0;
-        for (int p = Mb - 1; p >= 0; --p) {
-            const int lo = sig0 > p ? sig0 : p, hi = sig1 < p + Nb - 1 ? sig1 : p + Nb - 1;
-            const int cnt = hi >= lo ? hi - lo + 1 : 0;
-            if (b < cnt) {
-                P = p;
-                sig = lo + b;
-                break;
-            }
-            b -= cnt;
+    int sig = 0, P = -1;
+    for (int b = blockIdx.x, p = Mb - 1; p >= 0; --p) {
+        const int lo = sig0 > p ? sig0 : p, hi = sig1 < p + Nb - 1 ? sig1 : p + Nb - 1;
+        const int cnt = hi >= lo ? hi - lo + 1 : 0;
+        if (b < cnt) {
+            P = p;
+            sig = lo + b;
+            break;
         }
-        if (P < 0) return;
-    } else {
-        sig = sig0 + blockIdx.y;
-        const int plo = sig - Nb + 1 > 0 ? sig - Nb + 1 : 0;
-        P = plo + blockIdx.x;
-        const int phi = sig < Mb - 1 ? sig : Mb - 1;
-        if (P > phi) return;
+        b -= cnt;
     }
+    if (P < 0) return;
     const int Q = sig - P;
     const int I0 = 2 * P, J0 = 2 * Q;
     auto in_band = [=](int r, int c) {
@@ -655,20 +644,15 @@ struct SolverRun {
         const int sigmax = int(L.Mt / 2 + L.Nt / 2 - 2);
         if (sig1 > sigmax) sig1 = sigmax;
         if (sig1 >= sig0) {
-            const int width = Mt < Nt ? Mt / 2 : Nt / 2;
             const bool top = K0 == 0 && K1 == int(L.Mt + L.Nt - 1);
             auto kern = top ? band_stage2_kernel<T, KSTEP> : band_stage2_kernel<T, 2 * KSTEP>;
-            dim3 grid(width, sig1 - sig0 + 1);
-            if (top) {  // one block per target block, longest K ranges first
-                int total = 0;
-                for (int p = 0; p < Mt / 2; ++p) {
-                    const int lo = sig0 > p ? sig0 : p, hi = sig1 < p + Nt / 2 - 1 ? sig1 : p + Nt / 2 - 1;
-                    total += hi >= lo ? hi - lo + 1 : 0;
-                }
-                grid = dim3(total);
+            int total = 0;  // target blocks
+            for (int p = 0; p < Mt / 2; ++p) {
+                const int lo = sig0 > p ? sig0 : p, hi = sig1 < p + Nt / 2 - 1 ? sig1 : p + Nt / 2 - 1;
+                total += hi >= lo ? hi - lo + 1 : 0;
             }
-            hipLaunchKernelGGL(kern, grid, dim3(Band<T>::THREADS2), 0, st, T1, NB, X, int(L.np), int(L.mp), Mt, Nt,
-                               K0, mid, K1, sig0, sig1, top ? 1 : 0);
+            hipLaunchKernelGGL(kern, dim3(total), dim3(Band<T>::THREADS2), 0, st, T1, NB, X, int(L.np), int(L.mp),
+                               Mt, Nt, K0, mid, K1, sig0, sig1);
             KQ_LAUNCHED("band_stage2_kernel");
         }
         return KQ_OK;
