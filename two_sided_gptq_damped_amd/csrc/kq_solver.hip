@@ -486,8 +486,9 @@ __global__ __launch_bounds__(Band<T>::THREADS) void band_stage1_kernel(const T* 
     const int I0 = 2 * P;  // first 32-row tile of the block
     const int jlo = K0 - I0 - 1 > 0 ? K0 - I0 - 1 : 0;
     const int jend = K1 - I0 < Nt ? K1 - I0 : Nt;  // exclusive, over both rows
-    const int Q = (jlo >> 1) + blockIdx.x;
-    if (2 * Q >= jend) return;
+    // the row's last block first: its K range is the longest at the top node
+    const int Q = ((jend - 1) >> 1) - int(blockIdx.x);
+    if (jend <= 0 || Q < (jlo >> 1)) return;
     const int kl = jlo;
     int kh = 2 * Q + 1;
     if (mid - 1 - I0 < kh) kh = mid - 1 - I0;
