@@ -383,6 +383,21 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     T dfin[E], zfin[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) dfin[i] = zfin[i] = T(0);
+    // The factor coefficients of step d depend on d only, so they are read one step
+    // ahead, while the entries of the current diagonal are rounded; after each
+    // barrier only the exchanged errors are read.
+    T nbn[E], nan_[E];
+    auto coef = [&](int d) {
+        const int as = d - b;  // column source (as, b)
+        const int asc = unsigned(as) > unsigned(ST - 1) ? ST : as;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            nbn[j] = sNB[asc * PB + ar[j]];
+            const int bs = d - ar[j];  // row source (ar[j], bs)
+            nan_[j] = sNAt[b * PA + (unsigned(bs) > unsigned(ST - 1) ? ST : bs)];
+        }
+    };
+    coef(0);
     for (int dq = 0; dq < (2 * ST - 2 + E) / E; ++dq) {
 #pragma unroll
         for (int i = 0; i < E; ++i) {
@@ -402,18 +417,15 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
                     }
                 }
                 __syncthreads();
-                // all LDS operands first, then unconditional updates
-                const int as = d - b;  // column source (as, b)
-                const int asc = unsigned(as) > unsigned(ST - 1) ? ST : as;
                 const T rv = dR[buf][b];
                 T nbv[E], ddv[E], nav[E];
 #pragma unroll
                 for (int j = 0; j < E; ++j) {
-                    nbv[j] = sNB[asc * PB + ar[j]];
                     ddv[j] = dD[buf][ar[j]];
-                    const int bs = d - ar[j];  // row source (ar[j], bs)
-                    nav[j] = sNAt[b * PA + (unsigned(bs) > unsigned(ST - 1) ? ST : bs)];
+                    nbv[j] = nbn[j];
+                    nav[j] = nan_[j];
                 }
+                if (d + 1 < 2 * ST - 1) coef(d + 1);
 #pragma unroll
                 for (int j = 0; j < E; ++j) {
                     const T cr = ddv[j] * nav[j];
