@@ -158,8 +158,32 @@ __device__ __forceinline__ void quantize_fast(T x, T s, T rs, T qmin, T qmax, T&
     v = s * z;
 }
 
-constexpr int LEAF_THREADS = 512;  // the sweep: two entries per thread
-constexpr int LEAF_E = ST * ST / LEAF_THREADS;
+// The value of v in the next lower lane of the wave (lane 0 gets 0): a DPP
+// shift of the whole wave by one lane.
+__device__ __forceinline__ float lane_below(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x138, 0xf, 0xf, false));
+}
+__device__ __forceinline__ double lane_below(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(u)), 0x138, 0xf, 0xf, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(u >> 32)), 0x138, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
+// N consecutive LDS entries as one vector access.
+template <typename T, int N>
+struct VecN {
+    typedef T V __attribute__((ext_vector_type(N)));
+    V v;
+    __device__ void load(const T* p) { v = *reinterpret_cast<const V*>(p); }
+    __device__ void store(T* p) const { *reinterpret_cast<V*>(p) = v; }
+    __device__ T operator[](int j) const { return v[j]; }
+    __device__ void set(int j, T x) { v[j] = x; }
+};
+
+constexpr int LEAF_THREADS = 512;   // the chunk products and the table set-up
+constexpr int SWEEP_THREADS = 512;  // the sweep: two entries per thread
+constexpr int LEAF_E = ST * ST / SWEEP_THREADS;
 
 template <typename T>
 __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
@@ -173,8 +197,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     constexpr int PK = ST + 4;  // k-major staging rows, 16-byte aligned
     __shared__ __attribute__((aligned(16))) T sNB[(ST + 1) * PB];  // sNB[as][a] = N_B[..as][..a], row ST = 0
     __shared__ T sNAt[ST * PA];                                    // sNAt[b][bs] = N_A[..bs][..b], col ST = 0
-    __shared__ __attribute__((aligned(16))) T dD[2][ST];           // errors of the current diagonal, by row
-    __shared__ T dR[2][ST];                                        // row-accumulated errors, by column
+    constexpr int NROUND = (2 * ST - 1 + LEAF_E - 1) / LEAF_E;  // sweep rounds
     // chunk operands of up to BATCH slices: A(r, k) at [k][r], B(k, c) at [k][c]
     constexpr int MAXS = 2 * (CHUNK - 1);                  // most slices a leaf needs
     constexpr int BATCH = sizeof(T) == 4 ? MAXS : MAXS / 2;  // staged together (LDS budget)
@@ -224,27 +247,31 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         if (u < BATCH && u < ns) fetch(u, pa[v], pb[v]);
     }
 
-    for (int e = t; e < ST * ST; e += LEAF_THREADS) {
-        const int r = e >> 5, c = e & 31;
+    constexpr int FE = ST * ST / LEAF_THREADS;  // factor-block entries per thread
+    T fnb[FE], fna[FE];                         // kept for the sweep's tables
+#pragma unroll
+    for (int u = 0; u < FE; ++u) {
+        const int e = t + u * LEAF_THREADS, r = e >> 5, c = e & 31;
         const T nb = NB ? NB[int64_t(I * ST + r) * mp + I * ST + c] : T(0);
-        sNB[r * PB + c] = r == c ? T(0) : nb;
+        fnb[u] = r == c ? T(0) : nb;
+        sNB[r * PB + c] = fnb[u];
         const T na = NA[int64_t(J * ST + r) * np + J * ST + c];
-        sNAt[c * PA + r] = r == c ? T(0) : na;
+        fna[u] = r == c ? T(0) : na;
+        sNAt[c * PA + r] = fna[u];
     }
     if (t < ST) {
         sNB[ST * PB + t] = T(0);
         sNAt[t * PA + ST] = T(0);
-        dD[0][t] = dD[1][t] = T(0);
-        dR[0][t] = dR[1][t] = T(0);
     }
 
     // Two layouts of the tile over the threads, both with column b = t % 32:
     //   block layout  threads t < 256, rows r0 + i (four each): vector LDS reads,
     //                 coalesced global access, the chunk products;
-    //   sweep layout  all threads, rows ar[i] = (E g - b + i) mod 32 with g = t / 32
-    //                 and E = LEAF_E entries each: entry i of every thread lies on
-    //                 an element diagonal congruent to i mod E, so the entry to
-    //                 round at step d sits in slot d % E of every thread.
+    //   sweep layout  threads t < SWEEP_THREADS, rows ar[i] = (E g - b + i) mod 32
+    //                 with g = t / 32 and E = LEAF_E entries each: entry i of every
+    //                 thread lies on an element diagonal congruent to i mod E, and
+    //                 all entries of diagonal d sit in slot d % E of group
+    //                 (d mod 32) / E.
     constexpr int E = LEAF_E;
     const int g = t >> 5;  // sweep layout: column b, rows (E g - b + i) mod 32
     int ar[E], dg[E];
@@ -368,82 +395,190 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         for (int i = 0; i < 4; ++i) acc[i] += crow[i] + ccol[i];
     }
 
-    // ---- to the sweep layout through LDS
-    __syncthreads();  // the prologue's reads of bufA are done
+    // ---- to the sweep layout through LDS, and the sweep's factor tables
+    // The staging area is free from here on.  Beside bufA / bufB it holds the
+    // factor coefficients in the form the sweep reads them: the coefficient of
+    // diagonal d's source for the entry (a, b) sits at a fixed offset from a
+    // per-entry base,
+    //   cB[(d - b + ST) PB + a] = N_B[d - b][a]   (column source (d - b, b))
+    //   cA[b PT + d - a + ST]   = N_A[d - a][b]   (row source (a, d - a)),
+    // zero wherever the source lies off the tile (and, as in sNB / sNAt, on and
+    // below the diagonal), so the unrolled sweep spends no arithmetic on addresses.
+    constexpr int NRB = 3 * ST + 4;  // rows of cB; d - b + ST stays in [1, NRB) for d <= 2 ST + 3
+    constexpr int PT = 3 * ST + 4;   // row pitch of cA (even: lanes step PT + 1 apart)
+    T* const cB = stg[0][0] + 2 * ST * PK;
+    T* const cA = cB + NRB * PB;
+    // the sweep's exchange, one slice per round: errors by row, row-accumulated
+    // errors by column
+    T* const xD = cA + ST * PT;           // [round][row][diagonal of the round]
+    T* const xR = xD + NROUND * ST * E;  // [round][column][diagonal of the round]
+    static_assert(2 * ST * PK + NRB * PB + ST * PT + 2 * NROUND * ST * E <= sizeof(stg) / sizeof(T),
+                  "staging area too small");
+    static_assert((2 * ST * PK + NRB * PB + ST * PT) % 8 == 0, "32-byte aligned exchange slices");
+    __syncthreads();  // the prologue's reads of the staging area are done
     if (blk) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) bufA[(r0 + i) * PK + b] = acc[i];
     }
+    {
+        // zero lines, four entries per store: cB rows [0, ST) and [2 ST, NRB), cA
+        // columns [0, ST) and [2 ST, PT) of every row; then the factor entries
+        constexpr int ZB0 = ST * PB / 4, ZB1 = (NRB - 2 * ST) * PB / 4;
+        constexpr int ZAR = ST / 4 + (PT - 2 * ST) / 4;  // per cA row
+        static_assert(PB % 4 == 0 && PT % 4 == 0 && (2 * ST * PK) % 4 == 0, "16-byte table lines");
+        Vec4<T> z4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z4.set(j, T(0));
+        for (int u = t; u < ZB0 + ZB1 + ST * ZAR; u += LEAF_THREADS) {
+            T* q;
+            if (u < ZB0) {
+                q = cB + 4 * u;
+            } else if (u < ZB0 + ZB1) {
+                q = cB + 2 * ST * PB + 4 * (u - ZB0);
+            } else {
+                const int v = u - ZB0 - ZB1, r = v / ZAR, k = v - r * ZAR;
+                q = cA + r * PT + (k < ST / 4 ? 4 * k : 2 * ST + 4 * (k - ST / 4));
+            }
+            z4.store(q);
+        }
+#pragma unroll
+        for (int u = 0; u < FE; ++u) {
+            const int e = t + u * LEAF_THREADS, r = e >> 5, c = e & 31;
+            cB[(r + ST) * PB + c] = fnb[u];  // N_B[r][c]
+            cA[c * PT + ST + r] = fna[u];    // N_A[r][c]
+        }
+    }
     __syncthreads();
+    if (t >= SWEEP_THREADS) return;  // the later barriers wait for the sweep's waves only
 #pragma unroll
     for (int i = 0; i < E; ++i) x[i] = bufA[ar[i] * PK + b];
 
-    // ---- the sweep: 2 ST - 1 element anti-diagonals, one barrier each
+    // ---- the sweep: 2 ST - 1 element anti-diagonals, E per round.
+    // A round takes diagonals d .. d + E - 1 (d a multiple of E), all held by group
+    // gd = (d mod ST) / E, slot k holding diagonal d + k.  For the entry (a, b) of
+    // slot k and m < k, diagonal d + m's column source (d + m - b, b) is slot m of
+    // the same thread and its row source (a, d + m - a) = (a, b - (k - m)) is slot m
+    // of the lane k - m below.  So the wave of group gd (the round's producer)
+    // rounds the round's diagonals one after the other, each slot first taking the
+    // feedback of the earlier ones (lane shifts bring the row sources), and
+    // publishes the errors; after a barrier every wave adds the feedback of d,
+    // d + 1, ... to its entries in turn: the same operations in the same order as
+    // one diagonal at a time.  The next round's producer does so right before its own rounding,
+    // in one stretch of code, so that its chain overlaps the rest of its feedback
+    // arithmetic.
+    // Sources that do not exist have zero coefficients and every value the group
+    // exchanges is finite, so it writes all of its slots, and diagonals past
+    // 2 ST - 2 (outside the tile) contribute nothing.  A rounded entry's error and
+    // code go straight to bufB (k-major, for the epilogue) and bufA; each entry of
+    // bufA is read (as x) and later written by the same thread.
+    using VE = VecN<T, E>;
     const T tqmin = T(qmin), tqmax = T(qmax);
-    T dfin[E], zfin[E];
+    const T* pB[E];  // + d PB: N_B coefficient of diagonal d for slot k
+    const T* pA[E];  // + d: N_A coefficient of diagonal d for slot k
 #pragma unroll
-    for (int i = 0; i < E; ++i) dfin[i] = zfin[i] = T(0);
-    // The factor coefficients of step d depend on d only, so they are read one step
-    // ahead, while the entries of the current diagonal are rounded; after each
-    // barrier only the exchanged errors are read.
-    T nbn[E], nan_[E];
-    auto coef = [&](int d) {
-        const int as = d - b;  // column source (as, b)
-        const int asc = unsigned(as) > unsigned(ST - 1) ? ST : as;
+    for (int k = 0; k < E; ++k) {
+        pB[k] = cB + (ST - b) * PB + ar[k];
+        pA[k] = cA + b * PT + ST - ar[k];
+    }
+    // coefficients of round d: [diagonal d + m][slot k]; the in-round chain's
+    // (m < k) are read first
+    auto coef = [&](int d, T (&nb)[E][E], T (&na)[E][E]) {
 #pragma unroll
-        for (int j = 0; j < E; ++j) {
-            nbn[j] = sNB[asc * PB + ar[j]];
-            const int bs = d - ar[j];  // row source (ar[j], bs)
-            nan_[j] = sNAt[b * PA + (unsigned(bs) > unsigned(ST - 1) ? ST : bs)];
-        }
+        for (int k = 1; k < E; ++k)
+#pragma unroll
+            for (int m = 0; m < k; ++m) {
+                nb[m][k] = pB[k][(d + m) * PB];
+                na[m][k] = pA[k][d + m];
+            }
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+#pragma unroll
+            for (int m = k; m < E; ++m) {
+                nb[m][k] = pB[k][(d + m) * PB];
+                na[m][k] = pA[k][d + m];
+            }
     };
-    coef(0);
-    for (int dq = 0; dq < (2 * ST - 2 + E) / E; ++dq) {
+    // round d's rounding chain (the wave of group gd) and its publication
+    auto chain = [&](int d, const T (&nb)[E][E], const T (&na)[E][E]) {
+        const int r = d / E;
+        T e[E], q[E], z[E];
+        T sh[E][E];  // sh[m][s]: e[m] of the lane s below
 #pragma unroll
-        for (int i = 0; i < E; ++i) {
-            const int d = E * dq + i;
-            if (d < 2 * ST - 1) {
-                const int buf = d & 1;
-                {
-                    // slot i holds this thread's entry on diagonal d, if it has one
-                    T z, v;
-                    quantize_fast(x[i], sc[i], rs[i], tqmin, tqmax, z, v);
-                    const T delta = v - x[i];
-                    if (dg[i] == d) {
-                        dD[buf][ar[i]] = delta;
-                        dR[buf][b] = rp[i] + delta;
-                        dfin[i] = delta;
-                        zfin[i] = z;
-                    }
-                }
-                __syncthreads();
-                const T rv = dR[buf][b];
-                T nbv[E], ddv[E], nav[E];
+        for (int k = 0; k < E; ++k) {
+            T xk = x[k], rk = rp[k];
 #pragma unroll
-                for (int j = 0; j < E; ++j) {
-                    ddv[j] = dD[buf][ar[j]];
-                    nbv[j] = nbn[j];
-                    nav[j] = nan_[j];
-                }
-                if (d + 1 < 2 * ST - 1) coef(d + 1);
+            for (int m = 0; m < k; ++m) {
+                xk = kfma(sh[m][k - m], na[m][k], kfma(nb[m][k], q[m], xk));
+                rk = kfma(sh[m][k - m], na[m][k], rk);
+            }
+            T v;
+            quantize_fast(xk, sc[k], rs[k], tqmin, tqmax, z[k], v);
+            e[k] = v - xk;
+            q[k] = rk + e[k];
+            T u = e[k];
 #pragma unroll
-                for (int j = 0; j < E; ++j) {
-                    const T cr = ddv[j] * nav[j];
-                    x[j] = kfma(nbv[j], rv, x[j]) + cr;
-                    rp[j] += cr;
-                }
+            for (int sft = 1; sft < E - k; ++sft) {
+                u = lane_below(u);
+                sh[k][sft] = u;
             }
         }
-    }
-
-    // ---- back to the block layout: errors k-major in bufB (for the epilogue), codes in bufA
-    __syncthreads();
+        if (g == ((d & (ST - 1)) / E)) {
+            VE qq;
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-        bufB[b * PK + ar[i]] = dfin[i];
-        bufA[ar[i] * PK + b] = zfin[i];
+            for (int k = 0; k < E; ++k) {
+                xD[(r * ST + ar[k]) * E + k] = e[k];
+                qq.set(k, q[k]);
+            }
+            qq.store(xR + (r * ST + b) * E);
+#pragma unroll
+            for (int k = 0; k < E; ++k)
+                if (dg[k] == d + k) {
+                    bufB[b * PK + ar[k]] = e[k];
+                    bufA[ar[k] * PK + b] = z[k];
+                }
+        }
+    };
+    // every entry takes round d's feedback
+    auto feedback = [&](const VE& rv, const VE (&dd)[E], const T (&nb)[E][E], const T (&na)[E][E]) {
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+#pragma unroll
+            for (int m = 0; m < E; ++m) {
+                x[j] = kfma(dd[j][m], na[m][j], kfma(nb[m][j], rv[m], x[j]));
+                rp[j] = kfma(dd[j][m], na[m][j], rp[j]);
+            }
+    };
+    constexpr int WAVE_GROUPS = 64 / ST;  // sweep groups per wave
+    auto producer = [&](int d) { return ((d & (ST - 1)) / E) / WAVE_GROUPS; };
+    T cnb[E][E], cna[E][E];
+    coef(0, cnb, cna);
+    if (wv == producer(0)) chain(0, cnb, cna);
+#pragma unroll
+    for (int d = 0; d < 2 * ST - 1; d += E) {
+        const int r = d / E;
+        __syncthreads();  // round r's errors are published
+        if (d + E >= 2 * ST - 1) break;  // every entry is rounded
+        VE rv, dd[E];
+        rv.load(xR + (r * ST + b) * E);
+#pragma unroll
+        for (int j = 0; j < E; ++j) dd[j].load(xD + (r * ST + ar[j]) * E);
+        T nnb[E][E], nna[E][E];
+        coef(d + E, nnb, nna);
+        if (wv == producer(d + E)) {
+            feedback(rv, dd, cnb, cna);
+            chain(d + E, nnb, nna);
+        } else {
+            feedback(rv, dd, cnb, cna);
+        }
+#pragma unroll
+        for (int m = 0; m < E; ++m)
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                cnb[m][k] = nnb[m][k];
+                cna[m][k] = nna[m][k];
+            }
     }
-    __syncthreads();
+    // the last round's barrier made the errors and codes in bufB / bufA complete
     if (!blk) return;  // no barriers follow
     T dblk[4];
 #pragma unroll
