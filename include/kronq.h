@@ -136,13 +136,21 @@ kq_status kron_row_scales(kq_dtype dtype, int64_t m, int64_t n, const void* W, i
  *   q      base quantizer (see kq_quantizer)
  *   codes  m x n int8 output, ldc >= n
  *   V      m x n output, V_ij = s_i * codes_ij, ldv >= n
+ *   loss_dev  optional device double (NULL: not computed): the proxy loss of the
+ *          result, tr(B_d (V - W) A_d (V - W)^T) with the damped factors U_A, U_B
+ *          stand for, taken from the solver's rounding errors Delta: the error
+ *          feedback makes V - W = L~_B Delta L~_A^T (FastKron page section 2.2), so the loss is
+ *          sum_ij (Delta_ij / ((U_B)_ii (U_A)_jj))^2, summed in fp64 in a fixed
+ *          order.  It equals kron_loss on the same factors up to the rounding of
+ *          the feedback sums (about 1e-6 relative in fp32, 1e-12 in fp64);
+ *          kron_loss recomputes it from W and V alone.  Must be NULL if m or n is 0.
  *   ws     workspace of kron_workspace_bytes(KQ_OP_QUANTIZE, dtype, m, n)
  * Non-finite W or scales give unspecified codes.
  */
 kq_status kron_quantize(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw,
                         const void* U_A, int64_t lda, const void* U_B, int64_t ldb,
                         const kq_quantizer* q, int8_t* codes, int64_t ldc, void* V, int64_t ldv,
-                        void* ws, size_t ws_bytes, void* stream);
+                        double* loss_dev, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Proxy loss D_{A,B} = tr(B_d (V - W) A_d (V - W)^T) (WaterKron page section 1,
@@ -167,7 +175,7 @@ const char* kron_status_string(kq_status status);
 /* Detail of the last failing call on this thread ("" if none). */
 const char* kron_last_error(void);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (kron_quantize gained loss_dev). */
 int32_t kron_abi_version(void);
 
 #ifdef __cplusplus

@@ -226,6 +226,29 @@ def test_loss_matches_oracle(m, n, bidentity):
         assert abs(got - want) <= 1e-12 * abs(want)
 
 
+# kron_quantize's own proxy loss (from its rounding errors) against kron_loss on
+# its output, the trace form from W and V alone.  The two agree up to the rounding
+# of the solver's feedback sums: fp64 1e-10 relative, fp32 1e-4 (the identity
+# V - W = L~_B Delta L~_A^T holds for exact sums; fp32 sums carry ~1e-7 relative
+# error per entry and the fp32-rounded U only approximates the factor of A_d).
+@pytest.mark.parametrize("m,n,two_sided", [(32, 32, True), (100, 70, True), (130, 300, False), (256, 256, True),
+                                           (300, 90, True)])
+def test_quantize_loss_matches_trace_form(m, n, two_sided):
+    say("quantize loss", m, n, two_sided)
+    c = synth.spectral(m, n, config=2)
+    _, UA, _, UB = oracle_factors(c["A"], c["B"] if two_sided else None)
+    s = dense.scales(c["W"], 3, True)
+    for dtype, tol in ((np.float64, 1e-10), (np.float32, 1e-4)):
+        Wt, st = up(c["W"], dtype), up(s, dtype)
+        lo = torch.zeros(1, dtype=torch.float64, device=DEV)
+        _, V, _ = pipeline.quantize(Wt, up(UA, dtype), up(UB, dtype) if two_sided else None, 3, True, scales=st,
+                                    loss_out=lo)
+        trace = pipeline.loss(Wt, V, up(c["A"], dtype), up(c["B"], dtype) if two_sided else None, 0.01).item()
+        got = lo.item()
+        say("  ", dtype.__name__, got, trace, abs(got - trace) / trace)
+        assert trace > 0 and abs(got - trace) <= tol * trace
+
+
 @pytest.mark.parametrize("per_row", [True, False])
 def test_row_scales_bit_exact(per_row):
     say("scales", per_row)
@@ -244,7 +267,7 @@ def test_pipeline_tiny_all_on_gpu_fp64():
     say("pipeline tiny fp64")
     c = synth.tiny()
     out = pipeline.quantize_layer(up(c["W"], np.float64), up(c["act"], np.float64), up(c["grad"], np.float64),
-                                  bits=4, per_row=False)
+                                  bits=4, per_row=False, check_loss=True)
     A = dense.factor_accumulate(c["act"], alpha=1 / 256)
     B = dense.factor_accumulate(c["grad"], alpha=1 / 256)
     Ad, UA, Bd, UB = oracle_factors(A, B)
@@ -253,5 +276,6 @@ def test_pipeline_tiny_all_on_gpu_fp64():
     Zg = out["codes"].cpu().numpy()
     assert np.all((Zg == Zo) | (compare.tie_distance(Yo) < 1e-9))
     lo = dense.proxy_loss(c["W"], Vo, Ad, Bd)
-    assert abs(out["loss"].item() - lo) <= 1e-10 * lo
+    assert abs(out["loss"].item() - lo) <= 1e-10 * lo  # from the solver's errors
+    assert abs(out["loss_check"].item() - lo) <= 1e-10 * lo  # kron_loss on W and V
     assert abs(out["trace_A"].item() * out["trace_B"].item() - dense.sensitivity(A, B)) <= 1e-12 * dense.sensitivity(A, B)

@@ -61,7 +61,7 @@ def library() -> ctypes.CDLL:
     lib.kron_row_scales.argtypes = [ctypes.c_int, i64, i64, vp, i64, i32, i32, vp, vp]
     lib.kron_quantize.restype = ctypes.c_int
     lib.kron_quantize.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64,
-                                  ctypes.POINTER(_Quantizer), vp, i64, vp, i64, vp, sz, vp]
+                                  ctypes.POINTER(_Quantizer), vp, i64, vp, i64, vp, vp, sz, vp]
     lib.kron_loss.restype = ctypes.c_int
     lib.kron_loss.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, dbl, vp, vp, sz, vp]
     lib.kron_status_string.restype = ctypes.c_char_p
@@ -146,14 +146,18 @@ def kron_row_scales(W: torch.Tensor, bits: int, per_row: bool, scales: torch.Ten
 
 
 def kron_quantize(W: torch.Tensor, U_A: torch.Tensor, U_B: torch.Tensor | None, bits: int, per_row: bool,
-                  scales: torch.Tensor, codes: torch.Tensor, V: torch.Tensor, ws: torch.Tensor):
-    """Two-sided GPTQ of W (m x n); U_B None means B = I.  Writes codes (int8) and V."""
+                  scales: torch.Tensor, codes: torch.Tensor, V: torch.Tensor, ws: torch.Tensor,
+                  loss: torch.Tensor | None = None):
+    """Two-sided GPTQ of W (m x n); U_B None means B = I.  Writes codes (int8) and V,
+    and, if given, loss[0] (fp64) = the proxy loss of V from the rounding errors."""
     m, n = W.shape
+    if loss is not None and (loss.dtype != torch.float64 or loss.numel() < 1):
+        raise ValueError("kron_quantize: loss must be a float64 tensor with at least one element")
     q = _Quantizer(int(bits), int(bool(per_row)), scales.data_ptr())
     ldb = _ld(U_B) if U_B is not None else 0
     _check(library().kron_quantize(_dtype_code(W), m, n, _ptr(W), _ld(W), _ptr(U_A), _ld(U_A), _ptr(U_B), ldb,
-                                   ctypes.byref(q), _ptr(codes), _ld(codes), _ptr(V), _ld(V), _ptr(ws), ws.numel(),
-                                   _stream(W.device)))
+                                   ctypes.byref(q), _ptr(codes), _ld(codes), _ptr(V), _ld(V), _ptr(loss), _ptr(ws),
+                                   ws.numel(), _stream(W.device)))
     return codes, V
 
 

@@ -20,7 +20,8 @@ size_t quantize_workspace_bytes(kq_dtype dtype, int64_t m, int64_t n);
 size_t prepare_workspace_bytes(int64_t d);
 size_t loss_workspace_bytes(int64_t m, int64_t n);
 kq_status quantize_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const void*, int64_t, const void*,
-                            int64_t, const kq_quantizer*, int8_t*, int64_t, void*, int64_t, void*, hipStream_t);
+                            int64_t, const kq_quantizer*, int8_t*, int64_t, void*, int64_t, double*, void*,
+                            hipStream_t);
 kq_status prepare_dispatch(kq_dtype, int64_t, const void*, int64_t, double, void*, int64_t, double*, double*,
                            int32_t*, void*, hipStream_t);
 kq_status factor_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, void*, int64_t, double, double,
@@ -59,7 +60,7 @@ using namespace kq;
 
 extern "C" {
 
-int32_t kron_abi_version(void) { return 1; }
+int32_t kron_abi_version(void) { return 2; }
 
 const char* kron_status_string(kq_status s) {
     switch (s) {
@@ -128,20 +129,23 @@ kq_status kron_row_scales(kq_dtype dtype, int64_t m, int64_t n, const void* W, i
 
 kq_status kron_quantize(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* U_A, int64_t lda,
                         const void* U_B, int64_t ldb, const kq_quantizer* q, int8_t* codes, int64_t ldc, void* V,
-                        int64_t ldv, void* ws, size_t ws_bytes, void* stream) {
+                        int64_t ldv, double* loss_dev, void* ws, size_t ws_bytes, void* stream) {
     set_error("");
     if (!dtype_ok(dtype)) return invalid("kron_quantize: dtype must be KQ_F32 or KQ_F64");
     if (m < 0 || n < 0 || m > MAX_DIM || n > MAX_DIM) return invalid("kron_quantize: m, n must be in [0, 65536]");
     if (!q) return invalid("kron_quantize: null quantizer");
     if (q->bits < 2 || q->bits > 8) return invalid("kron_quantize: bits must be in [2, 8]");
     if (q->per_row != 0 && q->per_row != 1) return invalid("kron_quantize: per_row must be 0 or 1");
-    if (m == 0 || n == 0) return KQ_OK;
+    if (m == 0 || n == 0) {
+        if (loss_dev) return invalid("kron_quantize: no loss for an empty matrix");
+        return KQ_OK;
+    }
     if (!W || !U_A || !codes || !V || !q->scales) return invalid("kron_quantize: null pointer");
     if (ldw < n || lda < n || ldc < n || ldv < n || (U_B && ldb < m))
         return invalid("kron_quantize: leading dimension too small");
     kq_status s = check_ws(ws, ws_bytes, quantize_workspace_bytes(dtype, m, n), "kron_quantize");
     if (s != KQ_OK) return s;
-    return quantize_dispatch(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, ws,
+    return quantize_dispatch(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev, ws,
                              static_cast<hipStream_t>(stream));
 }
 

@@ -539,4 +539,16 @@ __device__ __forceinline__ void for_each_acc(const WaveAcc<T>& acc, F&& f) {
         f(r0 + WaveAcc<T>::row(r, lane), c0 + WaveAcc<T>::col(r, lane), acc.get(r));
 }
 
+// Fixed-order sum of the 256 per-thread values of a workgroup.
+__device__ __forceinline__ double block_sum_256(double s, double* red) {
+    __syncthreads();  // earlier readers of red are done
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (int(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    return red[0];
+}
+
 }  // namespace kq

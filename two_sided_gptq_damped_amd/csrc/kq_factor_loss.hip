@@ -263,18 +263,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_tn_f64_big_kernel(const dou
     big_for_each(acc, [&](int r, int c, double v) { out[int64_t(r) * ldc + c] = v; });
 }
 
-// Fixed-order sum of the 256 per-thread values of a workgroup.
-__device__ __forceinline__ double block_sum_256(double s, double* red) {
-    __syncthreads();  // earlier readers of red are done
-    red[threadIdx.x] = s;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (int(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
-        __syncthreads();
-    }
-    return red[0];
-}
-
 // One 64 x 64 tile (I <= J) of a symmetric product S = X^T Y (X, Y: K x W
 // row-major), weighted by the damped factor F:
 //   partial[tile] = w sum_rc F[I r][J c] S_IJ[r][c],  w = 1 on the diagonal, 2 above.

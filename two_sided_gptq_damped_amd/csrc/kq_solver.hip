@@ -723,12 +723,55 @@ __global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T*
     });
 }
 
+// Proxy loss of the result from the solver's errors.  The feedback gives
+// V - W = L~_B Delta L~_A^T exactly in exact arithmetic (FastKron page, section
+// 2.2), and A_d^{-1} = U_A^T U_A with U_A = diag(U_A) N_A makes
+// A_d = L~_A^{-T} diag(U_A)^{-2} L~_A^{-1} (likewise B_d), so
+//   tr(B_d (V - W) A_d (V - W)^T) = sum_ij (Delta_ij / (U_B,ii U_A,jj))^2.
+// Rows go round-robin over ELOSS_PARTS workgroups; every sum runs in a fixed
+// order, so the result is deterministic.
+constexpr int ELOSS_PARTS = 512;
+
+template <typename T>
+__global__ void diag_recip_kernel(const T* __restrict__ U, int64_t ldu, int d, double* __restrict__ out) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < d) out[j] = 1.0 / double(U[int64_t(j) * ldu + j]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void error_loss_partial_kernel(const T* __restrict__ D, int64_t np, int m, int n,
+                                                                 const double* __restrict__ ra,
+                                                                 const double* __restrict__ rb,
+                                                                 double* __restrict__ partial) {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int i = blockIdx.x; i < m; i += gridDim.x) {
+        const double ri = rb ? rb[i] : 1.0;
+        const T* row = D + int64_t(i) * np;
+        for (int j = threadIdx.x; j < n; j += blockDim.x) {
+            const double q = double(row[j]) * ra[j] * ri;
+            s = __builtin_fma(q, q, s);
+        }
+    }
+    const double tot = block_sum_256(s, red);
+    if (threadIdx.x == 0) partial[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(256) void error_loss_final_kernel(const double* __restrict__ partial, int count,
+                                                               double* __restrict__ out) {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < count; i += blockDim.x) s += partial[i];
+    const double tot = block_sum_256(s, red);
+    if (threadIdx.x == 0) *out = tot;
+}
+
 // ------------------------------------------------------------------- host side
 
 struct SolverLayout {
     int64_t mp, np, Mt, Nt;  // padded extents; tile counts in 32-tiles
     size_t bytes;
-    size_t off_NA, off_NB, off_X, off_D, off_T1, off_S;
+    size_t off_NA, off_NB, off_X, off_D, off_T1, off_S, off_L;
 };
 
 SolverLayout solver_layout(kq_dtype dtype, int64_t m, int64_t n) {
@@ -750,6 +793,8 @@ SolverLayout solver_layout(kq_dtype dtype, int64_t m, int64_t n) {
     L.off_D = take(size_t(L.mp) * L.np);
     L.off_T1 = take(size_t(L.mp) * L.np);
     L.off_S = take(size_t(L.mp));
+    L.off_L = off;  // loss scratch (fp64): 1 / U_A,jj, 1 / U_B,ii, partial sums
+    off += align256((size_t(L.np) + size_t(L.mp) + ELOSS_PARTS) * sizeof(double));
     L.bytes = off;
     return L;
 }
@@ -827,7 +872,7 @@ struct SolverRun {
 template <typename T>
 kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T* UA, int64_t lda, const T* UB,
                          int64_t ldb, const kq_quantizer* q, int8_t* codes, int64_t ldc, T* V, int64_t ldv,
-                         void* ws, hipStream_t st) {
+                         double* loss_dev, void* ws, hipStream_t st) {
     const SolverLayout L = solver_layout(sizeof(T) == 8 ? KQ_F64 : KQ_F32, m, n);
     char* base = static_cast<char*>(ws);
     SolverRun<T> run{L, int(m), int(n), -(1 << (q->bits - 1)), (1 << (q->bits - 1)) - 1,
@@ -848,21 +893,37 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
     hipLaunchKernelGGL(init_solver_kernel<T>, blocks(L.mp * L.np), dim3(threads), 0, st, W, ldw, int(m), int(n),
                        int(L.mp), int(L.np), static_cast<const T*>(q->scales), q->per_row, run.X, run.S);
     KQ_LAUNCHED("init_solver_kernel");
-    return run.solve(0, int(L.Mt + L.Nt - 1));
+    const kq_status s = run.solve(0, int(L.Mt + L.Nt - 1));
+    if (s != KQ_OK || !loss_dev) return s;
+    double* ra = reinterpret_cast<double*>(base + L.off_L);
+    double* rb = ra + L.np;
+    double* part = rb + L.mp;
+    hipLaunchKernelGGL(diag_recip_kernel<T>, blocks(n), dim3(threads), 0, st, UA, lda, int(n), ra);
+    KQ_LAUNCHED("diag_recip_kernel");
+    if (UB) {
+        hipLaunchKernelGGL(diag_recip_kernel<T>, blocks(m), dim3(threads), 0, st, UB, ldb, int(m), rb);
+        KQ_LAUNCHED("diag_recip_kernel");
+    }
+    hipLaunchKernelGGL(error_loss_partial_kernel<T>, dim3(ELOSS_PARTS), dim3(256), 0, st, run.D, L.np, int(m),
+                       int(n), ra, UB ? rb : nullptr, part);
+    KQ_LAUNCHED("error_loss_partial_kernel");
+    hipLaunchKernelGGL(error_loss_final_kernel, dim3(1), dim3(256), 0, st, part, ELOSS_PARTS, loss_dev);
+    KQ_LAUNCHED("error_loss_final_kernel");
+    return KQ_OK;
 }
 
 size_t quantize_workspace_bytes(kq_dtype dtype, int64_t m, int64_t n) { return solver_layout(dtype, m, n).bytes; }
 
 kq_status quantize_dispatch(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* UA,
                             int64_t lda, const void* UB, int64_t ldb, const kq_quantizer* q, int8_t* codes,
-                            int64_t ldc, void* V, int64_t ldv, void* ws, hipStream_t st) {
+                            int64_t ldc, void* V, int64_t ldv, double* loss_dev, void* ws, hipStream_t st) {
     if (dtype == KQ_F64)
         return quantize_typed<double>(m, n, static_cast<const double*>(W), ldw, static_cast<const double*>(UA), lda,
                                       static_cast<const double*>(UB), ldb, q, codes, ldc, static_cast<double*>(V),
-                                      ldv, ws, st);
+                                      ldv, loss_dev, ws, st);
     return quantize_typed<float>(m, n, static_cast<const float*>(W), ldw, static_cast<const float*>(UA), lda,
-                                 static_cast<const float*>(UB), ldb, q, codes, ldc, static_cast<float*>(V), ldv, ws,
-                                 st);
+                                 static_cast<const float*>(UB), ldb, q, codes, ldc, static_cast<float*>(V), ldv,
+                                 loss_dev, ws, st);
 }
 
 }  // namespace kq

@@ -10,6 +10,10 @@ from the calibration data, factor them, run the core algorithm):
     codes, V = two-sided GPTQ(W, U_A, U_B, s)
     loss = tr(B_d (V - W) A_d (V - W)^T)
 
+The layer's loss comes from the solver's own rounding errors (kron_quantize's
+loss output, the error-feedback form of the same trace); with check_loss=True
+kron_loss also recomputes it from W and V alone, in fp64.
+
 The two factor chains (accumulate, then prepare) are independent until the
 solver needs both, and a prepare is a long chain of small dependent launches
 (one diagonal block per step).  quantize_layer therefore runs the B chain on a
@@ -43,7 +47,9 @@ def prepare(A: torch.Tensor, damp_rel: float, info: torch.Tensor | None = None):
     return U, tr, lam  # ws goes back to this stream's pool: stream-ordered reuse
 
 
-def quantize(W, U_A, U_B, bits, per_row, scales=None, ws=None):
+def quantize(W, U_A, U_B, bits, per_row, scales=None, ws=None, loss_out=None):
+    """codes, V, scales; loss_out (a float64 device tensor), if given, receives
+    the proxy loss of V from the rounding errors."""
     m, n = W.shape
     if scales is None:
         scales = torch.empty(m if per_row else 1, dtype=W.dtype, device=W.device)
@@ -52,7 +58,7 @@ def quantize(W, U_A, U_B, bits, per_row, scales=None, ws=None):
     V = torch.empty_like(W)
     if ws is None:
         ws = workspace(KQ_OP_QUANTIZE, W.dtype, m, n, W.device)
-    kron_quantize(W, U_A, U_B, bits, per_row, scales, codes, V, ws)
+    kron_quantize(W, U_A, U_B, bits, per_row, scales, codes, V, ws, loss=loss_out)
     return codes, V, scales
 
 
@@ -64,9 +70,10 @@ def loss(W, V, A, B, damp_rel):
     return out
 
 
-def quantize_layer(W, act, grad, bits, per_row=True, damp_rel=0.01, two_sided=True):
+def quantize_layer(W, act, grad, bits, per_row=True, damp_rel=0.01, two_sided=True, check_loss=False):
     """Run the whole path for one layer.  act: N x n activation rows, grad: N x m gradient rows.
-    Raises KronError if a damped factor is not positive definite."""
+    Raises KronError if a damped factor is not positive definite.  The result's
+    "loss" is the solver's; check_loss=True adds "loss_check" from kron_loss."""
     main = torch.cuda.current_stream(W.device)
     info = torch.zeros(2, dtype=torch.int32, device=W.device)
     A = factor(act)
@@ -89,6 +96,9 @@ def quantize_layer(W, act, grad, bits, per_row=True, damp_rel=0.01, two_sided=Tr
     for name, k in (("A", int(bad[0])), ("B", int(bad[1]))):
         if k != 0:
             raise KronError(2, f"kron_prepare: damped factor {name} is not positive definite (pivot step {k})")
-    codes, V, scales = quantize(W, U_A, U_B, bits, per_row)
-    return dict(A=A, B=B, U_A=U_A, U_B=U_B, trace_A=trA, trace_B=trB, codes=codes, V=V, scales=scales,
-                loss=loss(W, V, A, B, damp_rel))
+    lo = torch.empty(1, dtype=torch.float64, device=W.device)
+    codes, V, scales = quantize(W, U_A, U_B, bits, per_row, loss_out=lo)
+    out = dict(A=A, B=B, U_A=U_A, U_B=U_B, trace_A=trA, trace_B=trB, codes=codes, V=V, scales=scales, loss=lo)
+    if check_loss:
+        out["loss_check"] = loss(W, V, A, B, damp_rel)
+    return out
