@@ -5,11 +5,16 @@ is already resident in HBM: K-FAC factor accumulation for A (4096 activation
 rows) and B (4096 gradient rows), damped factor preparation of both, per-row
 scales, two-sided GPTQ (2-bit grid) and the proxy loss, which the solver takes
 from its own rounding errors (tr(B_d E A_d E^T) = sum (Delta_ij / (U_B,ii
-U_A,jj))^2 with the error-feedback identity E = L~_B Delta L~_A^T).  The B factor
-chain runs on a second stream beside the A chain; ``serial_breakdown_ms`` times
-the same calls one after another on one stream, and then kron_loss, which
-recomputes the loss from W and V alone in fp64 (outside the step; both values
-are reported under ``loss``).  ``value`` is weights
+U_A,jj))^2 with the error-feedback identity E = L~_B Delta L~_A^T).  The steps
+are the layers of a job, pipelined as a model block would be: the factor chains
+(A on one side stream, B on another) of layer k + 1 run while layer k is solved
+on the main stream, with two resident buffer sets; every step still computes
+everything from its inputs.  ``ms_per_step`` is the wall time of K steps over K,
+the pipeline fill included.  ``breakdown_ms.single_layer`` is one layer with
+nothing beside it; ``serial_breakdown_ms`` times one layer's calls one after
+another on one stream, and then kron_loss, which recomputes the loss from W and
+V alone in fp64 (outside the step; both values are reported under ``loss``).
+``value`` is weights
 per second of the whole step (m n / step time).  The core solver alone
 (kron_quantize with factors and scales resident, the pages' "core algorithm"
 timing) is reported under ``core``.
@@ -108,83 +113,121 @@ def main() -> int:
     rows = act.shape[0]
     damp = c["damp"]
 
-    # resident buffers and workspaces (allocated once, outside the timed region)
-    A = torch.empty(n, n, dtype=torch.float32, device=dev)
-    B = torch.empty(m, m, dtype=torch.float32, device=dev)
-    UA, UB = torch.empty_like(A), torch.empty_like(B)
-    trA, trB, lamA, lamB = (torch.empty(1, dtype=torch.float64, device=dev) for _ in range(4))
-    infoA, infoB = (torch.zeros(1, dtype=torch.int32, device=dev) for _ in range(2))
-    ws_pa = kq.workspace(kq.KQ_OP_PREPARE, torch.float32, n, 0)
-    ws_pb = kq.workspace(kq.KQ_OP_PREPARE, torch.float32, m, 0)
+    # resident buffers and workspaces (allocated once, outside the timed region).
+    # Two sets: the factor chains of layer k + 1 fill one while layer k is solved
+    # from the other.
+    def buffer_set():
+        S = {"A": torch.empty(n, n, dtype=torch.float32, device=dev),
+             "B": torch.empty(m, m, dtype=torch.float32, device=dev)}
+        S["UA"], S["UB"] = torch.empty_like(S["A"]), torch.empty_like(S["B"])
+        for k in ("trA", "trB", "lamA", "lamB", "loss"):
+            S[k] = torch.empty(1, dtype=torch.float64, device=dev)
+        S["infoA"], S["infoB"] = (torch.zeros(1, dtype=torch.int32, device=dev) for _ in range(2))
+        S["ws_pa"] = kq.workspace(kq.KQ_OP_PREPARE, torch.float32, n, 0)
+        S["ws_pb"] = kq.workspace(kq.KQ_OP_PREPARE, torch.float32, m, 0)
+        S["scales"] = torch.empty(m, dtype=torch.float32, device=dev)
+        S["codes"] = torch.empty(m, n, dtype=torch.int8, device=dev)
+        S["V"] = torch.empty_like(W)
+        for k in ("a_done", "ea", "eb", "q_done"):
+            S[k] = torch.cuda.Event()
+        return S
+
+    sets = [buffer_set(), buffer_set()]
     ws_q = kq.workspace(kq.KQ_OP_QUANTIZE, torch.float32, m, n)
     ws_l = kq.workspace(kq.KQ_OP_LOSS, torch.float32, m, n)
-    scales = torch.empty(m, dtype=torch.float32, device=dev)
-    codes = torch.empty(m, n, dtype=torch.int8, device=dev)
-    V = torch.empty_like(W)
-    loss = torch.empty(1, dtype=torch.float64, device=dev)
     loss_check = torch.empty(1, dtype=torch.float64, device=dev)
+    main = torch.cuda.current_stream()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+
+    def chains(S, k):
+        """Layer k's factor chains: A (product, prepare, then the scales) on sa,
+        B (product, prepare) on sb once the A product is done.  They wait for the
+        solve of layer k - 2, the last user of this buffer set."""
+        if k >= 2:
+            sa.wait_event(S["q_done"])  # sb follows through a_done
+        with torch.cuda.stream(sa):
+            kq.kron_factor_accumulate(act, S["A"], 1.0 / rows, 0.0)
+            S["a_done"].record(sa)
+        sb.wait_event(S["a_done"])
+        with torch.cuda.stream(sb):
+            kq.kron_factor_accumulate(grad, S["B"], 1.0 / rows, 0.0)
+            kq.kron_prepare(S["B"], damp, S["UB"], S["ws_pb"], trace_out=S["trB"], lambda_out=S["lamB"],
+                            info=S["infoB"])
+            S["eb"].record(sb)
+        with torch.cuda.stream(sa):
+            kq.kron_prepare(S["A"], damp, S["UA"], S["ws_pa"], trace_out=S["trA"], lambda_out=S["lamA"],
+                            info=S["infoA"])
+            kq.kron_row_scales(W, bits, True, S["scales"])
+            S["ea"].record(sa)
+
+    def solve(S):
+        """Layer k's solve on the main stream, with its proxy loss (from the
+        rounding errors), once both chains of the layer are done."""
+        main.wait_event(S["ea"])
+        main.wait_event(S["eb"])
+        kq.kron_quantize(W, S["UA"], S["UB"], bits, True, S["scales"], S["codes"], S["V"], ws_q, loss=S["loss"])
+        S["q_done"].record(main)
+
+    def step(k):
+        """One layer (step k of the run): its chains, then its solve.  Issued in
+        this order, the chains of layer k + 1 run beside the solve of layer k."""
+        S = sets[k % 2]
+        chains(S, k)
+        solve(S)
+
     names = ["factor", "prepare", "scales", "quantize_and_loss", "loss_check"]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()  # default priority
-    a_done = torch.cuda.Event()
-
-    def step(record=False):
-        """One layer.  The B chain (its product, then its prepare) runs on a
-        second stream once the A product is done, beside the A chain; the solver
-        waits for both and also returns the layer's proxy loss (from its rounding
-        errors).  Step k + 1's B chain starts after step k's solve, since it
-        waits on an event recorded later on the in-order main stream."""
-        if record:
-            ev[0].record()
-        kq.kron_factor_accumulate(act, A, 1.0 / rows, 0.0)
-        a_done.record(main)
-        side.wait_event(a_done)
-        with torch.cuda.stream(side):
-            kq.kron_factor_accumulate(grad, B, 1.0 / rows, 0.0)
-            kq.kron_prepare(B, damp, UB, ws_pb, trace_out=trB, lambda_out=lamB, info=infoB)
-        kq.kron_prepare(A, damp, UA, ws_pa, trace_out=trA, lambda_out=lamA, info=infoA)
-        kq.kron_row_scales(W, bits, True, scales)
-        main.wait_stream(side)
-        if record:
-            ev[1].record()
-        kq.kron_quantize(W, UA, UB, bits, True, scales, codes, V, ws_q, loss=loss)
-        if record:
-            ev[2].record()
 
     def serial_step():
-        """The same calls one after another on one stream, timed per phase, then
-        kron_loss: the same loss recomputed from W and V alone (not part of the step)."""
+        """One layer's calls one after another on one stream, timed per phase,
+        then kron_loss: the same loss recomputed from W and V alone (not part of
+        the step)."""
+        S = sets[0]
         ev[0].record()
-        kq.kron_factor_accumulate(act, A, 1.0 / rows, 0.0)
-        kq.kron_factor_accumulate(grad, B, 1.0 / rows, 0.0)
+        kq.kron_factor_accumulate(act, S["A"], 1.0 / rows, 0.0)
+        kq.kron_factor_accumulate(grad, S["B"], 1.0 / rows, 0.0)
         ev[1].record()
-        kq.kron_prepare(A, damp, UA, ws_pa, trace_out=trA, lambda_out=lamA, info=infoA)
-        kq.kron_prepare(B, damp, UB, ws_pb, trace_out=trB, lambda_out=lamB, info=infoB)
+        kq.kron_prepare(S["A"], damp, S["UA"], S["ws_pa"], trace_out=S["trA"], lambda_out=S["lamA"],
+                        info=S["infoA"])
+        kq.kron_prepare(S["B"], damp, S["UB"], S["ws_pb"], trace_out=S["trB"], lambda_out=S["lamB"],
+                        info=S["infoB"])
         ev[2].record()
-        kq.kron_row_scales(W, bits, True, scales)
+        kq.kron_row_scales(W, bits, True, S["scales"])
         ev[3].record()
-        kq.kron_quantize(W, UA, UB, bits, True, scales, codes, V, ws_q, loss=loss)
+        kq.kron_quantize(W, S["UA"], S["UB"], bits, True, S["scales"], S["codes"], S["V"], ws_q, loss=S["loss"])
         ev[4].record()
-        kq.kron_loss(W, V, A, B, damp, loss_check, ws_l)
+        kq.kron_loss(W, S["V"], S["A"], S["B"], damp, loss_check, ws_l)
         ev[5].record()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    k = 0
     for _ in range(args.warmup):
-        step()
+        step(k)
+        k += 1
     torch.cuda.synchronize()
-    assert infoA.item() == 0 and infoB.item() == 0, "factor not positive definite"
+    for S in sets[:min(2, max(1, args.warmup))]:
+        assert S["infoA"].item() == 0 and S["infoB"].item() == 0, "factor not positive definite"
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(record=True)  # events are re-recorded each step; the last step's remain
+        step(k)
+        k += 1
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    overlapped = {"factors_prepares_scales": ev[0].elapsed_time(ev[1]),
-                  "quantize_and_loss": ev[1].elapsed_time(ev[2])}
+
+    # one layer alone (nothing before or after it in flight): its chains, then its solve
+    single = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        ev[0].record()
+        sa.wait_stream(main)  # the chains start after the first event
+        step(0)  # k = 0: no wait on an earlier solve; both sets are idle here
+        ev[1].record()
+        torch.cuda.synchronize()
+        single.append(ev[0].elapsed_time(ev[1]))
 
     serial = {k: [] for k in names}
     for _ in range(3):
@@ -192,6 +235,8 @@ def main() -> int:
         torch.cuda.synchronize()
         for i, k in enumerate(names):
             serial[k].append(ev[i].elapsed_time(ev[i + 1]))
+    loss = sets[0]["loss"]
+    UA, UB, scales, codes, V = (sets[0][x] for x in ("UA", "UB", "scales", "codes", "V"))
     # the step's loss (from the solver's errors) against kron_loss on the same output
     l_solver, l_trace = float(loss.item()), float(loss_check.item())
 
@@ -226,13 +271,14 @@ def main() -> int:
                         f"A, B from {rows} activation / gradient rows with lognormal channel scales; "
                         f"damping 0.01; {bits}-bit grid, per-row scales",
             "m": m, "n": n, "bits": bits, "calibration_rows": rows,
-            "step": "[factor_accumulate(A), prepare(A), row_scales] beside [factor_accumulate(B), prepare(B)] "
-                    "on a second stream, then quantize with its proxy loss (from the rounding errors)",
+            "step": "one layer: [factor_accumulate(A), prepare(A), row_scales] beside [factor_accumulate(B), "
+                    "prepare(B)] on two side streams, then quantize with its proxy loss (from the rounding errors) "
+                    "on the main stream; layers are pipelined, layer k + 1's chains beside layer k's solve",
         },
         "loss": {"solver": l_solver, "kron_loss": l_trace, "rel_diff": abs(l_solver - l_trace) / l_trace,
                  "note": "kron_loss (trace form from W and V, fp64) runs after the timed steps as a check; "
                          "its time is serial_breakdown_ms.loss_check"},
-        "breakdown_ms": overlapped,
+        "breakdown_ms": {"single_layer": float(np.median(single))},
         "serial_breakdown_ms": {k: float(np.median(v)) for k, v in serial.items()},
         "core": {
             "what": "kron_quantize only, factors and scales resident (median of repeats)",

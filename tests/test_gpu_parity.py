@@ -261,6 +261,28 @@ def test_row_scales_bit_exact(per_row):
         assert np.array_equal(s.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("two_sided", [True, False])
+def test_pipelined_layers_equal_one_at_a_time(two_sided):
+    # quantize_layers overlaps layer k + 1's factor chains with layer k's solve;
+    # every result must equal quantize_layer on that layer alone, bit for bit
+    # (the path is deterministic), across shapes that change from layer to layer.
+    say("pipelined layers", two_sided)
+    shapes = [(96, 64), (64, 130), (100, 100), (33, 70)]
+    for dtype in (np.float64, np.float32):
+        layers = []
+        for i, (m, n) in enumerate(shapes):
+            layers.append((up(synth.gaussian(300 + i, (m, n)), dtype),
+                           up(synth.channel_scaled_rows(310 + i, 320 + i, 256, n), dtype),
+                           up(synth.channel_scaled_rows(330 + i, 340 + i, 256, m), dtype)))
+        piped = pipeline.quantize_layers(layers, bits=3, two_sided=two_sided)
+        for (W, act, grad), got in zip(layers, piped):
+            want = pipeline.quantize_layer(W, act, grad, bits=3, two_sided=two_sided)
+            assert torch.equal(got["codes"], want["codes"])
+            assert torch.equal(got["V"], want["V"])
+            assert got["loss"].item() == want["loss"].item()
+            assert torch.equal(got["U_A"], want["U_A"])
+
+
 def test_pipeline_tiny_all_on_gpu_fp64():
     # Every step on the GPU (factor, prepare, scales, quantize, loss) against the
     # oracle's own pipeline on the same samples; factors differ only by rounding.

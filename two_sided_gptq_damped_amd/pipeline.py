@@ -19,6 +19,12 @@ solver needs both, and a prepare is a long chain of small dependent launches
 (one diagonal block per step).  quantize_layer therefore runs the B chain on a
 second stream, started once the A product is done, so that it fills the device
 beside the A chain; the solver waits for both.
+
+quantize_layers takes a sequence of layers (a model block, quantized one layer
+after another) and pipelines them: the factor chains of layer k + 1 run on the
+two side streams while layer k is solved on the caller's stream.  The solver's
+leaves occupy at most one workgroup per tile of a tile-diagonal, so the
+latency-bound prepare chains find free compute units beside them.
 """
 from __future__ import annotations
 
@@ -102,3 +108,71 @@ def quantize_layer(W, act, grad, bits, per_row=True, damp_rel=0.01, two_sided=Tr
     if check_loss:
         out["loss_check"] = loss(W, V, A, B, damp_rel)
     return out
+
+
+def _factor_chains(W, act, grad, bits, per_row, damp_rel, two_sided, sa, sb):
+    """Issue one layer's factor chains: A (and the scales) on stream sa, B on
+    stream sb once the A product is done.  Returns the layer's tensors and the
+    events that mark the two chains done."""
+    ea, eb = torch.cuda.Event(), torch.cuda.Event()
+    with torch.cuda.stream(sa):
+        info = torch.zeros(2, dtype=torch.int32, device=W.device)  # cleared on sa, before both chains
+        A = factor(act)
+        a_done = torch.cuda.Event()
+        a_done.record(sa)
+    out = dict(info=info, B=None, U_B=None, trace_B=None)
+    if two_sided:
+        sb.wait_event(a_done)
+        with torch.cuda.stream(sb):
+            B = factor(grad)
+            U_B, trB, _ = prepare(B, damp_rel, info[1:])
+            eb.record(sb)
+        for t in (grad, info, B, U_B, trB):
+            t.record_stream(sb)
+        out.update(B=B, U_B=U_B, trace_B=trB)
+    with torch.cuda.stream(sa):
+        U_A, trA, _ = prepare(A, damp_rel, info[:1])
+        scales = torch.empty(W.shape[0] if per_row else 1, dtype=W.dtype, device=W.device)
+        kron_row_scales(W, bits, per_row, scales)
+        ea.record(sa)
+    for t in (act, W):
+        t.record_stream(sa)
+    out.update(A=A, U_A=U_A, trace_A=trA, scales=scales, events=(ea, eb) if two_sided else (ea,))
+    return out
+
+
+def quantize_layers(layers, bits, per_row=True, damp_rel=0.01, two_sided=True, check_loss=False):
+    """Quantize a sequence of layers [(W, act, grad), ...] with the factor chains
+    of layer k + 1 running beside the solve of layer k.  Returns one dict per
+    layer, as quantize_layer does.  The positive-definiteness of every damped
+    factor is checked once, after the last layer has been issued (a host wait
+    per layer would stop the pipeline); KronError names the first failing layer."""
+    main = torch.cuda.current_stream()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(main)
+    sb.wait_stream(main)  # every input is ready
+    results = []
+    nxt = _factor_chains(*layers[0], bits, per_row, damp_rel, two_sided, sa, sb) if layers else None
+    for k, (W, act, grad) in enumerate(layers):
+        cur = nxt
+        if k + 1 < len(layers):
+            nxt = _factor_chains(*layers[k + 1], bits, per_row, damp_rel, two_sided, sa, sb)
+        for e in cur["events"]:
+            main.wait_event(e)
+        for key in ("A", "B", "U_A", "U_B", "trace_A", "trace_B", "scales", "info"):
+            if cur[key] is not None:
+                cur[key].record_stream(main)
+        lo = torch.empty(1, dtype=torch.float64, device=W.device)
+        codes, V, scales = quantize(W, cur["U_A"], cur["U_B"], bits, per_row, scales=cur["scales"], loss_out=lo)
+        out = dict(A=cur["A"], B=cur["B"], U_A=cur["U_A"], U_B=cur["U_B"], trace_A=cur["trace_A"],
+                   trace_B=cur["trace_B"], codes=codes, V=V, scales=scales, loss=lo, info=cur["info"])
+        if check_loss:
+            out["loss_check"] = loss(W, V, cur["A"], cur["B"], damp_rel)
+        results.append(out)
+    for k, out in enumerate(results):
+        bad = out.pop("info").cpu()
+        for name, piv in (("A", int(bad[0])), ("B", int(bad[1]))):
+            if piv != 0:
+                raise KronError(2, f"kron_prepare: layer {k}: damped factor {name} is not positive definite "
+                                   f"(pivot step {piv})")
+    return results
