@@ -171,6 +171,20 @@ __device__ __forceinline__ double lane_below(double v) {
 }
 
 // N consecutive LDS entries as one vector access.
+// v of lane l - 32 in the upper half of the wave (lanes 32..63); the lower half
+// keeps its own v (permlane32_swap of v with itself).
+__device__ __forceinline__ float lanes_up32(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_permlane32_swap(u, u, false, false)[0]);
+}
+__device__ __forceinline__ double lanes_up32(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const unsigned lo = unsigned(u), hi = unsigned(u >> 32);
+    const unsigned slo = __builtin_amdgcn_permlane32_swap(lo, lo, false, false)[0];
+    const unsigned shi = __builtin_amdgcn_permlane32_swap(hi, hi, false, false)[0];
+    return __builtin_bit_cast(double, (uint64_t(shi) << 32) | slo);
+}
+
 template <typename T, int N>
 struct VecN {
     typedef T V __attribute__((ext_vector_type(N)));
@@ -197,7 +211,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     constexpr int PK = ST + 4;  // k-major staging rows, 16-byte aligned
     __shared__ __attribute__((aligned(16))) T sNB[(ST + 1) * PB];  // sNB[as][a] = N_B[..as][..a], row ST = 0
     __shared__ T sNAt[ST * PA];                                    // sNAt[b][bs] = N_A[..bs][..b], col ST = 0
-    constexpr int NROUND = (2 * ST - 1 + LEAF_E - 1) / LEAF_E;  // sweep rounds
+    constexpr int RD = 2 * LEAF_E;                      // diagonals per sweep round (one wave's two groups)
+    constexpr int NROUND = (2 * ST - 1 + RD - 1) / RD;  // sweep rounds
     // chunk operands of up to BATCH slices: A(r, k) at [k][r], B(k, c) at [k][c]
     constexpr int MAXS = 2 * (CHUNK - 1);                  // most slices a leaf needs
     constexpr int BATCH = sizeof(T) == 4 ? MAXS : MAXS / 2;  // staged together (LDS budget)
@@ -410,9 +425,9 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     T* const cA = cB + NRB * PB;
     // the sweep's exchange, one slice per round: errors by row, row-accumulated
     // errors by column
-    T* const xD = cA + ST * PT;           // [round][row][diagonal of the round]
-    T* const xR = xD + NROUND * ST * E;  // [round][column][diagonal of the round]
-    static_assert(2 * ST * PK + NRB * PB + ST * PT + 2 * NROUND * ST * E <= sizeof(stg) / sizeof(T),
+    T* const xD = cA + ST * PT;            // [round][row][diagonal of the round]
+    T* const xR = xD + NROUND * ST * RD;  // [round][column][diagonal of the round]
+    static_assert(2 * ST * PK + NRB * PB + ST * PT + 2 * NROUND * ST * RD <= sizeof(stg) / sizeof(T),
                   "staging area too small");
     static_assert((2 * ST * PK + NRB * PB + ST * PT) % 8 == 0, "32-byte aligned exchange slices");
     __syncthreads();  // the prologue's reads of the staging area are done
@@ -453,25 +468,30 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
 #pragma unroll
     for (int i = 0; i < E; ++i) x[i] = bufA[ar[i] * PK + b];
 
-    // ---- the sweep: 2 ST - 1 element anti-diagonals, E per round.
-    // A round takes diagonals d .. d + E - 1 (d a multiple of E), all held by group
-    // gd = (d mod ST) / E, slot k holding diagonal d + k.  For the entry (a, b) of
-    // slot k and m < k, diagonal d + m's column source (d + m - b, b) is slot m of
-    // the same thread and its row source (a, d + m - a) = (a, b - (k - m)) is slot m
-    // of the lane k - m below.  So the wave of group gd (the round's producer)
-    // rounds the round's diagonals one after the other, each slot first taking the
-    // feedback of the earlier ones (lane shifts bring the row sources), and
-    // publishes the errors; after a barrier every wave adds the feedback of d,
-    // d + 1, ... to its entries in turn: the same operations in the same order as
-    // one diagonal at a time.  The next round's producer does so right before its own rounding,
-    // in one stretch of code, so that its chain overlaps the rest of its feedback
-    // arithmetic.
-    // Sources that do not exist have zero coefficients and every value the group
-    // exchanges is finite, so it writes all of its slots, and diagonals past
-    // 2 ST - 2 (outside the tile) contribute nothing.  A rounded entry's error and
-    // code go straight to bufB (k-major, for the epilogue) and bufA; each entry of
-    // bufA is read (as x) and later written by the same thread.
-    using VE = VecN<T, E>;
+    // ---- the sweep: 2 ST - 1 element anti-diagonals, four per round.
+    // Slot i of group g holds diagonal 2 g + i (and 2 g + i + 32, entries past the
+    // tile's main anti-diagonal), so the four diagonals d0 .. d0 + 3 of round
+    // d0 / 4 sit in the two groups of one wave, the round's producer: its lower
+    // half-wave (group 2 w) holds d0 in slot 0 and d0 + 1 in slot 1, its upper half
+    // (group 2 w + 1) d0 + 2 and d0 + 3.  For the entry (a, b) on diagonal D and an
+    // earlier diagonal d of the round, the column source (d - b, b) is slot d mod 2
+    // of lane b of the group holding d, and the row source (a, d - a) is the same
+    // slot of lane b - (D - d).  So the producer rounds d0, gives d0's feedback to
+    // its d0 + 1 entries (a lane shift brings the row source) and rounds d0 + 1;
+    // permlane32_swap then hands the lower half's errors to the upper half at the
+    // same lane, lane shifts line up the row sources, and the upper half takes the
+    // feedback of d0 and d0 + 1, rounds d0 + 2, passes its feedback on within the
+    // half and rounds d0 + 3.  One barrier publishes the round; every wave then adds
+    // the feedback of d0, d0 + 1, d0 + 2, d0 + 3 to its entries in turn: the same
+    // operations in the same order as one diagonal at a time.  The next round's
+    // producer does so right before its own chain, in one stretch of code.
+    // Sources that do not exist have zero coefficients and every value exchanged
+    // is finite, so a group writes all of its slots, and diagonal 2 ST - 1 (the
+    // last round's fourth, outside the tile) contributes nothing.  A rounded
+    // entry's error and code go straight to bufB (k-major, for the epilogue) and
+    // bufA; each entry of bufA is read (as x) and later written by the same thread.
+    static_assert(E == 2 && RD == 4, "the sweep holds two entries per thread, four diagonals per round");
+    using VR = VecN<T, RD>;
     const T tqmin = T(qmin), tqmax = T(qmax);
     const T* pB[E];  // + d PB: N_B coefficient of diagonal d for slot k
     const T* pA[E];  // + d: N_A coefficient of diagonal d for slot k
@@ -480,98 +500,108 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         pB[k] = cB + (ST - b) * PB + ar[k];
         pA[k] = cA + b * PT + ST - ar[k];
     }
-    // coefficients of round d: [diagonal d + m][slot k]; the in-round chain's
-    // (m < k) are read first
-    auto coef = [&](int d, T (&nb)[E][E], T (&na)[E][E]) {
+    const bool upper = (g & 1) != 0;  // the half-wave holding the round's last two diagonals
+    // coefficients of the round's diagonals d0 + m for slot k
+    auto coef = [&](int d0, T (&nb)[RD][E], T (&na)[RD][E]) {
 #pragma unroll
-        for (int k = 1; k < E; ++k)
-#pragma unroll
-            for (int m = 0; m < k; ++m) {
-                nb[m][k] = pB[k][(d + m) * PB];
-                na[m][k] = pA[k][d + m];
-            }
-#pragma unroll
-        for (int k = 0; k < E; ++k)
-#pragma unroll
-            for (int m = k; m < E; ++m) {
-                nb[m][k] = pB[k][(d + m) * PB];
-                na[m][k] = pA[k][d + m];
-            }
-    };
-    // round d's rounding chain (the wave of group gd) and its publication
-    auto chain = [&](int d, const T (&nb)[E][E], const T (&na)[E][E]) {
-        const int r = d / E;
-        T e[E], q[E], z[E];
-        T sh[E][E];  // sh[m][s]: e[m] of the lane s below
-#pragma unroll
-        for (int k = 0; k < E; ++k) {
-            T xk = x[k], rk = rp[k];
-#pragma unroll
-            for (int m = 0; m < k; ++m) {
-                xk = kfma(sh[m][k - m], na[m][k], kfma(nb[m][k], q[m], xk));
-                rk = kfma(sh[m][k - m], na[m][k], rk);
-            }
-            T v;
-            quantize_fast(xk, sc[k], rs[k], tqmin, tqmax, z[k], v);
-            e[k] = v - xk;
-            q[k] = rk + e[k];
-            T u = e[k];
-#pragma unroll
-            for (int sft = 1; sft < E - k; ++sft) {
-                u = lane_below(u);
-                sh[k][sft] = u;
-            }
-        }
-        if (g == ((d & (ST - 1)) / E)) {
-            VE qq;
+        for (int m = 0; m < RD; ++m)
 #pragma unroll
             for (int k = 0; k < E; ++k) {
-                xD[(r * ST + ar[k]) * E + k] = e[k];
-                qq.set(k, q[k]);
+                nb[m][k] = pB[k][(d0 + m) * PB];
+                na[m][k] = pA[k][d0 + m];
             }
-            qq.store(xR + (r * ST + b) * E);
-#pragma unroll
-            for (int k = 0; k < E; ++k)
-                if (dg[k] == d + k) {
-                    bufB[b * PK + ar[k]] = e[k];
-                    bufA[ar[k] * PK + b] = z[k];
-                }
+    };
+    // the producer's chain for round r (diagonals d0 = 4 r ..), then its publication
+    auto chain = [&](int r, const T (&nb)[RD][E], const T (&na)[RD][E]) {
+        const int d0 = RD * r;
+        // lower half: d0 in slot 0, d0 + 1 in slot 1 (the upper half computes the
+        // same operations on its own entries; nothing of that is kept)
+        T z0, z1, v;
+        quantize_fast(x[0], sc[0], rs[0], tqmin, tqmax, z0, v);
+        const T e0 = v - x[0];
+        const T q0 = rp[0] + e0;
+        const T el = lane_below(e0);  // row source of slot 1 on d0
+        const T x1 = kfma(el, na[0][1], kfma(nb[0][1], q0, x[1]));
+        quantize_fast(x1, sc[1], rs[1], tqmin, tqmax, z1, v);
+        const T e1 = v - x1;
+        const T q1 = kfma(el, na[0][1], rp[1]) + e1;
+        // the lower half's errors at the same lane of the upper half
+        const T se0 = lanes_up32(e0), se1 = lanes_up32(e1), sq0 = lanes_up32(q0), sq1 = lanes_up32(q1);
+        const T e0s1 = lane_below(se0), e0s2 = lane_below(e0s1), e0s3 = lane_below(e0s2);
+        const T e1s1 = lane_below(se1), e1s2 = lane_below(e1s1);
+        // upper half: d0 + 2 in slot 0, after the feedback of d0 and d0 + 1
+        T z2, z3;
+        T x2 = kfma(e0s2, na[0][0], kfma(nb[0][0], sq0, x[0]));
+        x2 = kfma(e1s1, na[1][0], kfma(nb[1][0], sq1, x2));
+        T r2 = kfma(e0s2, na[0][0], rp[0]);
+        r2 = kfma(e1s1, na[1][0], r2);
+        quantize_fast(x2, sc[0], rs[0], tqmin, tqmax, z2, v);
+        const T e2 = v - x2;
+        const T q2 = r2 + e2;
+        // d0 + 3 in slot 1, after the feedback of d0, d0 + 1 and d0 + 2
+        T x3 = kfma(e0s3, na[0][1], kfma(nb[0][1], sq0, x[1]));
+        x3 = kfma(e1s2, na[1][1], kfma(nb[1][1], sq1, x3));
+        T r3 = kfma(e0s3, na[0][1], rp[1]);
+        r3 = kfma(e1s2, na[1][1], r3);
+        const T e2l = lane_below(e2);  // row source of slot 1 on d0 + 2
+        x3 = kfma(e2l, na[2][1], kfma(nb[2][1], q2, x3));
+        r3 = kfma(e2l, na[2][1], r3);
+        quantize_fast(x3, sc[1], rs[1], tqmin, tqmax, z3, v);
+        const T e3 = v - x3;
+        const T q3 = r3 + e3;
+        if (g == ((d0 & (ST - 1)) >> 1) || g == ((d0 & (ST - 1)) >> 1) + 1) {
+            // each half publishes its two diagonals: errors by row, row-accumulated errors by column
+            const int m0 = upper ? 2 : 0;
+            const T ea = upper ? e2 : e0, eb = upper ? e3 : e1;
+            xD[(r * ST + ar[0]) * RD + m0] = ea;
+            xD[(r * ST + ar[1]) * RD + m0 + 1] = eb;
+            xR[(r * ST + b) * RD + m0] = upper ? q2 : q0;
+            xR[(r * ST + b) * RD + m0 + 1] = upper ? q3 : q1;
+            if (dg[0] == d0 + m0) {
+                bufB[b * PK + ar[0]] = ea;
+                bufA[ar[0] * PK + b] = upper ? z2 : z0;
+            }
+            if (dg[1] == d0 + m0 + 1) {
+                bufB[b * PK + ar[1]] = eb;
+                bufA[ar[1] * PK + b] = upper ? z3 : z1;
+            }
         }
     };
-    // every entry takes round d's feedback
-    auto feedback = [&](const VE& rv, const VE (&dd)[E], const T (&nb)[E][E], const T (&na)[E][E]) {
+    // every entry takes round r's feedback
+    auto feedback = [&](const VR& rv, const VR (&dd)[E], const T (&nb)[RD][E], const T (&na)[RD][E]) {
 #pragma unroll
         for (int j = 0; j < E; ++j)
 #pragma unroll
-            for (int m = 0; m < E; ++m) {
+            for (int m = 0; m < RD; ++m) {
                 x[j] = kfma(dd[j][m], na[m][j], kfma(nb[m][j], rv[m], x[j]));
                 rp[j] = kfma(dd[j][m], na[m][j], rp[j]);
             }
     };
-    constexpr int WAVE_GROUPS = 64 / ST;  // sweep groups per wave
-    auto producer = [&](int d) { return ((d & (ST - 1)) / E) / WAVE_GROUPS; };
-    T cnb[E][E], cna[E][E];
+    auto producer = [&](int r) { return (RD * r & (ST - 1)) / RD; };  // wave of groups 2 w, 2 w + 1
+    // coefficients of round r (cnb / cna, its feedback) and of round r + 1 (read
+    // after round r's barrier, for the next producer's chain)
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform: scalar branches on the producer
+    T cnb[RD][E], cna[RD][E];
     coef(0, cnb, cna);
-    if (wv == producer(0)) chain(0, cnb, cna);
+    if (wvu == producer(0)) chain(0, cnb, cna);
 #pragma unroll
-    for (int d = 0; d < 2 * ST - 1; d += E) {
-        const int r = d / E;
+    for (int r = 0; r < NROUND; ++r) {
         __syncthreads();  // round r's errors are published
-        if (d + E >= 2 * ST - 1) break;  // every entry is rounded
-        VE rv, dd[E];
-        rv.load(xR + (r * ST + b) * E);
+        if (r + 1 == NROUND) break;  // every entry is rounded
+        VR rv, dd[E];
+        rv.load(xR + (r * ST + b) * RD);
 #pragma unroll
-        for (int j = 0; j < E; ++j) dd[j].load(xD + (r * ST + ar[j]) * E);
-        T nnb[E][E], nna[E][E];
-        coef(d + E, nnb, nna);
-        if (wv == producer(d + E)) {
+        for (int j = 0; j < E; ++j) dd[j].load(xD + (r * ST + ar[j]) * RD);
+        T nnb[RD][E], nna[RD][E];
+        coef(RD * (r + 1), nnb, nna);
+        if (wvu == producer(r + 1)) {
             feedback(rv, dd, cnb, cna);
-            chain(d + E, nnb, nna);
+            chain(r + 1, nnb, nna);
         } else {
             feedback(rv, dd, cnb, cna);
         }
 #pragma unroll
-        for (int m = 0; m < E; ++m)
+        for (int m = 0; m < RD; ++m)
 #pragma unroll
             for (int k = 0; k < E; ++k) {
                 cnb[m][k] = nnb[m][k];
