@@ -87,6 +87,9 @@ def main() -> int:
     ap.add_argument("--n", type=int, default=4096)
     ap.add_argument("--bits", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shapes", action="store_true",
+                    help="only report kron_quantize at every configured shape (two- and one-sided) and the "
+                         "Llama-block pipeline, one JSON line each")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -99,6 +102,8 @@ def main() -> int:
 
     if args.copy_probe:
         return copy_probe(torch, args.copy_probe)
+    if args.shapes:
+        return shape_report(torch)
 
     import synth
     import two_sided_gptq_damped_amd as kq
@@ -304,6 +309,104 @@ def main() -> int:
         print("[bench] cpu baseline (oracle pipeline)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(c, bits)
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def shape_report(torch):
+    """kron_quantize alone (factors, scales and workspace resident; median of
+    repeats, HIP events on torch's stream) at the configured shapes, two-sided and
+    one-sided (U_B = NULL), with F = m n (m + n - 2) and F1 = m n (n - 1) against
+    the fp32 / fp64 matrix-core peaks; then the Llama-3-8B-shaped block, all seven
+    sublayers through pipeline.quantize_layers (factor products, prepares, scales,
+    solves with their losses), as one timed job."""
+    import synth
+    import two_sided_gptq_damped_amd as kq
+    from two_sided_gptq_damped_amd import pipeline
+
+    dev = "cuda"
+
+    def up(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)
+
+    def core_times(W, UA, UB, bits, scales, reps):
+        m, n = W.shape
+        codes = torch.empty(m, n, dtype=torch.int8, device=dev)
+        V = torch.empty_like(W)
+        ws = kq.workspace(kq.KQ_OP_QUANTIZE, W.dtype, m, n)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(reps + 1):  # the first call warms up
+            a.record()
+            kq.kron_quantize(W, UA, UB, bits, True, scales, codes, V, ws)
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts[1:]))
+
+    def factors(W, act, grad, damp):
+        n, m = act.shape[1], grad.shape[1]
+        A = torch.empty(n, n, dtype=W.dtype, device=dev)
+        B = torch.empty(m, m, dtype=W.dtype, device=dev)
+        kq.kron_factor_accumulate(act, A, 1.0 / act.shape[0], 0.0)
+        kq.kron_factor_accumulate(grad, B, 1.0 / grad.shape[0], 0.0)
+        UA, UB = torch.empty_like(A), torch.empty_like(B)
+        kq.kron_prepare(A, damp, UA, kq.workspace(kq.KQ_OP_PREPARE, W.dtype, n, 0))
+        kq.kron_prepare(B, damp, UB, kq.workspace(kq.KQ_OP_PREPARE, W.dtype, m, 0))
+        return UA, UB
+
+    cases = [("config 2: 256x256", synth.spectral(256, 256, config=2), 3, np.float32),
+             ("config 2: 256x256", synth.spectral(256, 256, config=2), 3, np.float64),
+             ("config 3: 4096x4096", synth.llm(4096, 4096, 2, config=3), 2, np.float32),
+             ("config 4: 1024x4096", synth.llm(1024, 4096, 3, config=4), 3, np.float32),
+             ("config 4: 14336x4096", synth.llm(14336, 4096, 3, config=4), 3, np.float32)]
+    for label, c, bits, dt in cases:
+        print(f"[shapes] {label} {np.dtype(dt).name}", file=sys.stderr, flush=True)
+        W = up(c["W"], dt)
+        m, n = W.shape
+        if "A" in c:  # config 2: the spectral factors themselves
+            UA, UB = torch.empty(n, n, dtype=W.dtype, device=dev), torch.empty(m, m, dtype=W.dtype, device=dev)
+            kq.kron_prepare(up(c["A"], dt), 0.01, UA, kq.workspace(kq.KQ_OP_PREPARE, W.dtype, n, 0))
+            kq.kron_prepare(up(c["B"], dt), 0.01, UB, kq.workspace(kq.KQ_OP_PREPARE, W.dtype, m, 0))
+        else:
+            UA, UB = factors(W, up(c["act"], dt), up(c["grad"], dt), c["damp"])
+        scales = torch.empty(m, dtype=W.dtype, device=dev)
+        kq.kron_row_scales(W, bits, True, scales)
+        reps = 3 if m * n > 3e7 else 10
+        t2 = core_times(W, UA, UB, bits, scales, reps)
+        t1 = core_times(W, UA, None, bits, scales, reps)
+        peak = PEAK_FP64_MFMA if dt == np.float64 else PEAK_FP32_MFMA
+        F, F1 = solver_flops(m, n), float(m) * n * (n - 1)
+        print(json.dumps({"shape": label, "dtype": np.dtype(dt).name, "m": m, "n": n, "bits": bits,
+                          "two_sided_ms": t2, "two_sided_weights_per_s": m * n / (t2 * 1e-3),
+                          "two_sided_tflops": F / (t2 * 1e-3) / 1e12, "two_sided_frac_peak": F / (t2 * 1e-3) / peak,
+                          "one_sided_ms": t1, "one_sided_weights_per_s": m * n / (t1 * 1e-3),
+                          "one_sided_tflops": F1 / (t1 * 1e-3) / 1e12, "one_sided_frac_peak": F1 / (t1 * 1e-3) / peak,
+                          "two_over_one_sided": t2 / t1}), flush=True)
+        del W, UA, UB, scales
+        torch.cuda.empty_cache()
+
+    print("[shapes] config 5: Llama-3-8B-shaped block", file=sys.stderr, flush=True)
+    layers, F, weights = [], 0.0, 0
+    for i in range(7):
+        print(f"[shapes] generating sublayer {i}", file=sys.stderr, flush=True)
+        c = synth.block_sublayer(i)
+        layers.append((up(c["W"], np.float32), up(c["act"], np.float32), up(c["grad"], np.float32)))
+        F += solver_flops(c["m"], c["n"])
+        weights += c["m"] * c["n"]
+    times = []
+    for _ in range(3):  # the first run warms up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out = pipeline.quantize_layers(layers, bits=2)
+        torch.cuda.synchronize()
+        times.append((time.perf_counter() - t0) * 1e3)
+    ms = float(np.median(times[1:]))
+    print(json.dumps({"shape": "config 5: Llama-3-8B-shaped block (q, k, v, o, gate, up, down)", "dtype": "float32",
+                      "bits": 2, "block_ms": ms, "weights": weights, "weights_per_s": weights / (ms * 1e-3),
+                      "solver_tflops_over_block_time": F / (ms * 1e-3) / 1e12,
+                      "what": "whole path per sublayer (factor products, prepares, scales, solve with its loss), "
+                              "sublayers pipelined; host wall clock, median of 2 after a warm-up",
+                      "losses": [float(o["loss"].item()) for o in out]}), flush=True)
     return 0
 
 

@@ -11,11 +11,14 @@
 // U = J L_c^{-1} J.  Steps, all on 64 x 64 fp64 blocks of a padded dp x dp copy:
 //   1. trace and damping; C = J A_d J (identity in the padding)
 //   2. right-looking blocked Cholesky: diagonal-block factor + its inverse,
-//      panel (C_ik <- C_ik L_kk^{-T}) and trailing update (C_ij -= C_ik C_jk^T),
-//      the last two on fp64 matrix cores
+//      panel (C_ik <- C_ik L_kk^{-T}) and updates (C_ij -= C_ik C_jk^T) in two
+//      levels (inside a panel of PANEL block columns, then the whole trailing
+//      matrix once per panel), the last two on fp64 matrix cores
 //   3. lower-triangular inverse by recursive halving of the block range,
 //      one pair of matrix-core launches per recursion level
 //   4. U[r][c] = Li[d-1-r][d-1-c] for c >= r, 0 below the diagonal.
+#include <algorithm>
+
 #include "kq_common.hpp"
 
 namespace kq {
@@ -223,7 +226,7 @@ __device__ __forceinline__ void diag_factor(double* __restrict__ C, int dp, int 
 }
 
 // The first diagonal block (the others are factored inside the trailing update
-// of the step before, see potrf_trailing_kernel).
+// of the step before, see potrf_update_kernel).
 __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ C, int dp, int k,
                                                          double* __restrict__ Dinv, int32_t* __restrict__ info) {
     __shared__ DiagSmem sm;
@@ -257,25 +260,58 @@ __global__ __launch_bounds__(GEMM_THREADS) void potrf_panel_kernel(double* __res
     for_each_acc(acc, [&](int r, int c, double v) { blk[int64_t(r) * dp + c] = v; });
 }
 
-// C[i][j] -= C[i][k] C[j][k]^T for k < j <= i.
-// C[i][j] -= C[i][k] C[j][k]^T for k < j <= i.  Block (k+1, k+1) instead updates
-// into LDS and goes on to factor it (diag_factor), so the next step's diagonal
-// factorisation runs while the rest of the trailing matrix is updated.
-__global__ __launch_bounds__(GEMM_THREADS) void potrf_trailing_kernel(double* __restrict__ C, int dp, int k,
-                                                                      double* __restrict__ Dinv,
-                                                                      int32_t* __restrict__ info) {
-    const int i = k + 1 + blockIdx.y, j = k + 1 + blockIdx.x;
-    if (j > i) return;
+// Two-level blocking: the factorisation takes panels of PANEL block columns.
+// Inside a panel, step k updates only the panel's later columns (k < j < panel
+// end) with block column k; after the panel's last step one update with the
+// panel's PANEL columns at once (K = PANEL * 64) brings the whole trailing matrix
+// up to date.  The trailing matrix is then read and written once per panel
+// rather than once per block column, which at d = 14336 is the difference
+// between streaming ~245 GB and ~61 GB.
+constexpr int PANEL = 4;
+
+// C[i][j] -= sum_{k0 <= k < k0 + kw} C[i][k] C[j][k]^T for the blocks t0 <= j <= i,
+// j < jend, with t0 = k0 + kw.  Workgroup 0 takes block (t0, t0): it updates it
+// into LDS and goes on to factor it (diag_factor), so the next diagonal
+// factorisation runs while the other blocks are updated.  The other blocks are
+// numbered row by row over the trapezoid (r = i - t0, c = j - t0, c <= r, c < w with
+// w = jend - t0): q = r (r + 1) / 2 + c for r < w, then w (w + 1) / 2 + (r - w) w + c;
+// workgroup q (q >= 1) takes block q.
+__device__ __forceinline__ void trapezoid_index(int q, int w, int& r, int& c) {
+    const int tri = w * (w + 1) / 2;
+    if (q < tri) {
+        r = int((sqrt(8.0 * q + 1.0) - 1.0) * 0.5);
+        while (r * (r + 1) / 2 > q) --r;
+        while ((r + 1) * (r + 2) / 2 <= q) ++r;
+        c = q - r * (r + 1) / 2;
+    } else {
+        r = w + (q - tri) / w;
+        c = (q - tri) % w;
+    }
+}
+
+__global__ __launch_bounds__(GEMM_THREADS) void potrf_update_kernel(double* __restrict__ C, int dp, int k0, int kw,
+                                                                    int jend, double* __restrict__ Dinv,
+                                                                    int32_t* __restrict__ info) {
     __shared__ union {
         GemmSmem<double> g;
         DiagSmem d;
     } sm;
+    const int t0 = k0 + kw;
+    int i, j;
+    if (blockIdx.x == 0) {
+        i = j = t0;
+    } else {
+        int r, c;
+        trapezoid_index(int(blockIdx.x), jend - t0, r, c);
+        i = t0 + r;
+        j = t0 + c;
+    }
     WaveAcc<double> acc;
     acc.zero();
-    const double* A = C + int64_t(i) * TILE * dp + int64_t(k) * TILE;
-    const double* B = C + int64_t(j) * TILE * dp + int64_t(k) * TILE;  // B(kk, c) = C[j*64+c][k*64+kk]
+    const double* A = C + int64_t(i) * TILE * dp + int64_t(k0) * TILE;
+    const double* B = C + int64_t(j) * TILE * dp + int64_t(k0) * TILE;  // B(kk, c) = C[j*64+c][k0*64+kk]
     double* out = C + int64_t(i) * TILE * dp + int64_t(j) * TILE;
-    const bool diag = i == k + 1 && j == k + 1;
+    const bool diag = blockIdx.x == 0;
     double pre[WaveAcc<double>::NREG];  // the diagonal block, loaded while the product runs
     if (diag) {
         const int t = threadIdx.x & 255, lane = t & 63, w = t >> 6;
@@ -284,7 +320,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void potrf_trailing_kernel(double* __
             pre[r] = out[int64_t((w >> 1) * 32 + WaveAcc<double>::row(r, lane)) * dp + (w & 1) * 32 +
                          WaveAcc<double>::col(r, lane)];
     }
-    tile_gemm<double, double, false, true, false>(A, dp, B, dp, TILE, TILE, TILE, sm.g, acc);
+    tile_gemm<double, double, false, true, false>(A, dp, B, dp, TILE, TILE, kw * TILE, sm.g, acc);
     if (diag) {
         __syncthreads();  // the product's LDS reads are done before L overwrites them
         const int t = threadIdx.x & 255, lane = t & 63, w = t >> 6;
@@ -292,7 +328,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void potrf_trailing_kernel(double* __
         for (int r = 0; r < WaveAcc<double>::NREG; ++r)
             sm.d.L[((w >> 1) * 32 + WaveAcc<double>::row(r, lane)) * DP + (w & 1) * 32 + WaveAcc<double>::col(r, lane)] =
                 pre[r] - acc.get(r);
-        diag_factor(C, dp, k + 1, Dinv, info, sm.d);
+        diag_factor(C, dp, t0, Dinv, info, sm.d);
         return;
     }
     for_each_acc(acc, [&](int r, int c, double v) { out[int64_t(r) * dp + c] -= v; });
@@ -419,12 +455,27 @@ kq_status prepare_typed(int64_t d, const T* A, int64_t lda, double damp_rel, T* 
     KQ_LAUNCHED("build_reversed_kernel");
     hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, st, C, dp, 0, Dinv, info);
     KQ_LAUNCHED("potrf_diag_kernel");
-    for (int k = 0; k + 1 < nt; ++k) {
-        const int rest = nt - k - 1;
-        hipLaunchKernelGGL(potrf_panel_kernel, dim3(rest), dim3(GEMM_THREADS), 0, st, C, dp, k, Dinv);
-        KQ_LAUNCHED("potrf_panel_kernel");
-        hipLaunchKernelGGL(potrf_trailing_kernel, dim3(rest, rest), dim3(GEMM_THREADS), 0, st, C, dp, k, Dinv, info);
-        KQ_LAUNCHED("potrf_trailing_kernel");
+    // blocks of the update of [t0, nt) x [t0, jend): the trapezoid below the diagonal
+    auto update = [&](int k0, int kw, int jend) {
+        const int t0 = k0 + kw, rows = nt - t0, w = jend - t0;
+        const int blocks = w * (w + 1) / 2 + (rows - w) * w;
+        hipLaunchKernelGGL(potrf_update_kernel, dim3(blocks), dim3(GEMM_THREADS), 0, st, C, dp, k0, kw, jend, Dinv,
+                           info);
+    };
+    for (int p0 = 0; p0 < nt; p0 += PANEL) {
+        const int p1 = std::min(p0 + PANEL, nt);
+        for (int k = p0; k < p1 && k + 1 < nt; ++k) {
+            hipLaunchKernelGGL(potrf_panel_kernel, dim3(nt - k - 1), dim3(GEMM_THREADS), 0, st, C, dp, k, Dinv);
+            KQ_LAUNCHED("potrf_panel_kernel");
+            if (k + 1 < p1) {  // the panel's later columns, and the next diagonal block
+                update(k, 1, p1);
+                KQ_LAUNCHED("potrf_update_kernel");
+            }
+        }
+        if (p1 < nt) {  // the whole trailing matrix with the panel's columns, and block p1
+            update(p0, p1 - p0, nt);
+            KQ_LAUNCHED("potrf_update_kernel");
+        }
     }
     hipLaunchKernelGGL(trtri_diag_kernel, dim3(nt), dim3(256), 0, st, Li, dp, Dinv);
     KQ_LAUNCHED("trtri_diag_kernel");
