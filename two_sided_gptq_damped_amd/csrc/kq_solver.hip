@@ -98,32 +98,16 @@ struct Vec4<double> {
     }
 };
 
-// o[i][j] += sum_k A(rr + i, k) B(k, cc + j) over a staged 32-deep slice (A at
-// [k][r], B at [k][c], rows PK apart).
-template <typename T, int PK>
-__device__ __forceinline__ void mac4x4_impl(const T* __restrict__ sa, const T* __restrict__ sb, int rr, int cc,
-                                            T (&o)[4][4]) {
-#pragma unroll 8
-    for (int k = 0; k < 32; ++k) {
-        Vec4<T> a4, b4;
-        a4.load(sa + k * PK + rr);
-        b4.load(sb + k * PK + cc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[i][j] = kfma(a4[i], b4[j], o[i][j]);
-    }
-}
-
-// Leaf: the tiles of one tile-diagonal K, one 256-thread workgroup per 32 x 32
-// tile.  Thread t owns four entries of column b = t % 32 (in the sweep, rows
-// (4g - b + i) mod 32 with g = t / 32, see the layouts below).  Right-looking
+// Leaf: the tiles of one tile-diagonal K, one 512-thread workgroup per 32 x 32
+// tile.  In the sweep thread t owns two entries of column b = t % 32, rows
+// (2g - b + i) mod 32 with g = t / 32 (see the layouts below).  Right-looking
 // in-tile feedback: after the entries of
 // element anti-diagonal d are rounded, each later entry adds the contribution of
 // the rounded entry in its row (Delta * L~_A) and of the one in its column
-// (L~_B * R, R the row-accumulated error).  One barrier per step
-// (double-buffered exchange arrays); finished errors and codes stay in the
-// owning thread's registers.
+// (L~_B * R, R the row-accumulated error).  One wave rounds four consecutive
+// diagonals per round and one barrier separates the rounds (the exchange
+// arrays hold every round's values, so nothing is overwritten while read);
+// finished errors and codes go to LDS for the epilogue.
 //
 // The tile's diagonal factor blocks sit in LDS with their unit diagonal
 // replaced by 0 and an extra all-zero row / column; a source that does not exist
@@ -144,29 +128,33 @@ __device__ __forceinline__ void mac4x4_impl(const T* __restrict__ sa, const T* _
 //   X[I, J] += N_B[I, I]^T rowpart + sum_{c0 - J <= I' < I} N_B[I', I]^T T1c[I', J]
 // and after the sweep the leaf writes T1c[I, J] = rowpart + Delta[I, J] N_A[J, J]
 // for the later diagonals of its chunk.  With B = I only rowpart is added.  The
-// 32 x 32 x 32 products are few and small: their operands are staged k-major in
-// LDS and each wave takes whole slices, every lane a 4 x 4 block of the product.
+// 32 x 32 x 32 products run on the matrix cores: their operands are staged
+// k-major in LDS, each slice is cut into four eight-deep K quarters, and every
+// wave accumulates the whole 32 x 32 block of the quarters it is dealt.
 //
 // The quotient x / s is formed as x * (1/s) (1/s rounded once per row): within
 // two ulps of the IEEE quotient, so it can change a rounding decision only for
 // values that sit within ~1e-15 (fp64) or ~1e-7 (fp32) grid units of a
 // midpoint.  A zero scale has 1/s = 0, so q = 0 and the code is 0 with no test
 // (for finite x).
+__device__ __forceinline__ float clamp_fast(float x, float lo, float hi) { return __builtin_amdgcn_fmed3f(x, lo, hi); }
+__device__ __forceinline__ double clamp_fast(double x, double lo, double hi) { return kclamp(x, lo, hi); }
 template <typename T>
 __device__ __forceinline__ void quantize_fast(T x, T s, T rs, T qmin, T qmax, T& z, T& v) {
-    z = kclamp(krint(x * rs), qmin, qmax);
+    z = clamp_fast(krint(x * rs), qmin, qmax);  // one median-of-three for fp32 (finite x)
     v = s * z;
 }
 
 // The value of v in the next lower lane of the wave (lane 0 gets 0): a DPP
-// shift of the whole wave by one lane.
+// shift of the whole wave by one lane.  With bound_ctrl the lane without a
+// source reads 0, so the shift can ride on the FMA that consumes it.
 __device__ __forceinline__ float lane_below(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x138, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x138, 0xf, 0xf, true));
 }
 __device__ __forceinline__ double lane_below(double v) {
     const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(u)), 0x138, 0xf, 0xf, false);
-    const uint32_t hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(u >> 32)), 0x138, 0xf, 0xf, false);
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(u)), 0x138, 0xf, 0xf, true);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(u >> 32)), 0x138, 0xf, 0xf, true);
     return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
 }
 
@@ -219,7 +207,6 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     __shared__ __attribute__((aligned(16))) T stg[BATCH][2][ST * PK];
     T* const bufA = stg[0][0];
     T* const bufB = stg[0][1];
-    auto mac4x4 = [](const T* a, const T* bm, int r, int c, T (&o)[4][4]) { mac4x4_impl<T, PK>(a, bm, r, c, o); };
 
     const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
     const int I = ilo + blockIdx.x;
@@ -232,7 +219,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     const bool blk = t < 256;
     const int b = l & 31, r0 = 8 * w + 4 * (l >> 5);
     const int fgrp = t >> 8;                    // staging loads: slices rotate over the 256-thread groups
-    const int wv = t >> 6, rr = 4 * ((t & 63) >> 3), cc = 4 * (t & 7);  // chunk products: wave, 4 x 4 block
+    const int wv = t >> 6, lane = t & 63;  // chunk products: wave, lane
     const int q8 = tb >> 3, c4 = 4 * (tb & 7);  // this thread's share of a 32 x 32 staging load
 
     // chunk sources: row tiles J' in [jl, J), column tiles I' in [il, I)
@@ -311,11 +298,9 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
 
     // ---- chunk prologue: rowpart (crow) and the column feedback (ccol), block layout
     if (ns > 0) {
-        T pr[4][4], pc[4][4];  // this wave's sums of row-part and column-part slices
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pr[i][j] = pc[i][j] = T(0);
+        WaveAcc<T> pr, pc;  // this wave's sums of row-part and column-part products
+        pr.zero();
+        pc.zero();
         for (int sb = 0; sb < ns; sb += BATCH) {
             if (sb > 0) {
                 __syncthreads();  // the previous batch is consumed
@@ -339,36 +324,34 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
                 }
             }
             __syncthreads();
-            // one wave per slice (slices u = wave, wave + 8, ...), each lane a 4 x 4
-            // block of the 32 x 32 product: two 16-byte LDS reads feed 16 FMAs
+            // matrix cores: the batch's slices cut into eight-deep K quarters,
+            // dealt round-robin to the waves; each wave accumulates whole 32 x 32
+            // blocks (reads stay k-major, 32 consecutive entries per half-wave)
             const int nbat = ns - sb < BATCH ? ns - sb : BATCH;
-            for (int u = wv; u < nbat; u += LEAF_THREADS / 64) {
-                const T* sa = stg[u][0];
-                const T* sbm = stg[u][1];
+            for (int f = wv; f < 4 * nbat; f += LEAF_THREADS / 64) {
+                const int u = f >> 2, k0 = 8 * (f & 3);
+                const T* sa = stg[u][0] + k0 * PK;
+                const T* sbm = stg[u][1] + k0 * PK;
                 if (sb + u < n1)
-                    mac4x4(sa, sbm, rr, cc, pr);
+                    pr.template mma_block<PK, PK, 8>(sa, sbm, lane);
                 else
-                    mac4x4(sa, sbm, rr, cc, pc);
+                    pc.template mma_block<PK, PK, 8>(sa, sbm, lane);
             }
         }
         // The waves' partial sums reach the block layout through the staging
         // area, added in wave order: first the row parts (rowpart, kept in LDS
         // as the right operand of the next product), then the column parts,
         // to which every wave has added its share of strict(N_B[I, I])^T rowpart
-        // (K split eight ways, 4 x 4 register blocks).
-        const int nw = ns < LEAF_THREADS / 64 ? ns : LEAF_THREADS / 64;  // waves that had a slice
-        const bool nbs = NB && n1 > 0;                                    // the in-tile column feedback
-        T* park = reinterpret_cast<T*>(stg);                             // [wave][32 x 32]
-        T* rowp = park + (LEAF_THREADS / 64) * ST * ST;                  // rowpart, [k][c]
+        // (K split eight ways).
+        const int nw = 4 * ns < LEAF_THREADS / 64 ? 4 * ns : LEAF_THREADS / 64;  // waves that had a quarter
+        const bool nbs = NB && n1 > 0;                                          // the in-tile column feedback
+        T* park = reinterpret_cast<T*>(stg);                                   // [wave][32 x 32]
+        T* rowp = park + (LEAF_THREADS / 64) * ST * ST;                        // rowpart, [k][c]
         static_assert(sizeof(stg) >= (LEAF_THREADS / 64 + 1) * ST * ST * sizeof(T), "staging area too small");
-        auto park_wave = [&](const T (&o)[4][4]) {
+        auto park_wave = [&](const WaveAcc<T>& o) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                Vec4<T> v4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v4.set(j, o[i][j]);
-                v4.store(park + wv * ST * ST + (rr + i) * ST + cc);
-            }
+            for (int r = 0; r < WaveAcc<T>::NREG; ++r)
+                park[wv * ST * ST + WaveAcc<T>::row(r, lane) * ST + WaveAcc<T>::col(r, lane)] = o.get(r);
         };
         __syncthreads();  // staged operands consumed
         if (wv < nw) park_wave(pr);
@@ -384,19 +367,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
             }
         }
         __syncthreads();  // rowpart complete; the row partials are read
-        if (nbs) {
-            const int k0 = 4 * wv;
-#pragma unroll
-            for (int k = k0; k < k0 + 4; ++k) {
-                Vec4<T> a4, b4;
-                a4.load(sNB + k * PB + rr);  // strict(N_B[I, I])^T (r, k) = N_B[k][r]
-                b4.load(rowp + k * ST + cc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) pc[i][j] = kfma(a4[i], b4[j], pc[i][j]);
-            }
-        }
+        // strict(N_B[I, I])^T (r, k) = N_B[k][r]: k-major in sNB already
+        if (nbs) pc.template mma_block<PB, ST, 4>(sNB + 4 * wv * PB, rowp + 4 * wv * ST, lane);
         const int nw2 = nbs ? LEAF_THREADS / 64 : nw;
         if (wv < nw2) park_wave(pc);
         __syncthreads();
