@@ -129,8 +129,8 @@ struct Vec4<double> {
 // and after the sweep the leaf writes T1c[I, J] = rowpart + Delta[I, J] N_A[J, J]
 // for the later diagonals of its chunk.  With B = I only rowpart is added.  The
 // 32 x 32 x 32 products run on the matrix cores: their operands are staged
-// k-major in LDS, each slice is cut into four eight-deep K quarters, and every
-// wave accumulates the whole 32 x 32 block of the quarters it is dealt.
+// k-major in LDS and each wave owns one 16 x 16 quadrant of one of the two sums,
+// over all of its slices, so the sums need no reduction across waves.
 //
 // The quotient x / s is formed as x * (1/s) (1/s rounded once per row): within
 // two ulps of the IEEE quotient, so it can change a rounding decision only for
@@ -181,6 +181,44 @@ struct VecN {
     __device__ void store(T* p) const { *reinterpret_cast<V*>(p) = v; }
     __device__ T operator[](int j) const { return v[j]; }
     __device__ void set(int j, T x) { v[j] = x; }
+};
+
+// One wave's 16 x 16 block on the matrix cores: acc += A (16 x KD) B (KD x 16)
+// with A(r, k) = As[k * SA + r] and B(k, c) = Bs[k * SB + c].  Operand lanes
+// A[r = l % 16][k = l / 16], B[k = l / 16][c = l % 16]; result register r of lane
+// l sits at row 4 (l / 16) + r (fp32) or l / 16 + 4 r (fp64), column l % 16
+// (measured on gfx950).
+template <typename T>
+struct Q16;
+template <>
+struct Q16<float> {
+    f32x4 c;
+    __device__ void zero() { c = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    template <int SA, int SB, int KD>
+    __device__ void mma(const float* As, const float* Bs, int lane) {
+        const int kr = lane >> 4, ix = lane & 15;
+#pragma unroll
+        for (int kk = 0; kk < KD; kk += 4)
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(As[(kk + kr) * SA + ix], Bs[(kk + kr) * SB + ix], c, 0, 0, 0);
+    }
+    __device__ float get(int r) const { return c[r]; }
+    static __device__ __forceinline__ int row(int r, int lane) { return 4 * (lane >> 4) + r; }
+    static __device__ __forceinline__ int col(int, int lane) { return lane & 15; }
+};
+template <>
+struct Q16<double> {
+    f64x4 c;
+    __device__ void zero() { c = f64x4{0.0, 0.0, 0.0, 0.0}; }
+    template <int SA, int SB, int KD>
+    __device__ void mma(const double* As, const double* Bs, int lane) {
+        const int kr = lane >> 4, ix = lane & 15;
+#pragma unroll
+        for (int kk = 0; kk < KD; kk += 4)
+            c = __builtin_amdgcn_mfma_f64_16x16x4f64(As[(kk + kr) * SA + ix], Bs[(kk + kr) * SB + ix], c, 0, 0, 0);
+    }
+    __device__ double get(int r) const { return c[r]; }
+    static __device__ __forceinline__ int row(int r, int lane) { return (lane >> 4) + 4 * r; }
+    static __device__ __forceinline__ int col(int, int lane) { return lane & 15; }
 };
 
 constexpr int LEAF_THREADS = 512;   // the chunk products and the table set-up
@@ -298,9 +336,15 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
 
     // ---- chunk prologue: rowpart (crow) and the column feedback (ccol), block layout
     if (ns > 0) {
-        WaveAcc<T> pr, pc;  // this wave's sums of row-part and column-part products
-        pr.zero();
-        pc.zero();
+        // Wave wv owns the 16 x 16 quadrant qd = wv % 4 of one part: the row part
+        // (rowpart) for wv < 4 and the column part for wv >= 4, accumulated over all
+        // of that part's slices, so no partial sums cross waves.  With B = I there
+        // is no column part: the two halves take the row slices of even and odd
+        // index and their quadrants are added once at the end.
+        const int part = wv >> 2, qd = wv & 3, qr = 16 * (qd >> 1), qc = 16 * (qd & 1);
+        const bool split = NB == nullptr;
+        Q16<T> pq;
+        pq.zero();
         for (int sb = 0; sb < ns; sb += BATCH) {
             if (sb > 0) {
                 __syncthreads();  // the previous batch is consumed
@@ -324,58 +368,53 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
                 }
             }
             __syncthreads();
-            // matrix cores: the batch's slices cut into eight-deep K quarters,
-            // dealt round-robin to the waves; each wave accumulates whole 32 x 32
-            // blocks (reads stay k-major, 32 consecutive entries per half-wave)
+            // this wave's slices of the batch: its part's, or every other one
             const int nbat = ns - sb < BATCH ? ns - sb : BATCH;
-            for (int f = wv; f < 4 * nbat; f += LEAF_THREADS / 64) {
-                const int u = f >> 2, k0 = 8 * (f & 3);
-                const T* sa = stg[u][0] + k0 * PK;
-                const T* sbm = stg[u][1] + k0 * PK;
-                if (sb + u < n1)
-                    pr.template mma_block<PK, PK, 8>(sa, sbm, lane);
-                else
-                    pc.template mma_block<PK, PK, 8>(sa, sbm, lane);
+            int u0, u1, du;
+            if (split) {
+                u0 = (sb + part) & 1 ? 1 : 0;
+                u1 = nbat;
+                du = 2;
+            } else if (part == 0) {
+                u0 = 0;
+                u1 = n1 - sb < nbat ? (n1 - sb > 0 ? n1 - sb : 0) : nbat;
+                du = 1;
+            } else {
+                u0 = n1 - sb > 0 ? n1 - sb : 0;
+                u1 = nbat;
+                du = 1;
             }
+            for (int u = u0; u < u1; u += du)
+                pq.template mma<PK, PK, ST>(stg[u][0] + qr, stg[u][1] + qc, lane);
         }
-        // The waves' partial sums reach the block layout through the staging
-        // area, added in wave order: first the row parts (rowpart, kept in LDS
-        // as the right operand of the next product), then the column parts,
-        // to which every wave has added its share of strict(N_B[I, I])^T rowpart
-        // (K split eight ways).
-        const int nw = 4 * ns < LEAF_THREADS / 64 ? 4 * ns : LEAF_THREADS / 64;  // waves that had a quarter
-        const bool nbs = NB && n1 > 0;                                          // the in-tile column feedback
-        T* park = reinterpret_cast<T*>(stg);                                   // [wave][32 x 32]
-        T* rowp = park + (LEAF_THREADS / 64) * ST * ST;                        // rowpart, [k][c]
-        static_assert(sizeof(stg) >= (LEAF_THREADS / 64 + 1) * ST * ST * sizeof(T), "staging area too small");
-        auto park_wave = [&](const WaveAcc<T>& o) {
+        // the quadrants reach the block layout through the staging area:
+        // park[0] = rowpart (also the right operand of the in-tile column
+        // feedback), park[1] = the column part
+        const bool nbs = NB && n1 > 0;  // the in-tile column feedback strict(N_B[I, I])^T rowpart
+        T* park = reinterpret_cast<T*>(stg);
+        static_assert(sizeof(stg) >= 2 * ST * ST * sizeof(T), "staging area too small");
+        auto park_quadrant = [&]() {
+            T* q = park + part * ST * ST + qr * ST + qc;
 #pragma unroll
-            for (int r = 0; r < WaveAcc<T>::NREG; ++r)
-                park[wv * ST * ST + WaveAcc<T>::row(r, lane) * ST + WaveAcc<T>::col(r, lane)] = o.get(r);
+            for (int r = 0; r < 4; ++r) q[Q16<T>::row(r, lane) * ST + Q16<T>::col(r, lane)] = pq.get(r);
         };
         __syncthreads();  // staged operands consumed
-        if (wv < nw) park_wave(pr);
-        __syncthreads();
-        if (blk) {
-            for (int v = 0; v < nw; ++v) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) crow[i] += park[v * ST * ST + (r0 + i) * ST + b];
-            }
-            if (nbs) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) rowp[(r0 + i) * ST + b] = crow[i];
+        if (part == 0 || !nbs) park_quadrant();
+        if (nbs) {
+            __syncthreads();  // rowpart complete
+            if (part == 1) {
+                // strict(N_B[I, I])^T (r, k) = N_B[k][r], k-major in sNB already
+                pq.template mma<PB, ST, ST>(sNB + qr, park + qc, lane);
+                park_quadrant();
             }
         }
-        __syncthreads();  // rowpart complete; the row partials are read
-        // strict(N_B[I, I])^T (r, k) = N_B[k][r]: k-major in sNB already
-        if (nbs) pc.template mma_block<PB, ST, 4>(sNB + 4 * wv * PB, rowp + 4 * wv * ST, lane);
-        const int nw2 = nbs ? LEAF_THREADS / 64 : nw;
-        if (wv < nw2) park_wave(pc);
         __syncthreads();
         if (blk) {
-            for (int v = 0; v < nw2; ++v) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ccol[i] += park[v * ST * ST + (r0 + i) * ST + b];
+            for (int i = 0; i < 4; ++i) {
+                const T p0 = park[(r0 + i) * ST + b], p1 = park[ST * ST + (r0 + i) * ST + b];
+                crow[i] = split ? p0 + p1 : p0;
+                ccol[i] = split ? T(0) : p1;
             }
         }
 #pragma unroll
