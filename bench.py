@@ -6,10 +6,12 @@ rows) and B (4096 gradient rows), damped factor preparation of both, per-row
 scales, two-sided GPTQ (2-bit grid) and the proxy loss, which the solver takes
 from its own rounding errors (tr(B_d E A_d E^T) = sum (Delta_ij / (U_B,ii
 U_A,jj))^2 with the error-feedback identity E = L~_B Delta L~_A^T).  The steps
-are the layers of a job, pipelined as a model block would be: the factor chains
-(A on one side stream, B on another) of layer k + 1 run while layer k is solved
-on the main stream, with two resident buffer sets; every step still computes
-everything from its inputs.  ``ms_per_step`` is the wall time of K steps over K,
+are the layers of a job, which are independent of one another, pipelined: the
+factor chains (A on one side stream, B on another) of the next layers run while
+the current ones are solved, and consecutive layers are solved on two alternate
+streams, so two solves share the GPU (the tile sweeps of one solve occupy at most
+half of the CUs).  Four resident buffer sets rotate over the layers; every step
+still computes everything from its inputs.  ``ms_per_step`` is the wall time of K steps over K,
 the pipeline fill included.  ``breakdown_ms.single_layer`` is one layer with
 nothing beside it; ``serial_breakdown_ms`` times one layer's calls one after
 another on one stream, and then kron_loss, which recomputes the loss from W and
@@ -119,8 +121,8 @@ def main() -> int:
     damp = c["damp"]
 
     # resident buffers and workspaces (allocated once, outside the timed region).
-    # Two sets: the factor chains of layer k + 1 fill one while layer k is solved
-    # from the other.
+    # NSETS sets rotate over the layers: two solves and the next layers' factor
+    # chains are in flight at once, each on its own set.
     def buffer_set():
         S = {"A": torch.empty(n, n, dtype=torch.float32, device=dev),
              "B": torch.empty(m, m, dtype=torch.float32, device=dev)}
@@ -137,18 +139,21 @@ def main() -> int:
             S[k] = torch.cuda.Event()
         return S
 
-    sets = [buffer_set(), buffer_set()]
-    ws_q = kq.workspace(kq.KQ_OP_QUANTIZE, torch.float32, m, n)
+    NSETS = 4
+    sets = [buffer_set() for _ in range(NSETS)]
+    ws_qs = [kq.workspace(kq.KQ_OP_QUANTIZE, torch.float32, m, n) for _ in range(2)]  # one per solve stream
+    ws_q = ws_qs[0]
     ws_l = kq.workspace(kq.KQ_OP_LOSS, torch.float32, m, n)
     loss_check = torch.empty(1, dtype=torch.float64, device=dev)
     main = torch.cuda.current_stream()
-    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    sa, sb, s2 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    solvers = (main, s2)  # consecutive layers are solved on alternate streams
 
     def chains(S, k):
         """Layer k's factor chains: A (product, prepare, then the scales) on sa,
         B (product, prepare) on sb once the A product is done.  They wait for the
-        solve of layer k - 2, the last user of this buffer set."""
-        if k >= 2:
+        solve of layer k - NSETS, the last user of this buffer set."""
+        if k >= NSETS:
             sa.wait_event(S["q_done"])  # sb follows through a_done
         with torch.cuda.stream(sa):
             kq.kron_factor_accumulate(act, S["A"], 1.0 / rows, 0.0)
@@ -165,20 +170,25 @@ def main() -> int:
             kq.kron_row_scales(W, bits, True, S["scales"])
             S["ea"].record(sa)
 
-    def solve(S):
-        """Layer k's solve on the main stream, with its proxy loss (from the
-        rounding errors), once both chains of the layer are done."""
-        main.wait_event(S["ea"])
-        main.wait_event(S["eb"])
-        kq.kron_quantize(W, S["UA"], S["UB"], bits, True, S["scales"], S["codes"], S["V"], ws_q, loss=S["loss"])
-        S["q_done"].record(main)
+    def solve(S, k):
+        """Layer k's solve, with its proxy loss (from the rounding errors), on
+        solve stream k % 2 once both chains of the layer are done."""
+        ss = solvers[k % 2]
+        ss.wait_event(S["ea"])
+        ss.wait_event(S["eb"])
+        with torch.cuda.stream(ss):
+            kq.kron_quantize(W, S["UA"], S["UB"], bits, True, S["scales"], S["codes"], S["V"], ws_qs[k % 2],
+                             loss=S["loss"])
+        S["q_done"].record(ss)
 
     def step(k):
         """One layer (step k of the run): its chains, then its solve.  Issued in
-        this order, the chains of layer k + 1 run beside the solve of layer k."""
-        S = sets[k % 2]
+        this order, the chains of layer k + 1 run beside the solve of layer k, and
+        the solve of layer k + 1 (on the other solve stream) beside it too once its
+        chains are done."""
+        S = sets[k % NSETS]
         chains(S, k)
-        solve(S)
+        solve(S, k)
 
     names = ["factor", "prepare", "scales", "quantize_and_loss", "loss_check"]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
@@ -210,7 +220,7 @@ def main() -> int:
         step(k)
         k += 1
     torch.cuda.synchronize()
-    for S in sets[:min(2, max(1, args.warmup))]:
+    for S in sets[:min(NSETS, max(1, args.warmup))]:
         assert S["infoA"].item() == 0 and S["infoB"].item() == 0, "factor not positive definite"
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
@@ -222,6 +232,10 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # every layer of the run has the same inputs: the sets written by the
+    # concurrent solves must hold identical codes
+    ref_codes = sets[(k - 1) % NSETS]["codes"].clone()
+    pipe_equal = all(torch.equal(S["codes"], ref_codes) for S in sets[:min(NSETS, k)])
 
     # one layer alone (nothing before or after it in flight): its chains, then its solve
     single = []
@@ -229,7 +243,7 @@ def main() -> int:
         torch.cuda.synchronize()
         ev[0].record()
         sa.wait_stream(main)  # the chains start after the first event
-        step(0)  # k = 0: no wait on an earlier solve; both sets are idle here
+        step(0)  # k = 0: no wait on an earlier solve; every set is idle here
         ev[1].record()
         torch.cuda.synchronize()
         single.append(ev[0].elapsed_time(ev[1]))
@@ -242,6 +256,7 @@ def main() -> int:
             serial[k].append(ev[i].elapsed_time(ev[i + 1]))
     loss = sets[0]["loss"]
     UA, UB, scales, codes, V = (sets[0][x] for x in ("UA", "UB", "scales", "codes", "V"))
+    pipe_equal = pipe_equal and torch.equal(codes, ref_codes)  # the serial step's codes too
     # the step's loss (from the solver's errors) against kron_loss on the same output
     l_solver, l_trace = float(loss.item()), float(loss_check.item())
 
@@ -278,11 +293,13 @@ def main() -> int:
             "m": m, "n": n, "bits": bits, "calibration_rows": rows,
             "step": "one layer: [factor_accumulate(A), prepare(A), row_scales] beside [factor_accumulate(B), "
                     "prepare(B)] on two side streams, then quantize with its proxy loss (from the rounding errors) "
-                    "on the main stream; layers are pipelined, layer k + 1's chains beside layer k's solve",
+                    "on one of two solve streams (alternating by layer); layers are pipelined: the next layers' "
+                    "chains and the other solve stream's layer run beside each solve",
         },
         "loss": {"solver": l_solver, "kron_loss": l_trace, "rel_diff": abs(l_solver - l_trace) / l_trace,
                  "note": "kron_loss (trace form from W and V, fp64) runs after the timed steps as a check; "
                          "its time is serial_breakdown_ms.loss_check"},
+        "pipeline_outputs_equal": bool(pipe_equal),
         "breakdown_ms": {"single_layer": float(np.median(single))},
         "serial_breakdown_ms": {k: float(np.median(v)) for k, v in serial.items()},
         "core": {

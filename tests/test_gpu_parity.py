@@ -263,11 +263,13 @@ def test_row_scales_bit_exact(per_row):
 
 @pytest.mark.parametrize("two_sided", [True, False])
 def test_pipelined_layers_equal_one_at_a_time(two_sided):
-    # quantize_layers overlaps layer k + 1's factor chains with layer k's solve;
-    # every result must equal quantize_layer on that layer alone, bit for bit
-    # (the path is deterministic), across shapes that change from layer to layer.
+    # quantize_layers overlaps layer k + 1's factor chains with layer k's solve
+    # and solves consecutive layers on two streams at once; every result must
+    # equal quantize_layer on that layer alone, bit for bit (the path is
+    # deterministic), across shapes that change from layer to layer (the last
+    # two large enough for both solves' band products to fill the GPU together).
     say("pipelined layers", two_sided)
-    shapes = [(96, 64), (64, 130), (100, 100), (33, 70)]
+    shapes = [(96, 64), (64, 130), (100, 100), (33, 70), (520, 384), (384, 640)]
     for dtype in (np.float64, np.float32):
         layers = []
         for i, (m, n) in enumerate(shapes):

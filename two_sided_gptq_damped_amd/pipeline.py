@@ -142,33 +142,45 @@ def _factor_chains(W, act, grad, bits, per_row, damp_rel, two_sided, sa, sb):
 
 
 def quantize_layers(layers, bits, per_row=True, damp_rel=0.01, two_sided=True, check_loss=False):
-    """Quantize a sequence of layers [(W, act, grad), ...] with the factor chains
-    of layer k + 1 running beside the solve of layer k.  Returns one dict per
-    layer, as quantize_layer does.  The positive-definiteness of every damped
-    factor is checked once, after the last layer has been issued (a host wait
-    per layer would stop the pipeline); KronError names the first failing layer."""
+    """Quantize a sequence of independent layers [(W, act, grad), ...].  The
+    factor chains of layer k + 1 run beside the solve of layer k, and consecutive
+    layers are solved on two alternate streams (the caller's and a second one),
+    so two solves share the GPU: the tile sweeps of one solve occupy at most half
+    of the CUs.  Returns one dict per layer, as quantize_layer does, ready on the
+    caller's stream.  The positive-definiteness of every damped factor is checked
+    once, after the last layer has been issued (a host wait per layer would stop
+    the pipeline); KronError names the first failing layer."""
     main = torch.cuda.current_stream()
-    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
-    sa.wait_stream(main)
-    sb.wait_stream(main)  # every input is ready
+    sa, sb, s2 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    for s in (sa, sb, s2):
+        s.wait_stream(main)  # every input is ready
+    solvers = (main, s2)
     results = []
     nxt = _factor_chains(*layers[0], bits, per_row, damp_rel, two_sided, sa, sb) if layers else None
     for k, (W, act, grad) in enumerate(layers):
         cur = nxt
         if k + 1 < len(layers):
             nxt = _factor_chains(*layers[k + 1], bits, per_row, damp_rel, two_sided, sa, sb)
+        ss = solvers[k % 2]
         for e in cur["events"]:
-            main.wait_event(e)
+            ss.wait_event(e)
         for key in ("A", "B", "U_A", "U_B", "trace_A", "trace_B", "scales", "info"):
             if cur[key] is not None:
-                cur[key].record_stream(main)
-        lo = torch.empty(1, dtype=torch.float64, device=W.device)
-        codes, V, scales = quantize(W, cur["U_A"], cur["U_B"], bits, per_row, scales=cur["scales"], loss_out=lo)
-        out = dict(A=cur["A"], B=cur["B"], U_A=cur["U_A"], U_B=cur["U_B"], trace_A=cur["trace_A"],
-                   trace_B=cur["trace_B"], codes=codes, V=V, scales=scales, loss=lo, info=cur["info"])
-        if check_loss:
-            out["loss_check"] = loss(W, V, cur["A"], cur["B"], damp_rel)
+                cur[key].record_stream(ss)
+        with torch.cuda.stream(ss):
+            lo = torch.empty(1, dtype=torch.float64, device=W.device)
+            codes, V, scales = quantize(W, cur["U_A"], cur["U_B"], bits, per_row, scales=cur["scales"], loss_out=lo)
+            out = dict(A=cur["A"], B=cur["B"], U_A=cur["U_A"], U_B=cur["U_B"], trace_A=cur["trace_A"],
+                       trace_B=cur["trace_B"], codes=codes, V=V, scales=scales, loss=lo, info=cur["info"])
+            if check_loss:
+                out["loss_check"] = loss(W, V, cur["A"], cur["B"], damp_rel)
+        if ss is not main:
+            W.record_stream(ss)
+            for key in ("codes", "V", "loss", "loss_check"):
+                if key in out:
+                    out[key].record_stream(main)  # made on s2, handed to the caller's stream
         results.append(out)
+    main.wait_stream(s2)
     for k, out in enumerate(results):
         bad = out.pop("info").cpu()
         for name, piv in (("A", int(bad[0])), ("B", int(bad[1]))):
