@@ -12,7 +12,10 @@ the current ones are solved, and consecutive layers are solved on two alternate
 streams, so two solves share the GPU (the tile sweeps of one solve occupy at most
 half of the CUs).  Four resident buffer sets rotate over the layers; every step
 still computes everything from its inputs.  ``ms_per_step`` is the wall time of K steps over K,
-the pipeline fill included.  ``breakdown_ms.single_layer`` is one layer with
+the pipeline fill included: the timed steps start from an idle device, so the
+first layer's factor chains (about 5 ms) run before any solve.  K is 50 layers by
+default; a job is many layers (a Llama-3-8B model has 224 sublayers), and the
+fill is paid once per job.  ``breakdown_ms.single_layer`` is one layer with
 nothing beside it; ``serial_breakdown_ms`` times one layer's calls one after
 another on one stream, and then kron_loss, which recomputes the loss from W and
 V alone in fp64 (outside the step; both values are reported under ``loss``).
@@ -29,7 +32,7 @@ cpu_baseline: the CPU oracle's whole pipeline (numpy fp64 factor products,
 inverse and Cholesky, the C left-looking loop with OpenMP, the loss) on the same
 4096 x 4096 workload, timed once on the host cores (rank 0, N = 1 only).
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 3] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -83,7 +86,7 @@ def solver_traffic(m: int, n: int):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--m", type=int, default=4096)
     ap.add_argument("--n", type=int, default=4096)
