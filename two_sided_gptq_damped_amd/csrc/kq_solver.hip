@@ -653,11 +653,13 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
 
 // Stage 1 at node [K0, K1) with split mid, on 64-row block P and 64-column block Q.
 // Band GEMMs run split-K inside the workgroup: their launches have few blocks
-// with long K ranges in the lower recursion levels, so each block gets BAND_G
+// with long K ranges in the lower recursion levels, so each block gets G = 2
 // groups of four waves (deterministic reduction, see tile_gemm_masked_splitk).
+// Four groups shorten a lone solve's small launches a little, but two leave
+// more of the device to the other work in flight beside them.
 template <typename T>
 struct Band {
-    static constexpr int G = sizeof(T) == 4 ? 4 : 2;  // stage 1: groups per block
+    static constexpr int G = 2;  // stage 1: groups per block
     static constexpr int THREADS = 256 * G;
     // Stage 2 has half the blocks of stage 1 at the top node with twice the K
     // each; there four-wave blocks at full occupancy balance better than split K.
