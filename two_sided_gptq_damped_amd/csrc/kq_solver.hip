@@ -38,34 +38,16 @@ constexpr int ST = 32;    // scheduling tile edge
 constexpr int CHUNK = 8;  // tile-diagonals per recursion leaf (chunk)
 
 // N[r][c] = U[r][c] / U[r][r] for c >= r inside d x d; identity in the padding.
+// Rows blockIdx.y, + gridDim.y, ...; each thread four consecutive columns (dp is
+// a multiple of 64, so they are in range and the store is 16-byte aligned).
 template <typename T>
 __global__ void normalize_factor_kernel(const T* __restrict__ U, int64_t ldu, int d, int dp,
-                                        T* __restrict__ N) {
-    const int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
-    if (idx >= int64_t(dp) * dp) return;
-    const int r = int(idx / dp), c = int(idx % dp);
-    T v;
-    if (r < d && c < d)
-        v = (c >= r) ? U[int64_t(r) * ldu + c] / U[int64_t(r) * ldu + r] : T(0);
-    else
-        v = (r == c) ? T(1) : T(0);
-    N[idx] = v;
-}
+                                        T* __restrict__ N);
 
 template <typename T>
 __global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, int n, int mp, int np,
                                    const T* __restrict__ scales, int per_row, T* __restrict__ X,
-                                   T* __restrict__ S) {
-    const int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
-    if (idx < int64_t(mp) * np) {
-        const int r = int(idx / np), c = int(idx % np);
-        X[idx] = (r < m && c < n) ? W[int64_t(r) * ldw + c] : T(0);
-    }
-    if (idx < mp) {
-        const int r = int(idx);
-        S[r] = r < m ? scales[per_row ? r : 0] : T(1);
-    }
-}
+                                   T* __restrict__ S);
 
 // Four consecutive elements (16-byte aligned), from global memory or LDS.
 template <typename T>
@@ -171,6 +153,46 @@ __device__ __forceinline__ double lanes_up32(double v) {
     const unsigned slo = __builtin_amdgcn_permlane32_swap(lo, lo, false, false)[0];
     const unsigned shi = __builtin_amdgcn_permlane32_swap(hi, hi, false, false)[0];
     return __builtin_bit_cast(double, (uint64_t(shi) << 32) | slo);
+}
+
+template <typename T>
+__global__ void normalize_factor_kernel(const T* __restrict__ U, int64_t ldu, int d, int dp,
+                                        T* __restrict__ N) {
+    const int c0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+    if (c0 >= dp) return;
+    for (int r = blockIdx.y; r < dp; r += gridDim.y) {
+        const T* row = U + int64_t(r) * ldu;
+        const T diag = r < d ? row[r] : T(1);
+        Vec4<T> v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c0 + u;
+            T x;
+            if (r < d && c < d)
+                x = (c >= r) ? row[c] / diag : T(0);
+            else
+                x = (r == c) ? T(1) : T(0);
+            v.set(u, x);
+        }
+        v.store(N + int64_t(r) * dp + c0);
+    }
+}
+
+// X = W zero-padded to mp x np; S = the scales, unit in the padding.  Rows as in
+// normalize_factor_kernel, four consecutive columns per thread.
+template <typename T>
+__global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, int n, int mp, int np,
+                                   const T* __restrict__ scales, int per_row, T* __restrict__ X,
+                                   T* __restrict__ S) {
+    const int c0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+    for (int r = blockIdx.y; r < mp; r += gridDim.y) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) S[r] = r < m ? scales[per_row ? r : 0] : T(1);
+        if (c0 >= np) continue;
+        Vec4<T> v;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v.set(u, (r < m && c0 + u < n) ? W[int64_t(r) * ldw + c0 + u] : T(0));
+        v.store(X + int64_t(r) * np + c0);
+    }
 }
 
 template <typename T, int N>
@@ -787,16 +809,23 @@ __global__ __launch_bounds__(256) void error_loss_partial_kernel(const T* __rest
                                                                  const double* __restrict__ rb,
                                                                  double* __restrict__ partial) {
     __shared__ double red[256];
-    double s = 0.0;
+    // four independent sums, so four loads per thread are in flight at once
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
     for (int i = blockIdx.x; i < m; i += gridDim.x) {
         const double ri = rb ? rb[i] : 1.0;
         const T* row = D + int64_t(i) * np;
-        for (int j = threadIdx.x; j < n; j += blockDim.x) {
-            const double q = double(row[j]) * ra[j] * ri;
-            s = __builtin_fma(q, q, s);
+        for (int j0 = threadIdx.x; j0 < n; j0 += 4 * 256) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + 256 * u;
+                if (j < n) {
+                    const double q = double(row[j]) * ra[j] * ri;
+                    s[u] = __builtin_fma(q, q, s[u]);
+                }
+            }
         }
     }
-    const double tot = block_sum_256(s, red);
+    const double tot = block_sum_256((s[0] + s[1]) + (s[2] + s[3]), red);
     if (threadIdx.x == 0) partial[blockIdx.x] = tot;
 }
 
@@ -925,15 +954,18 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
                      codes, ldc, V, ldv, st};
     const int threads = 256;
     auto blocks = [&](int64_t count) { return dim3(unsigned((count + threads - 1) / threads)); };
-    hipLaunchKernelGGL(normalize_factor_kernel<T>, blocks(L.np * L.np), dim3(threads), 0, st, UA, lda, int(n),
+    auto rows = [&](int64_t cols, int64_t nrows) {  // the kernels loop over rows beyond the grid's y extent
+        return dim3(unsigned((cols / 4 + threads - 1) / threads), unsigned(nrows < 65535 ? nrows : 65535));
+    };
+    hipLaunchKernelGGL(normalize_factor_kernel<T>, rows(L.np, L.np), dim3(threads), 0, st, UA, lda, int(n),
                        int(L.np), run.NA);
     KQ_LAUNCHED("normalize_factor_kernel");
     if (UB) {
-        hipLaunchKernelGGL(normalize_factor_kernel<T>, blocks(L.mp * L.mp), dim3(threads), 0, st, UB, ldb, int(m),
+        hipLaunchKernelGGL(normalize_factor_kernel<T>, rows(L.mp, L.mp), dim3(threads), 0, st, UB, ldb, int(m),
                            int(L.mp), run.NB);
         KQ_LAUNCHED("normalize_factor_kernel");
     }
-    hipLaunchKernelGGL(init_solver_kernel<T>, blocks(L.mp * L.np), dim3(threads), 0, st, W, ldw, int(m), int(n),
+    hipLaunchKernelGGL(init_solver_kernel<T>, rows(L.np, L.mp), dim3(threads), 0, st, W, ldw, int(m), int(n),
                        int(L.mp), int(L.np), static_cast<const T*>(q->scales), q->per_row, run.X, run.S);
     KQ_LAUNCHED("init_solver_kernel");
     const kq_status s = run.solve(0, int(L.Mt + L.Nt - 1));
