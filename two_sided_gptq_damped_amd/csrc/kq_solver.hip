@@ -795,7 +795,7 @@ __global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T*
 //   tr(B_d (V - W) A_d (V - W)^T) = sum_ij (Delta_ij / (U_B,ii U_A,jj))^2.
 // Rows go round-robin over ELOSS_PARTS workgroups; every sum runs in a fixed
 // order, so the result is deterministic.
-constexpr int ELOSS_PARTS = 512;
+constexpr int ELOSS_PARTS = 2048;
 
 template <typename T>
 __global__ void diag_recip_kernel(const T* __restrict__ U, int64_t ldu, int d, double* __restrict__ out) {
