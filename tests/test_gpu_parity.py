@@ -135,6 +135,18 @@ def test_ragged_shapes_fp64(m, n):
     check_fp64(c["W"], UA, UB, s, 4, True, f"ragged {m}x{n}")
 
 
+def test_tall_one_sided_at_the_largest_m():
+    # m = 65536, the largest the ABI takes: the solver's set-up kernels walk the
+    # rows past the 65535 that one grid dimension holds, and the leaves run 2049
+    # tile-diagonals of at most two tiles.  B = I, so no 65536^2 output factor.
+    m, n = 65536, 64
+    W = synth.gaussian(401, (m, n))
+    A = dense.factor_accumulate(synth.channel_scaled_rows(402, 403, 256, n), alpha=1 / 256)
+    _, UA, _, _ = oracle_factors(A, None)
+    s = dense.scales(W, 3, True)
+    check_fp64(W, UA, None, s, 3, True, "tall one-sided")
+
+
 @pytest.mark.parametrize("bits,per_row", [(2, True), (3, False), (5, True), (8, False)])
 def test_bits_and_scale_modes(bits, per_row):
     c = synth.spectral(96, 80, config=2)
