@@ -121,15 +121,6 @@ struct WaveAcc<float> {
             c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
         }
     }
-    // The wave's whole 32 x 32 block over KD values of k, operands k-major:
-    // A(r, k) = As[k * SA + r], B(k, c) = Bs[k * SB + c].
-    template <int SA, int SB, int KD>
-    __device__ void mma_block(const float* As, const float* Bs, int lane) {
-        const int kr = lane >> 5, ix = lane & 31;
-#pragma unroll
-        for (int kk = 0; kk < KD; kk += 2)
-            c = __builtin_amdgcn_mfma_f32_32x32x2f32(As[(kk + kr) * SA + ix], Bs[(kk + kr) * SB + ix], c, 0, 0, 0);
-    }
     static constexpr int NREG = 16;
     __device__ float get(int r) const { return c[r]; }
     __device__ void add(int r, float v) { c[r] += v; }
@@ -158,19 +149,6 @@ struct WaveAcc<double> {
             double a1 = As[(kk + kr) * S + wy * 32 + 16 + ix];
             double b0 = Bs[(kk + kr) * S + wx * 32 + ix];
             double b1 = Bs[(kk + kr) * S + wx * 32 + 16 + ix];
-            c[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, c[0][0], 0, 0, 0);
-            c[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, c[0][1], 0, 0, 0);
-            c[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, c[1][0], 0, 0, 0);
-            c[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, c[1][1], 0, 0, 0);
-        }
-    }
-    template <int SA, int SB, int KD>
-    __device__ void mma_block(const double* As, const double* Bs, int lane) {
-        const int kr = lane >> 4, ix = lane & 15;
-#pragma unroll
-        for (int kk = 0; kk < KD; kk += 4) {
-            const double a0 = As[(kk + kr) * SA + ix], a1 = As[(kk + kr) * SA + 16 + ix];
-            const double b0 = Bs[(kk + kr) * SB + ix], b1 = Bs[(kk + kr) * SB + 16 + ix];
             c[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, c[0][0], 0, 0, 0);
             c[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, c[0][1], 0, 0, 0);
             c[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, c[1][0], 0, 0, 0);
