@@ -176,9 +176,11 @@ def quantize_layers(layers, bits, per_row=True, damp_rel=0.01, two_sided=True, c
                 out["loss_check"] = loss(W, V, cur["A"], cur["B"], damp_rel)
         if ss is not main:
             W.record_stream(ss)
-            for key in ("codes", "V", "loss", "loss_check"):
-                if key in out:
-                    out[key].record_stream(main)  # made on s2, handed to the caller's stream
+            # everything handed back was made on a side stream: the caller's
+            # stream uses it from here on
+            for key in ("A", "B", "U_A", "U_B", "trace_A", "trace_B", "scales", "codes", "V", "loss", "loss_check"):
+                if out.get(key) is not None:
+                    out[key].record_stream(main)
         results.append(out)
     main.wait_stream(s2)
     for k, out in enumerate(results):
