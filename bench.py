@@ -5,22 +5,22 @@ is already resident in HBM: K-FAC factor accumulation for A (4096 activation
 rows) and B (4096 gradient rows), damped factor preparation of both, per-row
 scales, two-sided GPTQ (2-bit grid) and the proxy loss, which the solver takes
 from its own rounding errors (tr(B_d E A_d E^T) = sum (Delta_ij / (U_B,ii
-U_A,jj))^2 with the error-feedback identity E = L~_B Delta L~_A^T).  The steps
+U_A,jj))^2 with the error-feedback identity E = L~_B Delta L~_A^T). The steps
 are the layers of a job, which are independent of one another, pipelined: the
 factor chains (A on one side stream, B on another) of the next layers run while
 the current ones are solved, and consecutive layers are solved on two alternate
-streams, so two solves share the GPU (the tile sweeps of one solve occupy at most
-half of the CUs).  Four resident buffer sets rotate over the layers; every step
-still computes everything from its inputs.  ``ms_per_step`` is the wall time of K steps over K,
-the pipeline fill included: the timed steps start from an idle device, so the
-first layer's factor chains (about 5 ms) run before any solve.  K is 50 layers by
-default; a job is many layers (a Llama-3-8B model has 224 sublayers), and the
-fill is paid once per job.  ``breakdown_ms.single_layer`` is one layer with
-nothing beside it; ``serial_breakdown_ms`` times one layer's calls one after
-another on one stream, and then kron_loss, which recomputes the loss from W and
-V alone in fp64 (outside the step; both values are reported under ``loss``).
-``value`` is weights
-per second of the whole step (m n / step time).  The core solver alone
+streams, so two solves share the GPU (the tile sweeps of one solve occupy at
+most half of the CUs). Four resident buffer sets rotate over the layers; every
+step still computes everything from its inputs. ``ms_per_step`` is the wall time
+of K steps over K, the pipeline fill included: the timed steps start from an
+idle device, so the first layer's factor chains (about 5 ms) run before any
+solve. K is 50 layers by default; a job is many layers (a Llama-3-8B model has
+224 sublayers), and the fill is paid once per job. ``breakdown_ms.single_layer``
+is one layer with nothing beside it; ``serial_breakdown_ms`` times one layer's
+calls one after another on one stream, and then kron_loss, which recomputes the
+loss from W and V alone in fp64 (outside the step; both values are reported
+under ``loss``).  ``value`` is weights per second of the whole step (m n / step
+time).  The core solver alone
 (kron_quantize with factors and scales resident, the pages' "core algorithm"
 timing) is reported under ``core``.
 
