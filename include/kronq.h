@@ -132,7 +132,10 @@ kq_status kron_row_scales(kq_dtype dtype, int64_t m, int64_t n, const void* W, i
  *   W      m x n input weights (not modified), ldw >= n
  *   U_A    n x n upper factor from kron_prepare (U_A^T U_A = A_d^{-1}), lda >= n
  *   U_B    m x m upper factor of B_d, ldb >= m; NULL means B = I, which is
- *          standard one-sided GPTQ with input curvature A
+ *          standard one-sided GPTQ with input curvature A: every row is then its
+ *          own problem, and the library runs the recursive lazily batched GPTQ
+ *          of FastKron page section 2.4 (column ranges halved down to 64-column
+ *          leaves, the feedback between them as dense products), at one-sided cost
  *   q      base quantizer (see kq_quantizer)
  *   codes  m x n int8 output, ldc >= n
  *   V      m x n output, V_ij = s_i * codes_ij, ldv >= n

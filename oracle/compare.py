@@ -81,6 +81,25 @@ def trajectory_violations(Z_cand, Y_forced, bits, tie_tol):
     return int((differ & ~near).sum()), int(near.sum())
 
 
+def mismatch_roots(mask) -> np.ndarray:
+    """The differing entries that no other differing entry precedes.
+
+    An entry's pre-rounding value depends only on the codes to its top-left
+    (componentwise <=, FastKron page section 2.3), so where two runs first part
+    ways every later difference lies in the bottom-right cone of an earlier one.
+    A root is a difference with no other difference in its top-left rectangle:
+    every code it depends on is equal in both runs, so both saw the same exact
+    pre-rounding value there and the split can only be a near-tie decision.
+    """
+    M = np.asarray(mask, dtype=bool)
+    P = np.logical_or.accumulate(np.logical_or.accumulate(M, axis=0), axis=1)
+    above = np.zeros_like(M)
+    above[1:, :] = P[:-1, :]
+    left = np.zeros_like(M)
+    left[:, 1:] = P[:, :-1]
+    return M & ~above & ~left
+
+
 def mismatch_fraction(Z_a, Z_b) -> float:
     return float(np.mean(np.asarray(Z_a) != np.asarray(Z_b)))
 

@@ -124,3 +124,34 @@ def test_prepare_factor_loss_scales_reject_bad_arguments():
     assert lib.kron_row_scales(kq.KQ_F32, 8, 8, FAKE, 8, 1, 1, FAKE, None) == 1
     assert lib.kron_row_scales(kq.KQ_F32, 8, 8, FAKE, 8, 4, 3, FAKE, None) == 1
     assert lib.kron_row_scales(kq.KQ_F32, 8, 8, None, 8, 4, 1, FAKE, None) == 1
+
+
+def test_binding_rejects_mismatched_arguments():
+    # The C entry points see raw pointers only, so the binding checks element
+    # type, device and shape of every tensor before the call (CPU tensors here:
+    # each check fails before the library is reached).
+    torch = pytest.importorskip("torch")
+    m, n = 6, 5
+    W = torch.zeros(m, n)
+    UA, UB = torch.zeros(n, n), torch.zeros(m, m)
+    s, codes, V = torch.ones(m), torch.zeros(m, n, dtype=torch.int8), torch.zeros(m, n)
+    ws = torch.zeros(256, dtype=torch.uint8)
+    bad = [
+        dict(U_A=UA.double()), dict(U_B=UB[:4, :4]), dict(scales=s.double()), dict(scales=s[:3]),
+        dict(codes=codes.int()), dict(V=V.double()), dict(ws=ws.float()),
+        dict(loss=torch.zeros(1)), dict(codes=torch.zeros(n, m, dtype=torch.int8)),
+    ]
+    for change in bad:
+        args = dict(W=W, U_A=UA, U_B=UB, bits=3, per_row=True, scales=s, codes=codes, V=V, ws=ws, loss=None)
+        args.update(change)
+        with pytest.raises(ValueError):
+            kq.kron_quantize(**args)
+    with pytest.raises(ValueError):
+        kq.kron_prepare(UA, 0.01, UA.double(), ws)
+    with pytest.raises(ValueError):
+        kq.kron_prepare(UA, 0.01, UA, ws, info=torch.zeros(1, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        kq.kron_loss(W, V, UA, UB.double(), 0.01, torch.zeros(1, dtype=torch.float64), ws)
+    with pytest.raises(ValueError):
+        kq.kron_factor_accumulate(W, torch.zeros(n, n, dtype=torch.float64), 1.0, 0.0)
+

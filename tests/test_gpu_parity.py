@@ -166,6 +166,56 @@ def test_zero_row_scale_gives_zero_codes():
     assert np.all(Zg[5] == 0) and np.all(Vg[5] == 0)
 
 
+@pytest.mark.parametrize("per_row", [True, False])
+def test_identity_factors_round_to_nearest_with_exact_ties(per_row):
+    # A = B = I: no feedback reaches any entry, so two-sided GPTQ is round to
+    # nearest (FastKron page section 2.2 with identity curvature).  Every entry is
+    # an exact half-integer multiple of a power-of-two scale, so the GPU's
+    # rounding must be round-half-to-even at every entry, with no tie tolerance.
+    m, n, bits = 96, 80, 4
+    r = synth.rng(4242)
+    e = r.integers(-6, 3, size=m)
+    s = np.ldexp(1.0, e) if per_row else np.full(m, 0.125)
+    k = r.integers(-8, 8, size=(m, n)).astype(np.float64) + 0.5  # half-integers, some beyond the grid
+    k[:, 0] = 7.0  # the row maximum: max |W_i| / 7 is exactly s_i
+    k = np.clip(k, -7.0, 7.0)
+    W = k * s[:, None]
+    sc = dense.scales(W, bits, per_row)
+    assert np.array_equal(dense.row_scales(sc, m), s)
+    want = np.clip(np.rint(k), -8, 7)
+    assert np.sum(want != np.floor(k)) > 0 and np.sum(np.abs(k - np.floor(k) - 0.5) == 0) > m * n // 2
+    for dtype in (np.float64, np.float32):
+        for UB in (np.eye(m), None):
+            Zg, Vg = gpu_quantize(W, np.eye(n), UB, sc, bits, per_row, dtype)
+            say("rtn ties", np.dtype(dtype).name, "B=I" if UB is None else "two-sided", per_row)
+            assert np.array_equal(Zg.astype(np.float64), want)
+            assert np.array_equal(Vg.astype(np.float64), want * s[:, None])
+
+
+def test_exact_tie_at_the_first_entry():
+    # Entry (0, 0) receives no feedback, so x_00 = W_00 exactly; with W_00 = 2.5 s_0
+    # and s_0 a power of two both sides see an exact tie, which rounds to the even
+    # code 2.  Asserted without a tie tolerance, two-sided and B = I, fp64 and fp32.
+    c = synth.spectral(64, 64, config=2)
+    _, UA, _, UB = oracle_factors(c["A"], c["B"])
+    W = c["W"].copy()
+    W[0, :] = np.clip(W[0, :], -1.5, 1.5)
+    W[0, 5] = 1.75  # max |W_0| / 7 = 0.25
+    W[0, 0] = 2.5 * 0.25
+    s = dense.scales(W, 4, True)
+    assert s[0] == 0.25
+    for UBx in (UB, None):
+        Zo, _, Yo, _ = o3.solve(W, UA, UBx, s, 4)
+        assert Zo[0, 0] == 2 and Yo[0, 0] == 2.5
+        for dtype in (np.float64, np.float32):
+            Wd = W.astype(dtype).astype(np.float64)
+            Zg, Vg = gpu_quantize(Wd, UA, UBx, s, 4, True, dtype)
+            say("tie at origin", np.dtype(dtype).name, "B=I" if UBx is None else "two-sided")
+            assert Zg[0, 0] == 2 and Vg[0, 0] == 0.5
+            if dtype == np.float64:
+                assert np.array_equal(Zg, Zo)
+
+
 def test_deterministic_replay(spectral):
     c, Ad, UA, Bd, UB, s = spectral
     say("replay")
@@ -176,18 +226,44 @@ def test_deterministic_replay(spectral):
 
 # --------------------------------------------------------- other entry points
 
-@pytest.mark.parametrize("d", [1, 17, 64, 100, 256])
+def _check_prepare(A, label, tol64=1e-9, tol32=1e-5):
+    """kron_prepare against the oracle's damped factor (route (i): inverse, then
+    Cholesky), fp64 and fp32, plus U^T U A_d = I for the fp64 result."""
+    for dtype, tol in ((np.float64, tol64), (np.float32, tol32)):
+        Ar = A.astype(dtype)
+        U, tr, lam = pipeline.prepare(up(Ar, dtype), 0.01)
+        U = U.cpu().numpy().astype(np.float64)
+        Ad, Uo = dense.prepare(Ar.astype(np.float64), 0.01)
+        err = np.max(np.abs(U - Uo)) / np.max(np.abs(Uo))
+        say(label, np.dtype(dtype).name, f"max |U - U_oracle| / max |U_oracle| = {err:.2e}")
+        assert err <= tol, label
+        assert np.all(np.tril(U, -1) == 0)
+        assert abs(tr.item() - np.trace(Ar.astype(np.float64))) <= 1e-12 * abs(np.trace(A))
+        assert abs(lam.item() - 0.01 * np.trace(Ar.astype(np.float64)) / len(A)) <= 1e-12 * abs(lam.item())
+        if dtype == np.float64:
+            res = np.max(np.abs(U.T @ U @ Ad - np.eye(len(A))))
+            say(label, f"max |U^T U A_d - I| = {res:.2e}")
+            assert res <= 1e-6, label
+
+
+# d = 320, 1000: several four-block Cholesky panels (the cross-panel trailing
+# update) and the deeper levels of the recursive triangular inverse, with a
+# ragged last tile at 1000.
+@pytest.mark.parametrize("d", [1, 17, 64, 100, 256, 320, 1000])
 def test_prepare_matches_oracle(d):
     say("prepare", d)
     c = synth.spectral(d, d, config=2)
-    for dtype, tol in ((np.float64, 1e-9), (np.float32, 1e-5)):
-        A = c["A"].astype(dtype)
-        U, tr, lam = pipeline.prepare(up(A, dtype), 0.01)
-        U = U.cpu().numpy().astype(np.float64)
-        _, Uo = dense.prepare(A.astype(np.float64), 0.01)
-        assert np.max(np.abs(U - Uo)) <= tol * np.max(np.abs(Uo))
-        assert np.all(np.tril(U, -1) == 0)
-        assert abs(tr.item() - np.trace(A.astype(np.float64))) <= 1e-12 * abs(np.trace(A))
+    _check_prepare(c["A"], f"prepare spectral {d}")
+
+
+@pytest.mark.timeout(300)
+def test_prepare_matches_oracle_llm_4096():
+    # The workload's own factor: A = X^T X / 4096 from 4096 channel-scaled rows
+    # (lognormal channel scales), the 4096 x 4096 input factor of the 4096^2 layer.
+    say("prepare llm 4096")
+    X = synth.channel_scaled_rows(3003, 3004, 4096, 4096)
+    A = dense.factor_accumulate(X, alpha=1.0 / 4096)
+    _check_prepare(A, "prepare llm 4096")
 
 
 def test_prepare_detects_indefinite():

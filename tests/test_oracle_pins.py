@@ -355,6 +355,54 @@ def test_trajectory_check_accepts_near_tie_branch_and_rejects_wrong_code():
     assert viol >= 1
 
 
+def test_mismatch_roots_are_the_minimal_differences():
+    M = np.zeros((6, 7), bool)
+    M[1, 4] = M[3, 2] = True          # two roots: neither precedes the other
+    M[2, 5] = M[4, 4] = M[5, 6] = True  # inside the cones of the roots
+    M[0, 6] = True                     # a root far to the right
+    R = compare.mismatch_roots(M)
+    assert sorted(zip(*np.nonzero(R))) == [(0, 6), (1, 4), (3, 2)]
+    # brute force: a difference is a root iff no other difference is <= it componentwise
+    r = np.random.default_rng(3)
+    for _ in range(20):
+        M = r.random((9, 8)) < 0.08
+        want = np.zeros_like(M)
+        for i, j in zip(*np.nonzero(M)):
+            want[i, j] = not any(M[a, b] and (a, b) != (i, j) for a in range(i + 1) for b in range(j + 1))
+        assert np.array_equal(compare.mismatch_roots(M), want)
+
+
+def test_first_branch_of_a_forced_run_is_its_only_root():
+    # Forcing one code away from the oracle's changes only that entry's bottom-right cone.
+    c = synth.spectral(40, 30, config=2)
+    _, UA = dense.prepare(c["A"][:30, :30], 0.01)
+    _, UB = dense.prepare(c["B"][:40, :40], 0.01)
+    s = dense.scales(c["W"], 3, True)
+    Z = o3.solve(c["W"], UA, UB, s, 3)[0]
+    force = np.full(Z.shape, compare.NOT_FORCED, np.int32)
+    force[7, 9] = Z[7, 9] + (1 if Z[7, 9] < 3 else -1)
+    Zf = o3.solve(c["W"], UA, UB, s, 3, force=force)[0]
+    diff = Zf != Z
+    assert diff.sum() > 1 and not diff[:7, :].any() and not diff[:, :9].any()
+    assert sorted(zip(*np.nonzero(compare.mismatch_roots(diff)))) == [(7, 9)]
+
+
+def test_sensitivity_is_the_trace_of_the_kronecker_factor():
+    # KronQ page: the score of a sublayer is tr(H_X) tr(H_G).  For the printed
+    # 4x4 example H_X (x) H_G its trace is 8 + 10 + 12 + 15 = 45 = tr(H_X) tr(H_G).
+    g = read_golden("kronq_kron_example.txt")
+    P = g["PRINTED_KRON"]
+    assert dense.sensitivity(g["READING_H_X"], g["READING_H_G"]) == 45.0 == np.trace(P)
+    assert dense.sensitivity(np.diag([1.0, 2.0, 3.0]), np.diag([4.0, 5.0])) == 54.0
+    # the score uses the undamped factors; uniform relative damping delta would
+    # scale every score by (1 + delta)^2 and leave the ranking unchanged
+    r = np.random.default_rng(5)
+    A = r.standard_normal((6, 6)); A = A @ A.T
+    B = r.standard_normal((4, 4)); B = B @ B.T
+    sd = dense.sensitivity(dense.damp(A, 0.01), dense.damp(B, 0.01))
+    assert abs(sd - 1.01 ** 2 * dense.sensitivity(A, B)) <= 1e-12 * sd
+
+
 # ------------------------------------------------------------ mutation tests
 
 def test_pins_catch_planted_mistakes(tiny):

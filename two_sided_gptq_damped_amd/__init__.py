@@ -88,6 +88,22 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t, name: str, dtype: torch.dtype, device: torch.device, numel: int | None = None,
+            shape: tuple | None = None) -> None:
+    """Reject an argument whose element type, device or shape differs from what
+    the C entry point will read it as (the library sees only a raw pointer)."""
+    if t is None:
+        return
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected a tensor on {device}, got {t.device}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: expected at least {numel} elements, got {t.numel()}")
+
+
 def _ld(t: torch.Tensor) -> int:
     """Leading dimension of a row-major 2-D view (unit column stride required)."""
     if t.dim() != 2:
@@ -122,6 +138,7 @@ def workspace(op: int, dtype: torch.dtype, m: int, n: int, device="cuda") -> tor
 def kron_factor_accumulate(X: torch.Tensor, S: torch.Tensor, alpha: float, beta: float) -> torch.Tensor:
     """S <- beta S + alpha X^T X (X: rows x dim samples)."""
     rows, dim = X.shape
+    _expect(S, "S", X.dtype, X.device, shape=(dim, dim))
     _check(library().kron_factor_accumulate(_dtype_code(X), rows, dim, _ptr(X), _ld(X), _ptr(S), _ld(S),
                                             float(alpha), float(beta), _stream(X.device)))
     return S
@@ -132,6 +149,11 @@ def kron_prepare(A: torch.Tensor, damp_rel: float, U: torch.Tensor, ws: torch.Te
                  info: torch.Tensor | None = None) -> torch.Tensor:
     """U upper with U^T U = (A + damp_rel tr(A)/d I)^{-1}.  info=None waits and raises on failure."""
     d = A.shape[0]
+    _expect(U, "U", A.dtype, A.device, shape=(d, d))
+    _expect(ws, "ws", torch.uint8, A.device)
+    for t, name in ((trace_out, "trace_out"), (lambda_out, "lambda_out")):
+        _expect(t, name, torch.float64, A.device, 1)
+    _expect(info, "info", torch.int32, A.device, 1)
     _check(library().kron_prepare(_dtype_code(A), d, _ptr(A), _ld(A), float(damp_rel), _ptr(U), _ld(U),
                                   _ptr(trace_out), _ptr(lambda_out), _ptr(info), _ptr(ws), ws.numel(),
                                   _stream(A.device)))
@@ -140,6 +162,7 @@ def kron_prepare(A: torch.Tensor, damp_rel: float, U: torch.Tensor, ws: torch.Te
 
 def kron_row_scales(W: torch.Tensor, bits: int, per_row: bool, scales: torch.Tensor) -> torch.Tensor:
     m, n = W.shape
+    _expect(scales, "scales", W.dtype, W.device, m if per_row else 1)
     _check(library().kron_row_scales(_dtype_code(W), m, n, _ptr(W), _ld(W), int(bits), int(bool(per_row)),
                                      _ptr(scales), _stream(W.device)))
     return scales
@@ -151,8 +174,12 @@ def kron_quantize(W: torch.Tensor, U_A: torch.Tensor, U_B: torch.Tensor | None, 
     """Two-sided GPTQ of W (m x n); U_B None means B = I.  Writes codes (int8) and V,
     and, if given, loss[0] (fp64) = the proxy loss of V from the rounding errors."""
     m, n = W.shape
-    if loss is not None and (loss.dtype != torch.float64 or loss.numel() < 1):
-        raise ValueError("kron_quantize: loss must be a float64 tensor with at least one element")
+    for t, name, shp in ((U_A, "U_A", (n, n)), (U_B, "U_B", (m, m)), (V, "V", (m, n))):
+        _expect(t, name, W.dtype, W.device, shape=shp)
+    _expect(scales, "scales", W.dtype, W.device, m if per_row else 1)
+    _expect(codes, "codes", torch.int8, W.device, shape=(m, n))
+    _expect(ws, "ws", torch.uint8, W.device)
+    _expect(loss, "loss", torch.float64, W.device, 1)
     q = _Quantizer(int(bits), int(bool(per_row)), scales.data_ptr())
     ldb = _ld(U_B) if U_B is not None else 0
     _check(library().kron_quantize(_dtype_code(W), m, n, _ptr(W), _ld(W), _ptr(U_A), _ld(U_A), _ptr(U_B), ldb,
@@ -165,6 +192,10 @@ def kron_loss(W: torch.Tensor, V: torch.Tensor, A: torch.Tensor, B: torch.Tensor
               loss_out: torch.Tensor, ws: torch.Tensor) -> torch.Tensor:
     """loss_out[0] = tr(B_d (V - W) A_d (V - W)^T) in fp64; B None means B = I."""
     m, n = W.shape
+    for t, name, shp in ((V, "V", (m, n)), (A, "A", (n, n)), (B, "B", (m, m))):
+        _expect(t, name, W.dtype, W.device, shape=shp)
+    _expect(loss_out, "loss_out", torch.float64, W.device, 1)
+    _expect(ws, "ws", torch.uint8, W.device)
     ldb = _ld(B) if B is not None else 0
     _check(library().kron_loss(_dtype_code(W), m, n, _ptr(W), _ld(W), _ptr(V), _ld(V), _ptr(A), _ld(A), _ptr(B), ldb,
                                float(damp_rel), _ptr(loss_out), _ptr(ws), ws.numel(), _stream(W.device)))

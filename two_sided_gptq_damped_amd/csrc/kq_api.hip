@@ -54,6 +54,26 @@ static kq_status check_ws(void* ws, size_t have, size_t need, const char* op) {
     return KQ_OK;
 }
 
+// The host-checkable arguments of the quantize entry points (everything but the
+// scratch space).  KQ_OK with m == 0 or n == 0 means: nothing to do.
+kq_status quantize_checked_args(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* U_A,
+                                int64_t lda, const void* U_B, int64_t ldb, const kq_quantizer* q, int8_t* codes,
+                                int64_t ldc, void* V, int64_t ldv, double* loss_dev, const char* who) {
+    const std::string f(who);
+    if (!dtype_ok(dtype)) return invalid(f + ": dtype must be KQ_F32 or KQ_F64");
+    if (m < 0 || n < 0 || m > MAX_DIM || n > MAX_DIM) return invalid(f + ": m, n must be in [0, 65536]");
+    if (!q) return invalid(f + ": null quantizer");
+    if (q->bits < 2 || q->bits > 8) return invalid(f + ": bits must be in [2, 8]");
+    if (q->per_row != 0 && q->per_row != 1) return invalid(f + ": per_row must be 0 or 1");
+    if (m == 0 || n == 0) {
+        if (loss_dev) return invalid(f + ": no loss for an empty matrix");
+        return KQ_OK;
+    }
+    if (!W || !U_A || !codes || !V || !q->scales) return invalid(f + ": null pointer");
+    if (ldw < n || lda < n || ldc < n || ldv < n || (U_B && ldb < m)) return invalid(f + ": leading dimension too small");
+    return KQ_OK;
+}
+
 }  // namespace kq
 
 using namespace kq;
@@ -131,19 +151,10 @@ kq_status kron_quantize(kq_dtype dtype, int64_t m, int64_t n, const void* W, int
                         const void* U_B, int64_t ldb, const kq_quantizer* q, int8_t* codes, int64_t ldc, void* V,
                         int64_t ldv, double* loss_dev, void* ws, size_t ws_bytes, void* stream) {
     set_error("");
-    if (!dtype_ok(dtype)) return invalid("kron_quantize: dtype must be KQ_F32 or KQ_F64");
-    if (m < 0 || n < 0 || m > MAX_DIM || n > MAX_DIM) return invalid("kron_quantize: m, n must be in [0, 65536]");
-    if (!q) return invalid("kron_quantize: null quantizer");
-    if (q->bits < 2 || q->bits > 8) return invalid("kron_quantize: bits must be in [2, 8]");
-    if (q->per_row != 0 && q->per_row != 1) return invalid("kron_quantize: per_row must be 0 or 1");
-    if (m == 0 || n == 0) {
-        if (loss_dev) return invalid("kron_quantize: no loss for an empty matrix");
-        return KQ_OK;
-    }
-    if (!W || !U_A || !codes || !V || !q->scales) return invalid("kron_quantize: null pointer");
-    if (ldw < n || lda < n || ldc < n || ldv < n || (U_B && ldb < m))
-        return invalid("kron_quantize: leading dimension too small");
-    kq_status s = check_ws(ws, ws_bytes, quantize_workspace_bytes(dtype, m, n), "kron_quantize");
+    kq_status s = quantize_checked_args(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev,
+                                        "kron_quantize");
+    if (s != KQ_OK || m == 0 || n == 0) return s;
+    s = check_ws(ws, ws_bytes, quantize_workspace_bytes(dtype, m, n), "kron_quantize");
     if (s != KQ_OK) return s;
     return quantize_dispatch(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev, ws,
                              static_cast<hipStream_t>(stream));

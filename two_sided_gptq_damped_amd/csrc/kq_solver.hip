@@ -942,6 +942,10 @@ struct SolverRun {
 };
 
 template <typename T>
+kq_status onesided_solve(int m, int n, int mp, int np, int qmin, int qmax, const T* NA, T* X, T* D, const T* S,
+                         int8_t* Z, int64_t ldz, T* V, int64_t ldv, hipStream_t st);
+
+template <typename T>
 kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T* UA, int64_t lda, const T* UB,
                          int64_t ldb, const kq_quantizer* q, int8_t* codes, int64_t ldc, T* V, int64_t ldv,
                          double* loss_dev, void* ws, hipStream_t st) {
@@ -968,7 +972,10 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
     hipLaunchKernelGGL(init_solver_kernel<T>, rows(L.np, L.mp), dim3(threads), 0, st, W, ldw, int(m), int(n),
                        int(L.mp), int(L.np), static_cast<const T*>(q->scales), q->per_row, run.X, run.S);
     KQ_LAUNCHED("init_solver_kernel");
-    const kq_status s = run.solve(0, int(L.Mt + L.Nt - 1));
+    // B = I: one-sided GPTQ, rows independent, recursive over column ranges
+    const kq_status s = UB ? run.solve(0, int(L.Mt + L.Nt - 1))
+                           : onesided_solve<T>(int(m), int(n), int(L.mp), int(L.np), run.qmin, run.qmax, run.NA,
+                                               run.X, run.D, run.S, codes, ldc, V, ldv, st);
     if (s != KQ_OK || !loss_dev) return s;
     double* ra = reinterpret_cast<double*>(base + L.off_L);
     double* rb = ra + L.np;
