@@ -14,7 +14,8 @@
  *    number of columns).  W, V are m x n; A, U_A are n x n; B, U_B are m x m.
  *  - Every data pointer is DEVICE memory owned by the caller.  The library never
  *    allocates or frees device memory; scratch space comes from the caller's
- *    workspace (size from kron_workspace_bytes, alignment 256 bytes).
+ *    workspace (size from kron_workspace_bytes, alignment 256 bytes), except for
+ *    kron_quantize_noalloc, whose scratch is a fixed array in the library.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
  *    work is enqueued asynchronously on it; the only host synchronisation is
  *    kron_prepare with info_dev == NULL.
@@ -23,7 +24,8 @@
  *    returns KQ_ERR_HIP; kron_last_error() then holds the HIP message.
  *  - Floating-point type of every real array is `dtype` (fp32 or fp64).  The
  *    factor preparation always computes in fp64.
- *  - Calls are re-entrant; the only library state is a thread-local error string.
+ *  - Calls are re-entrant; the only library state is a thread-local error string
+ *    (and the per-GPU scratch array of kron_quantize_noalloc).
  */
 #ifndef KRONQ_H
 #define KRONQ_H
@@ -171,6 +173,27 @@ kq_status kron_loss(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t
                     const void* V, int64_t ldv, const void* A, int64_t lda, const void* B,
                     int64_t ldb, double damp_rel, double* loss_dev, void* ws, size_t ws_bytes,
                     void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc): kron_quantize
+ * with the same arguments and results but no workspace argument.  Its scratch
+ * space is a fixed array of KQ_NOALLOC_SCRATCH_BYTES in the library's device
+ * memory, one per GPU, held from the library's first use on that GPU until the
+ * process ends; the call itself allocates nothing.  The array is found on the
+ * device that is current at the call, which must be the device of `stream`.
+ *   - Sizes whose scratch need (kron_workspace_bytes(KQ_OP_QUANTIZE, dtype, m,
+ *     n)) exceeds KQ_NOALLOC_SCRATCH_BYTES return KQ_ERR_WORKSPACE before
+ *     anything is enqueued: e.g. fp32 up to 1792 x 1792 two-sided fits.
+ *   - Every call on one GPU uses that GPU's single array: calls that overlap on
+ *     one GPU (other streams, other threads) race and give undefined results.
+ *     Calls ordered on one stream are safe.
+ */
+#define KQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+kq_status kron_quantize_noalloc(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw,
+                                const void* U_A, int64_t lda, const void* U_B, int64_t ldb,
+                                const kq_quantizer* q, int8_t* codes, int64_t ldc, void* V, int64_t ldv,
+                                double* loss_dev, void* stream);
 
 /* Short static description of a status code. */
 const char* kron_status_string(kq_status status);

@@ -155,3 +155,19 @@ def test_binding_rejects_mismatched_arguments():
     with pytest.raises(ValueError):
         kq.kron_factor_accumulate(W, torch.zeros(n, n, dtype=torch.float64), 1.0, 0.0)
 
+
+def test_noalloc_rejects_before_any_device_call():
+    lib = kq.library()
+    # too large for the fixed scratch array: KQ_ERR_WORKSPACE, nothing enqueued
+    need = lib.kron_workspace_bytes(kq.KQ_OP_QUANTIZE, kq.KQ_F32, 4096, 4096)
+    assert need > kq.NOALLOC_SCRATCH_BYTES
+    assert lib.kron_quantize_noalloc(kq.KQ_F32, 4096, 4096, FAKE, 4096, FAKE, 4096, FAKE, 4096, q(), FAKE, 4096,
+                                     FAKE, 4096, None, None) == 3
+    assert b"scratch" in lib.kron_last_error()
+    # the argument checks of kron_quantize
+    assert lib.kron_quantize_noalloc(kq.KQ_F32, 64, 64, None, 64, FAKE, 64, FAKE, 64, q(), FAKE, 64,
+                                     FAKE, 64, None, None) == 1
+    assert lib.kron_quantize_noalloc(kq.KQ_F32, 64, 64, FAKE, 64, FAKE, 64, FAKE, 64, q(bits=9), FAKE, 64,
+                                     FAKE, 64, None, None) == 1
+    assert lib.kron_quantize_noalloc(kq.KQ_F32, 0, 64, None, 64, None, 64, None, 0, q(), None, 64,
+                                     None, 64, None, None) == 0

@@ -24,7 +24,9 @@ KQ_OP_FACTOR, KQ_OP_PREPARE, KQ_OP_QUANTIZE, KQ_OP_LOSS = 0, 1, 2, 3
 STATUS = {0: "KQ_OK", 1: "KQ_ERR_INVALID_ARG", 2: "KQ_ERR_NOT_PD", 3: "KQ_ERR_WORKSPACE",
           4: "KQ_ERR_HIP", 5: "KQ_ERR_UNSUPPORTED"}
 EXPORTED = ("kron_workspace_bytes", "kron_factor_accumulate", "kron_prepare", "kron_row_scales",
-            "kron_quantize", "kron_loss", "kron_status_string", "kron_last_error", "kron_abi_version")
+            "kron_quantize", "kron_loss", "kron_status_string", "kron_last_error", "kron_abi_version",
+            "kron_quantize_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KQ_NOALLOC_SCRATCH_BYTES
 
 
 class KronError(RuntimeError):
@@ -62,6 +64,9 @@ def library() -> ctypes.CDLL:
     lib.kron_quantize.restype = ctypes.c_int
     lib.kron_quantize.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64,
                                   ctypes.POINTER(_Quantizer), vp, i64, vp, i64, vp, vp, sz, vp]
+    lib.kron_quantize_noalloc.restype = ctypes.c_int
+    lib.kron_quantize_noalloc.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64,
+                                          ctypes.POINTER(_Quantizer), vp, i64, vp, i64, vp, vp]
     lib.kron_loss.restype = ctypes.c_int
     lib.kron_loss.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, dbl, vp, vp, sz, vp]
     lib.kron_status_string.restype = ctypes.c_char_p
@@ -185,6 +190,27 @@ def kron_quantize(W: torch.Tensor, U_A: torch.Tensor, U_B: torch.Tensor | None, 
     _check(library().kron_quantize(_dtype_code(W), m, n, _ptr(W), _ld(W), _ptr(U_A), _ld(U_A), _ptr(U_B), ldb,
                                    ctypes.byref(q), _ptr(codes), _ld(codes), _ptr(V), _ld(V), _ptr(loss), _ptr(ws),
                                    ws.numel(), _stream(W.device)))
+    return codes, V
+
+
+def kron_quantize_noalloc(W: torch.Tensor, U_A: torch.Tensor, U_B: torch.Tensor | None, bits: int, per_row: bool,
+                          scales: torch.Tensor, codes: torch.Tensor, V: torch.Tensor,
+                          loss: torch.Tensor | None = None):
+    """kron_quantize without a workspace: the library's fixed per-GPU scratch
+    array is used instead (nothing is allocated; sizes that need more than
+    NOALLOC_SCRATCH_BYTES raise KronError with KQ_ERR_WORKSPACE)."""
+    m, n = W.shape
+    for t, name, shp in ((U_A, "U_A", (n, n)), (U_B, "U_B", (m, m)), (V, "V", (m, n))):
+        _expect(t, name, W.dtype, W.device, shape=shp)
+    _expect(scales, "scales", W.dtype, W.device, m if per_row else 1)
+    _expect(codes, "codes", torch.int8, W.device, shape=(m, n))
+    _expect(loss, "loss", torch.float64, W.device, 1)
+    q = _Quantizer(int(bits), int(bool(per_row)), scales.data_ptr())
+    ldb = _ld(U_B) if U_B is not None else 0
+    with torch.cuda.device(W.device):
+        _check(library().kron_quantize_noalloc(_dtype_code(W), m, n, _ptr(W), _ld(W), _ptr(U_A), _ld(U_A), _ptr(U_B),
+                                               ldb, ctypes.byref(q), _ptr(codes), _ld(codes), _ptr(V), _ld(V),
+                                               _ptr(loss), _stream(W.device)))
     return codes, V
 
 
