@@ -23,7 +23,11 @@ checked in four ways:
       - loss within 1e-3 relative of the unforced fp64 oracle, or, where the
         oracle's own fp32 loop is farther than that from its fp64 loop on the
         same block (single-precision branches at near ties carry the loss with
-        them), within FLOOR_FACTOR times that distance;
+        them), within FLOOR_FACTOR times that distance; where neither holds (a
+        block so strongly coupled that one branch at a near tie moves the loss
+        by more than that), within the number of the GPU's near-tie branches
+        times the largest loss change that one such branch causes, measured by
+        flipping the oracle's three nearest ties one at a time;
       - trajectory: the oracle is re-run with every GPU code imposed, and each
         GPU code must be clamp(rne(y)) of the exact pre-rounding value y that
         the earlier codes imply, except within 1e-4 grid units of a boundary;
@@ -175,8 +179,30 @@ def check_fp32_block(g, bits, k1, k2, label):
                f"loss_gpu={lg:.6e} loss_oracle={lo:.6e} rel={rel:.3e} (oracle fp32 floor {rel_floor:.3e})")
     assert viol == 0, label
     assert far_roots == 0, label
-    assert rel <= 1e-3 or rel <= FLOOR_FACTOR * rel_floor, label
+    if rel > 1e-3 and rel > FLOOR_FACTOR * rel_floor:
+        # A strongly coupled block (the rank-deficient output factor of the gate
+        # shape): one legitimate branch at a near tie moves the loss by far more
+        # than 1e-3 there.  Measure how far one branch moves it, by flipping the
+        # oracle's nearest ties one at a time, and allow that much per branch the
+        # GPU took.
+        sens = flip_sensitivity(W, UA, UB, s, bits, Zo, Yo, lo, loss, La, Lb)
+        say(label, f"loss change of one near-tie branch (largest of 3): {sens:.3e}; GPU branches {near}")
+        assert near > 0 and rel <= near * sens, label
     assert mis <= 1e-3 or (int(roots.sum()) > 0 and mis <= FLOOR_FACTOR * floor), label
+
+
+def flip_sensitivity(W, UA, UB, s, bits, Zo, Yo, lo, loss, La, Lb, k=3):
+    """Largest relative loss change over k oracle runs, each taking the other
+    rounding at one of the k entries nearest to a tie (fp64)."""
+    td = compare.tie_distance(Yo)
+    worst = 0.0
+    for idx in np.argsort(td, axis=None)[:k]:
+        i, j = np.unravel_index(idx, Yo.shape)
+        force = np.full(Zo.shape, compare.NOT_FORCED, np.int32)
+        force[i, j] = Zo[i, j] + (1 if Yo[i, j] > Zo[i, j] else -1)
+        Vf = o3.solve(W, UA, UB, s, bits, force=force, La=La, Lb=Lb)[1]
+        worst = max(worst, compare.rel_diff(loss(Vf), lo))
+    return worst
 
 
 def check_fp32_rows(g, bits, rows, label):
