@@ -78,8 +78,12 @@ def normalized_factor(U: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 
-def grid(bits: int) -> tuple[int, int]:
-    """Symmetric b-bit integer grid [-2^(b-1), 2^(b-1)-1]."""
+def grid(bits):
+    """Symmetric b-bit integer grid [-2^(b-1), 2^(b-1)-1]; bits=None is the
+    unbounded integer alphabet of the WaterKron page (section 2.1: the integers
+    are not clipped), returned as infinite bounds."""
+    if bits is None:
+        return -np.inf, np.inf
     return -(1 << (bits - 1)), (1 << (bits - 1)) - 1
 
 
@@ -99,6 +103,37 @@ def scales(W: np.ndarray, bits: int, per_row: bool) -> np.ndarray:
 def row_scales(s: np.ndarray, m: int) -> np.ndarray:
     s = np.asarray(s, dtype=np.float64).reshape(-1)
     return np.full(m, s[0]) if s.size == 1 else s.copy()
+
+
+def entry_scale(s_row, alpha, i: int, j: int) -> float:
+    """The grid step of entry (i, j): the row scale, times the column scale
+    alpha_j when column scales are given (WaterKron page section 2.1: entry
+    (i, j) of V is beta_i alpha_j Z_ij; beta plays the role of the row scale)."""
+    return s_row[i] if alpha is None else s_row[i] * alpha[j]
+
+
+def waterkron_scales(UA, UB, step: float, m: int | None = None):
+    """WaterKron two-sided rate allocation (WaterKron page, section 3; section
+    2.4 for the one-sided WaterSIC rule): alpha_j proportional to
+    1 / L^(A)_jj and beta_i proportional to 1 / L^(B)_ii, with L the reverse
+    Cholesky factor of the damped factor.  Since U = RevCholesky(A_d)^{-T} is
+    upper triangular, 1 / L_jj = U_jj, so alpha = step * diag(U_A) and beta =
+    diag(U_B) (all ones when B = I, which is WaterSIC).  ``step`` is the free
+    proportionality constant: the grid step in the transformed geometry.
+    Returns (alpha, beta) in fp64."""
+    alpha = step * np.diag(np.asarray(UA, dtype=np.float64))
+    if UB is None:
+        return alpha, np.ones(int(m))
+    return alpha, np.diag(np.asarray(UB, dtype=np.float64)).copy()
+
+
+def empirical_entropy(Z) -> float:
+    """Bits per entry of the empirical distribution of the integer codes:
+    -sum_k p_k log2 p_k over the distinct values (the storage cost an entropy
+    coder approaches, WaterKron page sections 1 and 2.1)."""
+    _, counts = np.unique(np.asarray(Z).reshape(-1), return_counts=True)
+    p = counts / counts.sum()
+    return float(-np.sum(p * np.log2(p)))
 
 
 def quantize(x: float, s: float, qmin: int, qmax: int) -> tuple[float, float, float]:
@@ -121,7 +156,7 @@ def quantize(x: float, s: float, qmin: int, qmax: int) -> tuple[float, float, fl
 # ----------------------------------------------------------------------------
 
 
-def vectorized_kron_gptq(W, Ad, Bd, s, bits, return_factor=False):
+def vectorized_kron_gptq(W, Ad, Bd, s, bits, return_factor=False, alpha=None):
     """Standard GPTQ on w^ = vecop(W)^T with Hessian A_d (x) B_d.
 
     FastKron page, section 2.2: the two-sided extension is Algorithm 1 applied
@@ -129,7 +164,9 @@ def vectorized_kron_gptq(W, Ad, Bd, s, bits, return_factor=False):
     (Frantar et al.): for p in order, q = quantize(w_p); err = (w_p - q)/U^_pp;
     w_{p+1:} -= err * U^_{p, p+1:}, with U^ the upper Cholesky factor of the
     inverse Hessian.  Equivalently Babai's nearest plane (BaKron / GPTQ-2D
-    abstracts).
+    abstracts).  With column scales ``alpha`` the step of vecop entry p = i + m j
+    is s_i alpha_j (WaterKron page section 3: the scale vector of the
+    vectorised problem is alpha (x) beta); bits=None leaves the codes unclipped.
     """
     W = np.asarray(W, dtype=np.float64)
     m, n = W.shape
@@ -142,7 +179,7 @@ def vectorized_kron_gptq(W, Ad, Bd, s, bits, return_factor=False):
     v = np.zeros(m * n)
     y = np.zeros(m * n)
     for p in range(m * n):
-        z[p], v[p], y[p] = quantize(w[p], s_row[p % m], qmin, qmax)
+        z[p], v[p], y[p] = quantize(w[p], entry_scale(s_row, alpha, p % m, p // m), qmin, qmax)
         err = (w[p] - v[p]) / Uh[p, p]
         w[p + 1:] -= err * Uh[p, p + 1:]
     out = (z.reshape((m, n), order="F"), v.reshape((m, n), order="F"),
@@ -172,7 +209,7 @@ def entry_order(m: int, n: int, order: str):
     raise ValueError(order)
 
 
-def two_sided_naive(W, UA, UB, s, bits, order="column"):
+def two_sided_naive(W, UA, UB, s, bits, order="column", alpha=None):
     """FastKron-naive written in matrix space (FastKron page, sections 2.2-2.4).
 
     X := W; for each entry (i, j) in a valid order: quantize x = X[i, j], set
@@ -181,6 +218,9 @@ def two_sided_naive(W, UA, UB, s, bits, order="column"):
     W <- W + L_{:,i}^(B) Delta (L_{:,j}^(A))^T of section 2.4).  Only entries to the
     bottom-right change (section 2.3), so any order that visits (i', j') after
     every (i, j) <= (i', j') gives the same result.
+
+    With column scales ``alpha`` entry (i, j) uses the step s_i alpha_j; with
+    bits=None the codes are not clipped (the WaterKron alphabet).
 
     Returns (Z, V, Y, D): codes, dequantised values, pre-rounding value in grid
     units x/s, and the errors Delta.
@@ -194,7 +234,7 @@ def two_sided_naive(W, UA, UB, s, bits, order="column"):
     Z = np.zeros((m, n)); V = np.zeros((m, n)); Y = np.zeros((m, n)); D = np.zeros((m, n))
     for i, j in entry_order(m, n, order):
         x = X[i, j]
-        Z[i, j], V[i, j], Y[i, j] = quantize(x, s_row[i], qmin, qmax)
+        Z[i, j], V[i, j], Y[i, j] = quantize(x, entry_scale(s_row, alpha, i, j), qmin, qmax)
         D[i, j] = V[i, j] - x
         X[i:, j:] += D[i, j] * np.outer(NB[i, i:], NA[j, j:])
     return Z, V, Y, D
@@ -273,12 +313,14 @@ def two_sided_recursive_vecop(W, UA, UB, s, bits):
     return Z, V, Y, D
 
 
-def one_sided_gptq(W, UA, s, bits):
+def one_sided_gptq(W, UA, s, bits, alpha=None):
     """Standard one-sided GPTQ (Frantar et al.), Hessian A (x) I_m.
 
     Columns in order: q = quantize(W[:, j]) row-wise, err = (W[:, j] - q) / U[j, j],
     W[:, j+1:] -= err U[j, j+1:] (FastKron page section 2.2, Algorithm 1's
-    recurrence; U the upper Cholesky factor of A^{-1}).
+    recurrence; U the upper Cholesky factor of A^{-1}).  Column scales ``alpha``
+    give entry (i, j) the step s_i alpha_j (WaterSIC, WaterKron page section 2.4,
+    when alpha_j is proportional to U[j, j]); bits=None does not clip.
     """
     Wc = np.asarray(W, dtype=np.float64).copy()
     m, n = Wc.shape
@@ -287,7 +329,7 @@ def one_sided_gptq(W, UA, s, bits):
     Z = np.zeros((m, n)); V = np.zeros((m, n))
     for j in range(n):
         for i in range(m):
-            Z[i, j], V[i, j], _ = quantize(Wc[i, j], s_row[i], qmin, qmax)
+            Z[i, j], V[i, j], _ = quantize(Wc[i, j], entry_scale(s_row, alpha, i, j), qmin, qmax)
         err = (Wc[:, j] - V[:, j]) / UA[j, j]
         Wc[:, j + 1:] -= np.outer(err, UA[j, j + 1:])
     return Z, V

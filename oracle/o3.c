@@ -20,6 +20,11 @@
  * all earlier entries gives exactly the two sums above, so this loop performs
  * m n (m + n - 2) / 2 multiply-adds in total.
  *
+ * Grid step of entry (i, j): s_row[i], or s_row[i] * s_col[j] when column
+ * scales are given (the per-entry steps beta_i alpha_j of the WaterKron page,
+ * section 2.1).  Codes are clipped to [qmin, qmax] when `bounded` is nonzero;
+ * otherwise they are unbounded integers (WaterKron page section 2.1).
+ *
  * Build: compiled twice, with -DREAL=double (o3_f64) and -DREAL=float (o3_f32,
  * the fp32-arithmetic variant used to measure the oracle's own fp32 floor).
  */
@@ -34,27 +39,30 @@
 
 #define NOT_FORCED INT32_MIN
 
-static void quantize(REAL x, REAL s, int qmin, int qmax, REAL* z, REAL* v, double* y) {
+static void quantize(REAL x, REAL s, int bounded, int qmin, int qmax, REAL* z, REAL* v, double* y) {
     if (s == (REAL)0) { *z = 0; *v = 0; *y = 0.0; return; }
     REAL t = x / s;                 /* IEEE division, no reciprocal */
     REAL r = rint(t);               /* default rounding mode: half to even */
-    if (r < (REAL)qmin) r = (REAL)qmin;
-    if (r > (REAL)qmax) r = (REAL)qmax;
+    if (bounded) {
+        if (r < (REAL)qmin) r = (REAL)qmin;
+        if (r > (REAL)qmax) r = (REAL)qmax;
+    }
     *z = r; *v = s * r; *y = (double)t;
 }
 
 /*
  * m x n problem, all matrices row-major and contiguous.
- *   W[m*n], Lb[m*m] (NULL means B = I), La[n*n], s_row[m]
+ *   W[m*n], Lb[m*m] (NULL means B = I), La[n*n], s_row[m], s_col[n] (NULL: none)
  *   force[m*n] (NULL, or NOT_FORCED except where the code is imposed)
- * Outputs: Z[m*n] codes, V[m*n], Y[m*n] pre-rounding value in grid units,
+ * Outputs: Z[m*n] codes (int32), V[m*n], Y[m*n] pre-rounding value in grid units,
  *          D[m*n] errors.  Returns 0, or -1 if the scratch row buffer cannot
  *          be allocated.
  */
 int o3_solve(int64_t m, int64_t n, const REAL* W, const REAL* Lb, const REAL* La,
-             const REAL* s_row, int bits, const int32_t* force, int8_t* Z, REAL* V,
-             double* Y, REAL* D, int threads) {
-    const int qmin = -(1 << (bits - 1)), qmax = (1 << (bits - 1)) - 1;
+             const REAL* s_row, const REAL* s_col, int bits, const int32_t* force, int32_t* Z,
+             REAL* V, double* Y, REAL* D, int threads) {
+    const int bounded = bits > 0;
+    const int qmin = bounded ? -(1 << (bits - 1)) : 0, qmax = bounded ? (1 << (bits - 1)) - 1 : 0;
     /* R stored transposed, Rt[j][i], so the column sum reads contiguously. */
     REAL* Rt = (REAL*)malloc(sizeof(REAL) * (size_t)m * (size_t)n);
     if (!Rt) return -1;
@@ -78,9 +86,10 @@ int o3_solve(int64_t m, int64_t n, const REAL* W, const REAL* Lb, const REAL* La
             for (int64_t b = 0; b < j; ++b) row += d[b] * la[b];
             const REAL x = W[i * n + j] + col + row;
             REAL z, v; double y;
-            quantize(x, s_row[i], qmin, qmax, &z, &v, &y);
-            if (force && force[i * n + j] != NOT_FORCED) { z = (REAL)force[i * n + j]; v = s_row[i] * z; }
-            Z[i * n + j] = (int8_t)z;
+            const REAL sij = s_col ? s_row[i] * s_col[j] : s_row[i];
+            quantize(x, sij, bounded, qmin, qmax, &z, &v, &y);
+            if (force && force[i * n + j] != NOT_FORCED) { z = (REAL)force[i * n + j]; v = sij * z; }
+            Z[i * n + j] = (int32_t)z;
             V[i * n + j] = v;
             Y[i * n + j] = y;
             D[i * n + j] = v - x;

@@ -44,7 +44,7 @@ def _load(tag: str):
         lib = ctypes.CDLL(path)
         fn = lib.o3_solve
         fn.restype = ctypes.c_int
-        fn.argtypes = [ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 4 + \
+        fn.argtypes = [ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 5 + \
             [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
              ctypes.c_void_p, ctypes.c_int]
         _LIBS[tag] = fn
@@ -61,13 +61,16 @@ def lower_normalized(U: np.ndarray, dtype) -> np.ndarray:
     return np.ascontiguousarray((U / np.diag(U)[:, None]).T)
 
 
-def solve(W, UA, UB, s, bits, dtype=np.float64, force=None, threads=0, La=None, Lb=None):
+def solve(W, UA, UB, s, bits, dtype=np.float64, force=None, threads=0, La=None, Lb=None, alpha=None):
     """Left-looking two-sided GPTQ.  UB=None means B = I (one-sided GPTQ).
 
-    ``s`` has length m (per row) or 1 (per tensor).  ``force`` is an optional m x n
-    int32 array of imposed codes (NOT_FORCED elsewhere).  Precomputed La / Lb (as
+    ``s`` has length m (per row) or 1 (per tensor).  ``alpha`` (length n) adds
+    column scales: entry (i, j) then has the step s_i alpha_j (WaterKron).
+    bits=None leaves the codes unbounded.  ``force`` is an optional m x n int32
+    array of imposed codes (NOT_FORCED elsewhere).  Precomputed La / Lb (as
     returned by ``lower_normalized``) may be passed to skip re-normalising.
-    Returns (Z int8, V, Y fp64 pre-rounding value x/s, D errors).
+    Returns (Z, V, Y fp64 pre-rounding value x/s, D errors); Z is int8 for a
+    b-bit grid and int32 when unbounded.
     """
     dtype = np.dtype(dtype)
     tag = "f64" if dtype == np.float64 else "f32"
@@ -79,15 +82,18 @@ def solve(W, UA, UB, s, bits, dtype=np.float64, force=None, threads=0, La=None, 
         Lb = lower_normalized(UB, dtype)
     s = np.asarray(s, dtype=np.float64).reshape(-1)
     s_row = np.ascontiguousarray((np.full(m, s[0]) if s.size == 1 else s).astype(dtype))
+    s_col = None if alpha is None else np.ascontiguousarray(np.asarray(alpha, dtype=np.float64).astype(dtype))
+    if s_col is not None:
+        assert s_col.shape == (n,)
     if force is not None:
         force = np.ascontiguousarray(force, dtype=np.int32)
         assert force.shape == (m, n)
-    Z = np.zeros((m, n), np.int8)
+    Z = np.zeros((m, n), np.int32)
     V = np.zeros((m, n), dtype)
     Y = np.zeros((m, n), np.float64)
     D = np.zeros((m, n), dtype)
-    rc = _load(tag)(m, n, _ptr(W), _ptr(Lb), _ptr(La), _ptr(s_row), int(bits), _ptr(force),
-                    _ptr(Z), _ptr(V), _ptr(Y), _ptr(D), int(threads))
+    rc = _load(tag)(m, n, _ptr(W), _ptr(Lb), _ptr(La), _ptr(s_row), _ptr(s_col), 0 if bits is None else int(bits),
+                    _ptr(force), _ptr(Z), _ptr(V), _ptr(Y), _ptr(D), int(threads))
     if rc != 0:
         raise MemoryError("o3_solve could not allocate its scratch buffer")
-    return Z, V, Y, D
+    return (Z if bits is None else Z.astype(np.int8)), V, Y, D

@@ -421,3 +421,84 @@ def test_pins_catch_planted_mistakes(tiny):
     # Kronecker order swapped in the literal tier
     Zk, _, _ = dense.vectorized_kron_gptq(c["W"].T.copy(), Ad, Bd, s, 4)
     assert not np.array_equal(Zk.T, Z1)
+
+
+# ------------------------------------------------ WaterKron rate allocation
+
+def test_waterkron_scales_are_reverse_cholesky_reciprocals():
+    # WaterKron page section 3: alpha_j proportional to 1 / L_jj with L the reverse
+    # Cholesky factor (L^T L = A).  By hand for A = [[10, 2], [2, 4]]: L = [[3, 0],
+    # [1, 2]], so alpha = step * (1/3, 1/2); B = I gives beta = 1 (WaterSIC).
+    A = np.array([[10.0, 2.0], [2.0, 4.0]])
+    L = np.array([[3.0, 0.0], [1.0, 2.0]])
+    assert np.allclose(L.T @ L, A)
+    UA = dense.upper_factor_via_reverse_cholesky(A)
+    alpha, beta = dense.waterkron_scales(UA, None, 0.5, m=3)
+    assert np.allclose(alpha, [0.5 / 3, 0.25], rtol=1e-14) and np.array_equal(beta, np.ones(3))
+    B = np.array([[4.0, 0.0], [0.0, 9.0]])
+    _, beta = dense.waterkron_scales(UA, dense.upper_factor_via_inverse(B), 1.0)
+    assert np.allclose(beta, [0.5, 1.0 / 3.0], rtol=1e-14)
+
+
+def test_empirical_entropy_definition():
+    assert dense.empirical_entropy([0, 0, 1, 1]) == 1.0
+    assert dense.empirical_entropy(np.arange(8)) == 3.0
+    assert dense.empirical_entropy(np.full((4, 4), 7)) == 0.0
+    assert abs(dense.empirical_entropy([0, 0, 0, 1]) - (2 - 0.75 * np.log2(3))) < 1e-15
+
+
+@pytest.fixture(scope="module")
+def waterkron_tiny(tiny):
+    c, Ad, UA, Bd, UB, s = tiny
+    step = 0.05
+    alpha, beta = dense.waterkron_scales(UA, UB, step)
+    return c, Ad, UA, Bd, UB, alpha, beta
+
+
+def test_waterkron_tiers_agree(waterkron_tiny):
+    # Per-entry steps beta_i alpha_j and unbounded codes: the literal Kronecker
+    # GPTQ (with the vectorised scale alpha (x) beta), the matrix loop in two
+    # orders and the left-looking loop give the same codes.
+    c, Ad, UA, Bd, UB, alpha, beta = waterkron_tiny
+    Z1, V1, Y1 = dense.vectorized_kron_gptq(c["W"], Ad, Bd, beta, None, alpha=alpha)
+    assert compare.tie_distance(Y1).min() > 1e-9
+    Z2c, _, _, _ = dense.two_sided_naive(c["W"], UA, UB, beta, None, "column", alpha=alpha)
+    Z2a, _, _, _ = dense.two_sided_naive(c["W"], UA, UB, beta, None, "antidiagonal", alpha=alpha)
+    Z3, V3, _, D3 = o3.solve(c["W"], UA, UB, beta, None, alpha=alpha)
+    assert Z3.dtype == np.int32
+    for Z in (Z2c, Z2a, Z3):
+        assert np.array_equal(Z, Z1)
+    assert np.max(np.abs(Z1)) > 8  # beyond a 4-bit grid: the codes are not clipped
+    assert np.allclose(V3, V1, rtol=0, atol=1e-12)
+    l1 = dense.proxy_loss(c["W"], V1, Ad, Bd)
+    assert abs(l1 - dense.loss_from_errors(D3, UA, UB)) <= 1e-11 * l1
+
+
+def test_watersic_is_one_sided_gptq_with_column_scales():
+    c = synth.spectral(48, 40, config=2)
+    _, UA = dense.prepare(c["A"][:40, :40], 0.01)
+    alpha, beta = dense.waterkron_scales(UA, None, 0.02, m=48)
+    Zr, Vr = dense.one_sided_gptq(c["W"], UA, beta, None, alpha=alpha)
+    Z3, V3, Y3, _ = o3.solve(c["W"], UA, None, beta, None, alpha=alpha)
+    assert compare.tie_distance(Y3).min() > 1e-9
+    assert np.array_equal(Z3, Zr) and np.allclose(V3, Vr, rtol=0, atol=1e-12)
+
+
+def test_waterkron_high_rate_distortion_is_uniform():
+    # With alpha_j beta_i = step U_A,jj U_B,ii every rounding error, measured in
+    # the loss geometry (Delta_ij / (U_B,ii U_A,jj)), is step times a value in
+    # [-1/2, 1/2]; at a fine step these are uniform, so the proxy loss is
+    # m n step^2 / 12 (the high-rate regime of the WaterKron page, appendix C.2).
+    c = synth.spectral(64, 64, config=2)
+    Ad, UA = dense.prepare(c["A"], 0.01)
+    Bd, UB = dense.prepare(c["B"], 0.01)
+    # a step a thousandth of the weights' spread in the transformed geometry
+    step = 1e-3 * np.sqrt(np.mean((c["W"] / np.outer(np.diag(UB), np.diag(UA))) ** 2))
+    alpha, beta = dense.waterkron_scales(UA, UB, step)
+    Z, V, _, D = o3.solve(c["W"], UA, UB, beta, None, alpha=alpha)
+    S = np.outer(beta, alpha)
+    assert np.max(np.abs(D / S)) <= 0.5 + 1e-9
+    assert np.max(np.abs(Z)) > 127  # far beyond an 8-bit grid
+    loss = dense.proxy_loss(c["W"], V, Ad, Bd)
+    ratio = loss / (64 * 64 * step ** 2 / 12)
+    assert abs(ratio - 1.0) < 0.05, ratio
