@@ -158,6 +158,42 @@ kq_status kron_quantize(kq_dtype dtype, int64_t m, int64_t n, const void* W, int
                         double* loss_dev, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * WaterKron two-sided rate allocation (WaterKron page, section 3; section 2.4
+ * for WaterSIC, its B = I case): the column scales alpha_j proportional to
+ * 1 / L^(A)_jj and row scales beta_i proportional to 1 / L^(B)_ii, L the reverse
+ * Cholesky factor of the damped factor.  With U from kron_prepare,
+ * U = RevCholesky(A_d)^{-T}, so 1 / L_jj = U_jj:
+ *   alpha_j = step * U_A[j][j]   (the product formed in fp64, rounded once)
+ *   beta_i  = U_B[i][i]          (1 when U_B is NULL, B = I)
+ * `step` (> 0) is the free proportionality constant: the grid step in the
+ * geometry where every entry's rounding error weighs the same in the loss.
+ *   alpha  device array of n entries of dtype (output)
+ *   beta   device array of m entries of dtype (output)
+ */
+kq_status kron_waterkron_scales(kq_dtype dtype, int64_t m, int64_t n, const void* U_A, int64_t lda,
+                                const void* U_B, int64_t ldb, double step, void* alpha, void* beta,
+                                void* stream);
+
+/*
+ * Two-sided GPTQ with the WaterKron alphabet (WaterKron page, section 2.1):
+ * entry (i, j) of V is beta_i alpha_j Z_ij with Z an unbounded integer matrix
+ * (meant for entropy coding).  The solver is kron_quantize's, with the grid
+ * step of entry (i, j) s_ij = beta_i * alpha_j (one rounding in dtype) and
+ * z_ij = rne(x_ij / s_ij) without clipping (codes are held as int32 and clamped
+ * only at +-2^30).  U_B = NULL is WaterSIC (one-sided, column scales only when
+ * beta = 1).
+ *   alpha  n column scales (> 0), beta  m row scales (> 0), device, dtype
+ *   codes  m x n int32 output, ldc >= n
+ *   V      m x n output, V_ij = (beta_i alpha_j) codes_ij
+ *   loss_dev, ws  as for kron_quantize (same workspace size)
+ */
+kq_status kron_quantize_waterkron(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw,
+                                  const void* U_A, int64_t lda, const void* U_B, int64_t ldb,
+                                  const void* alpha, const void* beta, int32_t* codes, int64_t ldc,
+                                  void* V, int64_t ldv, double* loss_dev, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/*
  * Proxy loss D_{A,B} = tr(B_d (V - W) A_d (V - W)^T) (WaterKron page section 1,
  * item 1; FastKron page section 2.2) with E = V - W, A_d = A + damp_rel tr(A)/n I,
  * B_d likewise; damp_rel = 0 gives the undamped loss.  Computed in fp64 as
@@ -201,7 +237,8 @@ const char* kron_status_string(kq_status status);
 /* Detail of the last failing call on this thread ("" if none). */
 const char* kron_last_error(void);
 
-/* ABI version of this header: 2 (kron_quantize gained loss_dev). */
+/* ABI version of this header: 3 (2: kron_quantize gained loss_dev; 3: the WaterKron
+ * entry points and kron_quantize_noalloc). */
 int32_t kron_abi_version(void);
 
 #ifdef __cplusplus

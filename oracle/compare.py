@@ -70,9 +70,9 @@ def trajectory_violations(Z_cand, Y_forced, bits, tie_tol):
 
     Returns (violations, near_ties): violations are such entries with y farther
     than ``tie_tol`` from a rounding boundary; near_ties are the ones within it.
-    Non-finite y (a zero scale) expects code 0.
+    Non-finite y (a zero scale) expects code 0.  bits=None: unbounded codes.
     """
-    qmin, qmax = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    qmin, qmax = (-np.inf, np.inf) if bits is None else (-(1 << (bits - 1)), (1 << (bits - 1)) - 1)
     Y = np.asarray(Y_forced, dtype=np.float64)
     finite = np.isfinite(Y)
     own = np.where(finite, np.clip(np.rint(np.where(finite, Y, 0.0)), qmin, qmax), 0.0)

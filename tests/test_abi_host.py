@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = kq.library()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert kq.kron_abi_version() == 2
+    assert kq.kron_abi_version() == 3
     assert lib.kron_status_string(2) == b"factor not positive definite"
 
 
@@ -171,3 +171,21 @@ def test_noalloc_rejects_before_any_device_call():
                                      FAKE, 64, None, None) == 1
     assert lib.kron_quantize_noalloc(kq.KQ_F32, 0, 64, None, 64, None, 64, None, 0, q(), None, 64,
                                      None, 64, None, None) == 0
+
+
+def test_waterkron_entry_points_validate_on_the_host():
+    lib = kq.library()
+    F = FAKE
+    # kron_waterkron_scales: step must be positive and finite; null pointers; sizes
+    assert lib.kron_waterkron_scales(kq.KQ_F32, 8, 8, F, 8, None, 0, 0.0, F, F, None) == 1
+    assert lib.kron_waterkron_scales(kq.KQ_F32, 8, 8, F, 8, None, 0, float("inf"), F, F, None) == 1
+    assert lib.kron_waterkron_scales(kq.KQ_F32, 8, 8, None, 8, None, 0, 1.0, F, F, None) == 1
+    assert lib.kron_waterkron_scales(kq.KQ_F32, 0, 8, F, 8, None, 0, 1.0, F, F, None) == 1
+    assert lib.kron_waterkron_scales(kq.KQ_F32, 8, 8, F, 8, F, 4, 1.0, F, F, None) == 1
+    # kron_quantize_waterkron: null scales, leading dimensions, workspace
+    args = [kq.KQ_F64, 8, 8, F, 8, F, 8, F, 8, F, F, F, 8, F, 8, None, F, 1 << 40, None]
+    assert lib.kron_quantize_waterkron(*args[:9], None, *args[10:]) == 1
+    assert lib.kron_quantize_waterkron(*args[:12], 4, *args[13:]) == 1
+    assert lib.kron_quantize_waterkron(*args[:17], 16, None) == 3
+    assert lib.kron_quantize_waterkron(kq.KQ_F64, 0, 8, None, 8, None, 8, None, 0, None, None, None, 8, None, 8,
+                                       None, None, 0, None) == 0

@@ -25,7 +25,7 @@ STATUS = {0: "KQ_OK", 1: "KQ_ERR_INVALID_ARG", 2: "KQ_ERR_NOT_PD", 3: "KQ_ERR_WO
           4: "KQ_ERR_HIP", 5: "KQ_ERR_UNSUPPORTED"}
 EXPORTED = ("kron_workspace_bytes", "kron_factor_accumulate", "kron_prepare", "kron_row_scales",
             "kron_quantize", "kron_loss", "kron_status_string", "kron_last_error", "kron_abi_version",
-            "kron_quantize_noalloc")
+            "kron_quantize_noalloc", "kron_waterkron_scales", "kron_quantize_waterkron")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KQ_NOALLOC_SCRATCH_BYTES
 
 
@@ -67,6 +67,11 @@ def library() -> ctypes.CDLL:
     lib.kron_quantize_noalloc.restype = ctypes.c_int
     lib.kron_quantize_noalloc.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64,
                                           ctypes.POINTER(_Quantizer), vp, i64, vp, i64, vp, vp]
+    lib.kron_waterkron_scales.restype = ctypes.c_int
+    lib.kron_waterkron_scales.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, dbl, vp, vp, vp]
+    lib.kron_quantize_waterkron.restype = ctypes.c_int
+    lib.kron_quantize_waterkron.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64, vp, vp, vp, i64, vp,
+                                            i64, vp, vp, sz, vp]
     lib.kron_loss.restype = ctypes.c_int
     lib.kron_loss.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, dbl, vp, vp, sz, vp]
     lib.kron_status_string.restype = ctypes.c_char_p
@@ -211,6 +216,38 @@ def kron_quantize_noalloc(W: torch.Tensor, U_A: torch.Tensor, U_B: torch.Tensor 
         _check(library().kron_quantize_noalloc(_dtype_code(W), m, n, _ptr(W), _ld(W), _ptr(U_A), _ld(U_A), _ptr(U_B),
                                                ldb, ctypes.byref(q), _ptr(codes), _ld(codes), _ptr(V), _ld(V),
                                                _ptr(loss), _stream(W.device)))
+    return codes, V
+
+
+def kron_waterkron_scales(U_A: torch.Tensor, U_B: torch.Tensor | None, step: float, alpha: torch.Tensor,
+                          beta: torch.Tensor) -> tuple:
+    """WaterKron scales: alpha = step * diag(U_A) (n), beta = diag(U_B) or 1 (m)."""
+    n, m = U_A.shape[0], beta.numel()
+    _expect(U_B, "U_B", U_A.dtype, U_A.device, shape=(m, m))
+    _expect(alpha, "alpha", U_A.dtype, U_A.device, n)
+    _expect(beta, "beta", U_A.dtype, U_A.device, m)
+    ldb = _ld(U_B) if U_B is not None else 0
+    _check(library().kron_waterkron_scales(_dtype_code(U_A), m, n, _ptr(U_A), _ld(U_A), _ptr(U_B), ldb, float(step),
+                                           _ptr(alpha), _ptr(beta), _stream(U_A.device)))
+    return alpha, beta
+
+
+def kron_quantize_waterkron(W: torch.Tensor, U_A: torch.Tensor, U_B: torch.Tensor | None, alpha: torch.Tensor,
+                            beta: torch.Tensor, codes: torch.Tensor, V: torch.Tensor, ws: torch.Tensor,
+                            loss: torch.Tensor | None = None):
+    """Two-sided GPTQ with per-entry steps beta_i alpha_j and unbounded int32 codes."""
+    m, n = W.shape
+    for t, name, shp in ((U_A, "U_A", (n, n)), (U_B, "U_B", (m, m)), (V, "V", (m, n))):
+        _expect(t, name, W.dtype, W.device, shape=shp)
+    _expect(alpha, "alpha", W.dtype, W.device, n)
+    _expect(beta, "beta", W.dtype, W.device, m)
+    _expect(codes, "codes", torch.int32, W.device, shape=(m, n))
+    _expect(ws, "ws", torch.uint8, W.device)
+    _expect(loss, "loss", torch.float64, W.device, 1)
+    ldb = _ld(U_B) if U_B is not None else 0
+    _check(library().kron_quantize_waterkron(_dtype_code(W), m, n, _ptr(W), _ld(W), _ptr(U_A), _ld(U_A), _ptr(U_B),
+                                             ldb, _ptr(alpha), _ptr(beta), _ptr(codes), _ld(codes), _ptr(V), _ld(V),
+                                             _ptr(loss), _ptr(ws), ws.numel(), _stream(W.device)))
     return codes, V
 
 

@@ -29,6 +29,11 @@ kq_status factor_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, void
 kq_status loss_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const void*, int64_t, const void*, int64_t,
                         const void*, int64_t, double, double*, void*, hipStream_t);
 kq_status scales_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, int, int, void*, hipStream_t);
+kq_status waterkron_scales_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const void*, int64_t, double,
+                                    void*, void*, hipStream_t);
+kq_status waterkron_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const void*, int64_t, const void*,
+                             int64_t, const void*, const void*, int32_t*, int64_t, void*, int64_t, double*, void*,
+                             hipStream_t);
 
 // Largest supported matrix edge: keeps every tile index and padded extent in int.
 constexpr int64_t MAX_DIM = 1 << 16;
@@ -80,7 +85,7 @@ using namespace kq;
 
 extern "C" {
 
-int32_t kron_abi_version(void) { return 2; }
+int32_t kron_abi_version(void) { return 3; }
 
 const char* kron_status_string(kq_status s) {
     switch (s) {
@@ -158,6 +163,38 @@ kq_status kron_quantize(kq_dtype dtype, int64_t m, int64_t n, const void* W, int
     if (s != KQ_OK) return s;
     return quantize_dispatch(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev, ws,
                              static_cast<hipStream_t>(stream));
+}
+
+kq_status kron_waterkron_scales(kq_dtype dtype, int64_t m, int64_t n, const void* U_A, int64_t lda, const void* U_B,
+                                int64_t ldb, double step, void* alpha, void* beta, void* stream) {
+    set_error("");
+    if (!dtype_ok(dtype)) return invalid("kron_waterkron_scales: dtype must be KQ_F32 or KQ_F64");
+    if (m < 1 || n < 1 || m > MAX_DIM || n > MAX_DIM) return invalid("kron_waterkron_scales: m, n must be in [1, 65536]");
+    if (!U_A || !alpha || !beta) return invalid("kron_waterkron_scales: null pointer");
+    if (lda < n || (U_B && ldb < m)) return invalid("kron_waterkron_scales: leading dimension too small");
+    if (!(step > 0.0) || !std::isfinite(step)) return invalid("kron_waterkron_scales: step must be finite and > 0");
+    return waterkron_scales_dispatch(dtype, m, n, U_A, lda, U_B, ldb, step, alpha, beta,
+                                     static_cast<hipStream_t>(stream));
+}
+
+kq_status kron_quantize_waterkron(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* U_A,
+                                  int64_t lda, const void* U_B, int64_t ldb, const void* alpha, const void* beta,
+                                  int32_t* codes, int64_t ldc, void* V, int64_t ldv, double* loss_dev, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    set_error("");
+    if (!dtype_ok(dtype)) return invalid("kron_quantize_waterkron: dtype must be KQ_F32 or KQ_F64");
+    if (m < 0 || n < 0 || m > MAX_DIM || n > MAX_DIM) return invalid("kron_quantize_waterkron: m, n must be in [0, 65536]");
+    if (m == 0 || n == 0) {
+        if (loss_dev) return invalid("kron_quantize_waterkron: no loss for an empty matrix");
+        return KQ_OK;
+    }
+    if (!W || !U_A || !alpha || !beta || !codes || !V) return invalid("kron_quantize_waterkron: null pointer");
+    if (ldw < n || lda < n || ldc < n || ldv < n || (U_B && ldb < m))
+        return invalid("kron_quantize_waterkron: leading dimension too small");
+    kq_status s = check_ws(ws, ws_bytes, quantize_workspace_bytes(dtype, m, n), "kron_quantize_waterkron");
+    if (s != KQ_OK) return s;
+    return waterkron_dispatch(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, alpha, beta, codes, ldc, V, ldv, loss_dev, ws,
+                              static_cast<hipStream_t>(stream));
 }
 
 kq_status kron_loss(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* V, int64_t ldv,

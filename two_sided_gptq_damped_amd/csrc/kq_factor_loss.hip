@@ -499,6 +499,34 @@ kq_status scales_typed(int64_t m, int64_t n, const T* W, int64_t ldw, int bits, 
     return KQ_OK;
 }
 
+// WaterKron steps (WaterKron page, section 3): alpha_j = step * U_A[j, j] and
+// beta_i = U_B[i, i] (1 when B = I), the reciprocals of the reverse Cholesky
+// diagonals up to the free factor step.  The product is formed in fp64 and
+// rounded once to T.
+template <typename T>
+__global__ void waterkron_scales_kernel(const T* __restrict__ UA, int64_t lda, const T* __restrict__ UB, int64_t ldb,
+                                        int m, int n, double step, T* __restrict__ alpha, T* __restrict__ beta) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) alpha[i] = T(step * double(UA[int64_t(i) * lda + i]));
+    if (i < m) beta[i] = UB ? UB[int64_t(i) * ldb + i] : T(1);
+}
+
+kq_status waterkron_scales_dispatch(kq_dtype dtype, int64_t m, int64_t n, const void* UA, int64_t lda, const void* UB,
+                                    int64_t ldb, double step, void* alpha, void* beta, hipStream_t st) {
+    const int64_t d = m > n ? m : n;
+    const dim3 grid(unsigned((d + 255) / 256)), block(256);
+    if (dtype == KQ_F64)
+        hipLaunchKernelGGL(waterkron_scales_kernel<double>, grid, block, 0, st, static_cast<const double*>(UA), lda,
+                           static_cast<const double*>(UB), ldb, int(m), int(n), step, static_cast<double*>(alpha),
+                           static_cast<double*>(beta));
+    else
+        hipLaunchKernelGGL(waterkron_scales_kernel<float>, grid, block, 0, st, static_cast<const float*>(UA), lda,
+                           static_cast<const float*>(UB), ldb, int(m), int(n), step, static_cast<float*>(alpha),
+                           static_cast<float*>(beta));
+    KQ_LAUNCHED("waterkron_scales_kernel");
+    return KQ_OK;
+}
+
 kq_status scales_dispatch(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, int bits, int per_row,
                           void* scales, hipStream_t st) {
     if (dtype == KQ_F64)

@@ -25,6 +25,8 @@
 // Workspace (the two-sided solver's layout; the output-factor and stage buffers
 // are not touched): NA np x np, X mp x np (starts as W), D mp x np (errors),
 // S mp.  Padding as there: zero weights, unit scales, identity factor.
+#include <type_traits>
+
 #include "kq_common.hpp"
 
 namespace kq {
@@ -56,12 +58,15 @@ __device__ __forceinline__ double lane_value(double v, int l) {
 // errors are applied to the row's later sub-blocks in LDS, four columns at a
 // time.  The sub-block loop is not unrolled, so the code a lone wave runs is a
 // few kilobytes that stay in the instruction cache.
-template <typename T>
+// ENTRY (the WaterKron alphabet): entry (i, j) has the step S[i] * C[j] and the
+// codes are int32.
+template <typename T, bool ENTRY>
 __global__ __launch_bounds__(OS_ROWS) void onesided_leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
                                                                 const T* __restrict__ NA, const T* __restrict__ S,
-                                                                int np, int j0, int m, int n, int qmin, int qmax,
-                                                                int8_t* __restrict__ Z, int64_t ldz,
-                                                                T* __restrict__ V, int64_t ldv) {
+                                                                const T* __restrict__ C, int np, int j0, int m, int n,
+                                                                int qmin, int qmax,
+                                                                std::conditional_t<ENTRY, int32_t, int8_t>* __restrict__ Z,
+                                                                int64_t ldz, T* __restrict__ V, int64_t ldv) {
     constexpr int SB = 16;                       // sub-block width
     constexpr int VN = 16 / sizeof(T);           // entries per 16-byte access
     constexpr int SP = OS_BLK + 16 / sizeof(T);  // xs row pitch: 68 fp32 / 66 fp64
@@ -69,7 +74,8 @@ __global__ __launch_bounds__(OS_ROWS) void onesided_leaf_kernel(const T* __restr
     // cf[j][jj] = N[j0 + j][j0 + jj] strictly above the diagonal, 0 elsewhere
     __shared__ __attribute__((aligned(16))) T cf[OS_BLK][OS_BLK];
     __shared__ __attribute__((aligned(16))) T xs[OS_ROWS * SP];
-    __shared__ uint32_t zs[OS_BLK / 4][OS_ROWS + 1];  // packed codes, four per word (padded row)
+    // codes: int8 packed four per word, or int32 (ENTRY); rows padded by one word
+    __shared__ uint32_t zs[ENTRY ? OS_BLK : OS_BLK / 4][OS_ROWS + 1];
     const int lane = threadIdx.x, r0 = blockIdx.x * OS_ROWS;
     // 16-byte loads: LPR lanes cover one 64-entry row, RPI rows per instruction,
     // so the whole row block and the coefficient block are in flight at once
@@ -109,12 +115,24 @@ __global__ __launch_bounds__(OS_ROWS) void onesided_leaf_kernel(const T* __restr
             for (int e = 0; e < VN; ++e) x[VN * q + e] = v[e];
         }
         uint32_t zp[SB / 4] = {};
+        T se[ENTRY ? SB : 1], rse[ENTRY ? SB : 1];  // per-entry steps and their reciprocals
+        if (ENTRY) {
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                se[j] = s * C[j0 + c0 + j];
+                rse[j] = se[j] == T(0) ? T(0) : T(1) / se[j];
+            }
+        }
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
-            const T z = os_clamp(krint(x[j] * rs), tqmin, tqmax);
-            const T d = s * z - x[j];
+            const T sj = ENTRY ? se[j] : s, rj = ENTRY ? rse[j] : rs;
+            const T z = os_clamp(krint(x[j] * rj), tqmin, tqmax);
+            const T d = sj * z - x[j];
             x[j] = d;  // from here on x[j] holds the error
-            zp[j >> 2] |= (uint32_t(int(z)) & 0xffu) << (8 * (j & 3));
+            if (ENTRY)
+                zs[c0 + j][lane] = uint32_t(int(z));
+            else
+                zp[j >> 2] |= (uint32_t(int(z)) & 0xffu) << (8 * (j & 3));
 #pragma unroll
             for (int q = (j + 1) / VN; q < SB / VN; ++q) {
                 const VT c = *reinterpret_cast<const VT*>(&cf[c0 + j][c0 + VN * q]);
@@ -130,8 +148,10 @@ __global__ __launch_bounds__(OS_ROWS) void onesided_leaf_kernel(const T* __restr
             for (int e = 0; e < VN; ++e) v[e] = x[VN * q + e];
             *reinterpret_cast<VT*>(xr + c0 + VN * q) = v;
         }
+        if (!ENTRY) {
 #pragma unroll
-        for (int q = 0; q < SB / 4; ++q) zs[c0 / 4 + q][lane] = zp[q];
+            for (int q = 0; q < SB / 4; ++q) zs[c0 / 4 + q][lane] = zp[q];
+        }
         // the sub-block's errors into the row's later columns, VN at a time
 #pragma unroll 2
         for (int g = c0 + SB; g < OS_BLK; g += VN) {
@@ -152,11 +172,12 @@ __global__ __launch_bounds__(OS_ROWS) void onesided_leaf_kernel(const T* __restr
             *reinterpret_cast<const VT*>(&xs[(RPI * i + lr) * SP + lc]);
     // Z and V = s z row by row; row rr's scale is lane rr's s, read across the wave
     const bool col_ok = j0 + lane < n;
+    const T cl = ENTRY ? C[j0 + lane] : T(1);  // this lane's column scale
     for (int rr = 0; rr < OS_ROWS && r0 + rr < m; ++rr) {
-        const int z = int(int8_t(uint8_t(zs[lane >> 2][rr] >> (8 * (lane & 3)))));
-        const T sr = lane_value(s, rr);
+        const int z = ENTRY ? int(zs[lane][rr]) : int(int8_t(uint8_t(zs[lane >> 2][rr] >> (8 * (lane & 3)))));
+        const T sr = ENTRY ? lane_value(s, rr) * cl : lane_value(s, rr);
         if (col_ok) {
-            Z[int64_t(r0 + rr) * ldz + j0 + lane] = int8_t(z);
+            Z[int64_t(r0 + rr) * ldz + j0 + lane] = std::remove_reference_t<decltype(Z[0])>(z);
             V[int64_t(r0 + rr) * ldv + j0 + lane] = sr * T(z);
         }
     }
@@ -185,16 +206,20 @@ struct OneSidedRun {
     int m, n, mp, np, qmin, qmax;
     const T* NA;
     T *X, *D;
-    const T* S;
-    int8_t* Z;
+    const T *S, *C;  // C: column scales (WaterKron mode) or nullptr
+    void* Z;         // int8 codes, int32 in the WaterKron mode
     int64_t ldz;
     T* V;
     int64_t ldv;
     hipStream_t st;
 
     kq_status leaf(int j0) {
-        hipLaunchKernelGGL(onesided_leaf_kernel<T>, dim3(unsigned(mp / OS_ROWS)), dim3(OS_ROWS), 0, st, X, D, NA, S,
-                           np, j0, m, n, qmin, qmax, Z, ldz, V, ldv);
+        if (C)
+            hipLaunchKernelGGL((onesided_leaf_kernel<T, true>), dim3(unsigned(mp / OS_ROWS)), dim3(OS_ROWS), 0, st, X, D,
+                               NA, S, C, np, j0, m, n, qmin, qmax, static_cast<int32_t*>(Z), ldz, V, ldv);
+        else
+            hipLaunchKernelGGL((onesided_leaf_kernel<T, false>), dim3(unsigned(mp / OS_ROWS)), dim3(OS_ROWS), 0, st, X,
+                               D, NA, S, C, np, j0, m, n, qmin, qmax, static_cast<int8_t*>(Z), ldz, V, ldv);
         KQ_LAUNCHED("onesided_leaf_kernel");
         return KQ_OK;
     }
@@ -219,14 +244,15 @@ struct OneSidedRun {
 // mp, np: multiples of 64 (the padded extents of the workspace buffers).
 template <typename T>
 kq_status onesided_solve(int m, int n, int mp, int np, int qmin, int qmax, const T* NA, T* X, T* D, const T* S,
-                         int8_t* Z, int64_t ldz, T* V, int64_t ldv, hipStream_t st) {
-    OneSidedRun<T> run{m, n, mp, np, qmin, qmax, NA, X, D, S, Z, ldz, V, ldv, st};
+                         const T* C, void* Z, int64_t ldz, T* V, int64_t ldv, hipStream_t st) {
+    OneSidedRun<T> run{m, n, mp, np, qmin, qmax, NA, X, D, S, C, Z, ldz, V, ldv, st};
     return run.solve(0, np);
 }
 
 template kq_status onesided_solve<float>(int, int, int, int, int, int, const float*, float*, float*, const float*,
-                                         int8_t*, int64_t, float*, int64_t, hipStream_t);
+                                         const float*, void*, int64_t, float*, int64_t, hipStream_t);
 template kq_status onesided_solve<double>(int, int, int, int, int, int, const double*, double*, double*,
-                                          const double*, int8_t*, int64_t, double*, int64_t, hipStream_t);
+                                          const double*, const double*, void*, int64_t, double*, int64_t,
+                                          hipStream_t);
 
 }  // namespace kq

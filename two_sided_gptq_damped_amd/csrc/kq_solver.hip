@@ -30,6 +30,11 @@
 //   D   mp x np   errors Delta
 //   T1  mp x np   stage-1 products
 //   S   mp        per-row scales
+//   C   np        per-column scales (the WaterKron mode only; unit in the padding)
+// In the WaterKron mode (kron_quantize_waterkron) entry (i, j) has the grid step
+// S[i] * C[j] (one rounding) and int32 codes clamped only at +-2^30.
+#include <type_traits>
+
 #include "kq_common.hpp"
 
 namespace kq {
@@ -46,8 +51,8 @@ __global__ void normalize_factor_kernel(const T* __restrict__ U, int64_t ldu, in
 
 template <typename T>
 __global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, int n, int mp, int np,
-                                   const T* __restrict__ scales, int per_row, T* __restrict__ X,
-                                   T* __restrict__ S);
+                                   const T* __restrict__ scales, int per_row, const T* __restrict__ col_scales,
+                                   T* __restrict__ X, T* __restrict__ S, T* __restrict__ C);
 
 // Four consecutive elements (16-byte aligned), from global memory or LDS.
 template <typename T>
@@ -178,13 +183,18 @@ __global__ void normalize_factor_kernel(const T* __restrict__ U, int64_t ldu, in
     }
 }
 
-// X = W zero-padded to mp x np; S = the scales, unit in the padding.  Rows as in
-// normalize_factor_kernel, four consecutive columns per thread.
+// X = W zero-padded to mp x np; S = the scales, unit in the padding; with column
+// scales, C = them, unit in the padding.  Rows as in normalize_factor_kernel,
+// four consecutive columns per thread.
 template <typename T>
 __global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, int n, int mp, int np,
-                                   const T* __restrict__ scales, int per_row, T* __restrict__ X,
-                                   T* __restrict__ S) {
+                                   const T* __restrict__ scales, int per_row, const T* __restrict__ col_scales,
+                                   T* __restrict__ X, T* __restrict__ S, T* __restrict__ C) {
     const int c0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+    if (col_scales && blockIdx.y == 0 && c0 < np) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) C[c0 + u] = c0 + u < n ? col_scales[c0 + u] : T(1);
+    }
     for (int r = blockIdx.y; r < mp; r += gridDim.y) {
         if (blockIdx.x == 0 && threadIdx.x == 0) S[r] = r < m ? scales[per_row ? r : 0] : T(1);
         if (c0 >= np) continue;
@@ -247,13 +257,17 @@ constexpr int LEAF_THREADS = 512;   // the chunk products and the table set-up
 constexpr int SWEEP_THREADS = 512;  // the sweep: two entries per thread
 constexpr int LEAF_E = ST * ST / SWEEP_THREADS;
 
-template <typename T>
+template <bool ENTRY>
+using CodeT = std::conditional_t<ENTRY, int32_t, int8_t>;
+
+template <typename T, bool ENTRY>
 __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
                                                    const T* __restrict__ NA, const T* __restrict__ NB,
-                                                   const T* __restrict__ S, T* __restrict__ T1c, int np, int mp,
-                                                   int Mt, int Nt, int K, int c0, int c1, int m, int n, int qmin,
-                                                   int qmax, int8_t* __restrict__ Z, int64_t ldz,
-                                                   T* __restrict__ V, int64_t ldv) {
+                                                   const T* __restrict__ S, const T* __restrict__ CS,
+                                                   T* __restrict__ T1c, int np, int mp, int Mt, int Nt, int K,
+                                                   int c0, int c1, int m, int n, int qmin, int qmax,
+                                                   CodeT<ENTRY>* __restrict__ Z, int64_t ldz, T* __restrict__ V,
+                                                   int64_t ldv) {
     constexpr int PB = ST + 4;  // 16-byte aligned rows for the vector reads
     constexpr int PA = ST + 1;  // column ST is the zero sentinel
     constexpr int PK = ST + 4;  // k-major staging rows, 16-byte aligned
@@ -338,11 +352,12 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     const int g = t >> 5;  // sweep layout: column b, rows (E g - b + i) mod 32
     int ar[E], dg[E];
     T x[E], rp[E], sc[E], rs[E];
+    const T csb = ENTRY ? CS[J * ST + b] : T(1);  // this thread's column scale
 #pragma unroll
     for (int i = 0; i < E; ++i) {
         ar[i] = (E * g - b + i) & (ST - 1);
         dg[i] = b + ar[i];
-        sc[i] = S[I * ST + ar[i]];
+        sc[i] = ENTRY ? S[I * ST + ar[i]] * csb : S[I * ST + ar[i]];
         rs[i] = sc[i] == T(0) ? T(0) : T(1) / sc[i];
         rp[i] = T(0);
     }
@@ -350,7 +365,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         acc[i] = blk ? X[int64_t(I * ST + r0 + i) * np + J * ST + b] : T(0);
-        sblk[i] = blk ? S[I * ST + r0 + i] : T(0);
+        sblk[i] = blk ? (ENTRY ? S[I * ST + r0 + i] * csb : S[I * ST + r0 + i]) : T(0);
         crow[i] = T(0);
         ccol[i] = T(0);
     }
@@ -651,7 +666,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         const T z = bufA[(r0 + i) * PK + b];
         D[gi * np + gj] = dblk[i];
         if (gi < m && gj < n) {
-            Z[gi * ldz + gj] = int8_t(z);
+            Z[gi * ldz + gj] = CodeT<ENTRY>(z);
             V[gi * ldv + gj] = sblk[i] * z;
         }
     }
@@ -843,7 +858,7 @@ __global__ __launch_bounds__(256) void error_loss_final_kernel(const double* __r
 struct SolverLayout {
     int64_t mp, np, Mt, Nt;  // padded extents; tile counts in 32-tiles
     size_t bytes;
-    size_t off_NA, off_NB, off_X, off_D, off_T1, off_S, off_L;
+    size_t off_NA, off_NB, off_X, off_D, off_T1, off_S, off_C, off_L;
 };
 
 SolverLayout solver_layout(kq_dtype dtype, int64_t m, int64_t n) {
@@ -865,6 +880,7 @@ SolverLayout solver_layout(kq_dtype dtype, int64_t m, int64_t n) {
     L.off_D = take(size_t(L.mp) * L.np);
     L.off_T1 = take(size_t(L.mp) * L.np);
     L.off_S = take(size_t(L.mp));
+    L.off_C = take(size_t(L.np));
     L.off_L = off;  // loss scratch (fp64): 1 / U_A,jj, 1 / U_B,ii, partial sums
     off += align256((size_t(L.np) + size_t(L.mp) + ELOSS_PARTS) * sizeof(double));
     L.bytes = off;
@@ -876,7 +892,8 @@ struct SolverRun {
     const SolverLayout& L;
     int m, n, qmin, qmax;
     T *NA, *NB, *X, *D, *T1, *S;
-    int8_t* Z;
+    T* C;     // column scales (WaterKron mode) or nullptr
+    void* Z;  // int8 codes, or int32 in the WaterKron mode
     int64_t ldz;
     T* V;
     int64_t ldv;
@@ -886,8 +903,14 @@ struct SolverRun {
         const int Mt = int(L.Mt), Nt = int(L.Nt);
         const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
         const int ihi = K < Mt - 1 ? K : Mt - 1;
-        hipLaunchKernelGGL(leaf_kernel<T>, dim3(ihi - ilo + 1), dim3(LEAF_THREADS), 0, st, X, D, NA, NB, S, T1, int(L.np),
-                           int(L.mp), Mt, Nt, K, c0, c1, m, n, qmin, qmax, Z, ldz, V, ldv);
+        if (C)
+            hipLaunchKernelGGL((leaf_kernel<T, true>), dim3(ihi - ilo + 1), dim3(LEAF_THREADS), 0, st, X, D, NA, NB, S, C,
+                               T1, int(L.np), int(L.mp), Mt, Nt, K, c0, c1, m, n, qmin, qmax,
+                               static_cast<int32_t*>(Z), ldz, V, ldv);
+        else
+            hipLaunchKernelGGL((leaf_kernel<T, false>), dim3(ihi - ilo + 1), dim3(LEAF_THREADS), 0, st, X, D, NA, NB, S,
+                               C, T1, int(L.np), int(L.mp), Mt, Nt, K, c0, c1, m, n, qmin, qmax,
+                               static_cast<int8_t*>(Z), ldz, V, ldv);
         KQ_LAUNCHED("leaf_kernel");
         return KQ_OK;
     }
@@ -943,19 +966,33 @@ struct SolverRun {
 
 template <typename T>
 kq_status onesided_solve(int m, int n, int mp, int np, int qmin, int qmax, const T* NA, T* X, T* D, const T* S,
-                         int8_t* Z, int64_t ldz, T* V, int64_t ldv, hipStream_t st);
+                         const T* C, void* Z, int64_t ldz, T* V, int64_t ldv, hipStream_t st);
+
+// The base quantizer as the solver sees it: the step of entry (i, j) is
+// row_scales[per_row ? i : 0], times col_scales[j] when given; codes clamped to
+// [qmin, qmax] and stored as int8, or as int32 when col_scales is given (the
+// WaterKron alphabet).
+template <typename T>
+struct QuantSpec {
+    const T* row_scales;
+    int per_row;
+    const T* col_scales;
+    int qmin, qmax;
+    void* codes;
+    int64_t ldc;
+};
 
 template <typename T>
 kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T* UA, int64_t lda, const T* UB,
-                         int64_t ldb, const kq_quantizer* q, int8_t* codes, int64_t ldc, T* V, int64_t ldv,
-                         double* loss_dev, void* ws, hipStream_t st) {
+                         int64_t ldb, const QuantSpec<T>& q, T* V, int64_t ldv, double* loss_dev, void* ws,
+                         hipStream_t st) {
     const SolverLayout L = solver_layout(sizeof(T) == 8 ? KQ_F64 : KQ_F32, m, n);
     char* base = static_cast<char*>(ws);
-    SolverRun<T> run{L, int(m), int(n), -(1 << (q->bits - 1)), (1 << (q->bits - 1)) - 1,
+    SolverRun<T> run{L, int(m), int(n), q.qmin, q.qmax,
                      reinterpret_cast<T*>(base + L.off_NA), UB ? reinterpret_cast<T*>(base + L.off_NB) : nullptr,
                      reinterpret_cast<T*>(base + L.off_X), reinterpret_cast<T*>(base + L.off_D),
                      reinterpret_cast<T*>(base + L.off_T1), reinterpret_cast<T*>(base + L.off_S),
-                     codes, ldc, V, ldv, st};
+                     q.col_scales ? reinterpret_cast<T*>(base + L.off_C) : nullptr, q.codes, q.ldc, V, ldv, st};
     const int threads = 256;
     auto blocks = [&](int64_t count) { return dim3(unsigned((count + threads - 1) / threads)); };
     auto rows = [&](int64_t cols, int64_t nrows) {  // the kernels loop over rows beyond the grid's y extent
@@ -970,12 +1007,12 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
         KQ_LAUNCHED("normalize_factor_kernel");
     }
     hipLaunchKernelGGL(init_solver_kernel<T>, rows(L.np, L.mp), dim3(threads), 0, st, W, ldw, int(m), int(n),
-                       int(L.mp), int(L.np), static_cast<const T*>(q->scales), q->per_row, run.X, run.S);
+                       int(L.mp), int(L.np), q.row_scales, q.per_row, q.col_scales, run.X, run.S, run.C);
     KQ_LAUNCHED("init_solver_kernel");
     // B = I: one-sided GPTQ, rows independent, recursive over column ranges
     const kq_status s = UB ? run.solve(0, int(L.Mt + L.Nt - 1))
                            : onesided_solve<T>(int(m), int(n), int(L.mp), int(L.np), run.qmin, run.qmax, run.NA,
-                                               run.X, run.D, run.S, codes, ldc, V, ldv, st);
+                                               run.X, run.D, run.S, run.C, q.codes, q.ldc, V, ldv, st);
     if (s != KQ_OK || !loss_dev) return s;
     double* ra = reinterpret_cast<double*>(base + L.off_L);
     double* rb = ra + L.np;
@@ -996,16 +1033,44 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
 
 size_t quantize_workspace_bytes(kq_dtype dtype, int64_t m, int64_t n) { return solver_layout(dtype, m, n).bytes; }
 
+template <typename T>
+kq_status quantize_as(int64_t m, int64_t n, const void* W, int64_t ldw, const void* UA, int64_t lda, const void* UB,
+                      int64_t ldb, const QuantSpec<T>& q, void* V, int64_t ldv, double* loss_dev, void* ws,
+                      hipStream_t st) {
+    return quantize_typed<T>(m, n, static_cast<const T*>(W), ldw, static_cast<const T*>(UA), lda,
+                             static_cast<const T*>(UB), ldb, q, static_cast<T*>(V), ldv, loss_dev, ws, st);
+}
+
 kq_status quantize_dispatch(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* UA,
                             int64_t lda, const void* UB, int64_t ldb, const kq_quantizer* q, int8_t* codes,
                             int64_t ldc, void* V, int64_t ldv, double* loss_dev, void* ws, hipStream_t st) {
+    const int qmin = -(1 << (q->bits - 1)), qmax = (1 << (q->bits - 1)) - 1;
     if (dtype == KQ_F64)
-        return quantize_typed<double>(m, n, static_cast<const double*>(W), ldw, static_cast<const double*>(UA), lda,
-                                      static_cast<const double*>(UB), ldb, q, codes, ldc, static_cast<double*>(V),
-                                      ldv, loss_dev, ws, st);
-    return quantize_typed<float>(m, n, static_cast<const float*>(W), ldw, static_cast<const float*>(UA), lda,
-                                 static_cast<const float*>(UB), ldb, q, codes, ldc, static_cast<float*>(V), ldv,
-                                 loss_dev, ws, st);
+        return quantize_as<double>(m, n, W, ldw, UA, lda, UB, ldb,
+                                   {static_cast<const double*>(q->scales), q->per_row, nullptr, qmin, qmax, codes, ldc},
+                                   V, ldv, loss_dev, ws, st);
+    return quantize_as<float>(m, n, W, ldw, UA, lda, UB, ldb,
+                              {static_cast<const float*>(q->scales), q->per_row, nullptr, qmin, qmax, codes, ldc}, V,
+                              ldv, loss_dev, ws, st);
+}
+
+// WaterKron: steps beta_i alpha_j, int32 codes clamped only at +-2^30 (exact in
+// fp32 and fp64; far beyond any code a finite step gives for finite weights).
+constexpr int WK_CODE_BOUND = 1 << 30;
+
+kq_status waterkron_dispatch(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* UA,
+                             int64_t lda, const void* UB, int64_t ldb, const void* alpha, const void* beta,
+                             int32_t* codes, int64_t ldc, void* V, int64_t ldv, double* loss_dev, void* ws,
+                             hipStream_t st) {
+    if (dtype == KQ_F64)
+        return quantize_as<double>(m, n, W, ldw, UA, lda, UB, ldb,
+                                   {static_cast<const double*>(beta), 1, static_cast<const double*>(alpha),
+                                    -WK_CODE_BOUND, WK_CODE_BOUND, codes, ldc},
+                                   V, ldv, loss_dev, ws, st);
+    return quantize_as<float>(m, n, W, ldw, UA, lda, UB, ldb,
+                              {static_cast<const float*>(beta), 1, static_cast<const float*>(alpha), -WK_CODE_BOUND,
+                               WK_CODE_BOUND, codes, ldc},
+                              V, ldv, loss_dev, ws, st);
 }
 
 }  // namespace kq
