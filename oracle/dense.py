@@ -381,3 +381,68 @@ def prepare(A, delta):
     """Damped factor and its upper factor: (A_d, U) with U^T U = A_d^{-1}."""
     Ad = damp(A, delta)
     return Ad, upper_factor_via_inverse(Ad)
+
+
+# ----------------------------------------------------------------------------
+# Kronecker approximations of H = E[a a^T (x) b b^T] from paired samples
+# ----------------------------------------------------------------------------
+
+
+def kronecker_hessian(Xa, Xb) -> np.ndarray:
+    """H = (1/N) sum_s (a_s a_s^T) (x) (b_s b_s^T) for paired sample rows a_s of
+    Xa (N x n) and b_s of Xb (N x m): the mn x mn Hessian that the Kronecker
+    approximations target (WaterKron page Table 1; FastKron page section 3.2).
+    Only for tiny n, m (it is formed explicitly)."""
+    Xa = np.asarray(Xa, dtype=np.float64)
+    Xb = np.asarray(Xb, dtype=np.float64)
+    H = np.zeros((Xa.shape[1] * Xb.shape[1],) * 2)
+    for a, b in zip(Xa, Xb):
+        H += np.kron(np.outer(a, a), np.outer(b, b))
+    return H / len(Xa)
+
+
+def kronecker_factors(Xa, Xb, method: str, iters: int, delta: float = 0.0):
+    """Alternating fixed-point iteration for H ~ A (x) B, from B_0 = I (WaterKron
+    page section 5 and Table 1; FastKron page section 3.2).
+
+    'flipflop' -- the flip-flop maximum-likelihood iteration for the matrix
+      normal model (Dutilleul, cited on the WaterKron page) with the per-sample
+      matrices G_s = b_s a_s^T, so that vecop(G_s) vecop(G_s)^T = a a^T (x) b b^T:
+        A_{k+1} = (1/(N m)) sum_s (b_s^T B_k^{-1} b_s) a_s a_s^T
+        B_{k+1} = (1/(N n)) sum_s (a_s^T A_{k+1}^{-1} a_s) b_s b_s^T
+    'frobenius' -- the same iteration with A_{k+1}^{-1}, B_k^{-1} replaced by
+      A_{k+1}, B_k, normalised so that each half-step is the exact minimiser of
+      ||H - A (x) B||_F over one factor (the WaterKron page's power iteration):
+        A_{k+1} = sum_s (b_s^T B_k b_s) a_s a_s^T / (N ||B_k||_F^2)
+        B_{k+1} = sum_s (a_s^T A_{k+1} a_s) b_s b_s^T / (N ||A_{k+1}||_F^2)
+    The inverses use the damped factors M + delta tr(M)/d I (delta = 0: none),
+    the damping the WaterKron page adds to make PSD factors invertible.
+    ``iters`` full updates (A, then B).  Returns (A, B) in fp64.
+    """
+    Xa = np.asarray(Xa, dtype=np.float64)
+    Xb = np.asarray(Xb, dtype=np.float64)
+    N, n = Xa.shape
+    m = Xb.shape[1]
+    B = np.eye(m)
+    A = None
+    for _ in range(iters):
+        if method == "flipflop":
+            w = np.einsum("si,ij,sj->s", Xb, np.linalg.inv(damp(B, delta)), Xb)
+            A = (Xa.T * w) @ Xa / (N * m)
+            v = np.einsum("si,ij,sj->s", Xa, np.linalg.inv(damp(A, delta)), Xa)
+            B = (Xb.T * v) @ Xb / (N * n)
+        elif method == "frobenius":
+            w = np.einsum("si,ij,sj->s", Xb, B, Xb)
+            A = (Xa.T * w) @ Xa / (N * np.sum(B * B))
+            v = np.einsum("si,ij,sj->s", Xa, A, Xa)
+            B = (Xb.T * v) @ Xb / (N * np.sum(A * A))
+        else:
+            raise ValueError(method)
+    return A, B
+
+
+def mismatch_factor(H, A, B) -> float:
+    """Phi = tr(H (A (x) B)^{-1}) / (m n): the distortion penalty of the
+    Kronecker approximation (WaterKron page, section 4)."""
+    K = np.kron(np.asarray(A, dtype=np.float64), np.asarray(B, dtype=np.float64))
+    return float(np.trace(np.linalg.solve(K, np.asarray(H, dtype=np.float64))) / len(K))

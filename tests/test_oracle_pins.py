@@ -502,3 +502,96 @@ def test_waterkron_high_rate_distortion_is_uniform():
     loss = dense.proxy_loss(c["W"], V, Ad, Bd)
     ratio = loss / (64 * 64 * step ** 2 / 12)
     assert abs(ratio - 1.0) < 0.05, ratio
+
+
+# ------------------------------------- Kronecker approximations (FlipFlop, Frobenius)
+
+def _paired_samples(seed, N, n, m):
+    r = synth.rng(seed)
+    Xa = r.standard_normal((N, n)) * np.exp(r.standard_normal(n))[None, :]
+    # gradients correlated with the inputs, so H is not itself a Kronecker product
+    Xb = r.standard_normal((N, m)) * (1.0 + 0.5 * np.abs(Xa[:, :1]))
+    return Xa, Xb
+
+
+def test_kronecker_hessian_convention():
+    # one sample: H = a a^T (x) b b^T = vecop(b a^T) vecop(b a^T)^T (column-major vec)
+    a, b = np.array([1.0, 2.0]), np.array([3.0, -1.0, 0.5])
+    G = np.outer(b, a)
+    g = G.reshape(-1, order="F")
+    assert np.allclose(dense.kronecker_hessian(a[None, :], b[None, :]), np.outer(g, g))
+
+
+def test_frobenius_iteration_reaches_the_best_kronecker_product():
+    # Van Loan-Pitsianis: min ||H - A (x) B||_F is the top singular pair of the
+    # rearrangement R(H)[(i, j), (k, l)] = H[i m + k, j m + l] = A_ij B_kl.
+    n, m = 3, 2
+    Xa, Xb = _paired_samples(61, 40, n, m)
+    H = dense.kronecker_hessian(Xa, Xb)
+    R = H.reshape(n, m, n, m).transpose(0, 2, 1, 3).reshape(n * n, m * m)
+    U, S, Vt = np.linalg.svd(R)
+    best = S[0] * np.kron(U[:, 0].reshape(n, n), Vt[0].reshape(m, m))
+    A, B = dense.kronecker_factors(Xa, Xb, "frobenius", 60)
+    assert np.allclose(np.kron(A, B), best, rtol=0, atol=1e-9 * np.abs(best).max())
+    # each half-step is a least-squares minimiser: perturbing A increases the residual
+    res = np.linalg.norm(H - np.kron(A, B))
+    for eps in (1e-3, -1e-3):
+        assert np.linalg.norm(H - np.kron(A * (1 + eps), B)) > res
+
+
+def test_flipflop_iterates_have_unit_mismatch_factor():
+    # After every (undamped) B-update, tr(B^{-1} B) = m gives
+    # E[(a^T A^{-1} a)(b^T B^{-1} b)] = m n, i.e. Phi(H, A (x) B) = 1 exactly.
+    n, m = 3, 2
+    Xa, Xb = _paired_samples(62, 50, n, m)
+    H = dense.kronecker_hessian(Xa, Xb)
+    for iters in (1, 2, 5):
+        A, B = dense.kronecker_factors(Xa, Xb, "flipflop", iters)
+        assert abs(dense.mismatch_factor(H, A, B) - 1.0) < 1e-12
+    # the Frobenius approximation generally does not have Phi = 1
+    A, B = dense.kronecker_factors(Xa, Xb, "frobenius", 5)
+    assert abs(dense.mismatch_factor(H, A, B) - 1.0) > 1e-3
+
+
+def test_flipflop_fixed_point_is_the_matrix_normal_mle():
+    # The flip-flop fixed point maximises the matrix-normal likelihood of the
+    # samples G_s = b_s a_s^T; compare with a generic optimiser of the negative
+    # log-likelihood over Cholesky parametrisations of A and B (tiny sizes).
+    from scipy.optimize import minimize
+    n, m = 2, 2
+    Xa, Xb = _paired_samples(63, 60, n, m)
+    A, B = dense.kronecker_factors(Xa, Xb, "flipflop", 300)
+    tri_n, tri_m = np.tril_indices(n), np.tril_indices(m)
+
+    def unpack(p):
+        La = np.zeros((n, n)); La[tri_n] = p[:len(tri_n[0])]
+        Lb = np.zeros((m, m)); Lb[tri_m] = p[len(tri_n[0]):]
+        La[np.diag_indices(n)] = np.exp(np.diag(La)); Lb[np.diag_indices(m)] = np.exp(np.diag(Lb))
+        return La @ La.T, Lb @ Lb.T
+
+    def nll(p):
+        Ap, Bp = unpack(p)
+        qa = np.einsum("si,ij,sj->s", Xa, np.linalg.inv(Ap), Xa)
+        qb = np.einsum("si,ij,sj->s", Xb, np.linalg.inv(Bp), Xb)
+        N = len(Xa)
+        return 0.5 * (N * m * np.linalg.slogdet(Ap)[1] + N * n * np.linalg.slogdet(Bp)[1] + np.sum(qa * qb))
+
+    res = minimize(nll, np.zeros(len(tri_n[0]) + len(tri_m[0])), method="BFGS", options={"gtol": 1e-10})
+    Ao, Bo = unpack(res.x)
+    K, Ko = np.kron(A, B), np.kron(Ao, Bo)
+    assert np.allclose(K, Ko, rtol=1e-5, atol=1e-6 * np.abs(K).max())
+
+
+def test_kronecker_factor_pins_catch_planted_mistakes():
+    n, m = 3, 2
+    Xa, Xb = _paired_samples(64, 50, n, m)
+    H = dense.kronecker_hessian(Xa, Xb)
+    N = len(Xa)
+    # FlipFlop with the normalisers of the two factors swapped: Phi is off
+    A, B = dense.kronecker_factors(Xa, Xb, "flipflop", 3)
+    w = np.einsum("si,ij,sj->s", Xa, np.linalg.inv(A), Xa)
+    B_bad = (Xb.T * w) @ Xb / (N * m)
+    assert abs(dense.mismatch_factor(H, A, B_bad) - 1.0) > 1e-3
+    # FlipFlop without the inverse (the Frobenius weighting) is not the MLE: Phi != 1
+    A2, B2 = dense.kronecker_factors(Xa, Xb, "frobenius", 3)
+    assert abs(dense.mismatch_factor(H, A2, B2) - 1.0) > 1e-3
