@@ -193,6 +193,42 @@ kq_status kron_quantize_waterkron(kq_dtype dtype, int64_t m, int64_t n, const vo
                                   void* V, int64_t ldv, double* loss_dev, void* ws, size_t ws_bytes,
                                   void* stream);
 
+/* Kronecker approximation methods for kron_factor_kronecker. */
+typedef enum { KQ_KRON_FROBENIUS = 0, KQ_KRON_FLIPFLOP = 1 } kq_kron_method;
+
+/* Workspace bytes of kron_factor_kronecker for N samples, n inputs, m outputs
+ * (0 for invalid arguments). */
+size_t kron_kronecker_workspace_bytes(kq_dtype dtype, int64_t samples, int64_t n, int64_t m);
+
+/*
+ * Kronecker approximation A (x) B of H = E[a a^T (x) b b^T] from paired samples
+ * (WaterKron page, section 5 and Table 1; FastKron page section 3.2): the
+ * alternating fixed-point iteration started from B_0 = I, `iters` full updates
+ * (A, then B):
+ *   KQ_KRON_FLIPFLOP   A <- (1/(N m)) sum_s (b_s^T B_d^{-1} b_s) a_s a_s^T,
+ *                      B <- (1/(N n)) sum_s (a_s^T A_d^{-1} a_s) b_s b_s^T
+ *                      (the flip-flop matrix-normal maximum-likelihood iteration
+ *                      the WaterKron page cites; M_d = M + damp_rel tr(M)/d I)
+ *   KQ_KRON_FROBENIUS  A <- sum_s (b_s^T B b_s) a_s a_s^T / (N ||B||_F^2),
+ *                      B <- sum_s (a_s^T A a_s) b_s b_s^T / (N ||A||_F^2)
+ *                      (alternating least squares for ||H - A (x) B||_F; damp_rel
+ *                      unused)
+ * iters = 1 with FlipFlop and damp_rel = 0 gives A = E[|b|^2 a a^T] / m.
+ *   Xa  N x n activation rows (ldxa >= n), Xb  N x m gradient rows (ldxb >= m),
+ *       row s of both is one sample
+ *   A   n x n output (lda >= n), B  m x m output (ldb >= m), full symmetric
+ *   iters     1..64
+ *   info_dev  FlipFlop only, as for kron_prepare: non-NULL receives 0 or the
+ *             failing pivot step of the first damped factor that was not
+ *             positive definite (asynchronous); NULL makes the call wait and
+ *             return KQ_ERR_NOT_PD in that case
+ *   ws  workspace of kron_kronecker_workspace_bytes(dtype, N, n, m)
+ */
+kq_status kron_factor_kronecker(kq_dtype dtype, int32_t method, int64_t samples, int64_t n, int64_t m,
+                                const void* Xa, int64_t ldxa, const void* Xb, int64_t ldxb, int32_t iters,
+                                double damp_rel, void* A, int64_t lda, void* B, int64_t ldb,
+                                int32_t* info_dev, void* ws, size_t ws_bytes, void* stream);
+
 /*
  * Proxy loss D_{A,B} = tr(B_d (V - W) A_d (V - W)^T) (WaterKron page section 1,
  * item 1; FastKron page section 2.2) with E = V - W, A_d = A + damp_rel tr(A)/n I,
@@ -238,7 +274,7 @@ const char* kron_status_string(kq_status status);
 const char* kron_last_error(void);
 
 /* ABI version of this header: 3 (2: kron_quantize gained loss_dev; 3: the WaterKron
- * entry points and kron_quantize_noalloc). */
+ * entry points, kron_factor_kronecker and kron_quantize_noalloc). */
 int32_t kron_abi_version(void);
 
 #ifdef __cplusplus

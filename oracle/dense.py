@@ -425,16 +425,19 @@ def kronecker_factors(Xa, Xb, method: str, iters: int, delta: float = 0.0):
     m = Xb.shape[1]
     B = np.eye(m)
     A = None
+    def quad(X, M):  # x_s^T M x_s for every row x_s of X
+        return np.sum((X @ M) * X, axis=1)
+
     for _ in range(iters):
         if method == "flipflop":
-            w = np.einsum("si,ij,sj->s", Xb, np.linalg.inv(damp(B, delta)), Xb)
+            w = quad(Xb, np.linalg.inv(damp(B, delta)))
             A = (Xa.T * w) @ Xa / (N * m)
-            v = np.einsum("si,ij,sj->s", Xa, np.linalg.inv(damp(A, delta)), Xa)
+            v = quad(Xa, np.linalg.inv(damp(A, delta)))
             B = (Xb.T * v) @ Xb / (N * n)
         elif method == "frobenius":
-            w = np.einsum("si,ij,sj->s", Xb, B, Xb)
+            w = quad(Xb, B)
             A = (Xa.T * w) @ Xa / (N * np.sum(B * B))
-            v = np.einsum("si,ij,sj->s", Xa, A, Xa)
+            v = quad(Xa, A)
             B = (Xb.T * v) @ Xb / (N * np.sum(A * A))
         else:
             raise ValueError(method)

@@ -189,3 +189,22 @@ def test_waterkron_entry_points_validate_on_the_host():
     assert lib.kron_quantize_waterkron(*args[:17], 16, None) == 3
     assert lib.kron_quantize_waterkron(kq.KQ_F64, 0, 8, None, 8, None, 8, None, 0, None, None, None, 8, None, 8,
                                        None, None, 0, None) == 0
+
+
+def test_kronecker_entry_point_validates_on_the_host():
+    lib = kq.library()
+    F = FAKE
+    good = [kq.KQ_F32, kq.KQ_KRON_FLIPFLOP, 256, 64, 32, F, 64, F, 32, 2, 0.01, F, 64, F, 32, None, F, 1 << 40, None]
+    def call(**kw):
+        args = list(good)
+        for i, v in kw.items():
+            args[int(i[1:])] = v
+        return lib.kron_factor_kronecker(*args)
+    assert call(a1=2) == 1            # method
+    assert call(a9=0) == 1 and call(a9=65) == 1  # iters
+    assert call(a5=None) == 1         # Xa
+    assert call(a6=63) == 1           # ldxa < n
+    assert call(a10=-1.0) == 1        # damp_rel
+    assert call(a17=16) == 3          # workspace too small
+    need = lib.kron_kronecker_workspace_bytes(kq.KQ_F32, 256, 64, 32)
+    assert need > 256 * 64 * 4 and lib.kron_kronecker_workspace_bytes(kq.KQ_F32, 0, 64, 32) == 0

@@ -25,7 +25,9 @@ STATUS = {0: "KQ_OK", 1: "KQ_ERR_INVALID_ARG", 2: "KQ_ERR_NOT_PD", 3: "KQ_ERR_WO
           4: "KQ_ERR_HIP", 5: "KQ_ERR_UNSUPPORTED"}
 EXPORTED = ("kron_workspace_bytes", "kron_factor_accumulate", "kron_prepare", "kron_row_scales",
             "kron_quantize", "kron_loss", "kron_status_string", "kron_last_error", "kron_abi_version",
-            "kron_quantize_noalloc", "kron_waterkron_scales", "kron_quantize_waterkron")
+            "kron_quantize_noalloc", "kron_waterkron_scales", "kron_quantize_waterkron",
+            "kron_kronecker_workspace_bytes", "kron_factor_kronecker")
+KQ_KRON_FROBENIUS, KQ_KRON_FLIPFLOP = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KQ_NOALLOC_SCRATCH_BYTES
 
 
@@ -67,6 +69,11 @@ def library() -> ctypes.CDLL:
     lib.kron_quantize_noalloc.restype = ctypes.c_int
     lib.kron_quantize_noalloc.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64,
                                           ctypes.POINTER(_Quantizer), vp, i64, vp, i64, vp, vp]
+    lib.kron_kronecker_workspace_bytes.restype = sz
+    lib.kron_kronecker_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64]
+    lib.kron_factor_kronecker.restype = ctypes.c_int
+    lib.kron_factor_kronecker.argtypes = [ctypes.c_int, i32, i64, i64, i64, vp, i64, vp, i64, i32, dbl, vp, i64, vp,
+                                          i64, vp, vp, sz, vp]
     lib.kron_waterkron_scales.restype = ctypes.c_int
     lib.kron_waterkron_scales.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, dbl, vp, vp, vp]
     lib.kron_quantize_waterkron.restype = ctypes.c_int
@@ -217,6 +224,35 @@ def kron_quantize_noalloc(W: torch.Tensor, U_A: torch.Tensor, U_B: torch.Tensor 
                                                ldb, ctypes.byref(q), _ptr(codes), _ld(codes), _ptr(V), _ld(V),
                                                _ptr(loss), _stream(W.device)))
     return codes, V
+
+
+def kronecker_workspace(dtype: torch.dtype, samples: int, n: int, m: int, device="cuda") -> torch.Tensor:
+    """A device byte buffer for kron_factor_kronecker (256-byte aligned)."""
+    code = KQ_F64 if dtype == torch.float64 else KQ_F32
+    nbytes = int(library().kron_kronecker_workspace_bytes(code, samples, n, m))
+    buf = torch.empty(max(nbytes, 256) + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + max(nbytes, 256)]
+
+
+def kron_factor_kronecker(Xa: torch.Tensor, Xb: torch.Tensor, method: int, iters: int, damp_rel: float,
+                          A: torch.Tensor, B: torch.Tensor, ws: torch.Tensor, info: torch.Tensor | None = None):
+    """FlipFlop / Frobenius Kronecker factors A (n x n), B (m x m) from paired
+    sample rows Xa (N x n) and Xb (N x m).  info=None waits and raises if a
+    damped FlipFlop factor is not positive definite."""
+    N, n = Xa.shape
+    m = Xb.shape[1]
+    if Xb.shape[0] != N:
+        raise ValueError("Xa and Xb must have the same number of sample rows")
+    _expect(Xb, "Xb", Xa.dtype, Xa.device)
+    _expect(A, "A", Xa.dtype, Xa.device, shape=(n, n))
+    _expect(B, "B", Xa.dtype, Xa.device, shape=(m, m))
+    _expect(ws, "ws", torch.uint8, Xa.device)
+    _expect(info, "info", torch.int32, Xa.device, 1)
+    _check(library().kron_factor_kronecker(_dtype_code(Xa), int(method), N, n, m, _ptr(Xa), _ld(Xa), _ptr(Xb), _ld(Xb),
+                                           int(iters), float(damp_rel), _ptr(A), _ld(A), _ptr(B), _ld(B), _ptr(info),
+                                           _ptr(ws), ws.numel(), _stream(Xa.device)))
+    return A, B
 
 
 def kron_waterkron_scales(U_A: torch.Tensor, U_B: torch.Tensor | None, step: float, alpha: torch.Tensor,

@@ -29,6 +29,9 @@ kq_status factor_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, void
 kq_status loss_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const void*, int64_t, const void*, int64_t,
                         const void*, int64_t, double, double*, void*, hipStream_t);
 kq_status scales_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, int, int, void*, hipStream_t);
+size_t kronecker_workspace_bytes(kq_dtype, int64_t, int64_t, int64_t);
+kq_status kronecker_dispatch(kq_dtype, int, int64_t, int64_t, int64_t, const void*, int64_t, const void*, int64_t, int,
+                             double, void*, int64_t, void*, int64_t, int32_t*, void*, hipStream_t);
 kq_status waterkron_scales_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const void*, int64_t, double,
                                     void*, void*, hipStream_t);
 kq_status waterkron_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const void*, int64_t, const void*,
@@ -163,6 +166,34 @@ kq_status kron_quantize(kq_dtype dtype, int64_t m, int64_t n, const void* W, int
     if (s != KQ_OK) return s;
     return quantize_dispatch(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev, ws,
                              static_cast<hipStream_t>(stream));
+}
+
+size_t kron_kronecker_workspace_bytes(kq_dtype dtype, int64_t samples, int64_t n, int64_t m) {
+    if (!dtype_ok(dtype) || samples < 1 || samples > (int64_t(1) << 30) || n < 1 || m < 1 || n > MAX_DIM ||
+        m > MAX_DIM)
+        return 0;
+    return kronecker_workspace_bytes(dtype, samples, n, m);
+}
+
+kq_status kron_factor_kronecker(kq_dtype dtype, int32_t method, int64_t samples, int64_t n, int64_t m, const void* Xa,
+                                int64_t ldxa, const void* Xb, int64_t ldxb, int32_t iters, double damp_rel, void* A,
+                                int64_t lda, void* B, int64_t ldb, int32_t* info_dev, void* ws, size_t ws_bytes,
+                                void* stream) {
+    set_error("");
+    if (!dtype_ok(dtype)) return invalid("kron_factor_kronecker: dtype must be KQ_F32 or KQ_F64");
+    if (method != KQ_KRON_FROBENIUS && method != KQ_KRON_FLIPFLOP)
+        return invalid("kron_factor_kronecker: method must be KQ_KRON_FROBENIUS or KQ_KRON_FLIPFLOP");
+    if (samples < 1 || samples > (int64_t(1) << 30) || n < 1 || m < 1 || n > MAX_DIM || m > MAX_DIM)
+        return invalid("kron_factor_kronecker: samples must be in [1, 2^30] and n, m in [1, 65536]");
+    if (iters < 1 || iters > 64) return invalid("kron_factor_kronecker: iters must be in [1, 64]");
+    if (!Xa || !Xb || !A || !B) return invalid("kron_factor_kronecker: null pointer");
+    if (ldxa < n || ldxb < m || lda < n || ldb < m) return invalid("kron_factor_kronecker: leading dimension too small");
+    if (!(damp_rel >= 0.0) || !std::isfinite(damp_rel))
+        return invalid("kron_factor_kronecker: damp_rel must be finite and >= 0");
+    kq_status s = check_ws(ws, ws_bytes, kronecker_workspace_bytes(dtype, samples, n, m), "kron_factor_kronecker");
+    if (s != KQ_OK) return s;
+    return kronecker_dispatch(dtype, method, samples, n, m, Xa, ldxa, Xb, ldxb, iters, damp_rel, A, lda, B, ldb,
+                              info_dev, ws, static_cast<hipStream_t>(stream));
 }
 
 kq_status kron_waterkron_scales(kq_dtype dtype, int64_t m, int64_t n, const void* U_A, int64_t lda, const void* U_B,

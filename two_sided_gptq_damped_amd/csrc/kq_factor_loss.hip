@@ -17,21 +17,27 @@ namespace kq {
 // in the first wave of dispatches.
 // EXACT: dim is a multiple of 64, rows of 16 and ldx of 4, so every operand load
 // is in range and vector aligned and the bounds checks are dropped.
+// The weighted form S <- beta S + alpha X^T Y with Y = diag(w) X (the FlipFlop /
+// Frobenius factor updates) runs the same tiles with Y as the right operand:
+// X^T diag(w) X is symmetric, so the lower tiles and their mirrors give it all.
 template <typename T, bool EXACT>
-__device__ __forceinline__ void syrk_tile(const T* __restrict__ X, int64_t ldx, int rows, int dim,
-                                          T* __restrict__ S, int64_t lds, T alpha, T beta, int I, int J,
-                                          GemmSmem<T>& sm) {
+__device__ __forceinline__ void syrk_tile(const T* __restrict__ X, int64_t ldx, const T* __restrict__ Y, int64_t ldy,
+                                          int rows, int dim, T* __restrict__ S, int64_t lds, T alpha, T beta, int I,
+                                          int J, GemmSmem<T>& sm) {
     WaveAcc<T> acc;
     acc.zero();
     const int mv = dim - I * TILE, nv = dim - J * TILE;
-    // A(r, k) = X[k][I*64 + r]; B(k, c) = X[k][J*64 + c]
-    tile_gemm<T, T, true, false, !EXACT>(X + I * TILE, ldx, X + J * TILE, ldx, mv, nv, rows, sm, acc);
+    // A(r, k) = X[k][I*64 + r]; B(k, c) = Y[k][J*64 + c]
+    tile_gemm<T, T, true, false, !EXACT>(X + I * TILE, ldx, Y + J * TILE, ldy, mv, nv, rows, sm, acc);
+    // A diagonal tile keeps its lower triangle and mirrors it, so S is exactly
+    // symmetric also when Y differs from X (X^T diag(w) X computed as x_r (w x_c)
+    // and x_c (w x_r) would round differently).
     for_each_acc(acc, [&](int r, int c, T v) {
-        if (r >= mv || c >= nv) return;
+        if (r >= mv || c >= nv || (I == J && c > r)) return;
         const int64_t gi = int64_t(I) * TILE + r, gj = int64_t(J) * TILE + c;
         T* p = S + gi * lds + gj;
         *p = beta == T(0) ? alpha * v : beta * *p + alpha * v;
-        if (I != J) {
+        if (gi != gj) {
             T* q = S + gj * lds + gi;
             *q = beta == T(0) ? alpha * v : beta * *q + alpha * v;
         }
@@ -39,16 +45,17 @@ __device__ __forceinline__ void syrk_tile(const T* __restrict__ X, int64_t ldx, 
 }
 
 template <typename T, bool EXACT>
-__global__ __launch_bounds__(GEMM_THREADS) void syrk_kernel(const T* __restrict__ X, int64_t ldx, int rows, int dim,
+__global__ __launch_bounds__(GEMM_THREADS) void syrk_kernel(const T* __restrict__ X, int64_t ldx,
+                                                            const T* __restrict__ Y, int64_t ldy, int rows, int dim,
                                                             T* __restrict__ S, int64_t lds, T alpha, T beta,
                                                             int tiles) {
     __shared__ GemmSmem<T> sm;
     const int npairs = (tiles + 1) / 2;
     const int item = blockIdx.x;
     if (item < npairs) {  // diagonal tiles 2 item and 2 item + 1
-        syrk_tile<T, EXACT>(X, ldx, rows, dim, S, lds, alpha, beta, 2 * item, 2 * item, sm);
+        syrk_tile<T, EXACT>(X, ldx, Y, ldy, rows, dim, S, lds, alpha, beta, 2 * item, 2 * item, sm);
         if (2 * item + 1 < tiles)
-            syrk_tile<T, EXACT>(X, ldx, rows, dim, S, lds, alpha, beta, 2 * item + 1, 2 * item + 1, sm);
+            syrk_tile<T, EXACT>(X, ldx, Y, ldy, rows, dim, S, lds, alpha, beta, 2 * item + 1, 2 * item + 1, sm);
         return;
     }
     // below the diagonal: o = I (I - 1) / 2 + J with J < I
@@ -56,27 +63,33 @@ __global__ __launch_bounds__(GEMM_THREADS) void syrk_kernel(const T* __restrict_
     int I = int((1.0 + sqrt(1.0 + 8.0 * o)) * 0.5);
     while (I * (I - 1) / 2 > o) --I;
     while ((I + 1) * I / 2 <= o) ++I;
-    syrk_tile<T, EXACT>(X, ldx, rows, dim, S, lds, alpha, beta, I, o - I * (I - 1) / 2, sm);
+    syrk_tile<T, EXACT>(X, ldx, Y, ldy, rows, dim, S, lds, alpha, beta, I, o - I * (I - 1) / 2, sm);
+}
+
+// S <- beta S + alpha X^T Y, Y = X or diag(w) X (same leading-dimension rules).
+kq_status syrk_dispatch(kq_dtype dtype, int64_t rows, int64_t dim, const void* X, int64_t ldx, const void* Y,
+                        int64_t ldy, void* S, int64_t lds, double alpha, double beta, hipStream_t st) {
+    const int tiles = int((dim + TILE - 1) / TILE);
+    const size_t es = dtype == KQ_F64 ? 8 : 4;
+    const bool exact = dim % TILE == 0 && rows % KSTEP == 0 && ldx % 4 == 0 && ldy % 4 == 0 &&
+                       reinterpret_cast<uintptr_t>(X) % (4 * es) == 0 && reinterpret_cast<uintptr_t>(Y) % (4 * es) == 0;
+    const dim3 grid(unsigned((tiles + 1) / 2 + tiles * (tiles - 1) / 2)), block(GEMM_THREADS);
+    if (dtype == KQ_F64) {
+        auto k = exact ? syrk_kernel<double, true> : syrk_kernel<double, false>;
+        hipLaunchKernelGGL(k, grid, block, 0, st, static_cast<const double*>(X), ldx, static_cast<const double*>(Y),
+                           ldy, int(rows), int(dim), static_cast<double*>(S), lds, alpha, beta, tiles);
+    } else {
+        auto k = exact ? syrk_kernel<float, true> : syrk_kernel<float, false>;
+        hipLaunchKernelGGL(k, grid, block, 0, st, static_cast<const float*>(X), ldx, static_cast<const float*>(Y), ldy,
+                           int(rows), int(dim), static_cast<float*>(S), lds, float(alpha), float(beta), tiles);
+    }
+    KQ_LAUNCHED("syrk_kernel");
+    return KQ_OK;
 }
 
 kq_status factor_dispatch(kq_dtype dtype, int64_t rows, int64_t dim, const void* X, int64_t ldx, void* S, int64_t lds,
                           double alpha, double beta, hipStream_t st) {
-    const int tiles = int((dim + TILE - 1) / TILE);
-    const size_t es = dtype == KQ_F64 ? 8 : 4;
-    const bool exact = dim % TILE == 0 && rows % KSTEP == 0 && ldx % 4 == 0 &&
-                       reinterpret_cast<uintptr_t>(X) % (4 * es) == 0;
-    const dim3 grid(unsigned((tiles + 1) / 2 + tiles * (tiles - 1) / 2)), block(GEMM_THREADS);
-    if (dtype == KQ_F64) {
-        auto k = exact ? syrk_kernel<double, true> : syrk_kernel<double, false>;
-        hipLaunchKernelGGL(k, grid, block, 0, st, static_cast<const double*>(X), ldx, int(rows), int(dim),
-                           static_cast<double*>(S), lds, alpha, beta, tiles);
-    } else {
-        auto k = exact ? syrk_kernel<float, true> : syrk_kernel<float, false>;
-        hipLaunchKernelGGL(k, grid, block, 0, st, static_cast<const float*>(X), ldx, int(rows), int(dim),
-                           static_cast<float*>(S), lds, float(alpha), float(beta), tiles);
-    }
-    KQ_LAUNCHED("syrk_kernel");
-    return KQ_OK;
+    return syrk_dispatch(dtype, rows, dim, X, ldx, X, ldx, S, lds, alpha, beta, st);
 }
 
 // ------------------------------------------------------------------ the loss
