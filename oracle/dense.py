@@ -449,3 +449,62 @@ def mismatch_factor(H, A, B) -> float:
     Kronecker approximation (WaterKron page, section 4)."""
     K = np.kron(np.asarray(A, dtype=np.float64), np.asarray(B, dtype=np.float64))
     return float(np.trace(np.linalg.solve(K, np.asarray(H, dtype=np.float64))) / len(K))
+
+
+# ----------------------------------------------------------------------------
+# KronQ bidirectional incoherence processing (BiIP)
+# ----------------------------------------------------------------------------
+
+BIIP_MAX_BLOCK = 4096
+
+
+def hadamard_block(d: int, max_block: int = BIIP_MAX_BLOCK) -> int:
+    """Walsh-Hadamard block size for dimension d: the largest power of two that
+    divides d, at most max_block (a d that is not a power of two gets a
+    block-diagonal transform, which is still orthogonal)."""
+    return min(d & -d, max_block)
+
+
+def biip_rotation(d: int, signs, max_block: int = BIIP_MAX_BLOCK) -> np.ndarray:
+    """Q = (I_{d/h} (x) H_h / sqrt(h)) diag(signs), H_h the Sylvester
+    Walsh-Hadamard matrix (H_2 = [[1, 1], [1, -1]], the KronQ page's 2 x 2
+    example) and signs a +-1 vector (the randomised Hadamard transform)."""
+    from scipy.linalg import hadamard
+    h = hadamard_block(d, max_block)
+    H = hadamard(h).astype(np.float64) / np.sqrt(h)
+    return np.kron(np.eye(d // h), H) * np.asarray(signs, dtype=np.float64)[None, :]
+
+
+def biip_scales(M) -> np.ndarray:
+    """diag(M)^{-1/4} (KronQ page, BiIP: S_X = diag(H_X)^{-1/4}, S_G likewise);
+    1 where a diagonal entry is not positive."""
+    d = np.diag(np.asarray(M, dtype=np.float64))
+    return np.where(d > 0, np.abs(d) ** -0.25, 1.0)
+
+
+def biip_forward(W, A, B, signs_n, signs_m):
+    """KronQ BiIP (KronQ page, section "Kronecker-Factored Quantization"):
+    rescale W' = S_B W S_A with S = diag^{-1/4} of each factor, and the factors
+    by the inverse scales (A' = S_A^{-1} A S_A^{-1}, B' likewise), so that the
+    loss tr(B E A E^T) is unchanged; then rotate both sides, W'' = Q_B W' Q_A^T,
+    A'' = Q_A A' Q_A^T, B'' = Q_B B' Q_B^T (Theorem 1: invariance under
+    orthogonal Q_A, Q_B).  W is m x n, A n x n (H_X), B m x m (H_G).
+    Returns (W'', A'', B'', s_A, s_B)."""
+    W = np.asarray(W, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    m, n = W.shape
+    sa, sb = biip_scales(A), biip_scales(B)
+    Qa, Qb = biip_rotation(n, signs_n), biip_rotation(m, signs_m)
+    W2 = Qb @ (sb[:, None] * W * sa[None, :]) @ Qa.T
+    A2 = Qa @ (A / np.outer(sa, sa)) @ Qa.T
+    B2 = Qb @ (B / np.outer(sb, sb)) @ Qb.T
+    return W2, A2, B2, sa, sb
+
+
+def biip_inverse(V2, signs_n, signs_m, sa, sb):
+    """Back to the original coordinates: V = S_B^{-1} Q_B^T V'' Q_A S_A^{-1}."""
+    V2 = np.asarray(V2, dtype=np.float64)
+    m, n = V2.shape
+    Qa, Qb = biip_rotation(n, signs_n), biip_rotation(m, signs_m)
+    return (Qb.T @ V2 @ Qa) / np.asarray(sb)[:, None] / np.asarray(sa)[None, :]

@@ -595,3 +595,60 @@ def test_kronecker_factor_pins_catch_planted_mistakes():
     # FlipFlop without the inverse (the Frobenius weighting) is not the MLE: Phi != 1
     A2, B2 = dense.kronecker_factors(Xa, Xb, "frobenius", 3)
     assert abs(dense.mismatch_factor(H, A2, B2) - 1.0) > 1e-3
+
+
+# ------------------------------------------------------------ KronQ BiIP
+
+def test_biip_scales_and_hadamard_match_printed_example():
+    g = read_golden("kronq_biip_example.txt")
+    sx = dense.biip_scales(np.diag(g["DIAG_H_X"][0]))
+    sg = dense.biip_scales(np.diag(g["DIAG_H_G"][0]))
+    assert np.array_equal(np.round(sx, 2), g["PRINTED_S_X"][0])
+    assert np.array_equal(np.round(sg, 2), g["PRINTED_S_G"][0])
+    Q = dense.biip_rotation(2, [1, 1])
+    assert np.allclose(Q * np.sqrt(2), g["PRINTED_HADAMARD_TIMES_SQRT2"], atol=1e-15)
+
+
+def test_biip_rotation_is_orthogonal():
+    r = synth.rng(71)
+    for d in (2, 48, 64, 96, 7):
+        Q = dense.biip_rotation(d, np.where(r.random(d) < 0.5, -1.0, 1.0))
+        assert np.allclose(Q.T @ Q, np.eye(d), atol=1e-13)
+    assert dense.hadamard_block(14336) == 2048 and dense.hadamard_block(4096) == 4096
+    assert dense.hadamard_block(65536) == dense.BIIP_MAX_BLOCK and dense.hadamard_block(7) == 1
+
+
+def _biip_problem(seed, m, n):
+    c = synth.spectral(m, n, config=seed)
+    r = synth.rng(seed + 77)
+    sn = np.where(r.random(n) < 0.5, -1.0, 1.0)
+    sm = np.where(r.random(m) < 0.5, -1.0, 1.0)
+    # distinct diagonal magnitudes, so the rescale matters
+    A = c["A"] * np.outer(np.linspace(1, 3, n), np.linspace(1, 3, n))
+    B = c["B"] * np.outer(np.linspace(2, 0.5, m), np.linspace(2, 0.5, m))
+    return c["W"], A, B, sn, sm
+
+
+def test_biip_loss_is_invariant():
+    # KronQ page Theorem 1 (orthogonal rotations) together with the paired
+    # diagonal rescale: for any V'' in the processed coordinates,
+    # tr(B E A E^T) with E = inverse(V'') - W equals tr(B'' E'' A'' E''^T).
+    W, A, B, sn, sm = _biip_problem(81, 24, 40)
+    W2, A2, B2, sa, sb = dense.biip_forward(W, A, B, sn, sm)
+    V2 = W2 + 0.1 * synth.gaussian(82, W2.shape)
+    V = dense.biip_inverse(V2, sn, sm, sa, sb)
+    l2 = dense.proxy_loss(W2, V2, A2, B2)
+    assert abs(dense.proxy_loss(W, V, A, B) - l2) <= 1e-12 * l2
+    assert np.allclose(dense.biip_inverse(W2, sn, sm, sa, sb), W, atol=1e-12)
+    # planted mistake: factors scaled by S instead of S^{-1} break the invariance
+    A_bad = dense.biip_rotation(40, sn) @ (A * np.outer(sa, sa)) @ dense.biip_rotation(40, sn).T
+    assert abs(dense.proxy_loss(W2, V2, A_bad, B2) - l2) > 1e-3 * l2
+
+
+def test_biip_spreads_an_outlier():
+    W = 0.01 * synth.gaussian(83, (32, 64))
+    W[5, 7] = 10.0
+    A, B = np.eye(64), np.eye(32)
+    W2 = dense.biip_forward(W, A, B, np.ones(64), np.ones(32))[0]
+    peak = lambda M: np.abs(M).max() / np.sqrt(np.mean(M ** 2))
+    assert peak(W2) < 0.1 * peak(W)
