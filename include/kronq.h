@@ -229,6 +229,41 @@ kq_status kron_factor_kronecker(kq_dtype dtype, int32_t method, int64_t samples,
                                 double damp_rel, void* A, int64_t lda, void* B, int64_t ldb,
                                 int32_t* info_dev, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes of kron_biip_forward / kron_biip_inverse (0 if invalid). */
+size_t kron_biip_workspace_bytes(kq_dtype dtype, int64_t m, int64_t n);
+
+/*
+ * KronQ bidirectional incoherence processing (KronQ page, section
+ * "Kronecker-Factored Quantization": BiIP and Theorem 1).  With
+ * s_A = diag(A)^{-1/4}, s_B = diag(B)^{-1/4} (1 where a diagonal entry is not
+ * positive) and the randomised Walsh-Hadamard rotations Q = (I (x) H_h/sqrt(h))
+ * diag(signs) (Sylvester H_h on blocks of h = the largest power of two dividing
+ * the dimension, at most 4096; signs are +-1 drawn by the caller):
+ *   W_out = Q_B S_B W S_A Q_A^T              (m x n)
+ *   A_out = Q_A S_A^{-1} A S_A^{-1} Q_A^T     (n x n)
+ *   B_out = Q_B S_B^{-1} B S_B^{-1} Q_B^T     (m x m)
+ * so tr(B E A E^T) is unchanged when E is mapped back by kron_biip_inverse.
+ * Quantize W_out with factors from A_out, B_out, then map V back.
+ *   signs_n, signs_m  device int8 arrays of n and m entries (negative: -1)
+ *   scale_a, scale_b  device outputs s_A (n), s_B (m), dtype; kron_biip_inverse
+ *                     takes them back
+ *   ws  workspace of kron_biip_workspace_bytes(dtype, m, n)
+ * Every pass reads and writes its matrix once (HBM-bound).
+ */
+kq_status kron_biip_forward(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* A,
+                            int64_t lda, const void* B, int64_t ldb, const int8_t* signs_n,
+                            const int8_t* signs_m, void* W_out, int64_t ldwo, void* A_out, int64_t ldao,
+                            void* B_out, int64_t ldbo, void* scale_a, void* scale_b, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* V = S_B^{-1} Q_B^T V2 Q_A S_A^{-1}: a result of the processed problem (m x n)
+ * back in the original coordinates, with the signs and scales of the forward
+ * call.  Same workspace. */
+kq_status kron_biip_inverse(kq_dtype dtype, int64_t m, int64_t n, const void* V2, int64_t ldv2,
+                            const int8_t* signs_n, const int8_t* signs_m, const void* scale_a,
+                            const void* scale_b, void* V, int64_t ldv, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /*
  * Proxy loss D_{A,B} = tr(B_d (V - W) A_d (V - W)^T) (WaterKron page section 1,
  * item 1; FastKron page section 2.2) with E = V - W, A_d = A + damp_rel tr(A)/n I,
@@ -274,7 +309,7 @@ const char* kron_status_string(kq_status status);
 const char* kron_last_error(void);
 
 /* ABI version of this header: 3 (2: kron_quantize gained loss_dev; 3: the WaterKron
- * entry points, kron_factor_kronecker and kron_quantize_noalloc). */
+ * entry points, kron_factor_kronecker, the BiIP transforms and kron_quantize_noalloc). */
 int32_t kron_abi_version(void);
 
 #ifdef __cplusplus

@@ -208,3 +208,16 @@ def test_kronecker_entry_point_validates_on_the_host():
     assert call(a17=16) == 3          # workspace too small
     need = lib.kron_kronecker_workspace_bytes(kq.KQ_F32, 256, 64, 32)
     assert need > 256 * 64 * 4 and lib.kron_kronecker_workspace_bytes(kq.KQ_F32, 0, 64, 32) == 0
+
+
+def test_biip_entry_points_validate_on_the_host():
+    lib = kq.library()
+    F = FAKE
+    fw = [kq.KQ_F32, 64, 48, F, 48, F, 48, F, 64, F, F, F, 48, F, 48, F, 64, F, F, F, 1 << 40, None]
+    assert lib.kron_biip_forward(*fw[:9], None, *fw[10:]) == 1        # signs_n
+    assert lib.kron_biip_forward(*fw[:4], 40, *fw[5:]) == 1            # ldw < n
+    assert lib.kron_biip_forward(*fw[:20], 64, None) == 3              # workspace
+    inv = [kq.KQ_F64, 64, 48, F, 48, F, F, F, F, F, 48, F, 1 << 40, None]
+    assert lib.kron_biip_inverse(*inv[:7], None, *inv[8:]) == 1        # scale_a
+    assert lib.kron_biip_inverse(*inv[:10], 40, *inv[11:]) == 1        # ldv < n
+    assert lib.kron_biip_workspace_bytes(kq.KQ_F32, 64, 48) >= 2 * 64 * 64 * 4

@@ -26,7 +26,8 @@ STATUS = {0: "KQ_OK", 1: "KQ_ERR_INVALID_ARG", 2: "KQ_ERR_NOT_PD", 3: "KQ_ERR_WO
 EXPORTED = ("kron_workspace_bytes", "kron_factor_accumulate", "kron_prepare", "kron_row_scales",
             "kron_quantize", "kron_loss", "kron_status_string", "kron_last_error", "kron_abi_version",
             "kron_quantize_noalloc", "kron_waterkron_scales", "kron_quantize_waterkron",
-            "kron_kronecker_workspace_bytes", "kron_factor_kronecker")
+            "kron_kronecker_workspace_bytes", "kron_factor_kronecker", "kron_biip_workspace_bytes",
+            "kron_biip_forward", "kron_biip_inverse")
 KQ_KRON_FROBENIUS, KQ_KRON_FLIPFLOP = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KQ_NOALLOC_SCRATCH_BYTES
 
@@ -69,6 +70,13 @@ def library() -> ctypes.CDLL:
     lib.kron_quantize_noalloc.restype = ctypes.c_int
     lib.kron_quantize_noalloc.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64,
                                           ctypes.POINTER(_Quantizer), vp, i64, vp, i64, vp, vp]
+    lib.kron_biip_workspace_bytes.restype = sz
+    lib.kron_biip_workspace_bytes.argtypes = [ctypes.c_int, i64, i64]
+    lib.kron_biip_forward.restype = ctypes.c_int
+    lib.kron_biip_forward.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64, vp, vp, vp, i64, vp, i64, vp,
+                                      i64, vp, vp, vp, sz, vp]
+    lib.kron_biip_inverse.restype = ctypes.c_int
+    lib.kron_biip_inverse.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, vp, vp, vp, vp, i64, vp, sz, vp]
     lib.kron_kronecker_workspace_bytes.restype = sz
     lib.kron_kronecker_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64]
     lib.kron_factor_kronecker.restype = ctypes.c_int
@@ -253,6 +261,49 @@ def kron_factor_kronecker(Xa: torch.Tensor, Xb: torch.Tensor, method: int, iters
                                            int(iters), float(damp_rel), _ptr(A), _ld(A), _ptr(B), _ld(B), _ptr(info),
                                            _ptr(ws), ws.numel(), _stream(Xa.device)))
     return A, B
+
+
+def biip_workspace(dtype: torch.dtype, m: int, n: int, device="cuda") -> torch.Tensor:
+    """A device byte buffer for kron_biip_forward / kron_biip_inverse (256-byte aligned)."""
+    code = KQ_F64 if dtype == torch.float64 else KQ_F32
+    nbytes = int(library().kron_biip_workspace_bytes(code, m, n))
+    buf = torch.empty(max(nbytes, 256) + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + max(nbytes, 256)]
+
+
+def kron_biip_forward(W, A, B, signs_n, signs_m, W_out, A_out, B_out, scale_a, scale_b, ws):
+    """KronQ BiIP: W_out = Q_B S_B W S_A Q_A^T, A_out, B_out the matching factors;
+    scale_a = diag(A)^{-1/4}, scale_b = diag(B)^{-1/4}."""
+    m, n = W.shape
+    for t, name, shp in ((A, "A", (n, n)), (B, "B", (m, m)), (W_out, "W_out", (m, n)), (A_out, "A_out", (n, n)),
+                         (B_out, "B_out", (m, m))):
+        _expect(t, name, W.dtype, W.device, shape=shp)
+    _expect(signs_n, "signs_n", torch.int8, W.device, n)
+    _expect(signs_m, "signs_m", torch.int8, W.device, m)
+    _expect(scale_a, "scale_a", W.dtype, W.device, n)
+    _expect(scale_b, "scale_b", W.dtype, W.device, m)
+    _expect(ws, "ws", torch.uint8, W.device)
+    _check(library().kron_biip_forward(_dtype_code(W), m, n, _ptr(W), _ld(W), _ptr(A), _ld(A), _ptr(B), _ld(B),
+                                       _ptr(signs_n), _ptr(signs_m), _ptr(W_out), _ld(W_out), _ptr(A_out), _ld(A_out),
+                                       _ptr(B_out), _ld(B_out), _ptr(scale_a), _ptr(scale_b), _ptr(ws), ws.numel(),
+                                       _stream(W.device)))
+    return W_out, A_out, B_out
+
+
+def kron_biip_inverse(V2, signs_n, signs_m, scale_a, scale_b, V, ws):
+    """V = S_B^{-1} Q_B^T V2 Q_A S_A^{-1} (the processed problem's result mapped back)."""
+    m, n = V2.shape
+    _expect(V, "V", V2.dtype, V2.device, shape=(m, n))
+    _expect(signs_n, "signs_n", torch.int8, V2.device, n)
+    _expect(signs_m, "signs_m", torch.int8, V2.device, m)
+    _expect(scale_a, "scale_a", V2.dtype, V2.device, n)
+    _expect(scale_b, "scale_b", V2.dtype, V2.device, m)
+    _expect(ws, "ws", torch.uint8, V2.device)
+    _check(library().kron_biip_inverse(_dtype_code(V2), m, n, _ptr(V2), _ld(V2), _ptr(signs_n), _ptr(signs_m),
+                                       _ptr(scale_a), _ptr(scale_b), _ptr(V), _ld(V), _ptr(ws), ws.numel(),
+                                       _stream(V2.device)))
+    return V
 
 
 def kron_waterkron_scales(U_A: torch.Tensor, U_B: torch.Tensor | None, step: float, alpha: torch.Tensor,

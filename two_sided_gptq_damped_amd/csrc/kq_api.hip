@@ -30,6 +30,12 @@ kq_status loss_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const 
                         const void*, int64_t, double, double*, void*, hipStream_t);
 kq_status scales_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, int, int, void*, hipStream_t);
 size_t kronecker_workspace_bytes(kq_dtype, int64_t, int64_t, int64_t);
+size_t biip_workspace_bytes(kq_dtype, int64_t, int64_t);
+kq_status biip_forward_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const void*, int64_t, const void*,
+                                int64_t, const int8_t*, const int8_t*, void*, int64_t, void*, int64_t, void*, int64_t,
+                                void*, void*, void*, hipStream_t);
+kq_status biip_inverse_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const int8_t*, const int8_t*,
+                                const void*, const void*, void*, int64_t, void*, hipStream_t);
 kq_status kronecker_dispatch(kq_dtype, int, int64_t, int64_t, int64_t, const void*, int64_t, const void*, int64_t, int,
                              double, void*, int64_t, void*, int64_t, int32_t*, void*, hipStream_t);
 kq_status waterkron_scales_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const void*, int64_t, double,
@@ -194,6 +200,42 @@ kq_status kron_factor_kronecker(kq_dtype dtype, int32_t method, int64_t samples,
     if (s != KQ_OK) return s;
     return kronecker_dispatch(dtype, method, samples, n, m, Xa, ldxa, Xb, ldxb, iters, damp_rel, A, lda, B, ldb,
                               info_dev, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t kron_biip_workspace_bytes(kq_dtype dtype, int64_t m, int64_t n) {
+    if (!dtype_ok(dtype) || m < 1 || n < 1 || m > MAX_DIM || n > MAX_DIM) return 0;
+    return biip_workspace_bytes(dtype, m, n);
+}
+
+kq_status kron_biip_forward(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* A,
+                            int64_t lda, const void* B, int64_t ldb, const int8_t* signs_n, const int8_t* signs_m,
+                            void* W_out, int64_t ldwo, void* A_out, int64_t ldao, void* B_out, int64_t ldbo,
+                            void* scale_a, void* scale_b, void* ws, size_t ws_bytes, void* stream) {
+    set_error("");
+    if (!dtype_ok(dtype)) return invalid("kron_biip_forward: dtype must be KQ_F32 or KQ_F64");
+    if (m < 1 || n < 1 || m > MAX_DIM || n > MAX_DIM) return invalid("kron_biip_forward: m, n must be in [1, 65536]");
+    if (!W || !A || !B || !signs_n || !signs_m || !W_out || !A_out || !B_out || !scale_a || !scale_b)
+        return invalid("kron_biip_forward: null pointer");
+    if (ldw < n || lda < n || ldb < m || ldwo < n || ldao < n || ldbo < m)
+        return invalid("kron_biip_forward: leading dimension too small");
+    kq_status s = check_ws(ws, ws_bytes, biip_workspace_bytes(dtype, m, n), "kron_biip_forward");
+    if (s != KQ_OK) return s;
+    return biip_forward_dispatch(dtype, m, n, W, ldw, A, lda, B, ldb, signs_n, signs_m, W_out, ldwo, A_out, ldao, B_out,
+                                 ldbo, scale_a, scale_b, ws, static_cast<hipStream_t>(stream));
+}
+
+kq_status kron_biip_inverse(kq_dtype dtype, int64_t m, int64_t n, const void* V2, int64_t ldv2, const int8_t* signs_n,
+                            const int8_t* signs_m, const void* scale_a, const void* scale_b, void* V, int64_t ldv,
+                            void* ws, size_t ws_bytes, void* stream) {
+    set_error("");
+    if (!dtype_ok(dtype)) return invalid("kron_biip_inverse: dtype must be KQ_F32 or KQ_F64");
+    if (m < 1 || n < 1 || m > MAX_DIM || n > MAX_DIM) return invalid("kron_biip_inverse: m, n must be in [1, 65536]");
+    if (!V2 || !signs_n || !signs_m || !scale_a || !scale_b || !V) return invalid("kron_biip_inverse: null pointer");
+    if (ldv2 < n || ldv < n) return invalid("kron_biip_inverse: leading dimension too small");
+    kq_status s = check_ws(ws, ws_bytes, biip_workspace_bytes(dtype, m, n), "kron_biip_inverse");
+    if (s != KQ_OK) return s;
+    return biip_inverse_dispatch(dtype, m, n, V2, ldv2, signs_n, signs_m, scale_a, scale_b, V, ldv, ws,
+                                 static_cast<hipStream_t>(stream));
 }
 
 kq_status kron_waterkron_scales(kq_dtype dtype, int64_t m, int64_t n, const void* U_A, int64_t lda, const void* U_B,
