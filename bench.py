@@ -97,6 +97,10 @@ def main() -> int:
                          "Llama-block pipeline, one JSON line each")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (counter calibration)")
+    ap.add_argument("--core-calls", type=int, default=0, metavar="K",
+                    help="only run K kron_quantize calls on the 4096x4096 workload (factors prepared first), "
+                         "for kernel traces and counters; --one-sided runs them with U_B = NULL")
+    ap.add_argument("--one-sided", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -107,6 +111,8 @@ def main() -> int:
 
     if args.copy_probe:
         return copy_probe(torch, args.copy_probe)
+    if args.core_calls:
+        return core_calls(torch, args)
     if args.shapes:
         return shape_report(torch)
 
@@ -427,6 +433,38 @@ def shape_report(torch):
                       "what": "whole path per sublayer (factor products, prepares, scales, solve with its loss), "
                               "sublayers pipelined; host wall clock, median of 2 after a warm-up",
                       "losses": [float(o["loss"].item()) for o in out]}), flush=True)
+    return 0
+
+
+def core_calls(torch, args):
+    """K kron_quantize calls on the bench workload, nothing else timed or run
+    beside them (the profiled unit for kernel traces and counters)."""
+    import synth
+    import two_sided_gptq_damped_amd as kq
+    from two_sided_gptq_damped_amd import pipeline
+
+    m, n, bits = args.m, args.n, args.bits
+    c = synth.llm(m, n, bits, config=3)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+    W = f32(c["W"])
+    UA, _, _ = pipeline.prepare(pipeline.factor(f32(c["act"])), c["damp"])
+    UB = None if args.one_sided else pipeline.prepare(pipeline.factor(f32(c["grad"])), c["damp"])[0]
+    scales = torch.empty(m, dtype=torch.float32, device="cuda")
+    kq.kron_row_scales(W, bits, True, scales)
+    codes = torch.empty(m, n, dtype=torch.int8, device="cuda")
+    V = torch.empty_like(W)
+    ws = kq.workspace(kq.KQ_OP_QUANTIZE, torch.float32, m, n)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(args.core_calls):
+        a.record()
+        kq.kron_quantize(W, UA, UB, bits, True, scales, codes, V, ws)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    print(json.dumps({"core_calls": args.core_calls, "one_sided": bool(args.one_sided), "m": m, "n": n,
+                      "ms": ts}), flush=True)
     return 0
 
 
