@@ -433,7 +433,84 @@ def shape_report(torch):
                       "what": "whole path per sublayer (factor products, prepares, scales, solve with its loss), "
                               "sublayers pipelined; host wall clock, median of 2 after a warm-up",
                       "losses": [float(o["loss"].item()) for o in out]}), flush=True)
+    del layers, out
+    torch.cuda.empty_cache()
+    extras_report(torch, up)
     return 0
+
+
+def extras_report(torch, up):
+    """The other entry points on the 4096 x 4096 workload layer, one JSON line
+    each: WaterKron (per-entry steps, unbounded codes; the empirical entropy of
+    the codes), FlipFlop and Frobenius factor estimation from the 4096 paired
+    calibration rows (two iterations), and the KronQ BiIP transforms."""
+    import synth
+    import two_sided_gptq_damped_amd as kq
+    from two_sided_gptq_damped_amd import pipeline
+
+    dev = "cuda"
+    c = synth.llm(4096, 4096, 2, config=3)
+    W, act, grad = up(c["W"], np.float32), up(c["act"], np.float32), up(c["grad"], np.float32)
+    m, n = W.shape
+    A, B = pipeline.factor(act), pipeline.factor(grad)
+    UA, _, _ = pipeline.prepare(A, 0.01)
+    UB, _, _ = pipeline.prepare(B, 0.01)
+
+    def timed(fn, reps=5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(reps + 1):
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts[1:]))
+
+    # WaterKron: step = the spread of W / (U_B,ii U_A,jj)
+    dA = torch.diagonal(UA).double()
+    dB = torch.diagonal(UB).double()
+    step = float(torch.sqrt(torch.mean((W.double() / torch.outer(dB, dA)) ** 2)))
+    alpha, beta = torch.empty(n, device=dev), torch.empty(m, device=dev)
+    kq.kron_waterkron_scales(UA, UB, step, alpha, beta)
+    codes = torch.empty(m, n, dtype=torch.int32, device=dev)
+    V = torch.empty_like(W)
+    ws = kq.workspace(kq.KQ_OP_QUANTIZE, W.dtype, m, n)
+    loss = torch.zeros(1, dtype=torch.float64, device=dev)
+    ms = timed(lambda: kq.kron_quantize_waterkron(W, UA, UB, alpha, beta, codes, V, ws, loss=loss))
+    _, counts = torch.unique(codes, return_counts=True)
+    p = counts.double() / counts.sum()
+    entropy = float(-(p * torch.log2(p)).sum())
+    F = float(m) * n * (m + n - 2)
+    print(json.dumps({"entry": "kron_quantize_waterkron", "shape": "4096x4096 fp32", "step": step, "ms": ms,
+                      "weights_per_s": m * n / (ms * 1e-3), "frac_fp32_mfma_peak": F / (ms * 1e-3) / PEAK_FP32_MFMA,
+                      "entropy_bits_per_weight": entropy, "loss": float(loss.item()),
+                      "loss_over_mn_step2_12": float(loss.item()) / (m * n * step ** 2 / 12)}), flush=True)
+    del codes, V, ws
+    # FlipFlop / Frobenius factors from the paired rows
+    for name, method in (("flipflop", kq.KQ_KRON_FLIPFLOP), ("frobenius", kq.KQ_KRON_FROBENIUS)):
+        Ak, Bk = torch.empty_like(A), torch.empty_like(B)
+        wsk = kq.kronecker_workspace(torch.float32, act.shape[0], n, m)
+        ms = timed(lambda: kq.kron_factor_kronecker(act, grad, method, 2, 0.01, Ak, Bk, wsk, info=None), reps=3)
+        print(json.dumps({"entry": "kron_factor_kronecker", "method": name, "iterations": 2,
+                          "samples": int(act.shape[0]), "n": n, "m": m, "ms": ms}), flush=True)
+        del Ak, Bk, wsk
+    # BiIP: every pass reads and writes its matrix once; 4 passes per matrix
+    g = torch.Generator(device="cpu").manual_seed(3011)
+    sn = (torch.randint(0, 2, (n,), generator=g, dtype=torch.int8) * 2 - 1).to(dev)
+    sm = (torch.randint(0, 2, (m,), generator=g, dtype=torch.int8) * 2 - 1).to(dev)
+    Wo, Ao, Bo = torch.empty_like(W), torch.empty_like(A), torch.empty_like(B)
+    sa, sb = torch.empty(n, device=dev), torch.empty(m, device=dev)
+    wsb = kq.biip_workspace(torch.float32, m, n)
+    V2 = torch.empty_like(W)
+    ms_f = timed(lambda: kq.kron_biip_forward(W, A, B, sn, sm, Wo, Ao, Bo, sa, sb, wsb))
+    ms_i = timed(lambda: kq.kron_biip_inverse(Wo, sn, sm, sa, sb, V2, wsb))
+    moved = 4 * 2 * 4 * (m * n + n * n + m * m)  # bytes: 4 passes x (read + write) x fp32
+    print(json.dumps({"entry": "kron_biip_forward / kron_biip_inverse", "shape": "4096x4096 fp32",
+                      "forward_ms": ms_f, "inverse_ms": ms_i,
+                      "forward_gb_per_s": moved / (ms_f * 1e-3) / 1e9,
+                      "note": "forward transforms W, A and B; bytes counted as 4 passes (two row transforms, two "
+                              "transposes), each reading and writing the matrix once"}), flush=True)
 
 
 def core_calls(torch, args):
@@ -481,8 +558,24 @@ def copy_probe(torch, nbytes):
     return 0
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(c, bits):
-    from oracle import dense, o3
+    """The CPU oracle as it stands, on the host cores: the whole 4096 x 4096
+    workload once (numpy fp64 factors, inverse and Cholesky; the C left-looking
+    loop with OpenMP; the loss), then two small extras: the loop's own fp32
+    variant on the same layer (its mismatch against fp64, the fp32 floor) and the
+    256 x 256 spectral problem on one thread."""
+    from oracle import compare, dense, o3
+    import synth
     threads = len(os.sched_getaffinity(0))
     m, n = c["m"], c["n"]
     W = c["W"].astype(np.float32).astype(np.float64)
@@ -499,6 +592,14 @@ def cpu_baseline(c, bits):
     t2 = time.perf_counter()
     dense.proxy_loss(W, V, Ad, Bd)
     t3 = time.perf_counter()
+    Z32 = o3.solve(W, UA, UB, s, bits, dtype=np.float32, threads=threads)[0]
+    t4 = time.perf_counter()
+    sp = synth.spectral()
+    _, UAs = dense.prepare(sp["A"], 0.01)
+    _, UBs = dense.prepare(sp["B"], 0.01)
+    t5 = time.perf_counter()
+    o3.solve(sp["W"], UAs, UBs, dense.scales(sp["W"], 3, True), 3, threads=1)
+    t6 = time.perf_counter()
     return {
         "value": m * n / (t3 - t0),
         "unit": "weights/s",
@@ -507,7 +608,11 @@ def cpu_baseline(c, bits):
         "sample": f"the whole {m}x{n} workload, once: numpy fp64 factors/inverse/Cholesky "
                   f"({t1 - t0:.2f} s), C left-looking loop fp64 with OpenMP ({t2 - t1:.2f} s), "
                   f"loss ({t3 - t2:.2f} s)",
+        "cpu_model": cpu_model(),
         "core_weights_per_s": m * n / (t2 - t1),
+        "fp32_loop_s": t4 - t3,
+        "fp32_floor_mismatch": compare.mismatch_fraction(Z32, Z),
+        "spectral_256_one_thread_s": t6 - t5,
     }
 
 

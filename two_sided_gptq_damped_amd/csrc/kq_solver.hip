@@ -25,7 +25,8 @@
 // Workspace layout (row-major, padded to multiples of 64 with zero weights,
 // unit scales and identity factors, so padding never reaches a real entry):
 //   NA  np x np   normalised input factor
-//   NB  mp x mp   normalised output factor (absent when B = I)
+//   NB  mp x mp   normalised output factor
+// (B = I does not come here: kron_quantize runs the one-sided path for it.)
 //   X   mp x np   running pre-rounding values (starts as W)
 //   D   mp x np   errors Delta
 //   T1  mp x np   stage-1 products
@@ -114,7 +115,7 @@ struct Vec4<double> {
 //   rowpart = sum_{c0 - I <= J' < J} Delta[I, J'] N_A[J', J]
 //   X[I, J] += N_B[I, I]^T rowpart + sum_{c0 - J <= I' < I} N_B[I', I]^T T1c[I', J]
 // and after the sweep the leaf writes T1c[I, J] = rowpart + Delta[I, J] N_A[J, J]
-// for the later diagonals of its chunk.  With B = I only rowpart is added.  The
+// for the later diagonals of its chunk.  The
 // 32 x 32 x 32 products run on the matrix cores: their operands are staged
 // k-major in LDS and each wave owns one 16 x 16 quadrant of one of the two sums,
 // over all of its slices, so the sums need no reduction across waves.
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     const int jl = c0 - I > 0 ? c0 - I : 0;
     const int il = c0 - J > 0 ? c0 - J : 0;
     const int n1 = J - jl;
-    const int n2 = NB ? I - il : 0;
+    const int n2 = I - il;
     const int ns = n1 + n2;
     constexpr int NFG = LEAF_THREADS / 256;
     constexpr int SLOTS = (BATCH + NFG - 1) / NFG;  // slices of a batch held by one thread
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
 #pragma unroll
     for (int u = 0; u < FE; ++u) {
         const int e = t + u * LEAF_THREADS, r = e >> 5, c = e & 31;
-        const T nb = NB ? NB[int64_t(I * ST + r) * mp + I * ST + c] : T(0);
+        const T nb = NB[int64_t(I * ST + r) * mp + I * ST + c];
         fnb[u] = r == c ? T(0) : nb;
         sNB[r * PB + c] = fnb[u];
         const T na = NA[int64_t(J * ST + r) * np + J * ST + c];
@@ -375,11 +376,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     if (ns > 0) {
         // Wave wv owns the 16 x 16 quadrant qd = wv % 4 of one part: the row part
         // (rowpart) for wv < 4 and the column part for wv >= 4, accumulated over all
-        // of that part's slices, so no partial sums cross waves.  With B = I there
-        // is no column part: the two halves take the row slices of even and odd
-        // index and their quadrants are added once at the end.
+        // of that part's slices, so no partial sums cross waves.
         const int part = wv >> 2, qd = wv & 3, qr = 16 * (qd >> 1), qc = 16 * (qd & 1);
-        const bool split = NB == nullptr;
         Q16<T> pq;
         pq.zero();
         for (int sb = 0; sb < ns; sb += BATCH) {
@@ -405,29 +403,23 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
                 }
             }
             __syncthreads();
-            // this wave's slices of the batch: its part's, or every other one
+            // this wave's slices of the batch: those of its part
             const int nbat = ns - sb < BATCH ? ns - sb : BATCH;
-            int u0, u1, du;
-            if (split) {
-                u0 = (sb + part) & 1 ? 1 : 0;
-                u1 = nbat;
-                du = 2;
-            } else if (part == 0) {
+            int u0, u1;
+            if (part == 0) {
                 u0 = 0;
                 u1 = n1 - sb < nbat ? (n1 - sb > 0 ? n1 - sb : 0) : nbat;
-                du = 1;
             } else {
                 u0 = n1 - sb > 0 ? n1 - sb : 0;
                 u1 = nbat;
-                du = 1;
             }
-            for (int u = u0; u < u1; u += du)
+            for (int u = u0; u < u1; ++u)
                 pq.template mma<PK, PK, ST>(stg[u][0] + qr, stg[u][1] + qc, lane);
         }
         // the quadrants reach the block layout through the staging area:
         // park[0] = rowpart (also the right operand of the in-tile column
         // feedback), park[1] = the column part
-        const bool nbs = NB && n1 > 0;  // the in-tile column feedback strict(N_B[I, I])^T rowpart
+        const bool nbs = n1 > 0;  // the in-tile column feedback strict(N_B[I, I])^T rowpart
         T* park = reinterpret_cast<T*>(stg);
         static_assert(sizeof(stg) >= 2 * ST * ST * sizeof(T), "staging area too small");
         auto park_quadrant = [&]() {
@@ -450,8 +442,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const T p0 = park[(r0 + i) * ST + b], p1 = park[ST * ST + (r0 + i) * ST + b];
-                crow[i] = split ? p0 + p1 : p0;
-                ccol[i] = split ? T(0) : p1;
+                crow[i] = p0;
+                ccol[i] = p1;
             }
         }
 #pragma unroll
@@ -671,7 +663,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         }
     }
     // ---- chunk epilogue: T1c[I, J] = rowpart + Delta + Delta strict(N_A[J, J])
-    if (NB && K + 1 < c1) {
+    if (K + 1 < c1) {
         T o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = crow[i] + dblk[i];
@@ -777,15 +769,6 @@ __global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T*
         return ip < mid && k >= K0 && k < K1;
     };
     T* out = X + int64_t(I0) * ST * np + int64_t(J0) * ST;
-    if (!NB) {
-        const T* src = T1 + int64_t(I0) * ST * np + int64_t(J0) * ST;
-        for (int e = threadIdx.x; e < TILE * TILE; e += Band<T>::THREADS2) {
-            const int r = e >> 6, c = e & 63;
-            if (in_band(r, c) && t1_valid(I0 + (r >> 5), J0 + (c >> 5)))
-                out[int64_t(r) * np + c] += src[int64_t(r) * np + c];
-        }
-        return;
-    }
     const int kl = K0 - J0 - 1 > 0 ? K0 - J0 - 1 : 0;
     const int kh = I0 + 1 < mid - 1 ? I0 + 1 : mid - 1;
     if (kl > kh) return;
@@ -989,7 +972,7 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
     const SolverLayout L = solver_layout(sizeof(T) == 8 ? KQ_F64 : KQ_F32, m, n);
     char* base = static_cast<char*>(ws);
     SolverRun<T> run{L, int(m), int(n), q.qmin, q.qmax,
-                     reinterpret_cast<T*>(base + L.off_NA), UB ? reinterpret_cast<T*>(base + L.off_NB) : nullptr,
+                     reinterpret_cast<T*>(base + L.off_NA), reinterpret_cast<T*>(base + L.off_NB),
                      reinterpret_cast<T*>(base + L.off_X), reinterpret_cast<T*>(base + L.off_D),
                      reinterpret_cast<T*>(base + L.off_T1), reinterpret_cast<T*>(base + L.off_S),
                      q.col_scales ? reinterpret_cast<T*>(base + L.off_C) : nullptr, q.codes, q.ldc, V, ldv, st};
