@@ -12,13 +12,20 @@
 // I + J = K form tile-diagonal K and are independent for the same reason.
 // solve(K0, K1) over tile-diagonal ranges follows section 2.5's recursion:
 // solve(K0, mid); add the errors of the first half to the second half with two
-// batched products; solve(mid, K1):
-//   stage 1  T1[I', J] = sum_{J' : K0 <= I'+J' < mid} Delta[I', J'] N_A[J', J]
-//            for the tiles (I', J) a target can read (K0 <= I'+J < K1, I' < mid)
-//   stage 2  X[I, J] += sum_{I'} N_B[I', I]^T T1[I', J] for mid <= I+J < K1.
-// Both stages run on 64 x 64 matrix-core output blocks (2 x 2 scheduling tiles)
-// and mask at 32-tile granularity: source tiles outside the band and T1 tiles not
-// written by this node read as zero, targets outside the band are not written.
+// batched products; solve(mid, K1).  The feedback is separable: the error
+// Delta[I', J'] reaches X[I, J] as N_B[I', I]^T Delta[I', J'] N_A[J', J].  R[I', J]
+// holds the row-propagated errors sum_{J' <= J} Delta[I', J'] N_A[J', J] of tile
+// (I', J): it is accumulated by the nodes before the tile's chunk and completed by
+// the tile's leaf.  At node [K0, K1) with split mid, for the targets of
+// diagonals [mid, K1):
+//   stage 1  R[I', J] += sum_{J' : K0 <= I'+J' < mid} Delta[I', J'] N_A[J', J]
+//   stage 2  X[I, J] += sum_{I' : K0 <= I'+J < mid} N_B[I', I]^T R[I', J]
+// (stage 2 reads only left-half tiles, whose R is complete).  Each (source,
+// target) pair passes through one stage-1 or leaf row product and one stage-2
+// or leaf column product, so the band work is the method's own m n (m + n) up to
+// tile granularity.  Both stages run on 64 x 64 matrix-core output blocks
+// (2 x 2 scheduling tiles) and mask at 32-tile granularity: source tiles outside
+// the band read as zero, targets outside the band are not written.
 // A leaf is one tile-diagonal: each 32 x 32 tile runs the element-level
 // anti-diagonal sweep (63 steps) with the in-tile feedback, one workgroup per tile.
 //
@@ -29,7 +36,8 @@
 // (B = I does not come here: kron_quantize runs the one-sided path for it.)
 //   X   mp x np   running pre-rounding values (starts as W)
 //   D   mp x np   errors Delta
-//   T1  mp x np   stage-1 products
+//   R   mp x np   row-propagated errors (zero at the start)
+//   P   2 x min(Mt, Nt) x 2 x 32 x 32   the leaves' pre-accumulated chunk products
 //   S   mp        per-row scales
 //   C   np        per-column scales (the WaterKron mode only; unit in the padding)
 // In the WaterKron mode (kron_quantize_waterkron) entry (i, j) has the grid step
@@ -41,7 +49,7 @@
 namespace kq {
 
 constexpr int ST = 32;    // scheduling tile edge
-constexpr int CHUNK = 8;  // tile-diagonals per recursion leaf (chunk)
+constexpr int CHUNK = 16;  // tile-diagonals per recursion leaf (chunk)
 
 // N[r][c] = U[r][c] / U[r][r] for c >= r inside d x d; identity in the padding.
 // Rows blockIdx.y, + gridDim.y, ...; each thread four consecutive columns (dp is
@@ -53,7 +61,7 @@ __global__ void normalize_factor_kernel(const T* __restrict__ U, int64_t ldu, in
 template <typename T>
 __global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, int n, int mp, int np,
                                    const T* __restrict__ scales, int per_row, const T* __restrict__ col_scales,
-                                   T* __restrict__ X, T* __restrict__ S, T* __restrict__ C);
+                                   T* __restrict__ X, T* __restrict__ S, T* __restrict__ C, T* __restrict__ R);
 
 // Four consecutive elements (16-byte aligned), from global memory or LDS.
 template <typename T>
@@ -108,14 +116,13 @@ struct Vec4<double> {
 // Chunks.  The recursion stops at chunks of consecutive tile-diagonals
 // [c0, c1); inside a chunk the feedback between tiles is pulled by each leaf
 // (left-looking, the per-entry form of section 2.4 at tile granularity).  For
-// tile (I, J) on diagonal K of the chunk, with the chunk-local row-propagated
-// errors
-//   T1c[I', J] = sum_{J' <= J, I' + J' >= c0} Delta[I', J'] N_A[J', J]
-// (written by tile (I', J)'s own leaf), the chunk's contribution is
-//   rowpart = sum_{c0 - I <= J' < J} Delta[I, J'] N_A[J', J]
-//   X[I, J] += N_B[I, I]^T rowpart + sum_{c0 - J <= I' < I} N_B[I', I]^T T1c[I', J]
-// and after the sweep the leaf writes T1c[I, J] = rowpart + Delta[I, J] N_A[J, J]
-// for the later diagonals of its chunk.  The
+// tile (I, J) on diagonal K of the chunk:
+//   rowpart = R[I, J] + sum_{c0 - I <= J' < J} Delta[I, J'] N_A[J', J]
+//   X[I, J] += N_B[I, I]^T rowpart + sum_{c0 - J <= I' < I} N_B[I', I]^T R[I', J]
+// (R[I', J] of the chunk's earlier tiles is complete), and after the sweep the
+// leaf writes R[I, J] = rowpart + Delta[I, J] N_A[J, J].  The sums over the
+// slices before diagonal K - 1 are pre-accumulated by launch K - 1 (see the
+// kernel), so the leaf itself multiplies only the two freshest slices.  The
 // 32 x 32 x 32 products run on the matrix cores: their operands are staged
 // k-major in LDS and each wave owns one 16 x 16 quadrant of one of the two sums,
 // over all of its slices, so the sums need no reduction across waves.
@@ -185,12 +192,12 @@ __global__ void normalize_factor_kernel(const T* __restrict__ U, int64_t ldu, in
 }
 
 // X = W zero-padded to mp x np; S = the scales, unit in the padding; with column
-// scales, C = them, unit in the padding.  Rows as in normalize_factor_kernel,
+// scales, C = them, unit in the padding; R (when given) = 0.  Rows as in normalize_factor_kernel,
 // four consecutive columns per thread.
 template <typename T>
 __global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, int n, int mp, int np,
                                    const T* __restrict__ scales, int per_row, const T* __restrict__ col_scales,
-                                   T* __restrict__ X, T* __restrict__ S, T* __restrict__ C) {
+                                   T* __restrict__ X, T* __restrict__ S, T* __restrict__ C, T* __restrict__ R) {
     const int c0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
     if (col_scales && blockIdx.y == 0 && c0 < np) {
 #pragma unroll
@@ -203,6 +210,11 @@ __global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, 
 #pragma unroll
         for (int u = 0; u < 4; ++u) v.set(u, (r < m && c0 + u < n) ? W[int64_t(r) * ldw + c0 + u] : T(0));
         v.store(X + int64_t(r) * np + c0);
+        if (R) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v.set(u, T(0));
+            v.store(R + int64_t(r) * np + c0);
+        }
     }
 }
 
@@ -235,6 +247,7 @@ struct Q16<float> {
             c = __builtin_amdgcn_mfma_f32_16x16x4f32(As[(kk + kr) * SA + ix], Bs[(kk + kr) * SB + ix], c, 0, 0, 0);
     }
     __device__ float get(int r) const { return c[r]; }
+    __device__ void set(int r, float v) { c[r] = v; }
     static __device__ __forceinline__ int row(int r, int lane) { return 4 * (lane >> 4) + r; }
     static __device__ __forceinline__ int col(int, int lane) { return lane & 15; }
 };
@@ -250,6 +263,7 @@ struct Q16<double> {
             c = __builtin_amdgcn_mfma_f64_16x16x4f64(As[(kk + kr) * SA + ix], Bs[(kk + kr) * SB + ix], c, 0, 0, 0);
     }
     __device__ double get(int r) const { return c[r]; }
+    __device__ void set(int r, double v) { c[r] = v; }
     static __device__ __forceinline__ int row(int r, int lane) { return (lane >> 4) + 4 * r; }
     static __device__ __forceinline__ int col(int, int lane) { return lane & 15; }
 };
@@ -265,10 +279,10 @@ template <typename T, bool ENTRY>
 __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
                                                    const T* __restrict__ NA, const T* __restrict__ NB,
                                                    const T* __restrict__ S, const T* __restrict__ CS,
-                                                   T* __restrict__ T1c, int np, int mp, int Mt, int Nt, int K,
+                                                   T* __restrict__ R, int np, int mp, int Mt, int Nt, int K,
                                                    int c0, int c1, int m, int n, int qmin, int qmax,
                                                    CodeT<ENTRY>* __restrict__ Z, int64_t ldz, T* __restrict__ V,
-                                                   int64_t ldv) {
+                                                   int64_t ldv, T* __restrict__ P, int pt) {
     constexpr int PB = ST + 4;  // 16-byte aligned rows for the vector reads
     constexpr int PA = ST + 1;  // column ST is the zero sentinel
     constexpr int PK = ST + 4;  // k-major staging rows, 16-byte aligned
@@ -277,44 +291,63 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     constexpr int RD = 2 * LEAF_E;                      // diagonals per sweep round (one wave's two groups)
     constexpr int NROUND = (2 * ST - 1 + RD - 1) / RD;  // sweep rounds
     // chunk operands of up to BATCH slices: A(r, k) at [k][r], B(k, c) at [k][c]
-    constexpr int MAXS = 2 * (CHUNK - 1);                  // most slices a leaf needs
-    constexpr int BATCH = sizeof(T) == 4 ? MAXS : MAXS / 2;  // staged together (LDS budget)
+    constexpr int BATCH = sizeof(T) == 4 ? 14 : 7;  // staged together (LDS budget)
     __shared__ __attribute__((aligned(16))) T stg[BATCH][2][ST * PK];
     T* const bufA = stg[0][0];
     T* const bufB = stg[0][1];
 
+    // Launch K: workgroups [0, nk) sweep the tiles of diagonal K.  When diagonal
+    // K + 1 lies in the same chunk, workgroups [nk, nk + nk1) pre-accumulate its
+    // tiles' chunk products over every slice that is final before this launch
+    // (all but the two on diagonal K) into P, so that leaf K + 1 adds only the
+    // freshest two slices.  P holds two diagonals, alternating with K's parity.
     const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
-    const int I = ilo + blockIdx.x;
     const int ihi = K < Mt - 1 ? K : Mt - 1;
-    if (I > ihi) return;
-    const int J = K - I;
+    const int nk = ihi - ilo + 1;
+    const bool pre = int(blockIdx.x) >= nk;
+    const int Kt = pre ? K + 1 : K;  // the tile's diagonal
+    const int idx = pre ? int(blockIdx.x) - nk : int(blockIdx.x);
+    const int I = (Kt - Nt + 1 > 0 ? Kt - Nt + 1 : 0) + idx;
+    if (I > (Kt < Mt - 1 ? Kt : Mt - 1)) return;
+    const int J = Kt - I;
     // threads t < 256 also work in the block layout (four rows each); all
     // LEAF_THREADS threads take part in the sweep
     const int t = threadIdx.x, tb = t & 255, w = tb >> 6, l = tb & 63;
     const bool blk = t < 256;
     const int b = l & 31, r0 = 8 * w + 4 * (l >> 5);
     const int fgrp = t >> 8;                    // staging loads: slices rotate over the 256-thread groups
-    const int wv = t >> 6, lane = t & 63;  // chunk products: wave, lane
+    const int wv = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;  // wave (uniform: scalar branches), lane
     const int q8 = tb >> 3, c4 = 4 * (tb & 7);  // this thread's share of a 32 x 32 staging load
+    // chunk products: wave wv owns the 16 x 16 quadrant qd = wv % 4 of one part, the
+    // row part (rowpart) for wv < 4 and the column part for wv >= 4, accumulated
+    // over all of that part's slices, so no partial sums cross waves
+    const int part = wv >> 2, qd = wv & 3, qr = 16 * (qd >> 1), qc = 16 * (qd & 1);
+    T* const Pt = P + (int64_t((Kt & 1) * pt + idx) * 2 + part) * ST * ST + qr * ST + qc;
 
-    // chunk sources: row tiles J' in [jl, J), column tiles I' in [il, I)
+    // chunk sources of the tile: row tiles J' in [jl, J), column tiles I' in [il, I);
+    // the freshest of each (J - 1, I - 1) lies on diagonal Kt - 1
     const int jl = c0 - I > 0 ? c0 - I : 0;
     const int il = c0 - J > 0 ? c0 - J : 0;
-    const int n1 = J - jl;
-    const int n2 = I - il;
+    const int n1all = J - jl;
+    const int n2all = I - il;
+    // the slices this workgroup multiplies: row slices [jb, jb + n1), column
+    // slices [ib, ib + n2) (the older ones here, the freshest in the leaf)
+    const int jb = pre ? jl : J - 1, ib = pre ? il : I - 1;
+    const int n1 = pre ? (n1all > 1 ? n1all - 1 : 0) : (n1all > 0 ? 1 : 0);
+    const int n2 = pre ? (n2all > 1 ? n2all - 1 : 0) : (n2all > 0 ? 1 : 0);
     const int ns = n1 + n2;
     constexpr int NFG = LEAF_THREADS / 256;
     constexpr int SLOTS = (BATCH + NFG - 1) / NFG;  // slices of a batch held by one thread
     Vec4<T> pa[SLOTS], pb[SLOTS];
     auto fetch = [&](int sl, Vec4<T>& va, Vec4<T>& vb) {
         if (sl < n1) {
-            const int jp = jl + sl;
+            const int jp = jb + sl;
             va.load(D + int64_t(I * ST + q8) * np + jp * ST + c4);   // A(r = q8, k = c4 + j)
             vb.load(NA + int64_t(jp * ST + q8) * np + J * ST + c4);  // B(k = q8, c = c4 + j)
         } else {
-            const int ip = il + sl - n1;
+            const int ip = ib + sl - n1;
             va.load(NB + int64_t(ip * ST + q8) * mp + I * ST + c4);  // A(r = c4 + j, k = q8)
-            vb.load(T1c + int64_t(ip * ST + q8) * np + J * ST + c4); // B(k = q8, c = c4 + j)
+            vb.load(R + int64_t(ip * ST + q8) * np + J * ST + c4);   // B(k = q8, c = c4 + j)
         }
     };
     // every load of the first batch is in flight before anything waits on one
@@ -323,6 +356,68 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         const int u = NFG * v + fgrp;
         if (u < BATCH && u < ns) fetch(u, pa[v], pb[v]);
     }
+    // pq += this wave's part over the workgroup's slices, staged in batches
+    auto products = [&](Q16<T>& pq) {
+        for (int sb = 0; sb < ns; sb += BATCH) {
+            if (sb > 0) {
+                __syncthreads();  // the previous batch is consumed
+#pragma unroll
+                for (int v = 0; v < SLOTS; ++v) {
+                    const int u = NFG * v + fgrp;
+                    if (u < BATCH && sb + u < ns) fetch(sb + u, pa[v], pb[v]);
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < SLOTS; ++v) {
+                const int u = NFG * v + fgrp;
+                if (u < BATCH && sb + u < ns) {
+                    if (sb + u < n1) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) stg[u][0][(c4 + j) * PK + q8] = pa[v][j];
+                    } else {
+                        pa[v].store(stg[u][0] + q8 * PK + c4);
+                    }
+                    pb[v].store(stg[u][1] + q8 * PK + c4);
+                }
+            }
+            __syncthreads();
+            // this wave's slices of the batch: those of its part
+            const int nbat = ns - sb < BATCH ? ns - sb : BATCH;
+            int u0, u1;
+            if (part == 0) {
+                u0 = 0;
+                u1 = n1 - sb < nbat ? (n1 - sb > 0 ? n1 - sb : 0) : nbat;
+            } else {
+                u0 = n1 - sb > 0 ? n1 - sb : 0;
+                u1 = nbat;
+            }
+            for (int u = u0; u < u1; ++u)
+                pq.template mma<PK, PK, ST>(stg[u][0] + qr, stg[u][1] + qc, lane);
+        }
+    };
+    // the row part starts from R[I, J]: the row-propagated errors of every source
+    // before the chunk, accumulated by the band products of the recursion
+    T* const Rt = R + int64_t(I * ST + qr) * np + J * ST + qc;
+    if (pre) {
+        Q16<T> pq;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            pq.set(r, part == 0 ? Rt[int64_t(Q16<T>::row(r, lane)) * np + Q16<T>::col(r, lane)] : T(0));
+        products(pq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Pt[Q16<T>::row(r, lane) * ST + Q16<T>::col(r, lane)] = pq.get(r);
+        return;
+    }
+    // the leaf: this wave's quadrant of the pre-accumulated products, or at the
+    // chunk's first diagonal (no chunk sources) R[I, J] alone
+    // (one wave-uniform source and stride, so the loads need no select)
+    const T* const psrc = K > c0 ? Pt : Rt;
+    const int pld = K > c0 ? ST : np;
+    const bool pzero = K == c0 && part == 1;
+    T pin[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        pin[r] = pzero ? T(0) : psrc[Q16<T>::row(r, lane) * pld + Q16<T>::col(r, lane)];
 
     constexpr int FE = ST * ST / LEAF_THREADS;  // factor-block entries per thread
     T fnb[FE], fna[FE];                         // kept for the sweep's tables
@@ -372,54 +467,15 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     }
     __syncthreads();
 
-    // ---- chunk prologue: rowpart (crow) and the column feedback (ccol), block layout
-    if (ns > 0) {
-        // Wave wv owns the 16 x 16 quadrant qd = wv % 4 of one part: the row part
-        // (rowpart) for wv < 4 and the column part for wv >= 4, accumulated over all
-        // of that part's slices, so no partial sums cross waves.
-        const int part = wv >> 2, qd = wv & 3, qr = 16 * (qd >> 1), qc = 16 * (qd & 1);
+    // ---- prologue: rowpart (crow) and the column feedback (ccol), block layout
+    {
         Q16<T> pq;
-        pq.zero();
-        for (int sb = 0; sb < ns; sb += BATCH) {
-            if (sb > 0) {
-                __syncthreads();  // the previous batch is consumed
 #pragma unroll
-                for (int v = 0; v < SLOTS; ++v) {
-                    const int u = NFG * v + fgrp;
-                    if (u < BATCH && sb + u < ns) fetch(sb + u, pa[v], pb[v]);
-                }
-            }
-#pragma unroll
-            for (int v = 0; v < SLOTS; ++v) {
-                const int u = NFG * v + fgrp;
-                if (u < BATCH && sb + u < ns) {
-                    if (sb + u < n1) {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) stg[u][0][(c4 + j) * PK + q8] = pa[v][j];
-                    } else {
-                        pa[v].store(stg[u][0] + q8 * PK + c4);
-                    }
-                    pb[v].store(stg[u][1] + q8 * PK + c4);
-                }
-            }
-            __syncthreads();
-            // this wave's slices of the batch: those of its part
-            const int nbat = ns - sb < BATCH ? ns - sb : BATCH;
-            int u0, u1;
-            if (part == 0) {
-                u0 = 0;
-                u1 = n1 - sb < nbat ? (n1 - sb > 0 ? n1 - sb : 0) : nbat;
-            } else {
-                u0 = n1 - sb > 0 ? n1 - sb : 0;
-                u1 = nbat;
-            }
-            for (int u = u0; u < u1; ++u)
-                pq.template mma<PK, PK, ST>(stg[u][0] + qr, stg[u][1] + qc, lane);
-        }
+        for (int r = 0; r < 4; ++r) pq.set(r, pin[r]);
+        products(pq);  // the freshest slices
         // the quadrants reach the block layout through the staging area:
         // park[0] = rowpart (also the right operand of the in-tile column
         // feedback), park[1] = the column part
-        const bool nbs = n1 > 0;  // the in-tile column feedback strict(N_B[I, I])^T rowpart
         T* park = reinterpret_cast<T*>(stg);
         static_assert(sizeof(stg) >= 2 * ST * ST * sizeof(T), "staging area too small");
         auto park_quadrant = [&]() {
@@ -428,14 +484,13 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
             for (int r = 0; r < 4; ++r) q[Q16<T>::row(r, lane) * ST + Q16<T>::col(r, lane)] = pq.get(r);
         };
         __syncthreads();  // staged operands consumed
-        if (part == 0 || !nbs) park_quadrant();
-        if (nbs) {
-            __syncthreads();  // rowpart complete
-            if (part == 1) {
-                // strict(N_B[I, I])^T (r, k) = N_B[k][r], k-major in sNB already
-                pq.template mma<PB, ST, ST>(sNB + qr, park + qc, lane);
-                park_quadrant();
-            }
+        if (part == 0) park_quadrant();
+        __syncthreads();  // rowpart complete
+        if (part == 1) {
+            // the in-tile column feedback strict(N_B[I, I])^T rowpart;
+            // strict(N_B[I, I])^T (r, k) = N_B[k][r], k-major in sNB already
+            pq.template mma<PB, ST, ST>(sNB + qr, park + qc, lane);
+            park_quadrant();
         }
         __syncthreads();
         if (blk) {
@@ -620,10 +675,9 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     auto producer = [&](int r) { return (RD * r & (ST - 1)) / RD; };  // wave of groups 2 w, 2 w + 1
     // coefficients of round r (cnb / cna, its feedback) and of round r + 1 (read
     // after round r's barrier, for the next producer's chain)
-    const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform: scalar branches on the producer
     T cnb[RD][E], cna[RD][E];
     coef(0, cnb, cna);
-    if (wvu == producer(0)) chain(0, cnb, cna);
+    if (wv == producer(0)) chain(0, cnb, cna);
 #pragma unroll
     for (int r = 0; r < NROUND; ++r) {
         __syncthreads();  // round r's errors are published
@@ -634,7 +688,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         for (int j = 0; j < E; ++j) dd[j].load(xD + (r * ST + ar[j]) * RD);
         T nnb[RD][E], nna[RD][E];
         coef(RD * (r + 1), nnb, nna);
-        if (wvu == producer(r + 1)) {
+        if (wv == producer(r + 1)) {
             feedback(rv, dd, cnb, cna);
             chain(r + 1, nnb, nna);
         } else {
@@ -662,8 +716,10 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
             V[gi * ldv + gj] = sblk[i] * z;
         }
     }
-    // ---- chunk epilogue: T1c[I, J] = rowpart + Delta + Delta strict(N_A[J, J])
-    if (K + 1 < c1) {
+    // ---- epilogue: R[I, J] = rowpart + Delta + Delta strict(N_A[J, J]), the
+    // tile's complete row-propagated errors, read by the later leaves of the
+    // chunk and by the band products of the later nodes
+    {
         T o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = crow[i] + dblk[i];
@@ -676,11 +732,16 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
             for (int i = 0; i < 4; ++i) o[i] = kfma(d4[i], nak, o[i]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) T1c[int64_t(I * ST + r0 + i) * np + J * ST + b] = o[i];
+        for (int i = 0; i < 4; ++i) R[int64_t(I * ST + r0 + i) * np + J * ST + b] = o[i];
     }
 }
 
-// Stage 1 at node [K0, K1) with split mid, on 64-row block P and 64-column block Q.
+// Stage 1 at node [K0, K1) with split mid: for the target tiles (I', J) of
+// diagonals [mid, K1),
+//   R[I', J] += sum_{J' : K0 <= I' + J' < mid} Delta[I', J'] N_A[J', J],
+// on 64-row block P and 64-column block Q.  R starts at zero; it gathers each
+// tile's row-propagated errors over the nodes whose left half holds a source of
+// the tile's row, and the tile's leaf completes it.
 // Band GEMMs run split-K inside the workgroup: their launches have few blocks
 // with long K ranges in the lower recursion levels, so each block gets G = 2
 // groups of four waves (deterministic reduction, see tile_gemm_masked_splitk).
@@ -698,16 +759,17 @@ struct Band {
 template <typename T>
 __global__ __launch_bounds__(Band<T>::THREADS) void band_stage1_kernel(const T* __restrict__ D,
                                                                        const T* __restrict__ NA,
-                                                                       T* __restrict__ T1, int np, int Nt, int K0,
+                                                                       T* __restrict__ R, int np, int Nt, int K0,
                                                                        int mid, int K1, int P0) {
     __shared__ SplitSmem<T, Band<T>::G> sm;
     const int P = P0 + blockIdx.y;
     const int I0 = 2 * P;  // first 32-row tile of the block
     const int jlo = K0 - I0 - 1 > 0 ? K0 - I0 - 1 : 0;
     const int jend = K1 - I0 < Nt ? K1 - I0 : Nt;  // exclusive, over both rows
+    const int qlo = (mid - I0 - 1 > 0 ? mid - I0 - 1 : 0) >> 1;  // first block with a target in [mid, K1)
     // the row's last block first: its K range is the longest at the top node
     const int Q = ((jend - 1) >> 1) - int(blockIdx.x);
-    if (jend <= 0 || Q < (jlo >> 1)) return;
+    if (jend <= 0 || Q < qlo) return;
     const int kl = jlo;
     int kh = 2 * Q + 1;
     if (mid - 1 - I0 < kh) kh = mid - 1 - I0;
@@ -725,25 +787,34 @@ __global__ __launch_bounds__(Band<T>::THREADS) void band_stage1_kernel(const T* 
                                                              NoMask());
     }
     if (threadIdx.x >= 256) return;  // group 0 holds the product
-    T* out = T1 + int64_t(I0) * ST * np + int64_t(Q) * TILE;
-    for_each_acc(acc, [&](int r, int c, T v) { out[int64_t(r) * np + c] = v; });
+    T* out = R + int64_t(I0) * ST * np + int64_t(Q) * TILE;
+    for_each_acc(acc, [&](int r, int c, T v) {
+        const int k = I0 + (r >> 5) + 2 * Q + (c >> 5);  // the target tile's diagonal
+        if (k >= mid && k < K1) out[int64_t(r) * np + c] += v;
+    });
 }
 
-// Stage 2: X[I, J] += sum_{I'} N_B[I', I]^T T1[I', J] for the tiles of diagonals
-// [mid, K1), on 64 x 64 target block (P, Q) of block-diagonal sig = P + Q.
-// KS: K-slice depth of the product (16 at the top node, where many blocks share
-// each CU; 32 below, where a block's loads are its only latency hiding).
+// Stage 2 at node [K0, K1) with split mid: for the target tiles (I, J) of
+// diagonals [mid, K1),
+//   X[I, J] += sum_{I' : K0 <= I' + J < mid} N_B[I', I]^T R[I', J],
+// the column feedback of the left half's complete row-propagated tiles (every
+// source of R[I', J] lies on a diagonal before mid, so each of them was swept
+// already and R[I', J] is final).  Right-half sources reach X at the lower nodes
+// and in the leaves, so each (source, target) pair is applied once.  Tiles are
+// taken in 64 x 64 target blocks (P, Q) of block-diagonal sig = P + Q; the K
+// range of block (P, Q) spans at most mid - K0 + 1 source tiles, staged 32 deep
+// with two slices in flight (tile_gemm_masked_k2).
 // Block order: a 1-D grid walks the target blocks by block row P from the last
-// to the first (sig ascending within a row).  The K range of block (P, Q) grows
-// with P (at the top node it is 2 P + 2 tiles), so the long blocks are
-// dispatched first and the short ones fill in behind them, and no workgroup is
-// spent on an empty position.
-template <typename T, int KS>
-__global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T* __restrict__ T1,
+// to the first (sig ascending within a row), so the blocks with long K ranges
+// are dispatched first and the short ones fill in behind them, and no
+// workgroup is spent on an empty position.
+template <typename T>
+__global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T* __restrict__ R,
                                                                         const T* __restrict__ NB,
                                                                         T* __restrict__ X, int np, int mp, int Mt,
                                                                         int Nt, int K0, int mid, int K1, int sig0,
                                                                         int sig1) {
+    constexpr int KS = 2 * KSTEP;
     __shared__ GemmSmemK<T, KS> sm;
     const int Mb = Mt >> 1, Nb = Nt >> 1;
     int sig = 0, P = -1;
@@ -764,23 +835,20 @@ __global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T*
         const int k = I0 + (r >> 5) + J0 + (c >> 5);
         return k >= mid && k < K1;
     };
-    auto t1_valid = [=](int ip, int j) {  // T1 tile written by this node's stage 1
+    auto src_valid = [=](int ip, int j) {  // a complete tile R^[I', J] of the left half
         const int k = ip + j;
-        return ip < mid && k >= K0 && k < K1;
+        return k >= K0 && k < mid;
     };
     T* out = X + int64_t(I0) * ST * np + int64_t(J0) * ST;
     const int kl = K0 - J0 - 1 > 0 ? K0 - J0 - 1 : 0;
-    const int kh = I0 + 1 < mid - 1 ? I0 + 1 : mid - 1;
+    const int kh = I0 + 1 < mid - 1 - J0 ? I0 + 1 : mid - 1 - J0;
     if (kl > kh) return;
     WaveAcc<T> acc;
     acc.zero();
     const T* A = NB + int64_t(kl) * ST * mp + int64_t(I0) * ST;  // A(r, k) = NB[k][r]
-    const T* B = T1 + int64_t(kl) * ST * np + int64_t(J0) * ST;
-    auto mb = [=](int k, int c) { return t1_valid(kl + (k >> 5), J0 + (c >> 5)); };
-    if (KS == KSTEP)  // the top node: many blocks per CU hide the loads
-        tile_gemm_masked_k<T, KS, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
-    else
-        tile_gemm_masked_k2<T, KS, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
+    const T* B = R + int64_t(kl) * ST * np + int64_t(J0) * ST;
+    auto mb = [=](int k, int c) { return src_valid(kl + (k >> 5), J0 + (c >> 5)); };
+    tile_gemm_masked_k2<T, KS, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
     for_each_acc(acc, [&](int r, int c, T v) {
         if (in_band(r, c)) out[int64_t(r) * np + c] += v;
     });
@@ -841,7 +909,7 @@ __global__ __launch_bounds__(256) void error_loss_final_kernel(const double* __r
 struct SolverLayout {
     int64_t mp, np, Mt, Nt;  // padded extents; tile counts in 32-tiles
     size_t bytes;
-    size_t off_NA, off_NB, off_X, off_D, off_T1, off_S, off_C, off_L;
+    size_t off_NA, off_NB, off_X, off_D, off_R, off_P, off_S, off_C, off_L;
 };
 
 SolverLayout solver_layout(kq_dtype dtype, int64_t m, int64_t n) {
@@ -861,7 +929,9 @@ SolverLayout solver_layout(kq_dtype dtype, int64_t m, int64_t n) {
     L.off_NB = take(size_t(L.mp) * L.mp);
     L.off_X = take(size_t(L.mp) * L.np);
     L.off_D = take(size_t(L.mp) * L.np);
-    L.off_T1 = take(size_t(L.mp) * L.np);
+    L.off_R = take(size_t(L.mp) * L.np);
+    // the leaves' pre-accumulated chunk products: two tile-diagonals of two parts
+    L.off_P = take(size_t(2 * 2 * ST * ST) * size_t(L.Mt < L.Nt ? L.Mt : L.Nt));
     L.off_S = take(size_t(L.mp));
     L.off_C = take(size_t(L.np));
     L.off_L = off;  // loss scratch (fp64): 1 / U_A,jj, 1 / U_B,ii, partial sums
@@ -874,7 +944,7 @@ template <typename T>
 struct SolverRun {
     const SolverLayout& L;
     int m, n, qmin, qmax;
-    T *NA, *NB, *X, *D, *T1, *S;
+    T *NA, *NB, *X, *D, *R, *P, *S;
     T* C;     // column scales (WaterKron mode) or nullptr
     void* Z;  // int8 codes, or int32 in the WaterKron mode
     int64_t ldz;
@@ -884,16 +954,20 @@ struct SolverRun {
 
     kq_status leaf(int K, int c0, int c1) {
         const int Mt = int(L.Mt), Nt = int(L.Nt);
-        const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
-        const int ihi = K < Mt - 1 ? K : Mt - 1;
+        auto tiles = [&](int k) {  // tiles on tile-diagonal k
+            return (k < Mt - 1 ? k : Mt - 1) - (k - Nt + 1 > 0 ? k - Nt + 1 : 0) + 1;
+        };
+        // the sweep of diagonal K, and the chunk products of K + 1 when it is in the chunk
+        const dim3 grid(tiles(K) + (K + 1 < c1 ? tiles(K + 1) : 0));
+        const int pt = int(L.Mt < L.Nt ? L.Mt : L.Nt);
         if (C)
-            hipLaunchKernelGGL((leaf_kernel<T, true>), dim3(ihi - ilo + 1), dim3(LEAF_THREADS), 0, st, X, D, NA, NB, S, C,
-                               T1, int(L.np), int(L.mp), Mt, Nt, K, c0, c1, m, n, qmin, qmax,
-                               static_cast<int32_t*>(Z), ldz, V, ldv);
+            hipLaunchKernelGGL((leaf_kernel<T, true>), grid, dim3(LEAF_THREADS), 0, st, X, D, NA, NB, S, C, R,
+                               int(L.np), int(L.mp), Mt, Nt, K, c0, c1, m, n, qmin, qmax, static_cast<int32_t*>(Z),
+                               ldz, V, ldv, P, pt);
         else
-            hipLaunchKernelGGL((leaf_kernel<T, false>), dim3(ihi - ilo + 1), dim3(LEAF_THREADS), 0, st, X, D, NA, NB, S,
-                               C, T1, int(L.np), int(L.mp), Mt, Nt, K, c0, c1, m, n, qmin, qmax,
-                               static_cast<int8_t*>(Z), ldz, V, ldv);
+            hipLaunchKernelGGL((leaf_kernel<T, false>), grid, dim3(LEAF_THREADS), 0, st, X, D, NA, NB, S, C, R,
+                               int(L.np), int(L.mp), Mt, Nt, K, c0, c1, m, n, qmin, qmax, static_cast<int8_t*>(Z),
+                               ldz, V, ldv, P, pt);
         KQ_LAUNCHED("leaf_kernel");
         return KQ_OK;
     }
@@ -905,8 +979,8 @@ struct SolverRun {
         const int row1 = mid < Mt ? mid : Mt;  // exclusive
         if (row1 > row0) {
             const int P0 = row0 >> 1, P1 = (row1 - 1) >> 1;
-            hipLaunchKernelGGL(band_stage1_kernel<T>, dim3((K1 - K0) / 2 + 2, P1 - P0 + 1), dim3(Band<T>::THREADS), 0,
-                               st, D, NA, T1, int(L.np), Nt, K0, mid, K1, P0);
+            hipLaunchKernelGGL(band_stage1_kernel<T>, dim3((K1 - mid) / 2 + 2, P1 - P0 + 1), dim3(Band<T>::THREADS), 0,
+                               st, D, NA, R, int(L.np), Nt, K0, mid, K1, P0);
             KQ_LAUNCHED("band_stage1_kernel");
         }
         // stage 2 target block-diagonals sig with [2 sig, 2 sig + 2] meeting [mid, K1)
@@ -915,14 +989,13 @@ struct SolverRun {
         const int sigmax = int(L.Mt / 2 + L.Nt / 2 - 2);
         if (sig1 > sigmax) sig1 = sigmax;
         if (sig1 >= sig0) {
-            const bool top = K0 == 0 && K1 == int(L.Mt + L.Nt - 1);
-            auto kern = top ? band_stage2_kernel<T, KSTEP> : band_stage2_kernel<T, 2 * KSTEP>;
             int total = 0;  // target blocks
             for (int p = 0; p < Mt / 2; ++p) {
                 const int lo = sig0 > p ? sig0 : p, hi = sig1 < p + Nt / 2 - 1 ? sig1 : p + Nt / 2 - 1;
                 total += hi >= lo ? hi - lo + 1 : 0;
             }
-            hipLaunchKernelGGL(kern, dim3(total), dim3(Band<T>::THREADS2), 0, st, T1, NB, X, int(L.np), int(L.mp),
+            hipLaunchKernelGGL(band_stage2_kernel<T>, dim3(total), dim3(Band<T>::THREADS2), 0, st, R, NB, X,
+                               int(L.np), int(L.mp),
                                Mt, Nt, K0, mid, K1, sig0, sig1);
             KQ_LAUNCHED("band_stage2_kernel");
         }
@@ -974,7 +1047,8 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
     SolverRun<T> run{L, int(m), int(n), q.qmin, q.qmax,
                      reinterpret_cast<T*>(base + L.off_NA), reinterpret_cast<T*>(base + L.off_NB),
                      reinterpret_cast<T*>(base + L.off_X), reinterpret_cast<T*>(base + L.off_D),
-                     reinterpret_cast<T*>(base + L.off_T1), reinterpret_cast<T*>(base + L.off_S),
+                     reinterpret_cast<T*>(base + L.off_R), reinterpret_cast<T*>(base + L.off_P),
+                     reinterpret_cast<T*>(base + L.off_S),
                      q.col_scales ? reinterpret_cast<T*>(base + L.off_C) : nullptr, q.codes, q.ldc, V, ldv, st};
     const int threads = 256;
     auto blocks = [&](int64_t count) { return dim3(unsigned((count + threads - 1) / threads)); };
@@ -990,7 +1064,8 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
         KQ_LAUNCHED("normalize_factor_kernel");
     }
     hipLaunchKernelGGL(init_solver_kernel<T>, rows(L.np, L.mp), dim3(threads), 0, st, W, ldw, int(m), int(n),
-                       int(L.mp), int(L.np), q.row_scales, q.per_row, q.col_scales, run.X, run.S, run.C);
+                       int(L.mp), int(L.np), q.row_scales, q.per_row, q.col_scales, run.X, run.S, run.C,
+                       UB ? run.R : nullptr);
     KQ_LAUNCHED("init_solver_kernel");
     // B = I: one-sided GPTQ, rows independent, recursive over column ranges
     const kq_status s = UB ? run.solve(0, int(L.Mt + L.Nt - 1))
