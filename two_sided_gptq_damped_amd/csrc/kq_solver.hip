@@ -742,50 +742,53 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
 // on 64-row block P and 64-column block Q.  R starts at zero; it gathers each
 // tile's row-propagated errors over the nodes whose left half holds a source of
 // the tile's row, and the tile's leaf completes it.
-// Band GEMMs run split-K inside the workgroup: their launches have few blocks
-// with long K ranges in the lower recursion levels, so each block gets G = 2
-// groups of four waves (deterministic reduction, see tile_gemm_masked_splitk).
-// Four groups shorten a lone solve's small launches a little, but two leave
-// more of the device to the other work in flight beside them.
+//
+// Stage 2 at the same node: for the target tiles (I, J) of diagonals [mid, K1),
+//   X[I, J] += sum_{I' : K0 <= I' + J < mid} N_B[I', I]^T R[I', J],
+// the column feedback of the left half's complete row-propagated tiles (every
+// source of R[I', J] lies on a diagonal before mid, so each of them was swept
+// already and R[I', J] is final).  Right-half sources reach X at the lower nodes
+// and in the leaves, so each (source, target) pair is applied once.
+//
+// The two stages touch disjoint data (stage 1 writes R of right-half tiles,
+// stage 2 reads R of left-half tiles and writes X), so one launch per node runs
+// both: blocks [0, n1) are stage 1's, the rest stage 2's.  Each block is a 64 x 64
+// output computed split-K by G = 2 groups of four waves (deterministic
+// reduction, see tile_gemm_masked_splitk): the small launches of the lower
+// recursion levels have few blocks with long K ranges.  Masks work at 32-tile
+// granularity; a masked operand element is replaced by zero with a select, so
+// the stale contents of tiles outside the band never reach a sum.
 template <typename T>
 struct Band {
-    static constexpr int G = 2;  // stage 1: groups per block
+    static constexpr int G = 2;  // groups per block
     static constexpr int THREADS = 256 * G;
-    // Stage 2 has half the blocks of stage 1 at the top node with twice the K
-    // each; there four-wave blocks at full occupancy balance better than split K.
-    static constexpr int THREADS2 = GEMM_THREADS;
 };
 
+// Stage 1 block: row block P, the qi-th column block counted from the row's last
+// (the last has the longest K range at the top node).
 template <typename T>
-__global__ __launch_bounds__(Band<T>::THREADS) void band_stage1_kernel(const T* __restrict__ D,
-                                                                       const T* __restrict__ NA,
-                                                                       T* __restrict__ R, int np, int Nt, int K0,
-                                                                       int mid, int K1, int P0) {
-    __shared__ SplitSmem<T, Band<T>::G> sm;
-    const int P = P0 + blockIdx.y;
+__device__ void band_stage1(const T* __restrict__ D, const T* __restrict__ NA, T* __restrict__ R, int np,
+                            int Nt, int K0, int mid, int K1, int P, int qi, SplitSmem<T, Band<T>::G>& sm) {
     const int I0 = 2 * P;  // first 32-row tile of the block
     const int jlo = K0 - I0 - 1 > 0 ? K0 - I0 - 1 : 0;
     const int jend = K1 - I0 < Nt ? K1 - I0 : Nt;  // exclusive, over both rows
     const int qlo = (mid - I0 - 1 > 0 ? mid - I0 - 1 : 0) >> 1;  // first block with a target in [mid, K1)
-    // the row's last block first: its K range is the longest at the top node
-    const int Q = ((jend - 1) >> 1) - int(blockIdx.x);
+    const int Q = ((jend - 1) >> 1) - qi;
     if (jend <= 0 || Q < qlo) return;
     const int kl = jlo;
     int kh = 2 * Q + 1;
     if (mid - 1 - I0 < kh) kh = mid - 1 - I0;
     if (Nt - 1 < kh) kh = Nt - 1;
+    if (kh < kl) return;  // no source: nothing to add
     WaveAcc<T> acc;
     acc.zero();
-    if (kh >= kl) {
-        const T* A = D + int64_t(I0) * ST * np + int64_t(kl) * ST;
-        const T* B = NA + int64_t(kl) * ST * np + int64_t(Q) * TILE;
-        auto ma = [=](int r, int k) {
-            const int s = I0 + (r >> 5) + kl + (k >> 5);  // tile-diagonal of the source tile
-            return s >= K0 && s < mid;
-        };
-        tile_gemm_masked_splitk<T, Band<T>::G, false, false>(A, np, B, np, (kh - kl + 1) * ST, sm, acc, ma,
-                                                             NoMask());
-    }
+    const T* A = D + int64_t(I0) * ST * np + int64_t(kl) * ST;
+    const T* B = NA + int64_t(kl) * ST * np + int64_t(Q) * TILE;
+    auto ma = [=](int r, int k) {
+        const int s = I0 + (r >> 5) + kl + (k >> 5);  // tile-diagonal of the source tile
+        return s >= K0 && s < mid;
+    };
+    tile_gemm_masked_splitk<T, Band<T>::G, false, false>(A, np, B, np, (kh - kl + 1) * ST, sm, acc, ma, NoMask());
     if (threadIdx.x >= 256) return;  // group 0 holds the product
     T* out = R + int64_t(I0) * ST * np + int64_t(Q) * TILE;
     for_each_acc(acc, [&](int r, int c, T v) {
@@ -794,31 +797,19 @@ __global__ __launch_bounds__(Band<T>::THREADS) void band_stage1_kernel(const T* 
     });
 }
 
-// Stage 2 at node [K0, K1) with split mid: for the target tiles (I, J) of
-// diagonals [mid, K1),
-//   X[I, J] += sum_{I' : K0 <= I' + J < mid} N_B[I', I]^T R[I', J],
-// the column feedback of the left half's complete row-propagated tiles (every
-// source of R[I', J] lies on a diagonal before mid, so each of them was swept
-// already and R[I', J] is final).  Right-half sources reach X at the lower nodes
-// and in the leaves, so each (source, target) pair is applied once.  Tiles are
-// taken in 64 x 64 target blocks (P, Q) of block-diagonal sig = P + Q; the K
-// range of block (P, Q) spans at most mid - K0 + 1 source tiles, staged 32 deep
-// with two slices in flight (tile_gemm_masked_k2).
-// Block order: a 1-D grid walks the target blocks by block row P from the last
-// to the first (sig ascending within a row), so the blocks with long K ranges
-// are dispatched first and the short ones fill in behind them, and no
+// Stage 2 block bi: target blocks (P, Q) of block-diagonal sig = P + Q in
+// [sig0, sig1], walked by block row P from the last to the first (sig ascending
+// within a row), so the blocks with long K ranges are dispatched first and no
 // workgroup is spent on an empty position.
-template <typename T>
-__global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T* __restrict__ R,
-                                                                        const T* __restrict__ NB,
-                                                                        T* __restrict__ X, int np, int mp, int Mt,
-                                                                        int Nt, int K0, int mid, int K1, int sig0,
-                                                                        int sig1) {
-    constexpr int KS = 2 * KSTEP;
-    __shared__ GemmSmemK<T, KS> sm;
+// The product runs split-K over the workgroup's two groups (SPLIT, in the
+// 512-thread launch shared with stage 1) or on one 256-thread group with two
+// 32-deep slices in flight (a launch of its own).
+template <typename T, bool SPLIT, typename Smem>
+__device__ void band_stage2(const T* __restrict__ R, const T* __restrict__ NB, T* __restrict__ X, int np, int mp,
+                            int Mt, int Nt, int K0, int mid, int K1, int sig0, int sig1, int bi, Smem& sm) {
     const int Mb = Mt >> 1, Nb = Nt >> 1;
     int sig = 0, P = -1;
-    for (int b = blockIdx.x, p = Mb - 1; p >= 0; --p) {
+    for (int b = bi, p = Mb - 1; p >= 0; --p) {
         const int lo = sig0 > p ? sig0 : p, hi = sig1 < p + Nb - 1 ? sig1 : p + Nb - 1;
         const int cnt = hi >= lo ? hi - lo + 1 : 0;
         if (b < cnt) {
@@ -831,28 +822,61 @@ __global__ __launch_bounds__(Band<T>::THREADS2) void band_stage2_kernel(const T*
     if (P < 0) return;
     const int Q = sig - P;
     const int I0 = 2 * P, J0 = 2 * Q;
-    auto in_band = [=](int r, int c) {
-        const int k = I0 + (r >> 5) + J0 + (c >> 5);
-        return k >= mid && k < K1;
-    };
-    auto src_valid = [=](int ip, int j) {  // a complete tile R^[I', J] of the left half
-        const int k = ip + j;
-        return k >= K0 && k < mid;
-    };
-    T* out = X + int64_t(I0) * ST * np + int64_t(J0) * ST;
     const int kl = K0 - J0 - 1 > 0 ? K0 - J0 - 1 : 0;
     const int kh = I0 + 1 < mid - 1 - J0 ? I0 + 1 : mid - 1 - J0;
     if (kl > kh) return;
+    auto src_valid = [=](int ip, int j) {  // a complete tile R[I', J] of the left half
+        const int k = ip + j;
+        return k >= K0 && k < mid;
+    };
     WaveAcc<T> acc;
     acc.zero();
     const T* A = NB + int64_t(kl) * ST * mp + int64_t(I0) * ST;  // A(r, k) = NB[k][r]
     const T* B = R + int64_t(kl) * ST * np + int64_t(J0) * ST;
     auto mb = [=](int k, int c) { return src_valid(kl + (k >> 5), J0 + (c >> 5)); };
-    tile_gemm_masked_k2<T, KS, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
+    if constexpr (SPLIT) {
+        tile_gemm_masked_splitk<T, Band<T>::G, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
+        if (threadIdx.x >= 256) return;  // group 0 holds the product
+    } else {
+        tile_gemm_masked_k2<T, 2 * KSTEP, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
+    }
+    T* out = X + int64_t(I0) * ST * np + int64_t(J0) * ST;
     for_each_acc(acc, [&](int r, int c, T v) {
-        if (in_band(r, c)) out[int64_t(r) * np + c] += v;
+        const int k = I0 + (r >> 5) + J0 + (c >> 5);
+        if (k >= mid && k < K1) out[int64_t(r) * np + c] += v;
     });
 }
+
+// Both stages of node [K0, K1): blocks [0, n1) are stage 1's (row blocks P0 ..,
+// nq column blocks each), the rest stage 2's (none when stage 2 has its own launch).
+template <typename T>
+__global__ __launch_bounds__(Band<T>::THREADS) void band_kernel(const T* __restrict__ D, const T* __restrict__ NA,
+                                                                const T* __restrict__ NB, T* __restrict__ R,
+                                                                T* __restrict__ X, int np, int mp, int Mt, int Nt,
+                                                                int K0, int mid, int K1, int P0, int nq, int n1,
+                                                                int sig0, int sig1) {
+    __shared__ SplitSmem<T, Band<T>::G> sm;
+    const int b = blockIdx.x;
+    if (b < n1)
+        band_stage1(D, NA, R, np, Nt, K0, mid, K1, P0 + b / nq, b % nq, sm);
+    else
+        band_stage2<T, true>(R, NB, X, np, mp, Mt, Nt, K0, mid, K1, sig0, sig1, b - n1, sm);
+}
+
+// Stage 2 alone, one 256-thread workgroup per target block.
+template <typename T>
+__global__ __launch_bounds__(GEMM_THREADS) void band_stage2_kernel(const T* __restrict__ R, const T* __restrict__ NB,
+                                                                   T* __restrict__ X, int np, int mp, int Mt, int Nt,
+                                                                   int K0, int mid, int K1, int sig0, int sig1) {
+    __shared__ GemmSmemK<T, 2 * KSTEP> sm;
+    band_stage2<T, false>(R, NB, X, np, mp, Mt, Nt, K0, mid, K1, sig0, sig1, int(blockIdx.x), sm);
+}
+
+// Nodes of up to BAND_FUSE_MAX blocks run both stages in one launch: there the
+// launches are short and latency-bound, and the two stages overlap.  Larger
+// nodes keep the 256-thread stage-2 workgroups (more of them per CU, two slices
+// in flight), which do better once the launch fills the device.
+constexpr int BAND_FUSE_MAX = 1200;
 
 // Proxy loss of the result from the solver's errors.  The feedback gives
 // V - W = L~_B Delta L~_A^T exactly in exact arithmetic (FastKron page, section
@@ -977,26 +1001,29 @@ struct SolverRun {
         // stage 1 rows I' with a source tile in [K0, mid): K0 - Nt < I' < mid
         const int row0 = K0 - Nt + 1 > 0 ? K0 - Nt + 1 : 0;
         const int row1 = mid < Mt ? mid : Mt;  // exclusive
-        if (row1 > row0) {
-            const int P0 = row0 >> 1, P1 = (row1 - 1) >> 1;
-            hipLaunchKernelGGL(band_stage1_kernel<T>, dim3((K1 - mid) / 2 + 2, P1 - P0 + 1), dim3(Band<T>::THREADS), 0,
-                               st, D, NA, R, int(L.np), Nt, K0, mid, K1, P0);
-            KQ_LAUNCHED("band_stage1_kernel");
-        }
+        const int P0 = row0 >> 1;
+        const int nq = (K1 - mid) / 2 + 2;  // column blocks per row block: targets in [mid, K1)
+        const int n1 = row1 > row0 ? nq * (((row1 - 1) >> 1) - P0 + 1) : 0;
         // stage 2 target block-diagonals sig with [2 sig, 2 sig + 2] meeting [mid, K1)
         const int sig0 = (mid - 1) >> 1 > 0 ? (mid - 1) >> 1 : 0;
         int sig1 = (K1 - 1) >> 1;
         const int sigmax = int(L.Mt / 2 + L.Nt / 2 - 2);
         if (sig1 > sigmax) sig1 = sigmax;
-        if (sig1 >= sig0) {
-            int total = 0;  // target blocks
-            for (int p = 0; p < Mt / 2; ++p) {
-                const int lo = sig0 > p ? sig0 : p, hi = sig1 < p + Nt / 2 - 1 ? sig1 : p + Nt / 2 - 1;
-                total += hi >= lo ? hi - lo + 1 : 0;
-            }
-            hipLaunchKernelGGL(band_stage2_kernel<T>, dim3(total), dim3(Band<T>::THREADS2), 0, st, R, NB, X,
-                               int(L.np), int(L.mp),
-                               Mt, Nt, K0, mid, K1, sig0, sig1);
+        int n2 = 0;  // target blocks
+        for (int p = 0; p < Mt / 2 && sig1 >= sig0; ++p) {
+            const int lo = sig0 > p ? sig0 : p, hi = sig1 < p + Nt / 2 - 1 ? sig1 : p + Nt / 2 - 1;
+            n2 += hi >= lo ? hi - lo + 1 : 0;
+        }
+        const bool fuse = n1 + n2 <= BAND_FUSE_MAX;
+        const int nb = fuse ? n1 + n2 : n1;  // blocks of the first launch
+        if (nb > 0) {
+            hipLaunchKernelGGL(band_kernel<T>, dim3(nb), dim3(Band<T>::THREADS), 0, st, D, NA, NB, R, X, int(L.np),
+                               int(L.mp), Mt, Nt, K0, mid, K1, P0, nq, n1, sig0, sig1);
+            KQ_LAUNCHED("band_kernel");
+        }
+        if (!fuse && n2 > 0) {
+            hipLaunchKernelGGL(band_stage2_kernel<T>, dim3(n2), dim3(GEMM_THREADS), 0, st, R, NB, X, int(L.np),
+                               int(L.mp), Mt, Nt, K0, mid, K1, sig0, sig1);
             KQ_LAUNCHED("band_stage2_kernel");
         }
         return KQ_OK;
