@@ -30,15 +30,24 @@ checked in four ways:
         flipping the oracle's three nearest ties one at a time;
       - trajectory: the oracle is re-run with every GPU code imposed, and each
         GPU code must be clamp(rne(y)) of the exact pre-rounding value y that
-        the earlier codes imply, except within 1e-4 grid units of a boundary;
+        the earlier codes imply, except within 1e-4 grid units of a boundary.
+        With no violation the GPU's codes are exactly the fp64 method's codes
+        with its near-tie branches (the codes that differ from clamp(rne(y))
+        there) taken the other way;
       - every mismatch root (a differing code with no other difference to its
         top-left, so both sides saw the same exact value there) must be a near
         tie of the fp64 oracle (within 1e-4 grid units): single precision may
         only part ways with the oracle at a near tie, and everything else that
         differs lies in the bottom-right cone of such a split;
-      - the mismatch fraction is at most 1e-3, or, once a near-tie split
-        exists, at most FLOOR_FACTOR times the oracle's own fp32 loop's
-        mismatch against its fp64 loop on the same block.
+      - the number of near-tie branches is at most NEAR_FACTOR times that of the
+        oracle's own fp32 loop on the same block (its trajectory checked the same
+        way), and at most NEAR_FACTOR * NEAR_FLOOR when the oracle's is smaller.
+        The branch count, not the mismatch fraction, is bounded: one branch
+        changes every later code in its cone that depends on it, anywhere from
+        a few entries to a third of the block, so the mismatch fraction of one
+        valid execution against another says nothing about either.  The
+        fraction is reported beside the oracle's fp32 floor and is at most 1e-3
+        when the GPU took no branch.
 With B = I every row is its own problem, so one-sided runs are also checked on
 rows spread over the whole matrix.
 """
@@ -58,7 +67,9 @@ import two_sided_gptq_damped_amd as kq  # noqa: E402
 from two_sided_gptq_damped_amd import pipeline  # noqa: E402
 
 DEV = "cuda"
-FLOOR_FACTOR = 4.0
+FLOOR_FACTOR = 4.0  # loss: allowed multiple of the oracle's own fp32 distance
+NEAR_FACTOR = 4     # near-tie branches: allowed multiple of the oracle fp32 loop's count
+NEAR_FLOOR = 2      # ... counted as at least this many
 
 
 def say(*a):
@@ -166,6 +177,8 @@ def check_fp32_block(g, bits, k1, k2, label):
     far_roots = int(np.sum(roots & (compare.tie_distance(Yo) >= 1e-4)))
     Yf = o3.solve(W, UA, UB, s, bits, force=Zg.astype(np.int32), La=La, Lb=Lb)[2]
     viol, near = compare.trajectory_violations(Zg, Yf, bits, 1e-4)
+    Yf32 = o3.solve(W, UA, UB, s, bits, force=Z32.astype(np.int32), La=La, Lb=Lb)[2]
+    viol32, near32 = compare.trajectory_violations(Z32, Yf32, bits, 1e-4)
     if k1 == m and k2 == n:
         Ad = dense.damp(host(g["A"]), g["damp"])
         Bd = np.eye(m) if g["B"] is None else dense.damp(host(g["B"]), g["damp"])
@@ -175,10 +188,13 @@ def check_fp32_block(g, bits, k1, k2, label):
     lg, lo, l32 = loss(Vg), loss(Vo), loss(V32.astype(np.float64))
     rel, rel_floor = compare.rel_diff(lg, lo), compare.rel_diff(l32, lo)
     say(label, f"fp32 block {k1}x{k2}: trajectory violations={viol} near-tie branches={near} "
+               f"(oracle fp32 loop: violations={viol32} branches={near32}) "
                f"mismatch={mis:.3e} (oracle fp32 floor {floor:.3e}) roots={int(roots.sum())} far roots={far_roots} "
                f"loss_gpu={lg:.6e} loss_oracle={lo:.6e} rel={rel:.3e} (oracle fp32 floor {rel_floor:.3e})")
     assert viol == 0, label
     assert far_roots == 0, label
+    assert viol32 == 0, label  # the oracle's own fp32 loop meets the same bar
+    assert near <= NEAR_FACTOR * max(near32, NEAR_FLOOR), label
     if rel > 1e-3 and rel > FLOOR_FACTOR * rel_floor:
         # A strongly coupled block (the rank-deficient output factor of the gate
         # shape): one legitimate branch at a near tie moves the loss by far more
@@ -188,7 +204,7 @@ def check_fp32_block(g, bits, k1, k2, label):
         sens = flip_sensitivity(W, UA, UB, s, bits, Zo, Yo, lo, loss, La, Lb)
         say(label, f"loss change of one near-tie branch (largest of 3): {sens:.3e}; GPU branches {near}")
         assert near > 0 and rel <= near * sens, label
-    assert mis <= 1e-3 or (int(roots.sum()) > 0 and mis <= FLOOR_FACTOR * floor), label
+    assert near > 0 or mis <= 1e-3, label
 
 
 def flip_sensitivity(W, UA, UB, s, bits, Zo, Yo, lo, loss, La, Lb, k=3):
