@@ -290,23 +290,48 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     __shared__ T sNAt[ST * PA];                                    // sNAt[b][bs] = N_A[..bs][..b], col ST = 0
     constexpr int RD = 2 * LEAF_E;                      // diagonals per sweep round (one wave's two groups)
     constexpr int NROUND = (2 * ST - 1 + RD - 1) / RD;  // sweep rounds
-    // chunk operands of up to BATCH slices: A(r, k) at [k][r], B(k, c) at [k][c]
+    // Chunk operands of up to BATCH slices: A(r, k) at [k][r], B(k, c) at [k][c]
+    // (the precompute workgroups), or the leaf's layout below.
     constexpr int BATCH = sizeof(T) == 4 ? 14 : 7;  // staged together (LDS budget)
     __shared__ __attribute__((aligned(16))) T stg[BATCH][2][ST * PK];
-    T* const bufA = stg[0][0];
-    T* const bufB = stg[0][1];
+    // The leaf's LDS: the sweep's factor tables cB and cA (in the form the sweep
+    // reads them, see below), the tile in the two layouts' exchange bufA / bufB,
+    // and the sweep's exchange xD / xR (one slice per round: errors by row,
+    // row-accumulated errors by column).  bufA .. xR are free until the sweep, so
+    // the prologue stages its two slices there (slice 0 in bufA / bufB, slice 1
+    // at xD) and parks its products at xD, and the tables are built while the
+    // first loads are in flight.
+    constexpr int NRB = 3 * ST + 4;  // rows of cB; d - b + ST stays in [1, NRB) for d <= 2 ST + 3
+    constexpr int PT = 3 * ST + 4;   // row pitch of cA (even: lanes step PT + 1 apart)
+    T* const cB = &stg[0][0][0];
+    T* const cA = cB + NRB * PB;
+    T* const bufA = cA + ST * PT;
+    T* const bufB = bufA + ST * PK;
+    T* const xD = bufB + ST * PK;          // [round][row][diagonal of the round]
+    T* const xR = xD + NROUND * ST * RD;  // [round][column][diagonal of the round]
+    static_assert(NRB * PB + ST * PT + 2 * ST * PK + 2 * NROUND * ST * RD <= sizeof(stg) / sizeof(T),
+                  "staging area too small");
+    static_assert((NRB * PB + ST * PT) % 4 == 0 && (NRB * PB + ST * PT + 2 * ST * PK) % 8 == 0,
+                  "16-byte aligned bufA / bufB, 32-byte aligned exchange slices");
+    static_assert(2 * ST * PK + 2 * ST * ST <= 2 * ST * PK + 2 * NROUND * ST * RD, "prologue staging fits");
 
     // Launch K: workgroups [0, nk) sweep the tiles of diagonal K.  When diagonal
-    // K + 1 lies in the same chunk, workgroups [nk, nk + nk1) pre-accumulate its
-    // tiles' chunk products over every slice that is final before this launch
-    // (all but the two on diagonal K) into P, so that leaf K + 1 adds only the
-    // freshest two slices.  P holds two diagonals, alternating with K's parity.
+    // K + 1 lies in the same chunk, workgroups [nk + xpad, nk + xpad + nk1)
+    // pre-accumulate its tiles' chunk products over every slice that is final
+    // before this launch (all but the two on diagonal K) into P, so that leaf
+    // K + 1 adds only the freshest two slices.  P holds two diagonals,
+    // alternating with K's parity.  Workgroup b runs on XCD b mod 8 (each XCD
+    // has its own L2); the xpad idle workgroups put the workgroup that writes a
+    // tile's P on the XCD where the next launch sweeps that tile (index idx in
+    // both), so the leaf reads P from its own L2.
     const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
     const int ihi = K < Mt - 1 ? K : Mt - 1;
     const int nk = ihi - ilo + 1;
     const bool pre = int(blockIdx.x) >= nk;
+    const int xpad = (8 - nk % 8) % 8;
     const int Kt = pre ? K + 1 : K;  // the tile's diagonal
-    const int idx = pre ? int(blockIdx.x) - nk : int(blockIdx.x);
+    const int idx = pre ? int(blockIdx.x) - nk - xpad : int(blockIdx.x);
+    if (idx < 0) return;
     const int I = (Kt - Nt + 1 > 0 ? Kt - Nt + 1 : 0) + idx;
     if (I > (Kt < Mt - 1 ? Kt : Mt - 1)) return;
     const int J = Kt - I;
@@ -356,6 +381,10 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         const int u = NFG * v + fgrp;
         if (u < BATCH && u < ns) fetch(u, pa[v], pb[v]);
     }
+    // operand op (0: A, 1: B) of staged slice u
+    auto slot = [&](int u, int op) -> T* {
+        return pre ? stg[u][op] : (u == 0 ? bufA : xD) + op * ST * PK;
+    };
     // pq += this wave's part over the workgroup's slices, staged in batches
     auto products = [&](Q16<T>& pq) {
         for (int sb = 0; sb < ns; sb += BATCH) {
@@ -373,11 +402,11 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
                 if (u < BATCH && sb + u < ns) {
                     if (sb + u < n1) {
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) stg[u][0][(c4 + j) * PK + q8] = pa[v][j];
+                        for (int j = 0; j < 4; ++j) slot(u, 0)[(c4 + j) * PK + q8] = pa[v][j];
                     } else {
-                        pa[v].store(stg[u][0] + q8 * PK + c4);
+                        pa[v].store(slot(u, 0) + q8 * PK + c4);
                     }
-                    pb[v].store(stg[u][1] + q8 * PK + c4);
+                    pb[v].store(slot(u, 1) + q8 * PK + c4);
                 }
             }
             __syncthreads();
@@ -392,7 +421,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
                 u1 = nbat;
             }
             for (int u = u0; u < u1; ++u)
-                pq.template mma<PK, PK, ST>(stg[u][0] + qr, stg[u][1] + qc, lane);
+                pq.template mma<PK, PK, ST>(slot(u, 0) + qr, slot(u, 1) + qc, lane);
         }
     };
     // the row part starts from R[I, J]: the row-propagated errors of every source
@@ -420,16 +449,53 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         pin[r] = pzero ? T(0) : psrc[Q16<T>::row(r, lane) * pld + Q16<T>::col(r, lane)];
 
     constexpr int FE = ST * ST / LEAF_THREADS;  // factor-block entries per thread
-    T fnb[FE], fna[FE];                         // kept for the sweep's tables
+    T fnb[FE], fna[FE];
 #pragma unroll
     for (int u = 0; u < FE; ++u) {
         const int e = t + u * LEAF_THREADS, r = e >> 5, c = e & 31;
-        const T nb = NB[int64_t(I * ST + r) * mp + I * ST + c];
-        fnb[u] = r == c ? T(0) : nb;
+        fnb[u] = NB[int64_t(I * ST + r) * mp + I * ST + c];
+        fna[u] = NA[int64_t(J * ST + r) * np + J * ST + c];
+    }
+    // The sweep's factor tables: the coefficient of diagonal d's source for the
+    // entry (a, b) sits at a fixed offset from a per-entry base,
+    //   cB[(d - b + ST) PB + a] = N_B[d - b][a]   (column source (d - b, b))
+    //   cA[b PT + d - a + ST]   = N_A[d - a][b]   (row source (a, d - a)),
+    // zero wherever the source lies off the tile (and, as in sNB / sNAt, on and
+    // below the diagonal), so the unrolled sweep spends no arithmetic on
+    // addresses.  First the zero lines, four entries per store (cB rows [0, ST)
+    // and [2 ST, NRB), cA columns [0, ST) and [2 ST, PT) of every row), while the
+    // loads are in flight; then the factor entries.
+    {
+        constexpr int ZB0 = ST * PB / 4, ZB1 = (NRB - 2 * ST) * PB / 4;
+        constexpr int ZAR = ST / 4 + (PT - 2 * ST) / 4;  // per cA row
+        static_assert(PB % 4 == 0 && PT % 4 == 0, "16-byte table lines");
+        Vec4<T> z4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z4.set(j, T(0));
+        for (int u = t; u < ZB0 + ZB1 + ST * ZAR; u += LEAF_THREADS) {
+            T* q;
+            if (u < ZB0) {
+                q = cB + 4 * u;
+            } else if (u < ZB0 + ZB1) {
+                q = cB + 2 * ST * PB + 4 * (u - ZB0);
+            } else {
+                const int v = u - ZB0 - ZB1, r = v / ZAR, k = v - r * ZAR;
+                q = cA + r * PT + (k < ST / 4 ? 4 * k : 2 * ST + 4 * (k - ST / 4));
+            }
+            z4.store(q);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < FE; ++u) {
+        const int e = t + u * LEAF_THREADS, r = e >> 5, c = e & 31;
+        if (r == c) {
+            fnb[u] = T(0);
+            fna[u] = T(0);
+        }
         sNB[r * PB + c] = fnb[u];
-        const T na = NA[int64_t(J * ST + r) * np + J * ST + c];
-        fna[u] = r == c ? T(0) : na;
         sNAt[c * PA + r] = fna[u];
+        cB[(r + ST) * PB + c] = fnb[u];  // N_B[r][c]
+        cA[c * PT + ST + r] = fna[u];    // N_A[r][c]
     }
     if (t < ST) {
         sNB[ST * PB + t] = T(0);
@@ -476,8 +542,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         // the quadrants reach the block layout through the staging area:
         // park[0] = rowpart (also the right operand of the in-tile column
         // feedback), park[1] = the column part
-        T* park = reinterpret_cast<T*>(stg);
-        static_assert(sizeof(stg) >= 2 * ST * ST * sizeof(T), "staging area too small");
+        T* const park = xD;
         auto park_quadrant = [&]() {
             T* q = park + part * ST * ST + qr * ST + qc;
 #pragma unroll
@@ -505,58 +570,11 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         for (int i = 0; i < 4; ++i) acc[i] += crow[i] + ccol[i];
     }
 
-    // ---- to the sweep layout through LDS, and the sweep's factor tables
-    // The staging area is free from here on.  Beside bufA / bufB it holds the
-    // factor coefficients in the form the sweep reads them: the coefficient of
-    // diagonal d's source for the entry (a, b) sits at a fixed offset from a
-    // per-entry base,
-    //   cB[(d - b + ST) PB + a] = N_B[d - b][a]   (column source (d - b, b))
-    //   cA[b PT + d - a + ST]   = N_A[d - a][b]   (row source (a, d - a)),
-    // zero wherever the source lies off the tile (and, as in sNB / sNAt, on and
-    // below the diagonal), so the unrolled sweep spends no arithmetic on addresses.
-    constexpr int NRB = 3 * ST + 4;  // rows of cB; d - b + ST stays in [1, NRB) for d <= 2 ST + 3
-    constexpr int PT = 3 * ST + 4;   // row pitch of cA (even: lanes step PT + 1 apart)
-    T* const cB = stg[0][0] + 2 * ST * PK;
-    T* const cA = cB + NRB * PB;
-    // the sweep's exchange, one slice per round: errors by row, row-accumulated
-    // errors by column
-    T* const xD = cA + ST * PT;            // [round][row][diagonal of the round]
-    T* const xR = xD + NROUND * ST * RD;  // [round][column][diagonal of the round]
-    static_assert(2 * ST * PK + NRB * PB + ST * PT + 2 * NROUND * ST * RD <= sizeof(stg) / sizeof(T),
-                  "staging area too small");
-    static_assert((2 * ST * PK + NRB * PB + ST * PT) % 8 == 0, "32-byte aligned exchange slices");
-    __syncthreads();  // the prologue's reads of the staging area are done
+    // ---- to the sweep layout through bufA (free: the prologue staged and parked
+    // elsewhere, and every read of its staging happened before its last barrier)
     if (blk) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) bufA[(r0 + i) * PK + b] = acc[i];
-    }
-    {
-        // zero lines, four entries per store: cB rows [0, ST) and [2 ST, NRB), cA
-        // columns [0, ST) and [2 ST, PT) of every row; then the factor entries
-        constexpr int ZB0 = ST * PB / 4, ZB1 = (NRB - 2 * ST) * PB / 4;
-        constexpr int ZAR = ST / 4 + (PT - 2 * ST) / 4;  // per cA row
-        static_assert(PB % 4 == 0 && PT % 4 == 0 && (2 * ST * PK) % 4 == 0, "16-byte table lines");
-        Vec4<T> z4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) z4.set(j, T(0));
-        for (int u = t; u < ZB0 + ZB1 + ST * ZAR; u += LEAF_THREADS) {
-            T* q;
-            if (u < ZB0) {
-                q = cB + 4 * u;
-            } else if (u < ZB0 + ZB1) {
-                q = cB + 2 * ST * PB + 4 * (u - ZB0);
-            } else {
-                const int v = u - ZB0 - ZB1, r = v / ZAR, k = v - r * ZAR;
-                q = cA + r * PT + (k < ST / 4 ? 4 * k : 2 * ST + 4 * (k - ST / 4));
-            }
-            z4.store(q);
-        }
-#pragma unroll
-        for (int u = 0; u < FE; ++u) {
-            const int e = t + u * LEAF_THREADS, r = e >> 5, c = e & 31;
-            cB[(r + ST) * PB + c] = fnb[u];  // N_B[r][c]
-            cA[c * PT + ST + r] = fna[u];    // N_A[r][c]
-        }
     }
     __syncthreads();
     if (t >= SWEEP_THREADS) return;  // the later barriers wait for the sweep's waves only
@@ -981,8 +999,9 @@ struct SolverRun {
         auto tiles = [&](int k) {  // tiles on tile-diagonal k
             return (k < Mt - 1 ? k : Mt - 1) - (k - Nt + 1 > 0 ? k - Nt + 1 : 0) + 1;
         };
-        // the sweep of diagonal K, and the chunk products of K + 1 when it is in the chunk
-        const dim3 grid(tiles(K) + (K + 1 < c1 ? tiles(K + 1) : 0));
+        // the sweep of diagonal K, and the chunk products of K + 1 when it is in
+        // the chunk (behind up to 7 idle workgroups that align them with the XCDs)
+        const dim3 grid(tiles(K) + (K + 1 < c1 ? (8 - tiles(K) % 8) % 8 + tiles(K + 1) : 0));
         const int pt = int(L.Mt < L.Nt ? L.Mt : L.Nt);
         if (C)
             hipLaunchKernelGGL((leaf_kernel<T, true>), grid, dim3(LEAF_THREADS), 0, st, X, D, NA, NB, S, C, R,
