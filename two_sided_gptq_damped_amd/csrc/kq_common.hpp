@@ -262,62 +262,13 @@ __device__ void tile_gemm(const TIn* __restrict__ A, int64_t lda, const TIn* __r
     }
 }
 
-// Masked variant over padded, in-range operands: element (r, k) of A is used
+// Masked products over padded, in-range operands: element (r, k) of A is used
 // only where ma(r, k) holds and element (k, c) of B only where mb(k, c) holds;
 // elsewhere the operand reads as zero (a select, so non-finite stale values
-// never reach the sum).  K must be a multiple of 16.
+// never reach the sum).  NoMask keeps every element.
 struct NoMask {
     __device__ __forceinline__ bool operator()(int, int) const { return true; }
 };
-
-template <typename T, bool A_KMAJ, bool B_KMAJ, typename MA, typename MB>
-__device__ void tile_gemm_masked(const T* __restrict__ A, int64_t lda, const T* __restrict__ B, int64_t ldb, int K,
-                                 GemmSmem<T>& sm, WaveAcc<T>& acc, MA ma, MB mb) {
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int wy = w >> 1, wx = w & 1;
-    TileLoader<T, T, A_KMAJ, B_KMAJ, false> ld;
-    const int nk = K / KSTEP;
-    if (nk == 0) return;
-    auto apply = [&](int k0) {
-        if (!A_KMAJ) {
-            const int r = t >> 2, kq = (t & 3) * 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (!ma(r, k0 + kq + e)) ld.ra[e] = T(0);
-        } else {
-            const int k = t >> 4, rq = (t & 15) * 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (!ma(rq + e, k0 + k)) ld.ra[e] = T(0);
-        }
-        if (!B_KMAJ) {
-            const int k = t >> 4, cq = (t & 15) * 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (!mb(k0 + k, cq + e)) ld.rb[e] = T(0);
-        } else {
-            const int c = t >> 2, kq = (t & 3) * 4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (!mb(k0 + kq + e, c)) ld.rb[e] = T(0);
-        }
-    };
-    ld.fetch(A, lda, B, ldb, 0, TILE, TILE, K, t);
-    apply(0);
-    __syncthreads();
-    ld.stash(sm.a[0], sm.b[0], t);
-    __syncthreads();
-    for (int s = 0; s < nk; ++s) {
-        const int cur = s & 1;
-        if (s + 1 < nk) ld.fetch(A, lda, B, ldb, (s + 1) * KSTEP, TILE, TILE, K, t);
-        acc.mma(sm.a[cur], sm.b[cur], wy, wx, lane);
-        if (s + 1 < nk) {
-            apply((s + 1) * KSTEP);  // after the products, so the loads overlap them
-            ld.stash(sm.a[cur ^ 1], sm.b[cur ^ 1], t);
-            __syncthreads();
-        }
-    }
-}
 
 // K-slice depth as a parameter: KS = 16 R deep slices, each thread moving R
 // groups of the 16-deep loader pattern.  Deeper slices carry more matrix-core
@@ -374,38 +325,11 @@ struct GemmSmemK {
     T b[2][KS * LdsStride<T>::value];
 };
 
-// tile_gemm_masked with KS-deep slices; K must be a multiple of KS.
-template <typename T, int KS, bool A_KMAJ, bool B_KMAJ, typename MA, typename MB>
-__device__ void tile_gemm_masked_k(const T* __restrict__ A, int64_t lda, const T* __restrict__ B, int64_t ldb, int K,
-                                   GemmSmemK<T, KS>& sm, WaveAcc<T>& acc, MA ma, MB mb) {
-    constexpr int S = LdsStride<T>::value;
-    const int t = threadIdx.x & 255, lane = t & 63, w = t >> 6;
-    const int wy = w >> 1, wx = w & 1;
-    LoaderK<T, A_KMAJ, B_KMAJ, KS> ld;
-    const int nk = K / KS;
-    if (nk == 0) return;
-    ld.fetch(A, lda, B, ldb, 0, t);
-    ld.apply(0, t, ma, mb);
-    __syncthreads();
-    ld.stash(sm.a[0], sm.b[0], t);
-    __syncthreads();
-    for (int s = 0; s < nk; ++s) {
-        const int cur = s & 1;
-        if (s + 1 < nk) ld.fetch(A, lda, B, ldb, (s + 1) * KS, t);
-#pragma unroll
-        for (int q = 0; q < KS / KSTEP; ++q) acc.mma(sm.a[cur] + KSTEP * q * S, sm.b[cur] + KSTEP * q * S, wy, wx, lane);
-        if (s + 1 < nk) {
-            ld.apply((s + 1) * KS, t, ma, mb);  // after the products, so the loads overlap them
-            ld.stash(sm.a[cur ^ 1], sm.b[cur ^ 1], t);
-            __syncthreads();
-        }
-    }
-}
-
-// tile_gemm_masked_k with two slices in flight: while the matrix cores work on
-// slice s from LDS, the loads of slices s + 1 and s + 2 are both outstanding (two
-// register sets used in turn), so a block whose K loop is bound by the latency of
-// its own loads waits half as often.  K must be a multiple of KS.
+// A masked tile product with KS-deep slices and two slices in flight: while the
+// matrix cores work on slice s from LDS, the loads of slices s + 1 and s + 2 are
+// both outstanding (two register sets used in turn), so a block whose K loop is
+// bound by the latency of its own loads waits half as often.  K must be a
+// multiple of KS.
 template <typename T, int KS, bool A_KMAJ, bool B_KMAJ, typename MA, typename MB>
 __device__ void tile_gemm_masked_k2(const T* __restrict__ A, int64_t lda, const T* __restrict__ B, int64_t ldb, int K,
                                     GemmSmemK<T, KS>& sm, WaveAcc<T>& acc, MA ma, MB mb) {
