@@ -32,7 +32,7 @@
 namespace kq {
 
 constexpr int OS_BLK = 64;   // columns per leaf
-constexpr int OS_ROWS = 64;  // rows per leaf workgroup: one wave, one row per lane
+constexpr int OS_ROWS = 64;  // rows per leaf workgroup
 
 __device__ __forceinline__ float os_clamp(float x, float lo, float hi) { return __builtin_amdgcn_fmed3f(x, lo, hi); }
 __device__ __forceinline__ double os_clamp(double x, double lo, double hi) { return kclamp(x, lo, hi); }
@@ -48,39 +48,101 @@ __device__ __forceinline__ double lane_value(double v, int l) {
     return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
 }
 
-// Leaf over columns [j0, j0 + 64) for rows r0 = 64 blockIdx.x .. r0 + 63.
-// Global memory is read and written row by row (16-byte accesses, coalesced),
-// through the LDS tile xs that holds one row per lane (pitch 68: 16-byte
-// aligned rows, and a wave's 16-byte accesses cover all banks evenly).  The
-// 64 columns are taken in four sub-blocks of 16: a sub-block's pre-rounding
-// values sit in registers for its sweep (right-looking: once column j is
-// rounded its error goes into the sub-block's later columns), then its 16
-// errors are applied to the row's later sub-blocks in LDS, four columns at a
-// time.  The sub-block loop is not unrolled, so the code a lone wave runs is a
-// few kilobytes that stay in the instruction cache.
+// Leaf over columns [j0, j0 + 64) for rows r0 = 64 blockIdx.x .. r0 + 63, four
+// waves of 16 rows.  Each row is spread over the four lanes of a quad: lane q of
+// the quad owns the columns c = 4 i + q (i < 16), so every lane holds a quarter
+// of the row's later columns at every step.  The sweep is right-looking and
+// fully unrolled over the 64 columns: the owner of column j (lane j mod 4) rounds
+// it, a DPP quad broadcast hands its error to the row's other three lanes, and
+// each lane adds error * N[j][c] to its columns c > j (the ones with i >= j / 4,
+// known at compile time; the few with c <= j get an exact zero coefficient).  The
+// coefficients sit in LDS per lane class, cq[q][j][i] = N[j0 + j][j0 + 4 i + q]
+// strictly above the diagonal and 0 elsewhere, so a lane reads its four
+// consecutive i with one 16-byte access, and the lanes of a class share the
+// address (an LDS broadcast).  Global memory is read and written row by row
+// (16-byte accesses, coalesced) through the LDS tile xs (pitch 68 fp32 / 66 fp64).
 // ENTRY (the WaterKron alphabet): entry (i, j) has the step S[i] * C[j] and the
 // codes are int32.
+constexpr int OS_THREADS = 256;  // four waves
+constexpr int OS_WROWS = 16;     // rows per wave: four lanes per row
+
+// v of lane q of this lane's quad (q a constant: a DPP quad_perm broadcast).
+template <int Q>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), Q * 0x55, 0xf, 0xf, false));
+}
+template <int Q>
+__device__ __forceinline__ double quad_bcast(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_mov_dpp(int(uint32_t(u)), Q * 0x55, 0xf, 0xf, false);
+    const uint32_t hi = __builtin_amdgcn_mov_dpp(int(uint32_t(u >> 32)), Q * 0x55, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
+template <typename T, bool ENTRY, int J>
+struct OsSweep {
+    // column J: rounding by its owner, then its error into the later columns
+    static __device__ __forceinline__ void step(T (&x)[16], const T* __restrict__ cqr, int q, T s, T rs,
+                                                const T* __restrict__ C, int j0, T tqmin, T tqmax,
+                                                std::conditional_t<ENTRY, int32_t, int8_t>* __restrict__ zcol) {
+        constexpr int I = J >> 2, QJ = J & 3;
+        T sj = s, rj = rs;
+        if (ENTRY) {
+            sj = s * C[j0 + J];
+            rj = sj == T(0) ? T(0) : T(1) / sj;
+        }
+        const T z = os_clamp(krint(x[I] * rj), tqmin, tqmax);
+        const T d = sj * z - x[I];
+        const bool own = q == QJ;
+        if (own) {
+            x[I] = d;  // from here on the owner's x[I] holds the error
+            zcol[J * (OS_ROWS + 1)] = std::conditional_t<ENTRY, int32_t, int8_t>(int(z));
+        }
+        const T db = quad_bcast<QJ>(d);
+        // columns 4 i + q > J for i >= I (the owner's own column J, and the
+        // columns 4 I + q <= J of the lanes before it, have zero coefficients)
+        const T* cj = cqr + J * 16;
+#pragma unroll
+        for (int g = I >> 2; g < 4; ++g) {
+            typedef T V4 __attribute__((ext_vector_type(4)));
+            V4 c;
+            if (sizeof(T) == 4) {
+                c = *reinterpret_cast<const V4*>(cj + 4 * g);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) c[e] = cj[4 * g + e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * g + e >= I) x[4 * g + e] = kfma(db, c[e], x[4 * g + e]);
+        }
+        OsSweep<T, ENTRY, J + 1>::step(x, cqr, q, s, rs, C, j0, tqmin, tqmax, zcol);
+    }
+};
 template <typename T, bool ENTRY>
-__global__ __launch_bounds__(OS_ROWS) void onesided_leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
-                                                                const T* __restrict__ NA, const T* __restrict__ S,
-                                                                const T* __restrict__ C, int np, int j0, int m, int n,
-                                                                int qmin, int qmax,
-                                                                std::conditional_t<ENTRY, int32_t, int8_t>* __restrict__ Z,
-                                                                int64_t ldz, T* __restrict__ V, int64_t ldv) {
-    constexpr int SB = 16;                       // sub-block width
+struct OsSweep<T, ENTRY, OS_BLK> {
+    static __device__ __forceinline__ void step(T (&)[16], const T*, int, T, T, const T*, int, T, T,
+                                                std::conditional_t<ENTRY, int32_t, int8_t>*) {}
+};
+
+template <typename T, bool ENTRY>
+__global__ __launch_bounds__(OS_THREADS) void onesided_leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
+                                                                   const T* __restrict__ NA, const T* __restrict__ S,
+                                                                   const T* __restrict__ C, int np, int j0, int m,
+                                                                   int n, int qmin, int qmax,
+                                                                   std::conditional_t<ENTRY, int32_t, int8_t>* __restrict__ Z,
+                                                                   int64_t ldz, T* __restrict__ V, int64_t ldv) {
+    using CodeT = std::conditional_t<ENTRY, int32_t, int8_t>;
     constexpr int VN = 16 / sizeof(T);           // entries per 16-byte access
     constexpr int SP = OS_BLK + 16 / sizeof(T);  // xs row pitch: 68 fp32 / 66 fp64
     typedef T VT __attribute__((ext_vector_type(VN)));
-    // cf[j][jj] = N[j0 + j][j0 + jj] strictly above the diagonal, 0 elsewhere
-    __shared__ __attribute__((aligned(16))) T cf[OS_BLK][OS_BLK];
+    __shared__ __attribute__((aligned(16))) T cq[4][OS_BLK][16];
     __shared__ __attribute__((aligned(16))) T xs[OS_ROWS * SP];
-    // codes: int8 packed four per word, or int32 (ENTRY); rows padded by one word
-    __shared__ uint32_t zs[ENTRY ? OS_BLK : OS_BLK / 4][OS_ROWS + 1];
-    const int lane = threadIdx.x, r0 = blockIdx.x * OS_ROWS;
-    // 16-byte loads: LPR lanes cover one 64-entry row, RPI rows per instruction,
-    // so the whole row block and the coefficient block are in flight at once
-    constexpr int LPR = OS_BLK / VN, RPI = 64 / LPR, NI = OS_ROWS / RPI;
-    const int lr = lane / LPR, lc = (lane % LPR) * VN;
+    __shared__ CodeT zs[OS_BLK][OS_ROWS + 1];  // zs[column][row]
+    const int t = threadIdx.x, r0 = blockIdx.x * OS_ROWS;
+    // 16-byte loads: LPR threads cover one 64-entry row, RPI rows per pass
+    constexpr int LPR = OS_BLK / VN, RPI = OS_THREADS / LPR, NI = OS_ROWS / RPI;
+    const int lr = t / LPR, lc = (t % LPR) * VN;
     {
         VT xa[NI], ca[NI];
 #pragma unroll
@@ -93,93 +155,40 @@ __global__ __launch_bounds__(OS_ROWS) void onesided_leaf_kernel(const T* __restr
         for (int i = 0; i < NI; ++i) *reinterpret_cast<VT*>(&xs[(RPI * i + lr) * SP + lc]) = xa[i];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            VT c = ca[i];
+            const int j = RPI * i + lr;
 #pragma unroll
-            for (int e = 0; e < VN; ++e)
-                if (lc + e <= RPI * i + lr) c[e] = T(0);
-            *reinterpret_cast<VT*>(&cf[RPI * i + lr][lc]) = c;
+            for (int e = 0; e < VN; ++e) {
+                const int c = lc + e;
+                cq[c & 3][j][c >> 2] = c > j ? ca[i][e] : T(0);
+            }
         }
     }
-    const T s = S[r0 + lane];
+    const int w = t >> 6, lane = t & 63, q = lane & 3;
+    const int row = OS_WROWS * w + (lane >> 2);  // this lane's row in the block
+    const T s = S[r0 + row];
     const T rs = s == T(0) ? T(0) : T(1) / s;
-    const T tqmin = T(qmin), tqmax = T(qmax);
-    T* const xr = xs + lane * SP;
     __syncthreads();
-#pragma unroll 1
-    for (int c0 = 0; c0 < OS_BLK; c0 += SB) {
-        T x[SB];
+    T x[16];
 #pragma unroll
-        for (int q = 0; q < SB / VN; ++q) {
-            const VT v = *reinterpret_cast<const VT*>(xr + c0 + VN * q);
+    for (int i = 0; i < 16; ++i) x[i] = xs[row * SP + 4 * i + q];
+    OsSweep<T, ENTRY, 0>::step(x, &cq[q][0][0], q, s, rs, C, j0, T(qmin), T(qmax), &zs[0][row]);
 #pragma unroll
-            for (int e = 0; e < VN; ++e) x[VN * q + e] = v[e];
-        }
-        uint32_t zp[SB / 4] = {};
-        T se[ENTRY ? SB : 1], rse[ENTRY ? SB : 1];  // per-entry steps and their reciprocals
-        if (ENTRY) {
-#pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                se[j] = s * C[j0 + c0 + j];
-                rse[j] = se[j] == T(0) ? T(0) : T(1) / se[j];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < SB; ++j) {
-            const T sj = ENTRY ? se[j] : s, rj = ENTRY ? rse[j] : rs;
-            const T z = os_clamp(krint(x[j] * rj), tqmin, tqmax);
-            const T d = sj * z - x[j];
-            x[j] = d;  // from here on x[j] holds the error
-            if (ENTRY)
-                zs[c0 + j][lane] = uint32_t(int(z));
-            else
-                zp[j >> 2] |= (uint32_t(int(z)) & 0xffu) << (8 * (j & 3));
-#pragma unroll
-            for (int q = (j + 1) / VN; q < SB / VN; ++q) {
-                const VT c = *reinterpret_cast<const VT*>(&cf[c0 + j][c0 + VN * q]);
-#pragma unroll
-                for (int e = 0; e < VN; ++e)
-                    if (VN * q + e > j) x[VN * q + e] = kfma(d, c[e], x[VN * q + e]);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < SB / VN; ++q) {
-            VT v;
-#pragma unroll
-            for (int e = 0; e < VN; ++e) v[e] = x[VN * q + e];
-            *reinterpret_cast<VT*>(xr + c0 + VN * q) = v;
-        }
-        if (!ENTRY) {
-#pragma unroll
-            for (int q = 0; q < SB / 4; ++q) zs[c0 / 4 + q][lane] = zp[q];
-        }
-        // the sub-block's errors into the row's later columns, VN at a time
-#pragma unroll 2
-        for (int g = c0 + SB; g < OS_BLK; g += VN) {
-            VT acc = *reinterpret_cast<const VT*>(xr + g);
-#pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                const VT c = *reinterpret_cast<const VT*>(&cf[c0 + j][g]);
-#pragma unroll
-                for (int e = 0; e < VN; ++e) acc[e] = kfma(x[j], c[e], acc[e]);
-            }
-            *reinterpret_cast<VT*>(xr + g) = acc;
-        }
-    }
-    __syncthreads();  // every lane's row of errors and codes is complete
+    for (int i = 0; i < 16; ++i) xs[row * SP + 4 * i + q] = x[i];
+    __syncthreads();  // every row's errors and codes are complete
 #pragma unroll
     for (int i = 0; i < NI; ++i)
         *reinterpret_cast<VT*>(D + int64_t(r0 + RPI * i + lr) * np + j0 + lc) =
             *reinterpret_cast<const VT*>(&xs[(RPI * i + lr) * SP + lc]);
-    // Z and V = s z row by row; row rr's scale is lane rr's s, read across the wave
-    const bool col_ok = j0 + lane < n;
-    const T cl = ENTRY ? C[j0 + lane] : T(1);  // this lane's column scale
-    for (int rr = 0; rr < OS_ROWS && r0 + rr < m; ++rr) {
-        const int z = ENTRY ? int(zs[lane][rr]) : int(int8_t(uint8_t(zs[lane >> 2][rr] >> (8 * (lane & 3)))));
-        const T sr = ENTRY ? lane_value(s, rr) * cl : lane_value(s, rr);
-        if (col_ok) {
-            Z[int64_t(r0 + rr) * ldz + j0 + lane] = std::remove_reference_t<decltype(Z[0])>(z);
-            V[int64_t(r0 + rr) * ldv + j0 + lane] = sr * T(z);
-        }
+    // Z and V = step * z: column t % 64, rows t / 64 + 4 k
+    const int col = t & 63;
+    const bool col_ok = j0 + col < n;
+    const T cl = ENTRY ? C[j0 + col] : T(1);
+#pragma unroll 4
+    for (int rr = t >> 6; rr < OS_ROWS; rr += OS_THREADS / 64) {
+        if (r0 + rr >= m || !col_ok) continue;
+        const int z = int(zs[col][rr]);
+        Z[int64_t(r0 + rr) * ldz + j0 + col] = CodeT(z);
+        V[int64_t(r0 + rr) * ldv + j0 + col] = S[r0 + rr] * cl * T(z);
     }
 }
 
@@ -215,10 +224,10 @@ struct OneSidedRun {
 
     kq_status leaf(int j0) {
         if (C)
-            hipLaunchKernelGGL((onesided_leaf_kernel<T, true>), dim3(unsigned(mp / OS_ROWS)), dim3(OS_ROWS), 0, st, X, D,
-                               NA, S, C, np, j0, m, n, qmin, qmax, static_cast<int32_t*>(Z), ldz, V, ldv);
+            hipLaunchKernelGGL((onesided_leaf_kernel<T, true>), dim3(unsigned(mp / OS_ROWS)), dim3(OS_THREADS), 0, st, X,
+                               D, NA, S, C, np, j0, m, n, qmin, qmax, static_cast<int32_t*>(Z), ldz, V, ldv);
         else
-            hipLaunchKernelGGL((onesided_leaf_kernel<T, false>), dim3(unsigned(mp / OS_ROWS)), dim3(OS_ROWS), 0, st, X,
+            hipLaunchKernelGGL((onesided_leaf_kernel<T, false>), dim3(unsigned(mp / OS_ROWS)), dim3(OS_THREADS), 0, st, X,
                                D, NA, S, C, np, j0, m, n, qmin, qmax, static_cast<int8_t*>(Z), ldz, V, ldv);
         KQ_LAUNCHED("onesided_leaf_kernel");
         return KQ_OK;
