@@ -10,9 +10,11 @@
 // columns in order.  The feedback is batched over column ranges:
 //   solve(j0, j1) = solve(j0, mid); X[:, mid:j1] += Delta[:, j0:mid] N[j0:mid, mid:j1];
 //                   solve(mid, j1)
-// down to 64-column leaves.  All of the method's work, m n (n - 1) flops, is in
-// those dense rectangular products (matrix cores) except the leaves' in-block
-// triangles (m n 63 flops), and the sequential depth is n / 64 leaves.
+// down to chunks of four 64-column leaves; inside a chunk each leaf first pulls
+// the products of the chunk's earlier leaves, X[:, leaf] += Delta[:, chunk start
+// : leaf] N[.., leaf], then sweeps.  All of the method's work, m n (n - 1) flops,
+// is in those dense rectangular products (matrix cores) except the leaves'
+// in-block triangles (m n 63 flops), and the sequential depth is n / 64 leaves.
 //
 // Leaf: one lane per row, the block's 64 pre-rounding values in registers and
 // the 64 x 64 diagonal block of N in LDS (read as wave-wide broadcasts).  The
@@ -33,6 +35,7 @@ namespace kq {
 
 constexpr int OS_BLK = 64;   // columns per leaf
 constexpr int OS_ROWS = 64;  // rows per leaf workgroup
+constexpr int OS_CHUNK = 4;  // leaves per chunk: the recursion's lowest unit
 
 __device__ __forceinline__ float os_clamp(float x, float lo, float hi) { return __builtin_amdgcn_fmed3f(x, lo, hi); }
 __device__ __forceinline__ double os_clamp(double x, double lo, double hi) { return kclamp(x, lo, hi); }
@@ -128,8 +131,8 @@ struct OsSweep<T, ENTRY, OS_BLK> {
 template <typename T, bool ENTRY>
 __global__ __launch_bounds__(OS_THREADS) void onesided_leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
                                                                    const T* __restrict__ NA, const T* __restrict__ S,
-                                                                   const T* __restrict__ C, int np, int j0, int m,
-                                                                   int n, int qmin, int qmax,
+                                                                   const T* __restrict__ C, int np, int c0, int j0,
+                                                                   int m, int n, int qmin, int qmax,
                                                                    std::conditional_t<ENTRY, int32_t, int8_t>* __restrict__ Z,
                                                                    int64_t ldz, T* __restrict__ V, int64_t ldv) {
     using CodeT = std::conditional_t<ENTRY, int32_t, int8_t>;
@@ -139,6 +142,7 @@ __global__ __launch_bounds__(OS_THREADS) void onesided_leaf_kernel(const T* __re
     __shared__ __attribute__((aligned(16))) T cq[4][OS_BLK][16];
     __shared__ __attribute__((aligned(16))) T xs[OS_ROWS * SP];
     __shared__ CodeT zs[OS_BLK][OS_ROWS + 1];  // zs[column][row]
+    __shared__ GemmSmem<T> sg;                  // the chunk product's staging
     const int t = threadIdx.x, r0 = blockIdx.x * OS_ROWS;
     // 16-byte loads: LPR threads cover one 64-entry row, RPI rows per pass
     constexpr int LPR = OS_BLK / VN, RPI = OS_THREADS / LPR, NI = OS_ROWS / RPI;
@@ -162,6 +166,14 @@ __global__ __launch_bounds__(OS_THREADS) void onesided_leaf_kernel(const T* __re
                 cq[c & 3][j][c >> 2] = c > j ? ca[i][e] : T(0);
             }
         }
+    }
+    // the chunk's earlier leaves: X[rows, j0:j0+64] += D[rows, c0:j0] N[c0:j0, j0:j0+64]
+    if (j0 > c0) {
+        WaveAcc<T> acc;
+        acc.zero();
+        tile_gemm<T, T, false, false, false>(D + int64_t(r0) * np + c0, np, NA + int64_t(c0) * np + j0, np, TILE,
+                                             TILE, j0 - c0, sg, acc);
+        for_each_acc(acc, [&](int r, int c, T v) { xs[r * SP + c] += v; });
     }
     const int w = t >> 6, lane = t & 63, q = lane & 3;
     const int row = OS_WROWS * w + (lane >> 2);  // this lane's row in the block
@@ -222,13 +234,13 @@ struct OneSidedRun {
     int64_t ldv;
     hipStream_t st;
 
-    kq_status leaf(int j0) {
+    kq_status leaf(int c0, int j0) {
         if (C)
             hipLaunchKernelGGL((onesided_leaf_kernel<T, true>), dim3(unsigned(mp / OS_ROWS)), dim3(OS_THREADS), 0, st, X,
-                               D, NA, S, C, np, j0, m, n, qmin, qmax, static_cast<int32_t*>(Z), ldz, V, ldv);
+                               D, NA, S, C, np, c0, j0, m, n, qmin, qmax, static_cast<int32_t*>(Z), ldz, V, ldv);
         else
             hipLaunchKernelGGL((onesided_leaf_kernel<T, false>), dim3(unsigned(mp / OS_ROWS)), dim3(OS_THREADS), 0, st, X,
-                               D, NA, S, C, np, j0, m, n, qmin, qmax, static_cast<int8_t*>(Z), ldz, V, ldv);
+                               D, NA, S, C, np, c0, j0, m, n, qmin, qmax, static_cast<int8_t*>(Z), ldz, V, ldv);
         KQ_LAUNCHED("onesided_leaf_kernel");
         return KQ_OK;
     }
@@ -239,9 +251,16 @@ struct OneSidedRun {
         return KQ_OK;
     }
     kq_status solve(int j0, int j1) {
-        if (j1 - j0 <= OS_BLK) return leaf(j0);
         const int blocks = (j1 - j0) / OS_BLK;
-        const int mid = j0 + OS_BLK * (blocks / 2);
+        if (blocks <= OS_CHUNK) {  // a chunk: each leaf pulls its earlier leaves' products
+            for (int l = 0; l < blocks; ++l) {
+                const kq_status s = leaf(j0, j0 + OS_BLK * l);
+                if (s != KQ_OK) return s;
+            }
+            return KQ_OK;
+        }
+        const int chunks = (blocks + OS_CHUNK - 1) / OS_CHUNK;
+        const int mid = j0 + OS_BLK * OS_CHUNK * (chunks / 2);
         kq_status s = solve(j0, mid);
         if (s != KQ_OK) return s;
         s = update(j0, mid, j1);
