@@ -245,11 +245,12 @@ def check_fp32_rows(g, bits, rows, label):
 # 260 x 900 two levels; 1536 x 1024 (79) three; 2048^2 (127) three, with a top
 # node large enough to run its stage 2 as a launch of its own, so both band
 # launch forms and the row-propagated errors carried across levels meet the
-# oracle entry by entry.
+# oracle entry by entry.  B = I runs the one-sided recursion, over chunks of
+# four 64-column leaves: 384 x 640 has two levels, 512 x 2048 (32 leaves) four.
 
 @pytest.mark.parametrize("m,n,two_sided", [(512, 512, True), (640, 384, True), (384, 640, False),
                                            (1000, 300, True), (260, 900, True), (1536, 1024, True),
-                                           (2048, 2048, True)])
+                                           (2048, 2048, True), (512, 2048, False)])
 def test_multilevel_fp64_full(m, n, two_sided):
     say("multilevel", m, n, "two-sided" if two_sided else "one-sided")
     c = synth.llm(m, n, 3, config=4, rows=1024)

@@ -93,7 +93,7 @@ def check_fp64(W, UA, UB, step, label):
 
 @pytest.mark.parametrize("m,n,two_sided", [(256, 256, True), (100, 70, True), (65, 65, True), (127, 129, True),
                                            (1, 50, True), (50, 1, True), (96, 80, False), (384, 640, False),
-                                           (520, 384, True)])
+                                           (520, 384, True), (1024, 1024, True), (256, 1536, False)])
 def test_waterkron_fp64_matches_oracle(m, n, two_sided):
     c = synth.spectral(m, n, config=2)
     _, UA = dense.prepare(c["A"], 0.01)
