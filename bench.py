@@ -101,6 +101,8 @@ def main() -> int:
                     help="only run K kron_quantize calls on the 4096x4096 workload (factors prepared first), "
                          "for kernel traces and counters; --one-sided runs them with U_B = NULL")
     ap.add_argument("--one-sided", action="store_true")
+    ap.add_argument("--prepare-calls", type=int, default=0, metavar="K",
+                    help="only run K kron_prepare calls on the workload's input factor, for kernel traces")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -113,6 +115,8 @@ def main() -> int:
         return copy_probe(torch, args.copy_probe)
     if args.core_calls:
         return core_calls(torch, args)
+    if args.prepare_calls:
+        return prepare_calls(torch, args)
     if args.shapes:
         return shape_report(torch)
 
@@ -542,6 +546,37 @@ def core_calls(torch, args):
         ts.append(a.elapsed_time(b))
     print(json.dumps({"core_calls": args.core_calls, "one_sided": bool(args.one_sided), "m": m, "n": n,
                       "ms": ts}), flush=True)
+    return 0
+
+
+def prepare_calls(torch, args):
+    """K kron_prepare calls on the bench workload's input factor A (n x n, from the
+    fp32 activation rows; damped, factored and inverted in fp64), nothing else
+    timed or run beside them (the profiled unit for kernel traces)."""
+    import synth
+    import two_sided_gptq_damped_amd as kq
+    from two_sided_gptq_damped_amd import pipeline
+
+    m, n, bits = args.m, args.n, args.bits
+    c = synth.llm(m, n, bits, config=3)
+    A = pipeline.factor(torch.from_numpy(np.ascontiguousarray(c["act"], dtype=np.float32)).to("cuda"))
+    U = torch.empty_like(A)
+    tr = torch.empty(1, dtype=torch.float64, device="cuda")
+    lam = torch.empty(1, dtype=torch.float64, device="cuda")
+    info = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = kq.workspace(kq.KQ_OP_PREPARE, torch.float32, n, 0)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(args.prepare_calls):
+        a.record()
+        kq.kron_prepare(A, c["damp"], U, ws, trace_out=tr, lambda_out=lam, info=info)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    if int(info.item()) != 0:
+        raise RuntimeError(f"kron_prepare: not positive definite (pivot {int(info.item())})")
+    print(json.dumps({"prepare_calls": args.prepare_calls, "d": n, "ms": ts}), flush=True)
     return 0
 
 
