@@ -110,8 +110,9 @@ struct Vec4<double> {
 // (off the tile) is mapped to that zero line.  Because N is upper triangular,
 // every update whose source is not strictly to the left / above its target then
 // multiplies by an exact zero, so the updates need no predicates (finished
-// entries only ever receive +0).  The exchange arrays start at zero so the
-// multiplied values are always finite.
+// entries only ever receive +0).  Every exchange slot a round reads is written
+// by that round's producer before the round's barrier, so nothing left in that
+// LDS by the prologue reaches a product, and every multiplied value is finite.
 //
 // Chunks.  The recursion stops at chunks of consecutive tile-diagonals
 // [c0, c1); inside a chunk the feedback between tiles is pulled by each leaf
