@@ -105,7 +105,7 @@ def main() -> int:
                     help="only run K kron_prepare calls on the workload's input factor, for kernel traces")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1 "
                           "(the per-matrix solver is not sharded across GPUs)"}))
         return 2
 
