@@ -297,8 +297,9 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     __shared__ __attribute__((aligned(16))) T stg[BATCH][2][ST * PK];
     // The leaf's LDS: the sweep's factor tables cB and cA (in the form the sweep
     // reads them, see below), the tile in the two layouts' exchange bufA / bufB,
-    // and the sweep's exchange xD / xR (one slice per round: errors by row,
-    // row-accumulated errors by column).  bufA .. xR are free until the sweep, so
+    // the sweep's exchange xD / xR (one slice per round: errors by row,
+    // row-accumulated errors by column), and the epilogue's operand and product
+    // (sNAk, ep).  bufA .. xR are free until the sweep, so
     // the prologue stages its two slices there (slice 0 in bufA / bufB, slice 1
     // at xD) and parks its products at xD, and the tables are built while the
     // first loads are in flight.
@@ -310,7 +311,9 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     T* const bufB = bufA + ST * PK;
     T* const xD = bufB + ST * PK;          // [round][row][diagonal of the round]
     T* const xR = xD + NROUND * ST * RD;  // [round][column][diagonal of the round]
-    static_assert(NRB * PB + ST * PT + 2 * ST * PK + 2 * NROUND * ST * RD <= sizeof(stg) / sizeof(T),
+    T* const sNAk = xR + NROUND * ST * RD;  // sNAk[k][c] = N_A[..k][..c], the epilogue's right operand
+    T* const ep = sNAk + ST * PB;            // the epilogue's product, row-major
+    static_assert(NRB * PB + ST * PT + 2 * ST * PK + 2 * NROUND * ST * RD + ST * PB + ST * ST <= sizeof(stg) / sizeof(T),
                   "staging area too small");
     static_assert((NRB * PB + ST * PT) % 4 == 0 && (NRB * PB + ST * PT + 2 * ST * PK) % 8 == 0,
                   "16-byte aligned bufA / bufB, 32-byte aligned exchange slices");
@@ -497,6 +500,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         sNAt[c * PA + r] = fna[u];
         cB[(r + ST) * PB + c] = fnb[u];  // N_B[r][c]
         cA[c * PT + ST + r] = fna[u];    // N_A[r][c]
+        sNAk[r * PB + c] = fna[u];
     }
     if (t < ST) {
         sNB[ST * PB + t] = T(0);
@@ -528,7 +532,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         acc[i] = blk ? X[int64_t(I * ST + r0 + i) * np + J * ST + b] : T(0);
-        sblk[i] = blk ? (ENTRY ? S[I * ST + r0 + i] * csb : S[I * ST + r0 + i]) : T(0);
+        sblk[i] = ENTRY ? S[I * ST + r0 + i] * csb : S[I * ST + r0 + i];
         crow[i] = T(0);
         ccol[i] = T(0);
     }
@@ -721,38 +725,36 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
                 cna[m][k] = nna[m][k];
             }
     }
-    // the last round's barrier made the errors and codes in bufB / bufA complete
-    if (!blk) return;  // no barriers follow
-    T dblk[4];
+    // the last round's barrier made the errors and codes in bufB / bufA complete.
+    // Epilogue: R[I, J] = rowpart + Delta + Delta strict(N_A[J, J]), the tile's
+    // complete row-propagated errors (read by the later leaves of the chunk and by
+    // the band products of the later nodes).  Waves 0..3 form the product on the
+    // matrix cores, one 16 x 16 quadrant each (Delta k-major in bufB), while
+    // waves 4..7 store Delta, the codes and V.
+    if (wv < 4) {
+        Q16<T> pq;
+        pq.zero();
+        pq.template mma<PK, PB, ST>(bufB + qr, sNAk + qc, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t gi = int64_t(I) * ST + r0 + i, gj = int64_t(J) * ST + b;
-        dblk[i] = bufB[b * PK + r0 + i];
-        const T z = bufA[(r0 + i) * PK + b];
-        D[gi * np + gj] = dblk[i];
-        if (gi < m && gj < n) {
-            Z[gi * ldz + gj] = CodeT<ENTRY>(z);
-            V[gi * ldv + gj] = sblk[i] * z;
+        for (int r = 0; r < 4; ++r) ep[(qr + Q16<T>::row(r, lane)) * ST + qc + Q16<T>::col(r, lane)] = pq.get(r);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t gi = int64_t(I) * ST + r0 + i, gj = int64_t(J) * ST + b;
+            const T dv = bufB[b * PK + r0 + i];
+            const T z = bufA[(r0 + i) * PK + b];
+            D[gi * np + gj] = dv;
+            if (gi < m && gj < n) {
+                Z[gi * ldz + gj] = CodeT<ENTRY>(z);
+                V[gi * ldv + gj] = sblk[i] * z;
+            }
         }
     }
-    // ---- epilogue: R[I, J] = rowpart + Delta + Delta strict(N_A[J, J]), the
-    // tile's complete row-propagated errors, read by the later leaves of the
-    // chunk and by the band products of the later nodes
-    {
-        T o[4];
+    __syncthreads();
+    if (!blk) return;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = crow[i] + dblk[i];
-#pragma unroll 8
-        for (int k = 0; k < ST; ++k) {
-            Vec4<T> d4;
-            d4.load(bufB + k * PK + r0);
-            const T nak = sNAt[b * PA + k];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = kfma(d4[i], nak, o[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) R[int64_t(I * ST + r0 + i) * np + J * ST + b] = o[i];
-    }
+    for (int i = 0; i < 4; ++i)
+        R[int64_t(I * ST + r0 + i) * np + J * ST + b] = crow[i] + bufB[b * PK + r0 + i] + ep[(r0 + i) * ST + b];
 }
 
 // Stage 1 at node [K0, K1) with split mid: for the target tiles (I', J) of
