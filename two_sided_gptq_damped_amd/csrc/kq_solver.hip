@@ -121,7 +121,11 @@ struct Vec4<double> {
 //   rowpart = R[I, J] + sum_{c0 - I <= J' < J} Delta[I, J'] N_A[J', J]
 //   X[I, J] += N_B[I, I]^T rowpart + sum_{c0 - J <= I' < I} N_B[I', I]^T R[I', J]
 // (R[I', J] of the chunk's earlier tiles is complete), and after the sweep the
-// leaf writes R[I, J] = rowpart + Delta[I, J] N_A[J, J].  The sums over the
+// leaf writes R[I, J] = rowpart + Delta[I, J] N_A[J, J].  Both come out of the
+// sweep: N_B[I, I]^T rowpart is rowpart plus the in-tile column feedback of
+// rowpart, and the sweep's row-accumulated errors start at rowpart, so its column
+// feedback carries that part and every entry's final row-accumulated value is
+// its entry of R[I, J].  The sums over the
 // slices before diagonal K - 1 are pre-accumulated by launch K - 1 (see the
 // kernel), so the leaf itself multiplies only the two freshest slices.  The
 // 32 x 32 x 32 products run on the matrix cores: their operands are staged
@@ -285,21 +289,17 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
                                                    CodeT<ENTRY>* __restrict__ Z, int64_t ldz, T* __restrict__ V,
                                                    int64_t ldv, T* __restrict__ P, int pt) {
     constexpr int PB = ST + 4;  // 16-byte aligned rows for the vector reads
-    constexpr int PA = ST + 1;  // column ST is the zero sentinel
     constexpr int PK = ST + 4;  // k-major staging rows, 16-byte aligned
-    __shared__ __attribute__((aligned(16))) T sNB[(ST + 1) * PB];  // sNB[as][a] = N_B[..as][..a], row ST = 0
-    __shared__ T sNAt[ST * PA];                                    // sNAt[b][bs] = N_A[..bs][..b], col ST = 0
     constexpr int RD = 2 * LEAF_E;                      // diagonals per sweep round (one wave's two groups)
     constexpr int NROUND = (2 * ST - 1 + RD - 1) / RD;  // sweep rounds
     // Chunk operands of up to BATCH slices: A(r, k) at [k][r], B(k, c) at [k][c]
     // (the precompute workgroups), or the leaf's layout below.
-    constexpr int BATCH = sizeof(T) == 4 ? 14 : 7;  // staged together (LDS budget)
+    constexpr int BATCH = 7;  // staged together (LDS budget)
     __shared__ __attribute__((aligned(16))) T stg[BATCH][2][ST * PK];
     // The leaf's LDS: the sweep's factor tables cB and cA (in the form the sweep
     // reads them, see below), the tile in the two layouts' exchange bufA / bufB,
-    // the sweep's exchange xD / xR (one slice per round: errors by row,
-    // row-accumulated errors by column), and the epilogue's operand and product
-    // (sNAk, ep).  bufA .. xR are free until the sweep, so
+    // and the sweep's exchange xD / xR (one slice per round: errors by row,
+    // row-accumulated errors by column).  bufA .. xR are free until the sweep, so
     // the prologue stages its two slices there (slice 0 in bufA / bufB, slice 1
     // at xD) and parks its products at xD, and the tables are built while the
     // first loads are in flight.
@@ -311,9 +311,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     T* const bufB = bufA + ST * PK;
     T* const xD = bufB + ST * PK;          // [round][row][diagonal of the round]
     T* const xR = xD + NROUND * ST * RD;  // [round][column][diagonal of the round]
-    T* const sNAk = xR + NROUND * ST * RD;  // sNAk[k][c] = N_A[..k][..c], the epilogue's right operand
-    T* const ep = sNAk + ST * PB;            // the epilogue's product, row-major
-    static_assert(NRB * PB + ST * PT + 2 * ST * PK + 2 * NROUND * ST * RD + ST * PB + ST * ST <= sizeof(stg) / sizeof(T),
+    static_assert(NRB * PB + ST * PT + 2 * ST * PK + 2 * NROUND * ST * RD <= sizeof(stg) / sizeof(T),
                   "staging area too small");
     static_assert((NRB * PB + ST * PT) % 4 == 0 && (NRB * PB + ST * PT + 2 * ST * PK) % 8 == 0,
                   "16-byte aligned bufA / bufB, 32-byte aligned exchange slices");
@@ -464,8 +462,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     // entry (a, b) sits at a fixed offset from a per-entry base,
     //   cB[(d - b + ST) PB + a] = N_B[d - b][a]   (column source (d - b, b))
     //   cA[b PT + d - a + ST]   = N_A[d - a][b]   (row source (a, d - a)),
-    // zero wherever the source lies off the tile (and, as in sNB / sNAt, on and
-    // below the diagonal), so the unrolled sweep spends no arithmetic on
+    // zero wherever the source lies off the tile (and on and below the
+    // diagonal: the unit diagonal is replaced by 0), so the unrolled sweep spends no arithmetic on
     // addresses.  First the zero lines, four entries per store (cB rows [0, ST)
     // and [2 ST, NRB), cA columns [0, ST) and [2 ST, PT) of every row), while the
     // loads are in flight; then the factor entries.
@@ -496,15 +494,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
             fnb[u] = T(0);
             fna[u] = T(0);
         }
-        sNB[r * PB + c] = fnb[u];
-        sNAt[c * PA + r] = fna[u];
         cB[(r + ST) * PB + c] = fnb[u];  // N_B[r][c]
         cA[c * PT + ST + r] = fna[u];    // N_A[r][c]
-        sNAk[r * PB + c] = fna[u];
-    }
-    if (t < ST) {
-        sNB[ST * PB + t] = T(0);
-        sNAt[t * PA + ST] = T(0);
     }
 
     // Two layouts of the tile over the threads, both with column b = t % 32:
@@ -526,53 +517,43 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         dg[i] = b + ar[i];
         sc[i] = ENTRY ? S[I * ST + ar[i]] * csb : S[I * ST + ar[i]];
         rs[i] = sc[i] == T(0) ? T(0) : T(1) / sc[i];
-        rp[i] = T(0);
     }
-    T acc[4], crow[4], ccol[4], sblk[4];
+    T acc[4], sblk[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         acc[i] = blk ? X[int64_t(I * ST + r0 + i) * np + J * ST + b] : T(0);
         sblk[i] = ENTRY ? S[I * ST + r0 + i] * csb : S[I * ST + r0 + i];
-        crow[i] = T(0);
-        ccol[i] = T(0);
     }
     __syncthreads();
 
-    // ---- prologue: rowpart (crow) and the column feedback (ccol), block layout
+    // ---- prologue: rowpart (crow) and the chunk's column part (ccol), block layout.
+    // X gets rowpart + the column part here; the in-tile column feedback of
+    // rowpart, strict(N_B[I, I])^T rowpart, comes from the sweep: its
+    // row-accumulated values start at rowpart (rp below), so every entry's
+    // column sources pass their rowpart on with their errors, and each entry's
+    // final row-accumulated value is R[I, J] = rowpart + Delta N_A[J, J].
     {
         Q16<T> pq;
 #pragma unroll
         for (int r = 0; r < 4; ++r) pq.set(r, pin[r]);
         products(pq);  // the freshest slices
-        // the quadrants reach the block layout through the staging area:
-        // park[0] = rowpart (also the right operand of the in-tile column
-        // feedback), park[1] = the column part
+        // the quadrants reach the block and sweep layouts through the staging
+        // area: park[0] = rowpart, park[1] = the column part
         T* const park = xD;
-        auto park_quadrant = [&]() {
+        __syncthreads();  // staged operands consumed
+        {
             T* q = park + part * ST * ST + qr * ST + qc;
 #pragma unroll
             for (int r = 0; r < 4; ++r) q[Q16<T>::row(r, lane) * ST + Q16<T>::col(r, lane)] = pq.get(r);
-        };
-        __syncthreads();  // staged operands consumed
-        if (part == 0) park_quadrant();
-        __syncthreads();  // rowpart complete
-        if (part == 1) {
-            // the in-tile column feedback strict(N_B[I, I])^T rowpart;
-            // strict(N_B[I, I])^T (r, k) = N_B[k][r], k-major in sNB already
-            pq.template mma<PB, ST, ST>(sNB + qr, park + qc, lane);
-            park_quadrant();
         }
         __syncthreads();
         if (blk) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const T p0 = park[(r0 + i) * ST + b], p1 = park[ST * ST + (r0 + i) * ST + b];
-                crow[i] = p0;
-                ccol[i] = p1;
-            }
+            for (int i = 0; i < 4; ++i) acc[i] += park[(r0 + i) * ST + b] + park[ST * ST + (r0 + i) * ST + b];
         }
+        // read before the barrier below: the sweep's first round writes xD
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += crow[i] + ccol[i];
+        for (int i = 0; i < E; ++i) rp[i] = park[ar[i] * ST + b];
     }
 
     // ---- to the sweep layout through bufA (free: the prologue staged and parked
@@ -725,36 +706,29 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
                 cna[m][k] = nna[m][k];
             }
     }
-    // the last round's barrier made the errors and codes in bufB / bufA complete.
-    // Epilogue: R[I, J] = rowpart + Delta + Delta strict(N_A[J, J]), the tile's
-    // complete row-propagated errors (read by the later leaves of the chunk and by
-    // the band products of the later nodes).  Waves 0..3 form the product on the
-    // matrix cores, one 16 x 16 quadrant each (Delta k-major in bufB), while
-    // waves 4..7 store Delta, the codes and V.
-    if (wv < 4) {
-        Q16<T> pq;
-        pq.zero();
-        pq.template mma<PK, PB, ST>(bufB + qr, sNAk + qc, lane);
+    // The last round's barrier made the errors and codes in bufB / bufA and every
+    // entry's final row-accumulated value in xR complete.  Epilogue: waves 0..3
+    // write R[I, J] = rowpart + Delta N_A[J, J] (read by the later leaves of the
+    // chunk and by the band products of the later nodes), gathered from the
+    // rounds that published it; waves 4..7 store Delta, the codes and V.
+    if (blk) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ep[(qr + Q16<T>::row(r, lane)) * ST + qc + Q16<T>::col(r, lane)] = pq.get(r);
+        for (int i = 0; i < 4; ++i) {
+            const int d = r0 + i + b;  // the entry's element diagonal
+            R[int64_t(I * ST + r0 + i) * np + J * ST + b] = xR[((d / RD) * ST + b) * RD + d % RD];
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t gi = int64_t(I) * ST + r0 + i, gj = int64_t(J) * ST + b;
-            const T dv = bufB[b * PK + r0 + i];
             const T z = bufA[(r0 + i) * PK + b];
-            D[gi * np + gj] = dv;
+            D[gi * np + gj] = bufB[b * PK + r0 + i];
             if (gi < m && gj < n) {
                 Z[gi * ldz + gj] = CodeT<ENTRY>(z);
                 V[gi * ldv + gj] = sblk[i] * z;
             }
         }
     }
-    __syncthreads();
-    if (!blk) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        R[int64_t(I * ST + r0 + i) * np + J * ST + b] = crow[i] + bufB[b * PK + r0 + i] + ep[(r0 + i) * ST + b];
 }
 
 // Stage 1 at node [K0, K1) with split mid: for the target tiles (I', J) of
