@@ -276,6 +276,7 @@ struct Q16<double> {
 constexpr int LEAF_THREADS = 512;   // the chunk products and the table set-up
 constexpr int SWEEP_THREADS = 512;  // the sweep: two entries per thread
 constexpr int LEAF_E = ST * ST / SWEEP_THREADS;
+static_assert(SWEEP_THREADS == LEAF_THREADS, "every thread of the leaf takes part in the sweep");
 
 template <bool ENTRY>
 using CodeT = std::conditional_t<ENTRY, int32_t, int8_t>;
@@ -301,8 +302,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     // and the sweep's exchange xD / xR (one slice per round: errors by row,
     // row-accumulated errors by column).  bufA .. xR are free until the sweep, so
     // the prologue stages its two slices there (slice 0 in bufA / bufB, slice 1
-    // at xD) and parks its products at xD, and the tables are built while the
-    // first loads are in flight.
+    // at xD); it parks its products at pk, past the sweep's arrays, so the
+    // sweep can start as soon as they are read.
     constexpr int NRB = 3 * ST + 4;  // rows of cB; d - b + ST stays in [1, NRB) for d <= 2 ST + 3
     constexpr int PT = 3 * ST + 4;   // row pitch of cA (even: lanes step PT + 1 apart)
     T* const cB = &stg[0][0][0];
@@ -311,7 +312,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     T* const bufB = bufA + ST * PK;
     T* const xD = bufB + ST * PK;          // [round][row][diagonal of the round]
     T* const xR = xD + NROUND * ST * RD;  // [round][column][diagonal of the round]
-    static_assert(NRB * PB + ST * PT + 2 * ST * PK + 2 * NROUND * ST * RD <= sizeof(stg) / sizeof(T),
+    T* const pk = xR + NROUND * ST * RD;  // the prologue's products: rowpart, then the column part
+    static_assert(NRB * PB + ST * PT + 2 * ST * PK + 2 * NROUND * ST * RD + 2 * ST * ST <= sizeof(stg) / sizeof(T),
                   "staging area too small");
     static_assert((NRB * PB + ST * PT) % 4 == 0 && (NRB * PB + ST * PT + 2 * ST * PK) % 8 == 0,
                   "16-byte aligned bufA / bufB, 32-byte aligned exchange slices");
@@ -466,7 +468,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     // diagonal: the unit diagonal is replaced by 0), so the unrolled sweep spends no arithmetic on
     // addresses.  First the zero lines, four entries per store (cB rows [0, ST)
     // and [2 ST, NRB), cA columns [0, ST) and [2 ST, PT) of every row), while the
-    // loads are in flight; then the factor entries.
+    // loads are in flight; the factor entries follow once the prologue's products
+    // are issued (the tables are read only by the sweep).
     {
         constexpr int ZB0 = ST * PB / 4, ZB1 = (NRB - 2 * ST) * PB / 4;
         constexpr int ZAR = ST / 4 + (PT - 2 * ST) / 4;  // per cA row
@@ -487,16 +490,6 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
             z4.store(q);
         }
     }
-#pragma unroll
-    for (int u = 0; u < FE; ++u) {
-        const int e = t + u * LEAF_THREADS, r = e >> 5, c = e & 31;
-        if (r == c) {
-            fnb[u] = T(0);
-            fna[u] = T(0);
-        }
-        cB[(r + ST) * PB + c] = fnb[u];  // N_B[r][c]
-        cA[c * PT + ST + r] = fna[u];    // N_A[r][c]
-    }
 
     // Two layouts of the tile over the threads, both with column b = t % 32:
     //   block layout  threads t < 256, rows r0 + i (four each): vector LDS reads,
@@ -515,16 +508,13 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     for (int i = 0; i < E; ++i) {
         ar[i] = (E * g - b + i) & (ST - 1);
         dg[i] = b + ar[i];
+        x[i] = X[int64_t(I * ST + ar[i]) * np + J * ST + b];
         sc[i] = ENTRY ? S[I * ST + ar[i]] * csb : S[I * ST + ar[i]];
         rs[i] = sc[i] == T(0) ? T(0) : T(1) / sc[i];
     }
-    T acc[4], sblk[4];
+    T sblk[4];  // the block layout's row scales (V in the epilogue)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        acc[i] = blk ? X[int64_t(I * ST + r0 + i) * np + J * ST + b] : T(0);
-        sblk[i] = ENTRY ? S[I * ST + r0 + i] * csb : S[I * ST + r0 + i];
-    }
-    __syncthreads();
+    for (int i = 0; i < 4; ++i) sblk[i] = ENTRY ? S[I * ST + r0 + i] * csb : S[I * ST + r0 + i];
 
     // ---- prologue: rowpart (crow) and the chunk's column part (ccol), block layout.
     // X gets rowpart + the column part here; the in-tile column feedback of
@@ -537,35 +527,32 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
 #pragma unroll
         for (int r = 0; r < 4; ++r) pq.set(r, pin[r]);
         products(pq);  // the freshest slices
-        // the quadrants reach the block and sweep layouts through the staging
-        // area: park[0] = rowpart, park[1] = the column part
-        T* const park = xD;
-        __syncthreads();  // staged operands consumed
+        // the tables' factor entries, while the products run
+#pragma unroll
+        for (int u = 0; u < FE; ++u) {
+            const int e = t + u * LEAF_THREADS, r = e >> 5, c = e & 31;
+            if (r == c) {
+                fnb[u] = T(0);
+                fna[u] = T(0);
+            }
+            cB[(r + ST) * PB + c] = fnb[u];  // N_B[r][c]
+            cA[c * PT + ST + r] = fna[u];    // N_A[r][c]
+        }
+        // the quadrants reach the sweep layout through pk (row-major):
+        // pk[0] = rowpart, pk[1] = the column part
         {
-            T* q = park + part * ST * ST + qr * ST + qc;
+            T* q = pk + part * ST * ST + qr * ST + qc;
 #pragma unroll
             for (int r = 0; r < 4; ++r) q[Q16<T>::row(r, lane) * ST + Q16<T>::col(r, lane)] = pq.get(r);
         }
-        __syncthreads();
-        if (blk) {
+        __syncthreads();  // the products and the tables are complete
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] += park[(r0 + i) * ST + b] + park[ST * ST + (r0 + i) * ST + b];
+        for (int i = 0; i < E; ++i) {
+            const T rowpart = pk[ar[i] * ST + b];
+            x[i] += rowpart + pk[ST * ST + ar[i] * ST + b];
+            rp[i] = rowpart;
         }
-        // read before the barrier below: the sweep's first round writes xD
-#pragma unroll
-        for (int i = 0; i < E; ++i) rp[i] = park[ar[i] * ST + b];
     }
-
-    // ---- to the sweep layout through bufA (free: the prologue staged and parked
-    // elsewhere, and every read of its staging happened before its last barrier)
-    if (blk) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bufA[(r0 + i) * PK + b] = acc[i];
-    }
-    __syncthreads();
-    if (t >= SWEEP_THREADS) return;  // the later barriers wait for the sweep's waves only
-#pragma unroll
-    for (int i = 0; i < E; ++i) x[i] = bufA[ar[i] * PK + b];
 
     // ---- the sweep: 2 ST - 1 element anti-diagonals, four per round.
     // Slot i of group g holds diagonal 2 g + i (and 2 g + i + 32, entries past the
