@@ -313,7 +313,9 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
     T* const xD = bufB + ST * PK;          // [round][row][diagonal of the round]
     T* const xR = xD + NROUND * ST * RD;  // [round][column][diagonal of the round]
     T* const pk = xR + NROUND * ST * RD;  // the prologue's products: rowpart, then the column part
-    static_assert(NRB * PB + ST * PT + 2 * ST * PK + 2 * NROUND * ST * RD + 2 * ST * ST <= sizeof(stg) / sizeof(T),
+    T* const junk = pk + 2 * ST * ST;     // one slot per lane for the sweep's discarded stores
+    static_assert(NRB * PB + ST * PT + 2 * ST * PK + 2 * NROUND * ST * RD + 2 * ST * ST + 64 <=
+                      sizeof(stg) / sizeof(T),
                   "staging area too small");
     static_assert((NRB * PB + ST * PT) % 4 == 0 && (NRB * PB + ST * PT + 2 * ST * PK) % 8 == 0,
                   "16-byte aligned bufA / bufB, 32-byte aligned exchange slices");
@@ -635,23 +637,25 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict_
         quantize_fast(x3, sc[1], rs[1], tqmin, tqmax, z3, v);
         const T e3 = v - x3;
         const T q3 = r3 + e3;
-        if (g == ((d0 & (ST - 1)) >> 1) || g == ((d0 & (ST - 1)) >> 1) + 1) {
-            // each half publishes its two diagonals: errors by row, row-accumulated errors by column
-            const int m0 = upper ? 2 : 0;
-            const T ea = upper ? e2 : e0, eb = upper ? e3 : e1;
-            xD[(r * ST + ar[0]) * RD + m0] = ea;
-            xD[(r * ST + ar[1]) * RD + m0 + 1] = eb;
-            xR[(r * ST + b) * RD + m0] = upper ? q2 : q0;
-            xR[(r * ST + b) * RD + m0 + 1] = upper ? q3 : q1;
-            if (dg[0] == d0 + m0) {
-                bufB[b * PK + ar[0]] = ea;
-                bufA[ar[0] * PK + b] = upper ? z2 : z0;
-            }
-            if (dg[1] == d0 + m0 + 1) {
-                bufB[b * PK + ar[1]] = eb;
-                bufA[ar[1] * PK + b] = upper ? z3 : z1;
-            }
-        }
+        // The producer wave holds exactly the groups of d0 .. d0 + 3, so every lane
+        // publishes its half's two diagonals: errors by row, row-accumulated
+        // errors by column.
+        const int m0 = upper ? 2 : 0;
+        const T ea = upper ? e2 : e0, eb = upper ? e3 : e1;
+        xD[(r * ST + ar[0]) * RD + m0] = ea;
+        xD[(r * ST + ar[1]) * RD + m0 + 1] = eb;
+        xR[(r * ST + b) * RD + m0] = upper ? q2 : q0;
+        xR[(r * ST + b) * RD + m0 + 1] = upper ? q3 : q1;
+        // A rounded entry's error and code also go to bufB / bufA.  A slot whose
+        // entry lies on the diagonal 32 later (rounds before the middle) writes its
+        // stand-in values there too: the entry's own round overwrites them.  After
+        // the middle such entries are done, and those lanes write to junk instead.
+        const bool late = RD * r >= ST;
+        const bool keep0 = !late || dg[0] == d0 + m0, keep1 = !late || dg[1] == d0 + m0 + 1;
+        *(keep0 ? bufB + b * PK + ar[0] : junk + lane) = ea;
+        *(keep0 ? bufA + ar[0] * PK + b : junk + lane) = upper ? z2 : z0;
+        *(keep1 ? bufB + b * PK + ar[1] : junk + lane) = eb;
+        *(keep1 ? bufA + ar[1] * PK + b : junk + lane) = upper ? z3 : z1;
     };
     // every entry takes round r's feedback
     auto feedback = [&](const VR& rv, const VR (&dd)[E], const T (&nb)[RD][E], const T (&na)[RD][E]) {
