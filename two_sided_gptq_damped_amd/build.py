@@ -4,7 +4,10 @@
 
 Compiles every csrc/*.hip translation unit in parallel, then links one shared
 object.  The packed-fp32 target feature is disabled for device code (ordinary
-float code is still vectorised by the compiler where it helps).
+float code is still vectorised by the compiler where it helps).  Kernel
+arguments are preloaded into scalar registers at launch (gfx950 supports it; a
+kernel's first arguments need no memory load then, and the code still runs where
+the firmware does not preload, through a prologue that loads them).
 """
 from __future__ import annotations
 
@@ -22,6 +25,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-kernarg-preload-count=16",
           "-Wno-unused-result"]
 
 

@@ -51,6 +51,29 @@ namespace kq {
 constexpr int ST = 32;    // scheduling tile edge
 constexpr int CHUNK = 16;  // tile-diagonals per recursion leaf (chunk)
 
+// Byte offsets of the solver's arrays in its workspace (see the layout above),
+// from the 32-tile counts and the element size alone, so that a kernel finds
+// every array from the workspace base (its launch then carries one pointer).
+// The padded extents are multiples of 64, so every array size is a multiple of
+// 256 bytes and the arrays are 256-byte aligned.
+struct WsOffsets {
+    int64_t NA, NB, X, D, R, P, S, C, end;
+};
+__host__ __device__ inline WsOffsets ws_offsets(int64_t Mt, int64_t Nt, int64_t es) {
+    const int64_t mp = Mt * ST, np = Nt * ST;
+    WsOffsets o;
+    o.NA = 0;
+    o.NB = o.NA + np * np * es;
+    o.X = o.NB + mp * mp * es;
+    o.D = o.X + mp * np * es;
+    o.R = o.D + mp * np * es;
+    o.P = o.R + mp * np * es;  // two tile-diagonals of two 32 x 32 parts per tile
+    o.S = o.P + 2 * 2 * ST * ST * (Mt < Nt ? Mt : Nt) * es;
+    o.C = o.S + mp * es;
+    o.end = o.C + np * es;
+    return o;
+}
+
 // N[r][c] = U[r][c] / U[r][r] for c >= r inside d x d; identity in the padding.
 // Rows blockIdx.y, + gridDim.y, ...; each thread four consecutive columns (dp is
 // a multiple of 64, so they are in range and the store is 16-byte aligned).
@@ -282,13 +305,22 @@ template <bool ENTRY>
 using CodeT = std::conditional_t<ENTRY, int32_t, int8_t>;
 
 template <typename T, bool ENTRY>
-__global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(const T* __restrict__ X, T* __restrict__ D,
-                                                   const T* __restrict__ NA, const T* __restrict__ NB,
-                                                   const T* __restrict__ S, const T* __restrict__ CS,
-                                                   T* __restrict__ R, int np, int mp, int Mt, int Nt, int K,
-                                                   int c0, int c1, int m, int n, int qmin, int qmax,
+__global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(int K, int c0, int c1, int Mt, int Nt, int qmin, int qmax,
+                                                   char* __restrict__ ws, int m, int n,
                                                    CodeT<ENTRY>* __restrict__ Z, int64_t ldz, T* __restrict__ V,
-                                                   int64_t ldv, T* __restrict__ P, int pt) {
+                                                   int64_t ldv) {
+    // the arguments the kernel starts with come first (the launch preloads them
+    // into scalar registers); the arrays are found from the workspace base
+    const WsOffsets wo = ws_offsets(Mt, Nt, sizeof(T));
+    const int np = Nt * ST, mp = Mt * ST, pt = Mt < Nt ? Mt : Nt;
+    T* const D = reinterpret_cast<T*>(ws + wo.D);
+    T* const R = reinterpret_cast<T*>(ws + wo.R);
+    T* const P = reinterpret_cast<T*>(ws + wo.P);
+    const T* const NA = reinterpret_cast<const T*>(ws + wo.NA);
+    const T* const NB = reinterpret_cast<const T*>(ws + wo.NB);
+    const T* const X = reinterpret_cast<const T*>(ws + wo.X);
+    const T* const S = reinterpret_cast<const T*>(ws + wo.S);
+    const T* const CS = reinterpret_cast<const T*>(ws + wo.C);
     constexpr int PB = ST + 4;  // 16-byte aligned rows for the vector reads
     constexpr int PK = ST + 4;  // k-major staging rows, 16-byte aligned
     constexpr int RD = 2 * LEAF_E;                      // diagonals per sweep round (one wave's two groups)
@@ -929,24 +961,18 @@ SolverLayout solver_layout(kq_dtype dtype, int64_t m, int64_t n) {
     L.np = round_up(n, TILE);
     L.Mt = L.mp / ST;
     L.Nt = L.np / ST;
-    size_t off = 0;
-    auto take = [&](size_t count) {
-        size_t o = off;
-        off += align256(count * es);
-        return o;
-    };
-    L.off_NA = take(size_t(L.np) * L.np);
-    L.off_NB = take(size_t(L.mp) * L.mp);
-    L.off_X = take(size_t(L.mp) * L.np);
-    L.off_D = take(size_t(L.mp) * L.np);
-    L.off_R = take(size_t(L.mp) * L.np);
-    // the leaves' pre-accumulated chunk products: two tile-diagonals of two parts
-    L.off_P = take(size_t(2 * 2 * ST * ST) * size_t(L.Mt < L.Nt ? L.Mt : L.Nt));
-    L.off_S = take(size_t(L.mp));
-    L.off_C = take(size_t(L.np));
-    L.off_L = off;  // loss scratch (fp64): 1 / U_A,jj, 1 / U_B,ii, partial sums
-    off += align256((size_t(L.np) + size_t(L.mp) + ELOSS_PARTS) * sizeof(double));
-    L.bytes = off;
+    static_assert(TILE % 64 == 0, "array sizes stay multiples of 256 bytes");
+    const WsOffsets o = ws_offsets(L.Mt, L.Nt, int64_t(es));
+    L.off_NA = size_t(o.NA);
+    L.off_NB = size_t(o.NB);
+    L.off_X = size_t(o.X);
+    L.off_D = size_t(o.D);
+    L.off_R = size_t(o.R);
+    L.off_P = size_t(o.P);
+    L.off_S = size_t(o.S);
+    L.off_C = size_t(o.C);
+    L.off_L = align256(size_t(o.end));  // loss scratch (fp64): 1 / U_A,jj, 1 / U_B,ii, partial sums
+    L.bytes = L.off_L + align256((size_t(L.np) + size_t(L.mp) + ELOSS_PARTS) * sizeof(double));
     return L;
 }
 
@@ -961,6 +987,7 @@ struct SolverRun {
     T* V;
     int64_t ldv;
     hipStream_t st;
+    char* ws;  // the workspace base (the leaves find their arrays from it)
 
     kq_status leaf(int K, int c0, int c1) {
         const int Mt = int(L.Mt), Nt = int(L.Nt);
@@ -970,15 +997,12 @@ struct SolverRun {
         // the sweep of diagonal K, and the chunk products of K + 1 when it is in
         // the chunk (behind up to 7 idle workgroups that align them with the XCDs)
         const dim3 grid(tiles(K) + (K + 1 < c1 ? (8 - tiles(K) % 8) % 8 + tiles(K + 1) : 0));
-        const int pt = int(L.Mt < L.Nt ? L.Mt : L.Nt);
         if (C)
-            hipLaunchKernelGGL((leaf_kernel<T, true>), grid, dim3(LEAF_THREADS), 0, st, X, D, NA, NB, S, C, R,
-                               int(L.np), int(L.mp), Mt, Nt, K, c0, c1, m, n, qmin, qmax, static_cast<int32_t*>(Z),
-                               ldz, V, ldv, P, pt);
+            hipLaunchKernelGGL((leaf_kernel<T, true>), grid, dim3(LEAF_THREADS), 0, st, K, c0, c1, Mt, Nt, qmin,
+                               qmax, ws, m, n, static_cast<int32_t*>(Z), ldz, V, ldv);
         else
-            hipLaunchKernelGGL((leaf_kernel<T, false>), grid, dim3(LEAF_THREADS), 0, st, X, D, NA, NB, S, C, R,
-                               int(L.np), int(L.mp), Mt, Nt, K, c0, c1, m, n, qmin, qmax, static_cast<int8_t*>(Z),
-                               ldz, V, ldv, P, pt);
+            hipLaunchKernelGGL((leaf_kernel<T, false>), grid, dim3(LEAF_THREADS), 0, st, K, c0, c1, Mt, Nt, qmin,
+                               qmax, ws, m, n, static_cast<int8_t*>(Z), ldz, V, ldv);
         KQ_LAUNCHED("leaf_kernel");
         return KQ_OK;
     }
@@ -1063,7 +1087,7 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
                      reinterpret_cast<T*>(base + L.off_X), reinterpret_cast<T*>(base + L.off_D),
                      reinterpret_cast<T*>(base + L.off_R), reinterpret_cast<T*>(base + L.off_P),
                      reinterpret_cast<T*>(base + L.off_S),
-                     q.col_scales ? reinterpret_cast<T*>(base + L.off_C) : nullptr, q.codes, q.ldc, V, ldv, st};
+                     q.col_scales ? reinterpret_cast<T*>(base + L.off_C) : nullptr, q.codes, q.ldc, V, ldv, st, base};
     const int threads = 256;
     auto blocks = [&](int64_t count) { return dim3(unsigned((count + threads - 1) / threads)); };
     auto rows = [&](int64_t cols, int64_t nrows) {  // the kernels loop over rows beyond the grid's y extent
