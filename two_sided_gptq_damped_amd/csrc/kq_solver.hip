@@ -784,9 +784,9 @@ struct Band {
 
 // Stage 1 block: row block P, the qi-th column block counted from the row's last
 // (the last has the longest K range at the top node).
-template <typename T>
+template <typename T, bool SPLIT, typename Smem>
 __device__ void band_stage1(const T* __restrict__ D, const T* __restrict__ NA, T* __restrict__ R, int np,
-                            int Nt, int K0, int mid, int K1, int P, int qi, SplitSmem<T, Band<T>::G>& sm) {
+                            int Nt, int K0, int mid, int K1, int P, int qi, Smem& sm) {
     const int I0 = 2 * P;  // first 32-row tile of the block
     const int jlo = K0 - I0 - 1 > 0 ? K0 - I0 - 1 : 0;
     const int jend = K1 - I0 < Nt ? K1 - I0 : Nt;  // exclusive, over both rows
@@ -806,8 +806,12 @@ __device__ void band_stage1(const T* __restrict__ D, const T* __restrict__ NA, T
         const int s = I0 + (r >> 5) + kl + (k >> 5);  // tile-diagonal of the source tile
         return s >= K0 && s < mid;
     };
-    tile_gemm_masked_splitk<T, Band<T>::G, false, false>(A, np, B, np, (kh - kl + 1) * ST, sm, acc, ma, NoMask());
-    if (threadIdx.x >= 256) return;  // group 0 holds the product
+    if constexpr (SPLIT) {
+        tile_gemm_masked_splitk<T, Band<T>::G, false, false>(A, np, B, np, (kh - kl + 1) * ST, sm, acc, ma, NoMask());
+        if (threadIdx.x >= 256) return;  // group 0 holds the product
+    } else {
+        tile_gemm_masked_k2<T, 2 * KSTEP, false, false>(A, np, B, np, (kh - kl + 1) * ST, sm, acc, ma, NoMask());
+    }
     T* out = R + int64_t(I0) * ST * np + int64_t(Q) * TILE;
     for_each_acc(acc, [&](int r, int c, T v) {
         const int k = I0 + (r >> 5) + 2 * Q + (c >> 5);  // the target tile's diagonal
@@ -876,9 +880,19 @@ __global__ __launch_bounds__(Band<T>::THREADS) void band_kernel(const T* __restr
     __shared__ SplitSmem<T, Band<T>::G> sm;
     const int b = blockIdx.x;
     if (b < n1)
-        band_stage1(D, NA, R, np, Nt, K0, mid, K1, P0 + b / nq, b % nq, sm);
+        band_stage1<T, true>(D, NA, R, np, Nt, K0, mid, K1, P0 + b / nq, b % nq, sm);
     else
         band_stage2<T, true>(R, NB, X, np, mp, Mt, Nt, K0, mid, K1, sig0, sig1, b - n1, sm);
+}
+
+// Stage 1 alone, one 256-thread workgroup per target block (the large nodes).
+template <typename T>
+__global__ __launch_bounds__(GEMM_THREADS) void band_stage1_kernel(const T* __restrict__ D, const T* __restrict__ NA,
+                                                                   T* __restrict__ R, int np, int Nt, int K0, int mid,
+                                                                   int K1, int P0, int nq) {
+    __shared__ GemmSmemK<T, 2 * KSTEP> sm;
+    const int b = blockIdx.x;
+    band_stage1<T, false>(D, NA, R, np, Nt, K0, mid, K1, P0 + b / nq, b % nq, sm);
 }
 
 // Stage 2 alone, one 256-thread workgroup per target block.
@@ -892,7 +906,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void band_stage2_kernel(const T* __re
 
 // Nodes of up to BAND_FUSE_MAX blocks run both stages in one launch: there the
 // launches are short and latency-bound, and the two stages overlap.  Larger
-// nodes keep the 256-thread stage-2 workgroups (more of them per CU, two slices
+// nodes run each stage on 256-thread workgroups (more of them per CU, two slices
 // in flight), which do better once the launch fills the device.
 constexpr int BAND_FUSE_MAX = 1200;
 
@@ -1026,11 +1040,15 @@ struct SolverRun {
             n2 += hi >= lo ? hi - lo + 1 : 0;
         }
         const bool fuse = n1 + n2 <= BAND_FUSE_MAX;
-        const int nb = fuse ? n1 + n2 : n1;  // blocks of the first launch
-        if (nb > 0) {
-            hipLaunchKernelGGL(band_kernel<T>, dim3(nb), dim3(Band<T>::THREADS), 0, st, D, NA, NB, R, X, int(L.np),
-                               int(L.mp), Mt, Nt, K0, mid, K1, P0, nq, n1, sig0, sig1);
+        if (fuse && n1 + n2 > 0) {
+            hipLaunchKernelGGL(band_kernel<T>, dim3(n1 + n2), dim3(Band<T>::THREADS), 0, st, D, NA, NB, R, X,
+                               int(L.np), int(L.mp), Mt, Nt, K0, mid, K1, P0, nq, n1, sig0, sig1);
             KQ_LAUNCHED("band_kernel");
+        }
+        if (!fuse && n1 > 0) {
+            hipLaunchKernelGGL(band_stage1_kernel<T>, dim3(n1), dim3(GEMM_THREADS), 0, st, D, NA, R, int(L.np), Nt, K0,
+                               mid, K1, P0, nq);
+            KQ_LAUNCHED("band_stage1_kernel");
         }
         if (!fuse && n2 > 0) {
             hipLaunchKernelGGL(band_stage2_kernel<T>, dim3(n2), dim3(GEMM_THREADS), 0, st, R, NB, X, int(L.np),
