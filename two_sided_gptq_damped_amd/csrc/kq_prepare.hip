@@ -263,11 +263,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void potrf_panel_kernel(double* __res
 // Two-level blocking: the factorisation takes panels of PANEL block columns.
 // Inside a panel, step k updates only the panel's later columns (k < j < panel
 // end) with block column k; after the panel's last step one update with the
-// panel's PANEL columns at once (K = PANEL * 64) brings the whole trailing matrix
-// up to date.  The trailing matrix is then read and written once per panel
-// rather than once per block column, which at d = 14336 is the difference
-// between streaming ~245 GB and ~61 GB.
-constexpr int PANEL = 4;
+// panel's PANEL columns at once (K = PANEL * 64 = 1024) brings the whole trailing
+// matrix up to date.  The trailing matrix is then read and written once per
+// panel rather than once per block column: at d = 14336 about 15 GB streamed
+// instead of about 245 GB.  The updates keep two 32-deep K slices in flight.
+constexpr int PANEL = 16;
 
 // C[i][j] -= sum_{k0 <= k < k0 + kw} C[i][k] C[j][k]^T for the blocks t0 <= j <= i,
 // j < jend, with t0 = k0 + kw.  Workgroup 0 takes block (t0, t0): it updates it
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void potrf_update_kernel(double* __re
                                                                     int jend, double* __restrict__ Dinv,
                                                                     int32_t* __restrict__ info) {
     __shared__ union {
-        GemmSmem<double> g;
+        GemmSmemK<double, 2 * KSTEP> g;
         DiagSmem d;
     } sm;
     const int t0 = k0 + kw;
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void potrf_update_kernel(double* __re
             pre[r] = out[int64_t((w >> 1) * 32 + WaveAcc<double>::row(r, lane)) * dp + (w & 1) * 32 +
                          WaveAcc<double>::col(r, lane)];
     }
-    tile_gemm<double, double, false, true, false>(A, dp, B, dp, TILE, TILE, kw * TILE, sm.g, acc);
+    tile_gemm_masked_k2<double, 2 * KSTEP, false, true>(A, dp, B, dp, kw * TILE, sm.g, acc, NoMask(), NoMask());
     if (diag) {
         __syncthreads();  // the product's LDS reads are done before L overwrites them
         const int t = threadIdx.x & 255, lane = t & 63, w = t >> 6;
