@@ -263,11 +263,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void potrf_panel_kernel(double* __res
 // Two-level blocking: the factorisation takes panels of PANEL block columns.
 // Inside a panel, step k updates only the panel's later columns (k < j < panel
 // end) with block column k; after the panel's last step one update with the
-// panel's PANEL columns at once (K = PANEL * 64 = 1024) brings the whole trailing
+// panel's PANEL columns at once (K = PANEL * 64 = 512) brings the whole trailing
 // matrix up to date.  The trailing matrix is then read and written once per
-// panel rather than once per block column: at d = 14336 about 15 GB streamed
+// panel rather than once per block column: at d = 14336 about 31 GB streamed
 // instead of about 245 GB.  The updates keep two 32-deep K slices in flight.
-constexpr int PANEL = 16;
+constexpr int PANEL = 8;
 
 // C[i][j] -= sum_{k0 <= k < k0 + kw} C[i][k] C[j][k]^T for the blocks t0 <= j <= i,
 // j < jend, with t0 = k0 + kw.  Workgroup 0 takes block (t0, t0): it updates it
