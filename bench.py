@@ -57,7 +57,8 @@ def solver_flops(m: int, n: int) -> float:
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "solver_llm4096x4096_fp32_hbm_counters.txt")
-SOLVER_SOURCES = ("two_sided_gptq_damped_amd/csrc/kq_solver.hip", "two_sided_gptq_damped_amd/csrc/kq_common.hpp")
+SOLVER_SOURCES = ("two_sided_gptq_damped_amd/csrc/kq_solver.hip", "two_sided_gptq_damped_amd/csrc/kq_common.hpp",
+                  "two_sided_gptq_damped_amd/csrc/kq_chunk_sched.hpp")
 
 
 def solver_traffic(m: int, n: int):
@@ -101,6 +102,8 @@ def main() -> int:
                     help="only run K kron_quantize calls on the 4096x4096 workload (factors prepared first), "
                          "for kernel traces and counters; --one-sided runs them with U_B = NULL")
     ap.add_argument("--one-sided", action="store_true")
+    ap.add_argument("--persistent", action="store_true",
+                    help="with --core-calls: call kron_quantize_persistent (the persistent wavefront solver)")
     ap.add_argument("--prepare-calls", type=int, default=0, metavar="K",
                     help="only run K kron_prepare calls on the workload's input factor, for kernel traces")
     args = ap.parse_args()
@@ -540,11 +543,12 @@ def core_calls(torch, args):
     ts = []
     for _ in range(args.core_calls):
         a.record()
-        kq.kron_quantize(W, UA, UB, bits, True, scales, codes, V, ws)
+        kq.kron_quantize(W, UA, UB, bits, True, scales, codes, V, ws, persistent=args.persistent)
         b.record()
         b.synchronize()
         ts.append(a.elapsed_time(b))
-    print(json.dumps({"core_calls": args.core_calls, "one_sided": bool(args.one_sided), "m": m, "n": n,
+    print(json.dumps({"core_calls": args.core_calls, "one_sided": bool(args.one_sided),
+                      "persistent": bool(args.persistent), "m": m, "n": n,
                       "ms": ts}), flush=True)
     return 0
 

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = kq.library()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert kq.kron_abi_version() == 3
+    assert kq.kron_abi_version() == 4
     assert lib.kron_status_string(2) == b"factor not positive definite"
 
 
@@ -38,7 +38,8 @@ def test_workspace_sizes():
     q32 = lib.kron_workspace_bytes(kq.KQ_OP_QUANTIZE, kq.KQ_F32, 4096, 4096)
     q64 = lib.kron_workspace_bytes(kq.KQ_OP_QUANTIZE, kq.KQ_F64, 4096, 4096)
     # two factors plus three m x n buffers, at least
-    assert q32 >= 5 * 4096 * 4096 * 4 and q64 >= 2 * q32 - (1 << 17)  # the loss scratch is fp64 in both
+    # the loss scratch (fp64) and the chunk solver's flag words (int32) do not scale with the element size
+    assert q32 >= 5 * 4096 * 4096 * 4 and q64 >= 2 * q32 - (1 << 18)
     assert lib.kron_workspace_bytes(kq.KQ_OP_QUANTIZE, kq.KQ_F32, 100, 70) >= 5 * 128 * 128 * 4
     assert lib.kron_workspace_bytes(kq.KQ_OP_PREPARE, kq.KQ_F32, 4096, 0) >= 2 * 4096 * 4096 * 8
     assert lib.kron_workspace_bytes(kq.KQ_OP_LOSS, kq.KQ_F32, 64, 64) > 0

@@ -21,7 +21,7 @@ size_t prepare_workspace_bytes(int64_t d);
 size_t loss_workspace_bytes(int64_t m, int64_t n);
 kq_status quantize_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const void*, int64_t, const void*,
                             int64_t, const kq_quantizer*, int8_t*, int64_t, void*, int64_t, double*, void*,
-                            hipStream_t);
+                            hipStream_t, bool);
 kq_status prepare_dispatch(kq_dtype, int64_t, const void*, int64_t, double, void*, int64_t, double*, double*,
                            int32_t*, void*, hipStream_t);
 kq_status factor_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, void*, int64_t, double, double,
@@ -94,7 +94,7 @@ using namespace kq;
 
 extern "C" {
 
-int32_t kron_abi_version(void) { return 3; }
+int32_t kron_abi_version(void) { return 4; }
 
 const char* kron_status_string(kq_status s) {
     switch (s) {
@@ -171,7 +171,21 @@ kq_status kron_quantize(kq_dtype dtype, int64_t m, int64_t n, const void* W, int
     s = check_ws(ws, ws_bytes, quantize_workspace_bytes(dtype, m, n), "kron_quantize");
     if (s != KQ_OK) return s;
     return quantize_dispatch(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev, ws,
-                             static_cast<hipStream_t>(stream));
+                             static_cast<hipStream_t>(stream), false);
+}
+
+kq_status kron_quantize_persistent(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw,
+                                   const void* U_A, int64_t lda, const void* U_B, int64_t ldb, const kq_quantizer* q,
+                                   int8_t* codes, int64_t ldc, void* V, int64_t ldv, double* loss_dev, void* ws,
+                                   size_t ws_bytes, void* stream) {
+    set_error("");
+    kq_status s = quantize_checked_args(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev,
+                                        "kron_quantize_persistent");
+    if (s != KQ_OK || m == 0 || n == 0) return s;
+    s = check_ws(ws, ws_bytes, quantize_workspace_bytes(dtype, m, n), "kron_quantize_persistent");
+    if (s != KQ_OK) return s;
+    return quantize_dispatch(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev, ws,
+                             static_cast<hipStream_t>(stream), true);
 }
 
 size_t kron_kronecker_workspace_bytes(kq_dtype dtype, int64_t samples, int64_t n, int64_t m) {

@@ -21,7 +21,7 @@ namespace kq {
 
 kq_status quantize_dispatch(kq_dtype, int64_t, int64_t, const void*, int64_t, const void*, int64_t, const void*,
                             int64_t, const kq_quantizer*, int8_t*, int64_t, void*, int64_t, double*, void*,
-                            hipStream_t);
+                            hipStream_t, bool);
 size_t quantize_workspace_bytes(kq_dtype dtype, int64_t m, int64_t n);
 kq_status quantize_checked_args(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* U_A,
                                 int64_t lda, const void* U_B, int64_t ldb, const kq_quantizer* q, int8_t* codes,
@@ -79,5 +79,5 @@ extern "C" kq_status kron_quantize_noalloc(kq_dtype dtype, int64_t m, int64_t n,
     s = scratch_for_current_device(&ws);
     if (s != KQ_OK) return s;
     return quantize_dispatch(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev, ws,
-                             static_cast<hipStream_t>(stream));
+                             static_cast<hipStream_t>(stream), false);
 }

@@ -26,8 +26,13 @@
 // tile granularity.  Both stages run on 64 x 64 matrix-core output blocks
 // (2 x 2 scheduling tiles) and mask at 32-tile granularity: source tiles outside
 // the band read as zero, targets outside the band are not written.
-// A leaf is one tile-diagonal: each 32 x 32 tile runs the element-level
-// anti-diagonal sweep (63 steps) with the in-tile feedback, one workgroup per tile.
+// The recursion stops at chunks of CHUNK tile-diagonals.  Each 32 x 32 tile of a
+// chunk runs the element-level anti-diagonal sweep (63 steps) with the in-tile
+// feedback, one workgroup per tile, after pulling the feedback of the chunk's
+// earlier tiles.  One persistent launch runs a whole chunk (chunk_kernel): its
+// workgroups draw tile tasks in tile-diagonal order and a tile starts as soon as
+// the two tiles before it in its row and column are done (per-tile flags, see
+// kq_chunk_sched.hpp).
 //
 // Workspace layout (row-major, padded to multiples of 64 with zero weights,
 // unit scales and identity factors, so padding never reaches a real entry):
@@ -37,19 +42,21 @@
 //   X   mp x np   running pre-rounding values (starts as W)
 //   D   mp x np   errors Delta
 //   R   mp x np   row-propagated errors (zero at the start)
-//   P   2 x min(Mt, Nt) x 2 x 32 x 32   the leaves' pre-accumulated chunk products
+//   P   CHUNK x min(Mt, Nt) x 2 x 32 x 32   the leaves' pre-accumulated chunk products
 //   S   mp        per-row scales
 //   C   np        per-column scales (the WaterKron mode only; unit in the padding)
+//   F   int32 flag words of the chunk solver (per tile: swept, products
+//       pre-accumulated; a ticket counter per chunk; an abort word), zeroed per call
 // In the WaterKron mode (kron_quantize_waterkron) entry (i, j) has the grid step
 // S[i] * C[j] (one rounding) and int32 codes clamped only at +-2^30.
 #include <type_traits>
 
 #include "kq_common.hpp"
+#include "kq_chunk_sched.hpp"
 
 namespace kq {
 
-constexpr int ST = 32;    // scheduling tile edge
-constexpr int CHUNK = 16;  // tile-diagonals per recursion leaf (chunk)
+constexpr int ST = 32;  // scheduling tile edge (CHUNK, the tile-diagonals of a chunk, is in kq_chunk_sched.hpp)
 
 // Byte offsets of the solver's arrays in its workspace (see the layout above),
 // from the 32-tile counts and the element size alone, so that a kernel finds
@@ -57,8 +64,13 @@ constexpr int CHUNK = 16;  // tile-diagonals per recursion leaf (chunk)
 // The padded extents are multiples of 64, so every array size is a multiple of
 // 256 bytes and the arrays are 256-byte aligned.
 struct WsOffsets {
-    int64_t NA, NB, X, D, R, P, S, C, end;
+    int64_t NA, NB, X, D, R, P, S, C, F, end;
 };
+// the chunk solver's flags: per tile a sweep-done and a precompute-done word,
+// one ticket counter per chunk, one abort word (int32 each)
+__host__ __device__ inline int64_t flag_words(int64_t Mt, int64_t Nt) {
+    return 2 * Mt * Nt + (Mt + Nt - 1 + CHUNK - 1) / CHUNK + 1;
+}
 __host__ __device__ inline WsOffsets ws_offsets(int64_t Mt, int64_t Nt, int64_t es) {
     const int64_t mp = Mt * ST, np = Nt * ST;
     WsOffsets o;
@@ -67,10 +79,11 @@ __host__ __device__ inline WsOffsets ws_offsets(int64_t Mt, int64_t Nt, int64_t 
     o.X = o.NB + mp * mp * es;
     o.D = o.X + mp * np * es;
     o.R = o.D + mp * np * es;
-    o.P = o.R + mp * np * es;  // two tile-diagonals of two 32 x 32 parts per tile
-    o.S = o.P + 2 * 2 * ST * ST * (Mt < Nt ? Mt : Nt) * es;
+    o.P = o.R + mp * np * es;  // the CHUNK tile-diagonals of a chunk, two 32 x 32 parts per tile
+    o.S = o.P + int64_t(CHUNK) * 2 * ST * ST * (Mt < Nt ? Mt : Nt) * es;
     o.C = o.S + mp * es;
-    o.end = o.C + np * es;
+    o.F = o.C + np * es;
+    o.end = o.F + (flag_words(Mt, Nt) * 4 + 255) / 256 * 256;
     return o;
 }
 
@@ -304,13 +317,51 @@ static_assert(SWEEP_THREADS == LEAF_THREADS, "every thread of the leaf takes par
 template <bool ENTRY>
 using CodeT = std::conditional_t<ENTRY, int32_t, int8_t>;
 
-template <typename T, bool ENTRY>
-__global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(int K, int c0, int c1, int Mt, int Nt, int qmin, int qmax,
-                                                   char* __restrict__ ws, int m, int n,
-                                                   CodeT<ENTRY>* __restrict__ Z, int64_t ldz, T* __restrict__ V,
-                                                   int64_t ldv) {
-    // the arguments the kernel starts with come first (the launch preloads them
-    // into scalar registers); the arrays are found from the workspace base
+// Device-coherent element access (agent-scope relaxed atomics): the data that
+// chunk tasks hand to one another goes through the device's coherence point,
+// so no cache needs a write-back or an invalidation at a hand-over.
+template <bool CO, typename T>
+__device__ __forceinline__ T co_ld(const T* p) {
+    if constexpr (CO)
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        return *p;
+}
+template <bool CO, typename T>
+__device__ __forceinline__ void co_st(T* p, T v) {
+    if constexpr (CO)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+template <bool CO, typename T>
+__device__ __forceinline__ void co_ld4(Vec4<T>& v, const T* p) {
+    if constexpr (CO) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v.set(j, __hip_atomic_load(p + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    } else {
+        v.load(p);
+    }
+}
+
+// Bound on a chunk task's wait for one flag, in polls (each a device-coherent
+// load and a short sleep, about a microsecond): far beyond any wait of a
+// running chunk (a whole chunk takes a few hundred microseconds), so it only
+// ends a wait that could never be satisfied; the task then raises the abort
+// word, every later wait returns at once and the swept tiles store NaN in V.
+constexpr uint32_t CHUNK_SPIN_LIMIT = 1u << 18;
+
+// One leaf task on tile idx of tile-diagonal Kt of chunk [c0, c1): the sweep of
+// the tile, or (pre) the pre-accumulation of its chunk products over every
+// slice but its two freshest.  CHAINED: the task runs inside the persistent
+// chunk solver and waits for the tasks it depends on through the flags (see
+// kq_chunk_sched.hpp), then raises its own; otherwise the launch order provides
+// the dependencies (a launch per tile-diagonal).
+template <typename T, bool ENTRY, bool CHAINED>
+__device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int c1, int Mt, int Nt, int qmin,
+                                          int qmax, char* __restrict__ ws, int m, int n,
+                                          CodeT<ENTRY>* __restrict__ Z, int64_t ldz, T* __restrict__ V,
+                                          int64_t ldv) {
     const WsOffsets wo = ws_offsets(Mt, Nt, sizeof(T));
     const int np = Nt * ST, mp = Mt * ST, pt = Mt < Nt ? Mt : Nt;
     T* const D = reinterpret_cast<T*>(ws + wo.D);
@@ -353,29 +404,19 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(int K, int c0, int c
                   "16-byte aligned bufA / bufB, 32-byte aligned exchange slices");
     static_assert(2 * ST * PK + 2 * ST * ST <= 2 * ST * PK + 2 * NROUND * ST * RD, "prologue staging fits");
 
-    // Launch K: workgroups [0, nk) sweep the tiles of diagonal K.  When diagonal
-    // K + 1 lies in the same chunk, workgroups [nk + xpad, nk + xpad + nk1)
-    // pre-accumulate its tiles' chunk products over every slice that is final
-    // before this launch (all but the two on diagonal K) into P, so that leaf
-    // K + 1 adds only the freshest two slices.  P holds two diagonals,
-    // alternating with K's parity.  Workgroup b runs on XCD b mod 8 (each XCD
-    // has its own L2); the xpad idle workgroups put the workgroup that writes a
-    // tile's P on the XCD where the next launch sweeps that tile (index idx in
-    // both), so the leaf reads P from its own L2.
-    const int ilo = K - Nt + 1 > 0 ? K - Nt + 1 : 0;
-    const int ihi = K < Mt - 1 ? K : Mt - 1;
-    const int nk = ihi - ilo + 1;
-    const bool pre = int(blockIdx.x) >= nk;
-    const int xpad = (8 - nk % 8) % 8;
-    const int Kt = pre ? K + 1 : K;  // the tile's diagonal
-    const int idx = pre ? int(blockIdx.x) - nk - xpad : int(blockIdx.x);
-    if (idx < 0) return;
+    // P holds pre-accumulated products: in the chunk solver those of every tile
+    // of the chunk (tile idx of diagonal Kt at slot (Kt - c0) pt + idx), with a
+    // launch per tile-diagonal those of two diagonals (slot (Kt & 1) pt + idx).
     const int I = (Kt - Nt + 1 > 0 ? Kt - Nt + 1 : 0) + idx;
     if (I > (Kt < Mt - 1 ? Kt : Mt - 1)) return;
     const int J = Kt - I;
     // threads t < 256 also work in the block layout (four rows each); all
     // LEAF_THREADS threads take part in the sweep
-    const int t = threadIdx.x, tb = t & 255, w = tb >> 6, l = tb & 63;
+    int t = threadIdx.x;
+    // Opaque to the optimiser in the chunk solver's task loop: the thread's
+    // addresses are then recomputed per task rather than kept live across it.
+    if constexpr (CHAINED) asm volatile("" : "+v"(t));
+    const int tb = t & 255, w = tb >> 6, l = tb & 63;
     const bool blk = t < 256;
     const int b = l & 31, r0 = 8 * w + 4 * (l >> 5);
     const int fgrp = t >> 8;                    // staging loads: slices rotate over the 256-thread groups
@@ -385,7 +426,49 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(int K, int c0, int c
     // row part (rowpart) for wv < 4 and the column part for wv >= 4, accumulated
     // over all of that part's slices, so no partial sums cross waves
     const int part = wv >> 2, qd = wv & 3, qr = 16 * (qd >> 1), qc = 16 * (qd & 1);
-    T* const Pt = P + (int64_t((Kt & 1) * pt + idx) * 2 + part) * ST * ST + qr * ST + qc;
+    T* const Pt = P + (int64_t((CHAINED ? Kt - c0 : Kt & 1) * pt + idx) * 2 + part) * ST * ST + qr * ST + qc;
+    // the chunk solver's flags (CHAINED)
+    int* const flags = reinterpret_cast<int*>(ws + wo.F);
+    int* const abort_word = flags + 2 * Mt * Nt + (Mt + Nt - 1 + CHUNK - 1) / CHUNK;
+    __shared__ int s_aborted;
+    // wait until the tasks this one reads from have raised their flags (thread 0
+    // polls; the barrier and every thread's acquire fence then make their data
+    // visible here)
+    auto wait_deps = [&]() {
+        if (t == 0) {
+            const ChunkDeps dp = chunk_deps(ChunkTask{pre ? 1 : 0, Kt, idx}, c0, Mt, Nt);
+            int ab = __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                const int wd = u == 0 ? dp.w0 : u == 1 ? dp.w1 : dp.w2;
+                if (wd < 0 || ab) continue;
+                const int* f = flags + wd;
+                for (uint32_t it = 0; __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0; ++it) {
+                    if (it >= CHUNK_SPIN_LIMIT) {
+                        __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        ab = 1;
+                        break;
+                    }
+                    if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                        ab = 1;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            s_aborted = ab;
+        }
+        __syncthreads();
+    };
+    // every thread's stores reach the device before thread 0 raises flag `which`
+    // (0: the sweep of the tile is done, 1: its precompute is done)
+    auto raise_flag = [&](int which) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
+        __syncthreads();
+        if (t == 0)
+            __hip_atomic_store(flags + int64_t(which) * Mt * Nt + int64_t(I) * Nt + J, 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    };
 
     // chunk sources of the tile: row tiles J' in [jl, J), column tiles I' in [il, I);
     // the freshest of each (J - 1, I - 1) lies on diagonal Kt - 1
@@ -405,19 +488,28 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(int K, int c0, int c
     auto fetch = [&](int sl, Vec4<T>& va, Vec4<T>& vb) {
         if (sl < n1) {
             const int jp = jb + sl;
-            va.load(D + int64_t(I * ST + q8) * np + jp * ST + c4);   // A(r = q8, k = c4 + j)
+            co_ld4<CHAINED>(va, D + int64_t(I * ST + q8) * np + jp * ST + c4);  // A(r = q8, k = c4 + j)
             vb.load(NA + int64_t(jp * ST + q8) * np + J * ST + c4);  // B(k = q8, c = c4 + j)
         } else {
             const int ip = ib + sl - n1;
             va.load(NB + int64_t(ip * ST + q8) * mp + I * ST + c4);  // A(r = c4 + j, k = q8)
-            vb.load(R + int64_t(ip * ST + q8) * np + J * ST + c4);   // B(k = q8, c = c4 + j)
+            co_ld4<CHAINED>(vb, R + int64_t(ip * ST + q8) * np + J * ST + c4);  // B(k = q8, c = c4 + j)
         }
     };
     // every load of the first batch is in flight before anything waits on one
+    // (chained: once the slices are final, after the tile's own loads)
+    auto first_batch = [&]() {
 #pragma unroll
-    for (int v = 0; v < SLOTS; ++v) {
-        const int u = NFG * v + fgrp;
-        if (u < BATCH && u < ns) fetch(u, pa[v], pb[v]);
+        for (int v = 0; v < SLOTS; ++v) {
+            const int u = NFG * v + fgrp;
+            if (u < BATCH && u < ns) fetch(u, pa[v], pb[v]);
+        }
+    };
+    if constexpr (!CHAINED) {
+        first_batch();
+    } else if (pre) {
+        wait_deps();
+        first_batch();
     }
     // operand op (0: A, 1: B) of staged slice u
     auto slot = [&](int u, int op) -> T* {
@@ -472,19 +564,23 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(int K, int c0, int c
             pq.set(r, part == 0 ? Rt[int64_t(Q16<T>::row(r, lane)) * np + Q16<T>::col(r, lane)] : T(0));
         products(pq);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Pt[Q16<T>::row(r, lane) * ST + Q16<T>::col(r, lane)] = pq.get(r);
+        for (int r = 0; r < 4; ++r) co_st<CHAINED>(Pt + Q16<T>::row(r, lane) * ST + Q16<T>::col(r, lane), pq.get(r));
+        if constexpr (CHAINED) raise_flag(1);
         return;
     }
     // the leaf: this wave's quadrant of the pre-accumulated products, or at the
     // chunk's first diagonal (no chunk sources) R[I, J] alone
     // (one wave-uniform source and stride, so the loads need no select)
-    const T* const psrc = K > c0 ? Pt : Rt;
-    const int pld = K > c0 ? ST : np;
-    const bool pzero = K == c0 && part == 1;
+    const T* const psrc = Kt > c0 ? Pt : Rt;
+    const int pld = Kt > c0 ? ST : np;
+    const bool pzero = Kt == c0 && part == 1;
     T pin[4];
+    auto load_pin = [&]() {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-        pin[r] = pzero ? T(0) : psrc[Q16<T>::row(r, lane) * pld + Q16<T>::col(r, lane)];
+        for (int r = 0; r < 4; ++r)
+            pin[r] = pzero ? T(0) : co_ld<CHAINED>(psrc + Q16<T>::row(r, lane) * pld + Q16<T>::col(r, lane));
+    };
+    if constexpr (!CHAINED) load_pin();
 
     constexpr int FE = ST * ST / LEAF_THREADS;  // factor-block entries per thread
     T fnb[FE], fna[FE];
@@ -549,6 +645,13 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(int K, int c0, int c
     T sblk[4];  // the block layout's row scales (V in the epilogue)
 #pragma unroll
     for (int i = 0; i < 4; ++i) sblk[i] = ENTRY ? S[I * ST + r0 + i] * csb : S[I * ST + r0 + i];
+    // chained: the tile's own data is on its way; now wait for the freshest
+    // slices and the pre-accumulated products
+    if constexpr (CHAINED) {
+        wait_deps();
+        first_batch();
+        load_pin();
+    }
 
     // ---- prologue: rowpart (crow) and the chunk's column part (ccol), block layout.
     // X gets rowpart + the column part here; the in-tile column feedback of
@@ -738,19 +841,68 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(int K, int c0, int c
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int d = r0 + i + b;  // the entry's element diagonal
-            R[int64_t(I * ST + r0 + i) * np + J * ST + b] = xR[((d / RD) * ST + b) * RD + d % RD];
+            co_st<CHAINED>(R + int64_t(I * ST + r0 + i) * np + J * ST + b, xR[((d / RD) * ST + b) * RD + d % RD]);
         }
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t gi = int64_t(I) * ST + r0 + i, gj = int64_t(J) * ST + b;
             const T z = bufA[(r0 + i) * PK + b];
-            D[gi * np + gj] = bufB[b * PK + r0 + i];
+            co_st<CHAINED>(D + gi * np + gj, bufB[b * PK + r0 + i]);
             if (gi < m && gj < n) {
                 Z[gi * ldz + gj] = CodeT<ENTRY>(z);
-                V[gi * ldv + gj] = sblk[i] * z;
+                V[gi * ldv + gj] = CHAINED && s_aborted ? T(__builtin_nan("")) : sblk[i] * z;
             }
         }
+    }
+    if constexpr (CHAINED) raise_flag(0);
+}
+
+// Launch K: workgroups [0, nk) sweep the tiles of diagonal K.  When diagonal
+// K + 1 lies in the same chunk, workgroups [nk + xpad, nk + xpad + nk1)
+// pre-accumulate its tiles' chunk products over every slice that is final
+// before this launch (all but the two on diagonal K) into P, so that leaf
+// K + 1 adds only the freshest two slices.  Workgroup b runs on XCD b mod 8
+// (each XCD has its own L2); the xpad idle workgroups put the workgroup that
+// writes a tile's P on the XCD where the next launch sweeps that tile (index
+// idx in both), so the leaf reads P from its own L2.  The arguments the kernel
+// starts with come first (the launch preloads them into scalar registers); the
+// arrays are found from the workspace base.
+template <typename T, bool ENTRY>
+__global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(int K, int c0, int c1, int Mt, int Nt, int qmin, int qmax,
+                                                   char* __restrict__ ws, int m, int n,
+                                                   CodeT<ENTRY>* __restrict__ Z, int64_t ldz, T* __restrict__ V,
+                                                   int64_t ldv) {
+    const int nk = diag_tiles(K, Mt, Nt);
+    const bool pre = int(blockIdx.x) >= nk;
+    const int xpad = (8 - nk % 8) % 8;
+    const int idx = pre ? int(blockIdx.x) - nk - xpad : int(blockIdx.x);
+    if (idx < 0) return;
+    leaf_task<T, ENTRY, false>(pre, pre ? K + 1 : K, idx, c0, c1, Mt, Nt, qmin, qmax, ws, m, n, Z, ldz, V, ldv);
+}
+
+// The persistent chunk solver: one launch runs every leaf task of the chunk
+// [c0, c1) (the sweeps of its tile-diagonals and the pre-accumulation of their
+// chunk products), each workgroup drawing tickets until the chunk is done.  A
+// tile's sweep starts as soon as its two neighbours before it are swept and its
+// products are pre-accumulated, without waiting for the rest of the previous
+// tile-diagonal or for a launch; the task order is in kq_chunk_sched.hpp.
+template <typename T, bool ENTRY>
+__global__ __launch_bounds__(LEAF_THREADS) void chunk_kernel(int c0, int c1, int Mt, int Nt, int qmin, int qmax,
+                                                    char* __restrict__ ws, int m, int n,
+                                                    CodeT<ENTRY>* __restrict__ Z, int64_t ldz, T* __restrict__ V,
+                                                    int64_t ldv) {
+    const WsOffsets wo = ws_offsets(Mt, Nt, sizeof(T));
+    int* const counter = reinterpret_cast<int*>(ws + wo.F) + 2 * Mt * Nt + c0 / CHUNK;
+    __shared__ int s_ticket;
+    for (;;) {
+        __syncthreads();  // the previous task is done with the LDS and s_ticket
+        if (threadIdx.x == 0)
+            s_ticket = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const ChunkTask tk = chunk_task(__builtin_amdgcn_readfirstlane(s_ticket), c0, c1, Mt, Nt);
+        if (tk.kind < 0) return;
+        leaf_task<T, ENTRY, true>(tk.kind == 1, tk.Kt, tk.idx, c0, c1, Mt, Nt, qmin, qmax, ws, m, n, Z, ldz, V, ldv);
     }
 }
 
@@ -960,12 +1112,19 @@ __global__ __launch_bounds__(256) void error_loss_final_kernel(const double* __r
     if (threadIdx.x == 0) *out = tot;
 }
 
+__global__ void zero_words_kernel(int* __restrict__ p, int64_t count) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = 0;
+}
+
 // ------------------------------------------------------------------- host side
+
+constexpr int CHUNK_GRID = 256;  // workgroups of a persistent chunk launch: one per compute unit
 
 struct SolverLayout {
     int64_t mp, np, Mt, Nt;  // padded extents; tile counts in 32-tiles
     size_t bytes;
-    size_t off_NA, off_NB, off_X, off_D, off_R, off_P, off_S, off_C, off_L;
+    size_t off_NA, off_NB, off_X, off_D, off_R, off_P, off_S, off_C, off_F, off_L;
 };
 
 SolverLayout solver_layout(kq_dtype dtype, int64_t m, int64_t n) {
@@ -985,6 +1144,7 @@ SolverLayout solver_layout(kq_dtype dtype, int64_t m, int64_t n) {
     L.off_P = size_t(o.P);
     L.off_S = size_t(o.S);
     L.off_C = size_t(o.C);
+    L.off_F = size_t(o.F);
     L.off_L = align256(size_t(o.end));  // loss scratch (fp64): 1 / U_A,jj, 1 / U_B,ii, partial sums
     L.bytes = L.off_L + align256((size_t(L.np) + size_t(L.mp) + ELOSS_PARTS) * sizeof(double));
     return L;
@@ -1002,6 +1162,7 @@ struct SolverRun {
     int64_t ldv;
     hipStream_t st;
     char* ws;  // the workspace base (the leaves find their arrays from it)
+    bool chained;  // chunks on the persistent chunk solver, else a launch per tile-diagonal and role
 
     kq_status leaf(int K, int c0, int c1) {
         const int Mt = int(L.Mt), Nt = int(L.Nt);
@@ -1058,8 +1219,24 @@ struct SolverRun {
         return KQ_OK;
     }
 
+    // the leaf tasks of chunk [c0, c1) in one persistent launch
+    kq_status chunk(int c0, int c1) {
+        const int Mt = int(L.Mt), Nt = int(L.Nt);
+        const int tasks = chunk_tasks(c0, c1, Mt, Nt);
+        const dim3 grid(tasks < CHUNK_GRID ? tasks : CHUNK_GRID);
+        if (C)
+            hipLaunchKernelGGL((chunk_kernel<T, true>), grid, dim3(LEAF_THREADS), 0, st, c0, c1, Mt, Nt, qmin, qmax,
+                               ws, m, n, static_cast<int32_t*>(Z), ldz, V, ldv);
+        else
+            hipLaunchKernelGGL((chunk_kernel<T, false>), grid, dim3(LEAF_THREADS), 0, st, c0, c1, Mt, Nt, qmin,
+                               qmax, ws, m, n, static_cast<int8_t*>(Z), ldz, V, ldv);
+        KQ_LAUNCHED("chunk_kernel");
+        return KQ_OK;
+    }
+
     kq_status solve(int K0, int K1) {
         if (K1 - K0 <= CHUNK) {
+            if (chained) return chunk(K0, K1);
             for (int K = K0; K < K1; ++K) {
                 const kq_status s = leaf(K, K0, K1);
                 if (s != KQ_OK) return s;
@@ -1092,6 +1269,7 @@ struct QuantSpec {
     int qmin, qmax;
     void* codes;
     int64_t ldc;
+    bool chained;  // two-sided leaves on the persistent chunk solver
 };
 
 template <typename T>
@@ -1105,7 +1283,8 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
                      reinterpret_cast<T*>(base + L.off_X), reinterpret_cast<T*>(base + L.off_D),
                      reinterpret_cast<T*>(base + L.off_R), reinterpret_cast<T*>(base + L.off_P),
                      reinterpret_cast<T*>(base + L.off_S),
-                     q.col_scales ? reinterpret_cast<T*>(base + L.off_C) : nullptr, q.codes, q.ldc, V, ldv, st, base};
+                     q.col_scales ? reinterpret_cast<T*>(base + L.off_C) : nullptr, q.codes, q.ldc, V, ldv, st, base,
+                     q.chained};
     const int threads = 256;
     auto blocks = [&](int64_t count) { return dim3(unsigned((count + threads - 1) / threads)); };
     auto rows = [&](int64_t cols, int64_t nrows) {  // the kernels loop over rows beyond the grid's y extent
@@ -1123,6 +1302,12 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
                        int(L.mp), int(L.np), q.row_scales, q.per_row, q.col_scales, run.X, run.S, run.C,
                        UB ? run.R : nullptr);
     KQ_LAUNCHED("init_solver_kernel");
+    if (UB && run.chained) {  // the chunk solver's flags, ticket counters and abort word start at zero
+        const int64_t nw = flag_words(L.Mt, L.Nt);
+        hipLaunchKernelGGL(zero_words_kernel, blocks(nw), dim3(threads), 0, st,
+                           reinterpret_cast<int*>(base + L.off_F), nw);
+        KQ_LAUNCHED("zero_words_kernel");
+    }
     // B = I: one-sided GPTQ, rows independent, recursive over column ranges
     const kq_status s = UB ? run.solve(0, int(L.Mt + L.Nt - 1))
                            : onesided_solve<T>(int(m), int(n), int(L.mp), int(L.np), run.qmin, run.qmax, run.NA,
@@ -1157,14 +1342,18 @@ kq_status quantize_as(int64_t m, int64_t n, const void* W, int64_t ldw, const vo
 
 kq_status quantize_dispatch(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw, const void* UA,
                             int64_t lda, const void* UB, int64_t ldb, const kq_quantizer* q, int8_t* codes,
-                            int64_t ldc, void* V, int64_t ldv, double* loss_dev, void* ws, hipStream_t st) {
+                            int64_t ldc, void* V, int64_t ldv, double* loss_dev, void* ws, hipStream_t st,
+                            bool chained) {
     const int qmin = -(1 << (q->bits - 1)), qmax = (1 << (q->bits - 1)) - 1;
     if (dtype == KQ_F64)
         return quantize_as<double>(m, n, W, ldw, UA, lda, UB, ldb,
-                                   {static_cast<const double*>(q->scales), q->per_row, nullptr, qmin, qmax, codes, ldc},
+                                   {static_cast<const double*>(q->scales), q->per_row, nullptr, qmin, qmax, codes, ldc,
+                                    chained},
                                    V, ldv, loss_dev, ws, st);
     return quantize_as<float>(m, n, W, ldw, UA, lda, UB, ldb,
-                              {static_cast<const float*>(q->scales), q->per_row, nullptr, qmin, qmax, codes, ldc}, V,
+                              {static_cast<const float*>(q->scales), q->per_row, nullptr, qmin, qmax, codes, ldc,
+                               chained},
+                              V,
                               ldv, loss_dev, ws, st);
 }
 
@@ -1179,11 +1368,11 @@ kq_status waterkron_dispatch(kq_dtype dtype, int64_t m, int64_t n, const void* W
     if (dtype == KQ_F64)
         return quantize_as<double>(m, n, W, ldw, UA, lda, UB, ldb,
                                    {static_cast<const double*>(beta), 1, static_cast<const double*>(alpha),
-                                    -WK_CODE_BOUND, WK_CODE_BOUND, codes, ldc},
+                                    -WK_CODE_BOUND, WK_CODE_BOUND, codes, ldc, false},
                                    V, ldv, loss_dev, ws, st);
     return quantize_as<float>(m, n, W, ldw, UA, lda, UB, ldb,
                               {static_cast<const float*>(beta), 1, static_cast<const float*>(alpha), -WK_CODE_BOUND,
-                               WK_CODE_BOUND, codes, ldc},
+                               WK_CODE_BOUND, codes, ldc, false},
                               V, ldv, loss_dev, ws, st);
 }
 
