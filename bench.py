@@ -102,8 +102,8 @@ def main() -> int:
                     help="only run K kron_quantize calls on the 4096x4096 workload (factors prepared first), "
                          "for kernel traces and counters; --one-sided runs them with U_B = NULL")
     ap.add_argument("--one-sided", action="store_true")
-    ap.add_argument("--persistent", action="store_true",
-                    help="with --core-calls: call kron_quantize_persistent (the persistent wavefront solver)")
+    ap.add_argument("--per-diagonal", action="store_true",
+                    help="with --core-calls: call kron_quantize_per_diagonal (a launch per tile-diagonal)")
     ap.add_argument("--prepare-calls", type=int, default=0, metavar="K",
                     help="only run K kron_prepare calls on the workload's input factor, for kernel traces")
     args = ap.parse_args()
@@ -194,7 +194,7 @@ def main() -> int:
         ss.wait_event(S["eb"])
         with torch.cuda.stream(ss):
             kq.kron_quantize(W, S["UA"], S["UB"], bits, True, S["scales"], S["codes"], S["V"], ws_qs[k % 2],
-                             loss=S["loss"])
+                             loss=S["loss"], per_diagonal=True)
         S["q_done"].record(ss)
 
     def step(k):
@@ -310,7 +310,8 @@ def main() -> int:
             "step": "one layer: [factor_accumulate(A), prepare(A), row_scales] beside [factor_accumulate(B), "
                     "prepare(B)] on two side streams, then quantize with its proxy loss (from the rounding errors) "
                     "on one of two solve streams (alternating by layer); layers are pipelined: the next layers' "
-                    "chains and the other solve stream's layer run beside each solve",
+                    "chains and the other solve stream's layer run beside each solve; the solves use the "
+                    "per-diagonal schedule (kron_quantize_per_diagonal), which shares the device with that work",
         },
         "loss": {"solver": l_solver, "kron_loss": l_trace, "rel_diff": abs(l_solver - l_trace) / l_trace,
                  "note": "kron_loss (trace form from W and V, fp64) runs after the timed steps as a check; "
@@ -319,14 +320,15 @@ def main() -> int:
         "breakdown_ms": {"single_layer": float(np.median(single))},
         "serial_breakdown_ms": {k: float(np.median(v)) for k, v in serial.items()},
         "core": {
-            "what": "kron_quantize only, factors and scales resident (median of repeats)",
+            "what": "kron_quantize only (the persistent wavefront schedule), factors and scales resident "
+                    "(median of repeats)",
             "ms": core_ms,
             "weights_per_s": m * n / (core_ms * 1e-3),
             "algorithmic_tflops": achieved / 1e12,
             "frac_fp32_mfma_peak": achieved / PEAK_FP32_MFMA,
         },
         "roofline": {
-            "kernel": "two-sided GPTQ solver (kron_quantize: leaf sweeps + band-propagation GEMMs)",
+            "kernel": "two-sided GPTQ solver (kron_quantize: persistent chunk sweeps + band-propagation GEMMs)",
             "bound": "mfma",
             "achieved": achieved / 1e12,
             "peak": PEAK_FP32_MFMA / 1e12,
@@ -543,12 +545,12 @@ def core_calls(torch, args):
     ts = []
     for _ in range(args.core_calls):
         a.record()
-        kq.kron_quantize(W, UA, UB, bits, True, scales, codes, V, ws, persistent=args.persistent)
+        kq.kron_quantize(W, UA, UB, bits, True, scales, codes, V, ws, per_diagonal=args.per_diagonal)
         b.record()
         b.synchronize()
         ts.append(a.elapsed_time(b))
     print(json.dumps({"core_calls": args.core_calls, "one_sided": bool(args.one_sided),
-                      "persistent": bool(args.persistent), "m": m, "n": n,
+                      "per_diagonal": bool(args.per_diagonal), "m": m, "n": n,
                       "ms": ts}), flush=True)
     return 0
 

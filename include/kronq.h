@@ -127,7 +127,12 @@ kq_status kron_row_scales(kq_dtype dtype, int64_t m, int64_t n, const void* W, i
  * Two-sided GPTQ (FastKron / BaKron): the codes that GPTQ on vecop(W) with Hessian
  * A_d (x) B_d produces (FastKron page section 2.2), computed anti-diagonal by
  * anti-diagonal (section 2.3) with the error feedback batched by a recursion over
- * anti-diagonal ranges (sections 2.4-2.5).  In exact arithmetic every valid
+ * anti-diagonal ranges (sections 2.4-2.5).  The matrix is cut into 32 x 32
+ * tiles; the recursion's leaves, chunks of 16 tile-diagonals, each run as one
+ * persistent launch in which a tile starts as soon as the tiles before it in its
+ * row and column are done.  Every wait inside that launch is bounded (a wait
+ * that could never end, which the task order rules out, would end the launch
+ * with NaN in V).  In exact arithmetic every valid
  * processing order gives the same output (section 2.5); in floating point the
  * order of the feedback sums can move values that sit within rounding of a grid
  * midpoint.
@@ -158,26 +163,24 @@ kq_status kron_quantize(kq_dtype dtype, int64_t m, int64_t n, const void* W, int
                         double* loss_dev, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * kron_quantize with the two-sided leaves on a persistent wavefront solver
- * (FastKron page, section 2.3: the tiles of one tile-diagonal are independent;
- * BaKron review, key_machinery: a wavefront over anti-diagonals).  The codes,
- * V and loss are bitwise those of kron_quantize (the same operations in the
- * same order); only the schedule differs.  kron_quantize launches one kernel
- * per tile-diagonal of 32 x 32 tiles; here one launch runs each chunk of 16
- * tile-diagonals, its workgroups drawing tile tasks in order, and a tile
- * starts its sweep as soon as the two tiles before it in its row and column
- * are done, handed over through device-coherent flags and data.  On MI355X that
- * hand-over costs more than a kernel boundary, so kron_quantize is the faster
- * call (4096 x 4096 fp32: about 5.6 ms against 4.8 ms).  Arguments, workspace
- * (the same size), errors and U_B = NULL (the one-sided path, unchanged) are as
- * for kron_quantize.  Every wait of the solver is bounded: a wait that could
- * never end (none can, by the task order) would end the launch with NaN in V.
+ * kron_quantize with the two-sided leaves launched one kernel per tile-diagonal
+ * instead of on the persistent wavefront solver.  The codes, V and loss are
+ * bitwise those of kron_quantize (the same operations in the same order); only
+ * the schedule differs.  kron_quantize runs each chunk of 16 tile-diagonals of
+ * 32 x 32 tiles in one persistent launch whose workgroups hold a compute unit
+ * while they wait for the tiles before them (FastKron page, section 2.3: the
+ * tiles of a tile-diagonal are independent; BaKron review, key_machinery: a
+ * wavefront over anti-diagonals); this call never waits inside a kernel, so it
+ * is the one for callers that share the GPU with other long-running work.  At
+ * 4096 x 4096 fp32 on MI355X it takes about 4.7 ms against 4.5 ms.  Arguments,
+ * workspace (the same size), errors and U_B = NULL (the one-sided path,
+ * unchanged) are as for kron_quantize.
  */
-kq_status kron_quantize_persistent(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw,
-                                   const void* U_A, int64_t lda, const void* U_B, int64_t ldb,
-                                   const kq_quantizer* q, int8_t* codes, int64_t ldc, void* V,
-                                   int64_t ldv, double* loss_dev, void* ws, size_t ws_bytes,
-                                   void* stream);
+kq_status kron_quantize_per_diagonal(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw,
+                                     const void* U_A, int64_t lda, const void* U_B, int64_t ldb,
+                                     const kq_quantizer* q, int8_t* codes, int64_t ldc, void* V,
+                                     int64_t ldv, double* loss_dev, void* ws, size_t ws_bytes,
+                                     void* stream);
 
 /*
  * WaterKron two-sided rate allocation (WaterKron page, section 3; section 2.4
@@ -332,7 +335,7 @@ const char* kron_last_error(void);
 
 /* ABI version of this header: 4 (2: kron_quantize gained loss_dev; 3: the WaterKron
  * entry points, kron_factor_kronecker, the BiIP transforms and kron_quantize_noalloc;
- * 4: kron_quantize_persistent). */
+ * 4: kron_quantize on the persistent wavefront solver, kron_quantize_per_diagonal). */
 int32_t kron_abi_version(void);
 
 #ifdef __cplusplus

@@ -1,15 +1,16 @@
-"""GPU parity of kron_quantize_persistent, the persistent wavefront solver.
+"""GPU parity of the two schedules of the two-sided solver.
 
-kron_quantize_persistent runs the same leaf tasks as kron_quantize (the same
-operations in the same order, only the schedule differs: one persistent launch
-per chunk of tile-diagonals, tiles handed over through device-coherent flags),
-so its codes, V and loss must equal kron_quantize's bit for bit, whatever order
-the workgroups run the tasks in (FastKron page, section 2.3: the tiles of one
-tile-diagonal are independent).  It is also checked against the oracle on the
-32 x 32 fp64 problem (literal Kronecker GPTQ) and, in fp64, against the C
-left-looking loop up to the 1e-9 tie rule on a ragged shape with several chunks.
+kron_quantize runs the recursion's leaves as one persistent launch per chunk of
+tile-diagonals (tiles handed over through device-coherent flags);
+kron_quantize_per_diagonal launches one kernel per tile-diagonal.  Both run the
+same operations in the same order, so codes, V and loss must be equal bit for
+bit, whatever order the workgroups run the tasks in (FastKron page, section
+2.3: the tiles of one tile-diagonal are independent).  The persistent solver is
+also checked against the oracle on the 32 x 32 fp64 problem (literal Kronecker
+GPTQ) and, in fp64, against the C left-looking loop up to the 1e-9 tie rule.
 Shapes span one tile, ragged edges, several chunks and recursion levels, n > m,
-and the 4096 x 4096 and 1024 x 4096 workloads.
+and the 4096 x 4096 and 1024 x 4096 workloads; kron_quantize runs twice on one
+workspace (its flags are reset per call).
 """
 import numpy as np
 import pytest
@@ -38,15 +39,15 @@ def up(a, dtype):
 
 
 def both(W, UA, UB, s, bits, per_row):
-    """kron_quantize, then kron_quantize_persistent twice on the same workspace."""
+    """kron_quantize_per_diagonal, then kron_quantize twice, on the same workspace."""
     m, n = W.shape
     ws = kq.workspace(kq.KQ_OP_QUANTIZE, W.dtype, m, n)
     outs = []
-    for persistent in (False, True, True):
+    for per_diagonal in (True, False, False):
         codes = torch.full((m, n), 99, dtype=torch.int8, device=DEV)
         V = torch.full_like(W, float("nan"))
         loss = torch.zeros(1, dtype=torch.float64, device=DEV)
-        kq.kron_quantize(W, UA, UB, bits, per_row, s, codes, V, ws, loss=loss, persistent=persistent)
+        kq.kron_quantize(W, UA, UB, bits, per_row, s, codes, V, ws, loss=loss, per_diagonal=per_diagonal)
         torch.cuda.synchronize()
         outs.append((codes.cpu().numpy(), V.cpu().numpy(), float(loss.item())))
     return outs
@@ -73,7 +74,7 @@ def test_tiny_fp64_matches_literal_kronecker_gptq():
     Ad, UA = dense.prepare(A, 0.01)
     Bd, UB = dense.prepare(B, 0.01)
     s = dense.scales(c["W"], 4, False)
-    say("persistent tiny 32x32 fp64")
+    say("schedules tiny 32x32 fp64")
     outs = both(up(c["W"], np.float64), up(UA, np.float64), up(UB, np.float64), up(s, np.float64), 4, False)
     assert_same(outs, "tiny")
     Z1, _, _ = dense.vectorized_kron_gptq(c["W"], Ad, Bd, s, 4)
@@ -85,7 +86,7 @@ def test_tiny_fp64_matches_literal_kronecker_gptq():
 def test_ragged_equals_launch_form(m, n, dtype):
     c = synth.spectral(m, n, config=60 + m % 7)
     UA, UB, s = oracle_problem(c["W"], c["A"], c["B"], 3, True)
-    say("persistent", (m, n), np.dtype(dtype).name)
+    say("schedules", (m, n), np.dtype(dtype).name)
     outs = both(up(c["W"], dtype), up(UA, dtype), up(UB, dtype), up(s, dtype), 3, True)
     assert_same(outs, f"{m}x{n}")
     if dtype == np.float64 and m * n <= 520 * 610:
@@ -98,7 +99,7 @@ def test_per_tensor_scale_and_spectral_256():
     c = synth.spectral()
     UA, UB, s = oracle_problem(c["W"], c["A"], c["B"], 4, False)
     for dtype in (np.float32, np.float64):
-        say("persistent spectral 256 per-tensor", np.dtype(dtype).name)
+        say("schedules spectral 256 per-tensor", np.dtype(dtype).name)
         assert_same(both(up(c["W"], dtype), up(UA, dtype), up(UB, dtype), up(s, dtype), 4, False), "256")
 
 
@@ -111,7 +112,7 @@ def test_llm_workloads_equal_launch_form(m, n, bits):
     UB, _, _ = pipeline.prepare(pipeline.factor(f32(c["grad"])), c["damp"])
     s = torch.empty(m, dtype=torch.float32, device=DEV)
     kq.kron_row_scales(W, bits, True, s)
-    say("persistent llm", (m, n))
+    say("schedules llm", (m, n))
     outs = both(W, UA, UB, s, bits, True)
     assert_same(outs, f"llm {m}x{n}")
     assert not np.isnan(outs[1][1]).any()

@@ -27,7 +27,7 @@ EXPORTED = ("kron_workspace_bytes", "kron_factor_accumulate", "kron_prepare", "k
             "kron_quantize", "kron_loss", "kron_status_string", "kron_last_error", "kron_abi_version",
             "kron_quantize_noalloc", "kron_waterkron_scales", "kron_quantize_waterkron",
             "kron_kronecker_workspace_bytes", "kron_factor_kronecker", "kron_biip_workspace_bytes",
-            "kron_biip_forward", "kron_biip_inverse", "kron_quantize_persistent")
+            "kron_biip_forward", "kron_biip_inverse", "kron_quantize_per_diagonal")
 KQ_KRON_FROBENIUS, KQ_KRON_FLIPFLOP = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KQ_NOALLOC_SCRATCH_BYTES
 
@@ -67,8 +67,8 @@ def library() -> ctypes.CDLL:
     lib.kron_quantize.restype = ctypes.c_int
     lib.kron_quantize.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64,
                                   ctypes.POINTER(_Quantizer), vp, i64, vp, i64, vp, vp, sz, vp]
-    lib.kron_quantize_persistent.restype = ctypes.c_int
-    lib.kron_quantize_persistent.argtypes = lib.kron_quantize.argtypes
+    lib.kron_quantize_per_diagonal.restype = ctypes.c_int
+    lib.kron_quantize_per_diagonal.argtypes = lib.kron_quantize.argtypes
     lib.kron_quantize_noalloc.restype = ctypes.c_int
     lib.kron_quantize_noalloc.argtypes = [ctypes.c_int, i64, i64, vp, i64, vp, i64, vp, i64,
                                           ctypes.POINTER(_Quantizer), vp, i64, vp, i64, vp, vp]
@@ -197,11 +197,11 @@ def kron_row_scales(W: torch.Tensor, bits: int, per_row: bool, scales: torch.Ten
 
 def kron_quantize(W: torch.Tensor, U_A: torch.Tensor, U_B: torch.Tensor | None, bits: int, per_row: bool,
                   scales: torch.Tensor, codes: torch.Tensor, V: torch.Tensor, ws: torch.Tensor,
-                  loss: torch.Tensor | None = None, persistent: bool = False):
+                  loss: torch.Tensor | None = None, per_diagonal: bool = False):
     """Two-sided GPTQ of W (m x n); U_B None means B = I.  Writes codes (int8) and V,
     and, if given, loss[0] (fp64) = the proxy loss of V from the rounding errors.
-    persistent: call kron_quantize_persistent (the same results, the two-sided
-    leaves on the persistent wavefront solver)."""
+    per_diagonal: call kron_quantize_per_diagonal (the same results, the
+    two-sided leaves launched one kernel per tile-diagonal)."""
     m, n = W.shape
     for t, name, shp in ((U_A, "U_A", (n, n)), (U_B, "U_B", (m, m)), (V, "V", (m, n))):
         _expect(t, name, W.dtype, W.device, shape=shp)
@@ -211,7 +211,7 @@ def kron_quantize(W: torch.Tensor, U_A: torch.Tensor, U_B: torch.Tensor | None, 
     _expect(loss, "loss", torch.float64, W.device, 1)
     q = _Quantizer(int(bits), int(bool(per_row)), scales.data_ptr())
     ldb = _ld(U_B) if U_B is not None else 0
-    fn = library().kron_quantize_persistent if persistent else library().kron_quantize
+    fn = library().kron_quantize_per_diagonal if per_diagonal else library().kron_quantize
     _check(fn(_dtype_code(W), m, n, _ptr(W), _ld(W), _ptr(U_A), _ld(U_A), _ptr(U_B), ldb, ctypes.byref(q),
               _ptr(codes), _ld(codes), _ptr(V), _ld(V), _ptr(loss), _ptr(ws), ws.numel(), _stream(W.device)))
     return codes, V

@@ -171,21 +171,21 @@ kq_status kron_quantize(kq_dtype dtype, int64_t m, int64_t n, const void* W, int
     s = check_ws(ws, ws_bytes, quantize_workspace_bytes(dtype, m, n), "kron_quantize");
     if (s != KQ_OK) return s;
     return quantize_dispatch(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev, ws,
-                             static_cast<hipStream_t>(stream), false);
+                             static_cast<hipStream_t>(stream), true);
 }
 
-kq_status kron_quantize_persistent(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw,
-                                   const void* U_A, int64_t lda, const void* U_B, int64_t ldb, const kq_quantizer* q,
-                                   int8_t* codes, int64_t ldc, void* V, int64_t ldv, double* loss_dev, void* ws,
-                                   size_t ws_bytes, void* stream) {
+kq_status kron_quantize_per_diagonal(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t ldw,
+                                     const void* U_A, int64_t lda, const void* U_B, int64_t ldb,
+                                     const kq_quantizer* q, int8_t* codes, int64_t ldc, void* V, int64_t ldv,
+                                     double* loss_dev, void* ws, size_t ws_bytes, void* stream) {
     set_error("");
     kq_status s = quantize_checked_args(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev,
-                                        "kron_quantize_persistent");
+                                        "kron_quantize_per_diagonal");
     if (s != KQ_OK || m == 0 || n == 0) return s;
-    s = check_ws(ws, ws_bytes, quantize_workspace_bytes(dtype, m, n), "kron_quantize_persistent");
+    s = check_ws(ws, ws_bytes, quantize_workspace_bytes(dtype, m, n), "kron_quantize_per_diagonal");
     if (s != KQ_OK) return s;
     return quantize_dispatch(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev, ws,
-                             static_cast<hipStream_t>(stream), true);
+                             static_cast<hipStream_t>(stream), false);
 }
 
 size_t kron_kronecker_workspace_bytes(kq_dtype dtype, int64_t samples, int64_t n, int64_t m) {

@@ -79,5 +79,5 @@ extern "C" kq_status kron_quantize_noalloc(kq_dtype dtype, int64_t m, int64_t n,
     s = scratch_for_current_device(&ws);
     if (s != KQ_OK) return s;
     return quantize_dispatch(dtype, m, n, W, ldw, U_A, lda, U_B, ldb, q, codes, ldc, V, ldv, loss_dev, ws,
-                             static_cast<hipStream_t>(stream), false);
+                             static_cast<hipStream_t>(stream), true);
 }

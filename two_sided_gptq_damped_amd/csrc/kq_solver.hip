@@ -42,11 +42,11 @@
 //   X   mp x np   running pre-rounding values (starts as W)
 //   D   mp x np   errors Delta
 //   R   mp x np   row-propagated errors (zero at the start)
-//   P   CHUNK x min(Mt, Nt) x 2 x 32 x 32   the leaves' pre-accumulated chunk products
+//   P   2 x min(Mt, Nt) x 2 x 32 x 32   the leaves' pre-accumulated chunk products
 //   S   mp        per-row scales
 //   C   np        per-column scales (the WaterKron mode only; unit in the padding)
-//   F   int32 flag words of the chunk solver (per tile: swept, products
-//       pre-accumulated; a ticket counter per chunk; an abort word), zeroed per call
+//   F   int32 flag words of the persistent chunk solver (per tile: swept; a
+//       ticket counter per chunk; an abort word), zeroed per call
 // In the WaterKron mode (kron_quantize_waterkron) entry (i, j) has the grid step
 // S[i] * C[j] (one rounding) and int32 codes clamped only at +-2^30.
 #include <type_traits>
@@ -66,10 +66,10 @@ constexpr int ST = 32;  // scheduling tile edge (CHUNK, the tile-diagonals of a 
 struct WsOffsets {
     int64_t NA, NB, X, D, R, P, S, C, F, end;
 };
-// the chunk solver's flags: per tile a sweep-done and a precompute-done word,
-// one ticket counter per chunk, one abort word (int32 each)
+// the chunk solver's flags: per tile a sweep-done word, one ticket counter per
+// chunk, one abort word (int32 each)
 __host__ __device__ inline int64_t flag_words(int64_t Mt, int64_t Nt) {
-    return 2 * Mt * Nt + (Mt + Nt - 1 + CHUNK - 1) / CHUNK + 1;
+    return Mt * Nt + (Mt + Nt - 1 + CHUNK - 1) / CHUNK + 1;
 }
 __host__ __device__ inline WsOffsets ws_offsets(int64_t Mt, int64_t Nt, int64_t es) {
     const int64_t mp = Mt * ST, np = Nt * ST;
@@ -79,8 +79,8 @@ __host__ __device__ inline WsOffsets ws_offsets(int64_t Mt, int64_t Nt, int64_t 
     o.X = o.NB + mp * mp * es;
     o.D = o.X + mp * np * es;
     o.R = o.D + mp * np * es;
-    o.P = o.R + mp * np * es;  // the CHUNK tile-diagonals of a chunk, two 32 x 32 parts per tile
-    o.S = o.P + int64_t(CHUNK) * 2 * ST * ST * (Mt < Nt ? Mt : Nt) * es;
+    o.P = o.R + mp * np * es;  // two tile-diagonals of two 32 x 32 parts per tile
+    o.S = o.P + 2 * 2 * ST * ST * (Mt < Nt ? Mt : Nt) * es;
     o.C = o.S + mp * es;
     o.F = o.C + np * es;
     o.end = o.F + (flag_words(Mt, Nt) * 4 + 255) / 256 * 256;
@@ -334,13 +334,27 @@ __device__ __forceinline__ void co_st(T* p, T v) {
     else
         *p = v;
 }
+// Four consecutive elements at element offset off (this lane's) from a base
+// that is the same for the whole wave: with CO one 16-byte (fp32) or two
+// (fp64) device-coherent buffer loads (cache policy sc1), the form of an
+// agent-scope atomic load, four elements wide.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int CPOL_SC1 = 16;  // buffer-load cache policy: device scope
 template <bool CO, typename T>
-__device__ __forceinline__ void co_ld4(Vec4<T>& v, const T* p) {
+__device__ __forceinline__ void co_ld4(Vec4<T>& v, const T* base, int off) {
     if constexpr (CO) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v.set(j, __hip_atomic_load(p + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        // raw buffer over the wave's base (0x20000: 32-bit data format, no
+        // swizzle); offsets stay far below the 2 GiB record count
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), 0, 0x7fffffff, 0x00020000);
+        if constexpr (sizeof(T) == 4) {
+            v.v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off * 4, 0, CPOL_SC1));
+        } else {
+            v.lo = __builtin_bit_cast(f64x2, __builtin_amdgcn_raw_buffer_load_b128(r, off * 8, 0, CPOL_SC1));
+            v.hi = __builtin_bit_cast(f64x2, __builtin_amdgcn_raw_buffer_load_b128(r, off * 8 + 16, 0, CPOL_SC1));
+        }
     } else {
-        v.load(p);
+        v.load(base + off);
     }
 }
 
@@ -354,9 +368,10 @@ constexpr uint32_t CHUNK_SPIN_LIMIT = 1u << 18;
 // One leaf task on tile idx of tile-diagonal Kt of chunk [c0, c1): the sweep of
 // the tile, or (pre) the pre-accumulation of its chunk products over every
 // slice but its two freshest.  CHAINED: the task runs inside the persistent
-// chunk solver and waits for the tasks it depends on through the flags (see
-// kq_chunk_sched.hpp), then raises its own; otherwise the launch order provides
-// the dependencies (a launch per tile-diagonal).
+// chunk solver, sums the older slices' products itself (no pre tasks there),
+// waits for the tiles it reads through the flags (see kq_chunk_sched.hpp) and
+// raises its own when swept; otherwise the launch order provides the
+// dependencies (a launch per tile-diagonal, the pre role on its own workgroups).
 template <typename T, bool ENTRY, bool CHAINED>
 __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int c1, int Mt, int Nt, int qmin,
                                           int qmax, char* __restrict__ ws, int m, int n,
@@ -404,9 +419,8 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
                   "16-byte aligned bufA / bufB, 32-byte aligned exchange slices");
     static_assert(2 * ST * PK + 2 * ST * ST <= 2 * ST * PK + 2 * NROUND * ST * RD, "prologue staging fits");
 
-    // P holds pre-accumulated products: in the chunk solver those of every tile
-    // of the chunk (tile idx of diagonal Kt at slot (Kt - c0) pt + idx), with a
-    // launch per tile-diagonal those of two diagonals (slot (Kt & 1) pt + idx).
+    // P holds the pre-accumulated products of two tile-diagonals (slot
+    // (Kt & 1) pt + idx); the chunk solver keeps them in registers instead.
     const int I = (Kt - Nt + 1 > 0 ? Kt - Nt + 1 : 0) + idx;
     if (I > (Kt < Mt - 1 ? Kt : Mt - 1)) return;
     const int J = Kt - I;
@@ -426,21 +440,22 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
     // row part (rowpart) for wv < 4 and the column part for wv >= 4, accumulated
     // over all of that part's slices, so no partial sums cross waves
     const int part = wv >> 2, qd = wv & 3, qr = 16 * (qd >> 1), qc = 16 * (qd & 1);
-    T* const Pt = P + (int64_t((CHAINED ? Kt - c0 : Kt & 1) * pt + idx) * 2 + part) * ST * ST + qr * ST + qc;
+    T* const Pt = P + (int64_t((Kt & 1) * pt + idx) * 2 + part) * ST * ST + qr * ST + qc;
     // the chunk solver's flags (CHAINED)
     int* const flags = reinterpret_cast<int*>(ws + wo.F);
-    int* const abort_word = flags + 2 * Mt * Nt + (Mt + Nt - 1 + CHUNK - 1) / CHUNK;
+    int* const abort_word = flags + Mt * Nt + (Mt + Nt - 1 + CHUNK - 1) / CHUNK;
     __shared__ int s_aborted;
     // wait until the tasks this one reads from have raised their flags (thread 0
     // polls; the barrier and every thread's acquire fence then make their data
     // visible here)
-    auto wait_deps = [&]() {
+    // (fresh: the tiles of the two freshest slices, else those two tiles back)
+    auto wait_deps = [&](bool fresh) {
         if (t == 0) {
-            const ChunkDeps dp = chunk_deps(ChunkTask{pre ? 1 : 0, Kt, idx}, c0, Mt, Nt);
+            const ChunkDeps dp = chunk_deps(ChunkTask{Kt, idx}, c0, Nt);
             int ab = __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                const int wd = u == 0 ? dp.w0 : u == 1 ? dp.w1 : dp.w2;
+            for (int u = 0; u < 2; ++u) {
+                const int wd = fresh ? (u == 0 ? dp.f0 : dp.f1) : (u == 0 ? dp.o0 : dp.o1);
                 if (wd < 0 || ab) continue;
                 const int* f = flags + wd;
                 for (uint32_t it = 0; __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0; ++it) {
@@ -449,25 +464,22 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
                         ab = 1;
                         break;
                     }
-                    if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                    if ((it & 63) == 63 &&
+                        __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
                         ab = 1;
                         break;
                     }
-                    __builtin_amdgcn_s_sleep(1);
                 }
             }
             s_aborted = ab;
         }
         __syncthreads();
     };
-    // every thread's stores reach the device before thread 0 raises flag `which`
-    // (0: the sweep of the tile is done, 1: its precompute is done)
-    auto raise_flag = [&](int which) {
+    // every thread's stores reach the device before thread 0 raises the tile's flag
+    auto raise_flag = [&]() {
         __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
         __syncthreads();
-        if (t == 0)
-            __hip_atomic_store(flags + int64_t(which) * Mt * Nt + int64_t(I) * Nt + J, 1, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        if (t == 0) __hip_atomic_store(flags + int64_t(I) * Nt + J, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
 
     // chunk sources of the tile: row tiles J' in [jl, J), column tiles I' in [il, I);
@@ -476,24 +488,31 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
     const int il = c0 - J > 0 ? c0 - J : 0;
     const int n1all = J - jl;
     const int n2all = I - il;
-    // the slices this workgroup multiplies: row slices [jb, jb + n1), column
-    // slices [ib, ib + n2) (the older ones here, the freshest in the leaf)
-    const int jb = pre ? jl : J - 1, ib = pre ? il : I - 1;
-    const int n1 = pre ? (n1all > 1 ? n1all - 1 : 0) : (n1all > 0 ? 1 : 0);
-    const int n2 = pre ? (n2all > 1 ? n2all - 1 : 0) : (n2all > 0 ? 1 : 0);
-    const int ns = n1 + n2;
+    // the slices multiplied next: row slices [jb, jb + n1), column slices
+    // [ib, ib + n2): the older ones (pre, and first in the chunk solver), then
+    // the freshest (the leaf), staged in stg (older) or the leaf's buffers
+    bool older = pre || CHAINED;
+    int jb, ib, n1, n2, ns;
+    auto select_slices = [&]() {
+        jb = older ? jl : J - 1;
+        ib = older ? il : I - 1;
+        n1 = older ? (n1all > 1 ? n1all - 1 : 0) : (n1all > 0 ? 1 : 0);
+        n2 = older ? (n2all > 1 ? n2all - 1 : 0) : (n2all > 0 ? 1 : 0);
+        ns = n1 + n2;
+    };
+    select_slices();
     constexpr int NFG = LEAF_THREADS / 256;
     constexpr int SLOTS = (BATCH + NFG - 1) / NFG;  // slices of a batch held by one thread
     Vec4<T> pa[SLOTS], pb[SLOTS];
     auto fetch = [&](int sl, Vec4<T>& va, Vec4<T>& vb) {
         if (sl < n1) {
             const int jp = jb + sl;
-            co_ld4<CHAINED>(va, D + int64_t(I * ST + q8) * np + jp * ST + c4);  // A(r = q8, k = c4 + j)
+            co_ld4<CHAINED>(va, D + int64_t(I * ST) * np + jp * ST, q8 * np + c4);  // A(r = q8, k = c4 + j)
             vb.load(NA + int64_t(jp * ST + q8) * np + J * ST + c4);  // B(k = q8, c = c4 + j)
         } else {
             const int ip = ib + sl - n1;
             va.load(NB + int64_t(ip * ST + q8) * mp + I * ST + c4);  // A(r = c4 + j, k = q8)
-            co_ld4<CHAINED>(vb, R + int64_t(ip * ST + q8) * np + J * ST + c4);  // B(k = q8, c = c4 + j)
+            co_ld4<CHAINED>(vb, R + int64_t(ip * ST) * np + J * ST, q8 * np + c4);  // B(k = q8, c = c4 + j)
         }
     };
     // every load of the first batch is in flight before anything waits on one
@@ -505,15 +524,11 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
             if (u < BATCH && u < ns) fetch(u, pa[v], pb[v]);
         }
     };
-    if constexpr (!CHAINED) {
-        first_batch();
-    } else if (pre) {
-        wait_deps();
-        first_batch();
-    }
+    if constexpr (CHAINED) wait_deps(false);
+    first_batch();
     // operand op (0: A, 1: B) of staged slice u
     auto slot = [&](int u, int op) -> T* {
-        return pre ? stg[u][op] : (u == 0 ? bufA : xD) + op * ST * PK;
+        return older ? stg[u][op] : (u == 0 ? bufA : xD) + op * ST * PK;
     };
     // pq += this wave's part over the workgroup's slices, staged in batches
     auto products = [&](Q16<T>& pq) {
@@ -564,8 +579,7 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
             pq.set(r, part == 0 ? Rt[int64_t(Q16<T>::row(r, lane)) * np + Q16<T>::col(r, lane)] : T(0));
         products(pq);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) co_st<CHAINED>(Pt + Q16<T>::row(r, lane) * ST + Q16<T>::col(r, lane), pq.get(r));
-        if constexpr (CHAINED) raise_flag(1);
+        for (int r = 0; r < 4; ++r) Pt[Q16<T>::row(r, lane) * ST + Q16<T>::col(r, lane)] = pq.get(r);
         return;
     }
     // the leaf: this wave's quadrant of the pre-accumulated products, or at the
@@ -575,12 +589,23 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
     const int pld = Kt > c0 ? ST : np;
     const bool pzero = Kt == c0 && part == 1;
     T pin[4];
-    auto load_pin = [&]() {
+    if constexpr (CHAINED) {
+        // the older slices' products, from R[I, J] (zero for the column part)
+        Q16<T> pq;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            pin[r] = pzero ? T(0) : co_ld<CHAINED>(psrc + Q16<T>::row(r, lane) * pld + Q16<T>::col(r, lane));
-    };
-    if constexpr (!CHAINED) load_pin();
+            pq.set(r, part == 0 ? Rt[int64_t(Q16<T>::row(r, lane)) * np + Q16<T>::col(r, lane)] : T(0));
+        products(pq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pin[r] = pq.get(r);
+        __syncthreads();  // the staging area is free for the leaf's tables
+        older = false;
+        select_slices();  // the freshest slices, multiplied after the wait below
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            pin[r] = pzero ? T(0) : psrc[Q16<T>::row(r, lane) * pld + Q16<T>::col(r, lane)];
+    }
 
     constexpr int FE = ST * ST / LEAF_THREADS;  // factor-block entries per thread
     T fnb[FE], fna[FE];
@@ -648,9 +673,8 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
     // chained: the tile's own data is on its way; now wait for the freshest
     // slices and the pre-accumulated products
     if constexpr (CHAINED) {
-        wait_deps();
+        wait_deps(true);
         first_batch();
-        load_pin();
     }
 
     // ---- prologue: rowpart (crow) and the chunk's column part (ccol), block layout.
@@ -837,6 +861,8 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
     // write R[I, J] = rowpart + Delta N_A[J, J] (read by the later leaves of the
     // chunk and by the band products of the later nodes), gathered from the
     // rounds that published it; waves 4..7 store Delta, the codes and V.
+    // (chained: the codes and V after the tile's flag, off the path of the tiles waiting on it)
+    T zv[4];
     if (blk) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -847,15 +873,21 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t gi = int64_t(I) * ST + r0 + i, gj = int64_t(J) * ST + b;
-            const T z = bufA[(r0 + i) * PK + b];
+            zv[i] = bufA[(r0 + i) * PK + b];
             co_st<CHAINED>(D + gi * np + gj, bufB[b * PK + r0 + i]);
+        }
+    }
+    if constexpr (CHAINED) raise_flag();
+    if (!blk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t gi = int64_t(I) * ST + r0 + i, gj = int64_t(J) * ST + b;
             if (gi < m && gj < n) {
-                Z[gi * ldz + gj] = CodeT<ENTRY>(z);
-                V[gi * ldv + gj] = CHAINED && s_aborted ? T(__builtin_nan("")) : sblk[i] * z;
+                Z[gi * ldz + gj] = CodeT<ENTRY>(zv[i]);
+                V[gi * ldv + gj] = CHAINED && s_aborted ? T(__builtin_nan("")) : sblk[i] * zv[i];
             }
         }
     }
-    if constexpr (CHAINED) raise_flag(0);
 }
 
 // Launch K: workgroups [0, nk) sweep the tiles of diagonal K.  When diagonal
@@ -893,7 +925,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void chunk_kernel(int c0, int c1, int
                                                     CodeT<ENTRY>* __restrict__ Z, int64_t ldz, T* __restrict__ V,
                                                     int64_t ldv) {
     const WsOffsets wo = ws_offsets(Mt, Nt, sizeof(T));
-    int* const counter = reinterpret_cast<int*>(ws + wo.F) + 2 * Mt * Nt + c0 / CHUNK;
+    int* const counter = reinterpret_cast<int*>(ws + wo.F) + Mt * Nt + c0 / CHUNK;
     __shared__ int s_ticket;
     for (;;) {
         __syncthreads();  // the previous task is done with the LDS and s_ticket
@@ -901,8 +933,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void chunk_kernel(int c0, int c1, int
             s_ticket = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         const ChunkTask tk = chunk_task(__builtin_amdgcn_readfirstlane(s_ticket), c0, c1, Mt, Nt);
-        if (tk.kind < 0) return;
-        leaf_task<T, ENTRY, true>(tk.kind == 1, tk.Kt, tk.idx, c0, c1, Mt, Nt, qmin, qmax, ws, m, n, Z, ldz, V, ldv);
+        if (tk.Kt < 0) return;
+        leaf_task<T, ENTRY, true>(false, tk.Kt, tk.idx, c0, c1, Mt, Nt, qmin, qmax, ws, m, n, Z, ldz, V, ldv);
     }
 }
 

@@ -53,9 +53,10 @@ def prepare(A: torch.Tensor, damp_rel: float, info: torch.Tensor | None = None):
     return U, tr, lam  # ws goes back to this stream's pool: stream-ordered reuse
 
 
-def quantize(W, U_A, U_B, bits, per_row, scales=None, ws=None, loss_out=None):
+def quantize(W, U_A, U_B, bits, per_row, scales=None, ws=None, loss_out=None, per_diagonal=False):
     """codes, V, scales; loss_out (a float64 device tensor), if given, receives
-    the proxy loss of V from the rounding errors."""
+    the proxy loss of V from the rounding errors.  per_diagonal: the schedule
+    that never waits inside a kernel (kron_quantize_per_diagonal)."""
     m, n = W.shape
     if scales is None:
         scales = torch.empty(m if per_row else 1, dtype=W.dtype, device=W.device)
@@ -64,7 +65,7 @@ def quantize(W, U_A, U_B, bits, per_row, scales=None, ws=None, loss_out=None):
     V = torch.empty_like(W)
     if ws is None:
         ws = workspace(KQ_OP_QUANTIZE, W.dtype, m, n, W.device)
-    kron_quantize(W, U_A, U_B, bits, per_row, scales, codes, V, ws, loss=loss_out)
+    kron_quantize(W, U_A, U_B, bits, per_row, scales, codes, V, ws, loss=loss_out, per_diagonal=per_diagonal)
     return codes, V, scales
 
 
@@ -146,10 +147,14 @@ def quantize_layers(layers, bits, per_row=True, damp_rel=0.01, two_sided=True, c
     factor chains of layer k + 1 run beside the solve of layer k, and consecutive
     layers are solved on two alternate streams (the caller's and a second one),
     so two solves share the GPU: the tile sweeps of one solve occupy at most half
-    of the CUs.  Returns one dict per layer, as quantize_layer does, ready on the
-    caller's stream.  The positive-definiteness of every damped factor is checked
-    once, after the last layer has been issued (a host wait per layer would stop
-    the pipeline); KronError names the first failing layer."""
+    of the CUs.  The solves use the per-diagonal schedule, whose workgroups never
+    hold a compute unit while waiting for one another, so the work beside them
+    gets the CUs that the sweeps leave free (the persistent schedule of
+    kron_quantize is faster alone but slower shared).  Returns one dict per
+    layer, as quantize_layer does, ready on the caller's stream.  The
+    positive-definiteness of every damped factor is checked once, after the last
+    layer has been issued (a host wait per layer would stop the pipeline);
+    KronError names the first failing layer."""
     main = torch.cuda.current_stream()
     sa, sb, s2 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
     for s in (sa, sb, s2):
@@ -169,7 +174,8 @@ def quantize_layers(layers, bits, per_row=True, damp_rel=0.01, two_sided=True, c
                 cur[key].record_stream(ss)
         with torch.cuda.stream(ss):
             lo = torch.empty(1, dtype=torch.float64, device=W.device)
-            codes, V, scales = quantize(W, cur["U_A"], cur["U_B"], bits, per_row, scales=cur["scales"], loss_out=lo)
+            codes, V, scales = quantize(W, cur["U_A"], cur["U_B"], bits, per_row, scales=cur["scales"], loss_out=lo,
+                                        per_diagonal=True)
             out = dict(A=cur["A"], B=cur["B"], U_A=cur["U_A"], U_B=cur["U_B"], trace_A=cur["trace_A"],
                        trace_B=cur["trace_B"], codes=codes, V=V, scales=scales, loss=lo, info=cur["info"])
             if check_loss:
