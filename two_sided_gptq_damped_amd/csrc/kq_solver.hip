@@ -452,23 +452,23 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
     auto wait_deps = [&](bool fresh) {
         if (t == 0) {
             const ChunkDeps dp = chunk_deps(ChunkTask{Kt, idx}, c0, Nt);
+            const int w0 = fresh ? dp.f0 : dp.o0, w1 = fresh ? dp.f1 : dp.o1;
+            // both flags are polled together (two loads in flight per poll); a
+            // missing one counts as raised (its load reads word 0, unused)
+            const int* const p0 = flags + (w0 < 0 ? 0 : w0);
+            const int* const p1 = flags + (w1 < 0 ? 0 : w1);
+            bool r0 = w0 < 0, r1 = w1 < 0;
             int ab = __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int wd = fresh ? (u == 0 ? dp.f0 : dp.f1) : (u == 0 ? dp.o0 : dp.o1);
-                if (wd < 0 || ab) continue;
-                const int* f = flags + wd;
-                for (uint32_t it = 0; __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0; ++it) {
-                    if (it >= CHUNK_SPIN_LIMIT) {
-                        __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        ab = 1;
-                        break;
-                    }
-                    if ((it & 63) == 63 &&
-                        __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-                        ab = 1;
-                        break;
-                    }
+            for (uint32_t it = 0; !(r0 && r1) && !ab; ++it) {
+                const int v0 = __hip_atomic_load(p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int v1 = __hip_atomic_load(p1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                r0 = r0 || v0 != 0;
+                r1 = r1 || v1 != 0;
+                if (it >= CHUNK_SPIN_LIMIT) {
+                    __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    ab = 1;
+                } else if ((it & 63) == 63) {
+                    ab = __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
             s_aborted = ab;
