@@ -363,7 +363,7 @@ def shape_report(torch):
     def up(a, dt):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)
 
-    def core_times(W, UA, UB, bits, scales, reps):
+    def core_times(W, UA, UB, bits, scales, reps, per_diagonal=False):
         m, n = W.shape
         codes = torch.empty(m, n, dtype=torch.int8, device=dev)
         V = torch.empty_like(W)
@@ -372,7 +372,7 @@ def shape_report(torch):
         ts = []
         for _ in range(reps + 1):  # the first call warms up
             a.record()
-            kq.kron_quantize(W, UA, UB, bits, True, scales, codes, V, ws)
+            kq.kron_quantize(W, UA, UB, bits, True, scales, codes, V, ws, per_diagonal=per_diagonal)
             b.record()
             b.synchronize()
             ts.append(a.elapsed_time(b))
@@ -408,12 +408,14 @@ def shape_report(torch):
         kq.kron_row_scales(W, bits, True, scales)
         reps = 3 if m * n > 3e7 else 10
         t2 = core_times(W, UA, UB, bits, scales, reps)
+        t2d = core_times(W, UA, UB, bits, scales, reps, per_diagonal=True)
         t1 = core_times(W, UA, None, bits, scales, reps)
         peak = PEAK_FP64_MFMA if dt == np.float64 else PEAK_FP32_MFMA
         F, F1 = solver_flops(m, n), float(m) * n * (n - 1)
         print(json.dumps({"shape": label, "dtype": np.dtype(dt).name, "m": m, "n": n, "bits": bits,
                           "two_sided_ms": t2, "two_sided_weights_per_s": m * n / (t2 * 1e-3),
                           "two_sided_tflops": F / (t2 * 1e-3) / 1e12, "two_sided_frac_peak": F / (t2 * 1e-3) / peak,
+                          "two_sided_per_diagonal_ms": t2d,
                           "one_sided_ms": t1, "one_sided_weights_per_s": m * n / (t1 * 1e-3),
                           "one_sided_tflops": F1 / (t1 * 1e-3) / 1e12, "one_sided_frac_peak": F1 / (t1 * 1e-3) / peak,
                           "two_over_one_sided": t2 / t1}), flush=True)

@@ -316,7 +316,7 @@ kq_status kron_loss(kq_dtype dtype, int64_t m, int64_t n, const void* W, int64_t
  * device that is current at the call, which must be the device of `stream`.
  *   - Sizes whose scratch need (kron_workspace_bytes(KQ_OP_QUANTIZE, dtype, m,
  *     n)) exceeds KQ_NOALLOC_SCRATCH_BYTES return KQ_ERR_WORKSPACE before
- *     anything is enqueued: e.g. fp32 up to 1728 x 1728 two-sided fits.
+ *     anything is enqueued: e.g. fp32 up to 1792 x 1792 two-sided fits.
  *   - Every call on one GPU uses that GPU's single array: calls that overlap on
  *     one GPU (other streams, other threads) race and give undefined results.
  *     Calls ordered on one stream are safe.

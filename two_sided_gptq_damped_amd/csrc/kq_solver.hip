@@ -1400,11 +1400,11 @@ kq_status waterkron_dispatch(kq_dtype dtype, int64_t m, int64_t n, const void* W
     if (dtype == KQ_F64)
         return quantize_as<double>(m, n, W, ldw, UA, lda, UB, ldb,
                                    {static_cast<const double*>(beta), 1, static_cast<const double*>(alpha),
-                                    -WK_CODE_BOUND, WK_CODE_BOUND, codes, ldc, false},
+                                    -WK_CODE_BOUND, WK_CODE_BOUND, codes, ldc, true},
                                    V, ldv, loss_dev, ws, st);
     return quantize_as<float>(m, n, W, ldw, UA, lda, UB, ldb,
                               {static_cast<const float*>(beta), 1, static_cast<const float*>(alpha), -WK_CODE_BOUND,
-                               WK_CODE_BOUND, codes, ldc, false},
+                               WK_CODE_BOUND, codes, ldc, true},
                               V, ldv, loss_dev, ws, st);
 }
 
