@@ -130,9 +130,11 @@ kq_status kron_row_scales(kq_dtype dtype, int64_t m, int64_t n, const void* W, i
  * anti-diagonal ranges (sections 2.4-2.5).  The matrix is cut into 32 x 32
  * tiles; the recursion's leaves, chunks of 16 tile-diagonals, each run as one
  * persistent launch in which a tile starts as soon as the tiles before it in its
- * row and column are done.  Every wait inside that launch is bounded (a wait
- * that could never end, which the task order rules out, would end the launch
- * with NaN in V).  In exact arithmetic every valid
+ * row and column are done.  Every wait inside that launch is bounded, by 2^18
+ * polls or by the decimal value of the environment variable
+ * KQ_CHUNK_SPIN_LIMIT read at the call: a wait that reaches the bound (which
+ * the task order rules out for the default) ends the launch early, with NaN in
+ * V for the tiles swept after it.  In exact arithmetic every valid
  * processing order gives the same output (section 2.5); in floating point the
  * order of the feedback sums can move values that sit within rounding of a grid
  * midpoint.

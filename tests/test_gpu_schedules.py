@@ -38,10 +38,11 @@ def up(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(np.asarray(a).astype(dtype))).to(DEV)
 
 
-def both(W, UA, UB, s, bits, per_row):
+def both(W, UA, UB, s, bits, per_row, ws=None):
     """kron_quantize_per_diagonal, then kron_quantize twice, on the same workspace."""
     m, n = W.shape
-    ws = kq.workspace(kq.KQ_OP_QUANTIZE, W.dtype, m, n)
+    if ws is None:
+        ws = kq.workspace(kq.KQ_OP_QUANTIZE, W.dtype, m, n)
     outs = []
     for per_diagonal in (True, False, False):
         codes = torch.full((m, n), 99, dtype=torch.int8, device=DEV)
@@ -115,4 +116,29 @@ def test_llm_workloads_equal_launch_form(m, n, bits):
     say("schedules llm", (m, n))
     outs = both(W, UA, UB, s, bits, True)
     assert_same(outs, f"llm {m}x{n}")
+    assert not np.isnan(outs[1][1]).any()
+
+
+def test_bounded_wait_ends_the_launch(monkeypatch):
+    """Every wait of the persistent solver is bounded.  With the bound forced to
+    zero polls from the host (KQ_CHUNK_SPIN_LIMIT=0), a wait that is not
+    satisfied at its first poll gives up and raises the abort word: the launch
+    must still drain (the call returns) and the tiles swept after the abort
+    store NaN in V.  The next call, with the default bound, is exact again on the
+    same workspace (its flags are reset per call)."""
+    m = n = 512
+    c = synth.spectral(m, n, config=71)
+    UA, UB, s = oracle_problem(c["W"], c["A"], c["B"], 3, True)
+    W, UAt, UBt, st = (up(x, np.float32) for x in (c["W"], UA, UB, s))
+    ws = kq.workspace(kq.KQ_OP_QUANTIZE, W.dtype, m, n)
+    codes = torch.empty((m, n), dtype=torch.int8, device=DEV)
+    V = torch.empty_like(W)
+    say("schedules forced abort", (m, n))
+    monkeypatch.setenv("KQ_CHUNK_SPIN_LIMIT", "0")
+    kq.kron_quantize(W, UAt, UBt, 3, True, st, codes, V, ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(V).any(), "no wait gave up with a zero bound"
+    monkeypatch.delenv("KQ_CHUNK_SPIN_LIMIT")
+    outs = both(W, UAt, UBt, st, 3, True, ws)
+    assert_same(outs, "after a forced abort")
     assert not np.isnan(outs[1][1]).any()

@@ -49,6 +49,7 @@
 //       ticket counter per chunk; an abort word), zeroed per call
 // In the WaterKron mode (kron_quantize_waterkron) entry (i, j) has the grid step
 // S[i] * C[j] (one rounding) and int32 codes clamped only at +-2^30.
+#include <cstdlib>
 #include <type_traits>
 
 #include "kq_common.hpp"
@@ -363,7 +364,8 @@ __device__ __forceinline__ void co_ld4(Vec4<T>& v, const T* base, int off) {
 // running chunk (a whole chunk takes a few hundred microseconds), so it only
 // ends a wait that could never be satisfied; the task then raises the abort
 // word, every later wait returns at once and the swept tiles store NaN in V.
-constexpr uint32_t CHUNK_SPIN_LIMIT = 1u << 18;
+constexpr uint32_t CHUNK_SPIN_LIMIT = 1u << 18;  // the default; the environment variable
+                                                 // KQ_CHUNK_SPIN_LIMIT overrides it per call
 
 // One leaf task on tile idx of tile-diagonal Kt of chunk [c0, c1): the sweep of
 // the tile, or (pre) the pre-accumulation of its chunk products over every
@@ -376,7 +378,7 @@ template <typename T, bool ENTRY, bool CHAINED>
 __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int c1, int Mt, int Nt, int qmin,
                                           int qmax, char* __restrict__ ws, int m, int n,
                                           CodeT<ENTRY>* __restrict__ Z, int64_t ldz, T* __restrict__ V,
-                                          int64_t ldv) {
+                                          int64_t ldv, uint32_t spin_limit = CHUNK_SPIN_LIMIT) {
     const WsOffsets wo = ws_offsets(Mt, Nt, sizeof(T));
     const int np = Nt * ST, mp = Mt * ST, pt = Mt < Nt ? Mt : Nt;
     T* const D = reinterpret_cast<T*>(ws + wo.D);
@@ -464,7 +466,7 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
                 const int v1 = __hip_atomic_load(p1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 r0 = r0 || v0 != 0;
                 r1 = r1 || v1 != 0;
-                if (it >= CHUNK_SPIN_LIMIT) {
+                if (it >= spin_limit) {
                     __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     ab = 1;
                 } else if ((it & 63) == 63) {
@@ -923,7 +925,7 @@ template <typename T, bool ENTRY>
 __global__ __launch_bounds__(LEAF_THREADS) void chunk_kernel(int c0, int c1, int Mt, int Nt, int qmin, int qmax,
                                                     char* __restrict__ ws, int m, int n,
                                                     CodeT<ENTRY>* __restrict__ Z, int64_t ldz, T* __restrict__ V,
-                                                    int64_t ldv) {
+                                                    int64_t ldv, uint32_t spin_limit) {
     const WsOffsets wo = ws_offsets(Mt, Nt, sizeof(T));
     int* const counter = reinterpret_cast<int*>(ws + wo.F) + Mt * Nt + c0 / CHUNK;
     __shared__ int s_ticket;
@@ -934,7 +936,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void chunk_kernel(int c0, int c1, int
         __syncthreads();
         const ChunkTask tk = chunk_task(__builtin_amdgcn_readfirstlane(s_ticket), c0, c1, Mt, Nt);
         if (tk.Kt < 0) return;
-        leaf_task<T, ENTRY, true>(false, tk.Kt, tk.idx, c0, c1, Mt, Nt, qmin, qmax, ws, m, n, Z, ldz, V, ldv);
+        leaf_task<T, ENTRY, true>(false, tk.Kt, tk.idx, c0, c1, Mt, Nt, qmin, qmax, ws, m, n, Z, ldz, V, ldv,
+                                  spin_limit);
     }
 }
 
@@ -1144,6 +1147,18 @@ __global__ __launch_bounds__(256) void error_loss_final_kernel(const double* __r
     if (threadIdx.x == 0) *out = tot;
 }
 
+// The bound on one wait of the persistent chunk solver: CHUNK_SPIN_LIMIT, or
+// the value of the environment variable KQ_CHUNK_SPIN_LIMIT (a decimal count of
+// polls), read per call.  A small value makes waits end early on purpose: the
+// launch then still drains, with NaN in V (how the bound's exit path is tested).
+static uint32_t chunk_spin_limit() {
+    const char* e = std::getenv("KQ_CHUNK_SPIN_LIMIT");
+    if (!e || !*e) return CHUNK_SPIN_LIMIT;
+    char* end = nullptr;
+    const unsigned long v = std::strtoul(e, &end, 10);
+    return (end && *end == '\0' && v <= 0xffffffffu) ? uint32_t(v) : CHUNK_SPIN_LIMIT;
+}
+
 __global__ void zero_words_kernel(int* __restrict__ p, int64_t count) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < count) p[i] = 0;
@@ -1195,6 +1210,7 @@ struct SolverRun {
     hipStream_t st;
     char* ws;  // the workspace base (the leaves find their arrays from it)
     bool chained;  // chunks on the persistent chunk solver, else a launch per tile-diagonal and role
+    uint32_t spin_limit;  // the chunk solver's bound on one wait, in polls
 
     kq_status leaf(int K, int c0, int c1) {
         const int Mt = int(L.Mt), Nt = int(L.Nt);
@@ -1258,10 +1274,10 @@ struct SolverRun {
         const dim3 grid(tasks < CHUNK_GRID ? tasks : CHUNK_GRID);
         if (C)
             hipLaunchKernelGGL((chunk_kernel<T, true>), grid, dim3(LEAF_THREADS), 0, st, c0, c1, Mt, Nt, qmin, qmax,
-                               ws, m, n, static_cast<int32_t*>(Z), ldz, V, ldv);
+                               ws, m, n, static_cast<int32_t*>(Z), ldz, V, ldv, spin_limit);
         else
             hipLaunchKernelGGL((chunk_kernel<T, false>), grid, dim3(LEAF_THREADS), 0, st, c0, c1, Mt, Nt, qmin,
-                               qmax, ws, m, n, static_cast<int8_t*>(Z), ldz, V, ldv);
+                               qmax, ws, m, n, static_cast<int8_t*>(Z), ldz, V, ldv, spin_limit);
         KQ_LAUNCHED("chunk_kernel");
         return KQ_OK;
     }
@@ -1316,7 +1332,7 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
                      reinterpret_cast<T*>(base + L.off_R), reinterpret_cast<T*>(base + L.off_P),
                      reinterpret_cast<T*>(base + L.off_S),
                      q.col_scales ? reinterpret_cast<T*>(base + L.off_C) : nullptr, q.codes, q.ldc, V, ldv, st, base,
-                     q.chained};
+                     q.chained, chunk_spin_limit()};
     const int threads = 256;
     auto blocks = [&](int64_t count) { return dim3(unsigned((count + threads - 1) / threads)); };
     auto rows = [&](int64_t cols, int64_t nrows) {  // the kernels loop over rows beyond the grid's y extent
