@@ -1,15 +1,16 @@
 """Host check of the persistent chunk solver's task order (no GPU).
 
 The two-sided solver's leaves run as one persistent launch per chunk of
-tile-diagonals: workgroups draw tickets and wait on per-tile flags
-(`csrc/kq_chunk_sched.hpp`).  `chunk_sched_check.cpp` builds that header's
-ticket decoding and wait rules on the host and checks, for every chunk the
+tile-diagonals: workgroups draw tickets, and each task polls the values it
+reads (the outputs of the chunk's tiles before it in its row and column) until
+they are written (`csrc/kq_chunk_sched.hpp`).  `chunk_sched_check.cpp` builds
+that header's ticket decoding on the host and checks, for every chunk the
 recursion makes on the configured shapes and on small, ragged and degenerate
-tile grids, that every wait points to a smaller ticket of the same chunk (so a
-launch always drains, whatever number of its workgroups is resident), and that
-everything a task reads is final once its waits end (FastKron page, section 2.3:
-an entry depends on every entry above and to the left of it); then it runs
-chunks on host threads with random delays.
+tile grids, that every value a task reads is written by a task with a smaller
+ticket of the same chunk (so a launch always drains, whatever number of its
+workgroups is resident; FastKron page, section 2.3: an entry depends on every
+entry above and to the left of it); then it runs chunks on host threads with
+random delays.
 """
 import os
 import shutil

@@ -3,21 +3,20 @@
 // tile-diagonals is solved before the band products that follow it).
 //
 // One launch solves the tile-diagonals [c0, c1) of a chunk.  Its workgroups
-// draw tickets from one counter; ticket t names the sweep of a tile, in
+// draw tickets from one counter; ticket t names the task of one tile, in
 // tile-diagonal order and, on a diagonal, by increasing row I.  The task of
-// tile (I, J) on diagonal Kt first sums the tile's chunk products over every
-// slice older than its two freshest ones, then the two freshest, then sweeps
-// the tile.  It waits on per-tile flags, raised when a tile's sweep is done:
-//   before the older slices  the tiles two before it in its row and column,
-//                            (I, J - 2) and (I - 2, J), when they are in the chunk
-//                            (each of those waited for the tile before it in its
-//                            row and column, so every older slice is final too);
-//   before the freshest      (I, J - 1) and (I - 1, J).
-// Every task waits only on tasks with smaller tickets, and a workgroup waits
-// only on the task it drew last, so the holder of the smallest unfinished
-// ticket never waits on an unfinished task: the launch finishes whatever
-// number of its workgroups is resident (tests/chunk_sched_check.cpp verifies
-// the order on the host for every chunk of the configured shapes).
+// tile (I, J) on diagonal Kt sums the tile's chunk products, first over every
+// slice older than its two freshest ones, then over the freshest two, and
+// sweeps the tile.  A slice is a swept tile's output: the errors D of (I, J')
+// (a row slice) or the row-propagated errors RF of (I', J) (a column slice),
+// for the tiles of the chunk before (I, J) in its row and column.  The task
+// polls each value it reads until it is written (the values start as a pattern
+// no result has), so it waits exactly for the tasks that write what it reads:
+// tiles on earlier tile-diagonals, which have smaller tickets.  A workgroup
+// waits only on the task it drew last, so the holder of the smallest
+// unfinished ticket never waits on an unfinished task: the launch finishes
+// whatever number of its workgroups is resident (tests/chunk_sched_check.cpp
+// verifies the order on the host for every chunk of the configured shapes).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -63,28 +62,6 @@ __host__ __device__ inline int chunk_ticket(int Kt, int idx, int c0, int Mt, int
     int t = 0;
     for (int k = c0; k < Kt; ++k) t += diag_tiles(k, Mt, Nt);
     return t + idx;
-}
-
-// The flags a task waits on, at fixed slots (so a kernel keeps them in
-// registers): the flag word of a tile (word I Nt + J: the sweep of tile (I, J) is
-// done), or -1 where there is none.  o0, o1 before the older slices; f0, f1
-// before the freshest.
-struct ChunkDeps {
-    int o0, o1, f0, f1;
-};
-
-__host__ __device__ inline ChunkDeps chunk_deps(const ChunkTask& tk, int c0, int Nt) {
-    const int I = diag_lo(tk.Kt, Nt) + tk.idx, J = tk.Kt - I;
-    ChunkDeps d{-1, -1, -1, -1};
-    if (tk.Kt - 2 >= c0) {  // older slices: row tiles (I, J') with I + J' in [c0, Kt - 2], column tiles likewise
-        d.o0 = J >= 2 ? I * Nt + J - 2 : -1;
-        d.o1 = I >= 2 ? (I - 2) * Nt + J : -1;
-    }
-    if (tk.Kt - 1 >= c0) {
-        d.f0 = J >= 1 ? I * Nt + J - 1 : -1;
-        d.f1 = I >= 1 ? (I - 1) * Nt + J : -1;
-    }
-    return d;
 }
 
 }  // namespace kq

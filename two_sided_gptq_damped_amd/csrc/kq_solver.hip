@@ -41,12 +41,15 @@
 // (B = I does not come here: kron_quantize runs the one-sided path for it.)
 //   X   mp x np   running pre-rounding values (starts as W)
 //   D   mp x np   errors Delta
-//   R   mp x np   row-propagated errors (zero at the start)
+//   R   mp x np   row-propagated errors accumulated for the tiles not yet swept (zero at the start)
+//   RF  mp x np   each swept tile's complete row-propagated errors (its leaf writes them)
 //   P   2 x min(Mt, Nt) x 2 x 32 x 32   the leaves' pre-accumulated chunk products
 //   S   mp        per-row scales
 //   C   np        per-column scales (the WaterKron mode only; unit in the padding)
-//   F   int32 flag words of the persistent chunk solver (per tile: swept; a
-//       ticket counter per chunk; an abort word), zeroed per call
+//   F   int32 words of the persistent chunk solver (a ticket counter per chunk,
+//       an abort word), zeroed per call; in that solver D and RF start as an
+//       unreachable bit pattern (a signalling NaN) that marks a value as not yet
+//       written
 // In the WaterKron mode (kron_quantize_waterkron) entry (i, j) has the grid step
 // S[i] * C[j] (one rounding) and int32 codes clamped only at +-2^30.
 #include <cstdlib>
@@ -65,12 +68,22 @@ constexpr int ST = 32;  // scheduling tile edge (CHUNK, the tile-diagonals of a 
 // The padded extents are multiples of 64, so every array size is a multiple of
 // 256 bytes and the arrays are 256-byte aligned.
 struct WsOffsets {
-    int64_t NA, NB, X, D, R, P, S, C, F, end;
+    int64_t NA, NB, X, D, R, RF, P, S, C, F, end;
 };
-// the chunk solver's flags: per tile a sweep-done word, one ticket counter per
-// chunk, one abort word (int32 each)
+// The bit pattern that marks a handed-over value (D, RF) as not yet written in
+// the persistent solver: a signalling NaN, which no arithmetic result is (IEEE
+// operations quiet a signalling NaN), so every value a leaf stores differs from it.
+template <typename T>
+__host__ __device__ constexpr auto unwritten_bits() {
+    if constexpr (sizeof(T) == 4)
+        return uint32_t(0xFFA5A5A5u);
+    else
+        return uint64_t(0xFFF4A5A5A5A5A5A5ull);
+}
+
+// the chunk solver's words: one ticket counter per chunk, one abort word (int32)
 __host__ __device__ inline int64_t flag_words(int64_t Mt, int64_t Nt) {
-    return Mt * Nt + (Mt + Nt - 1 + CHUNK - 1) / CHUNK + 1;
+    return (Mt + Nt - 1 + CHUNK - 1) / CHUNK + 1;
 }
 __host__ __device__ inline WsOffsets ws_offsets(int64_t Mt, int64_t Nt, int64_t es) {
     const int64_t mp = Mt * ST, np = Nt * ST;
@@ -80,7 +93,8 @@ __host__ __device__ inline WsOffsets ws_offsets(int64_t Mt, int64_t Nt, int64_t 
     o.X = o.NB + mp * mp * es;
     o.D = o.X + mp * np * es;
     o.R = o.D + mp * np * es;
-    o.P = o.R + mp * np * es;  // two tile-diagonals of two 32 x 32 parts per tile
+    o.RF = o.R + mp * np * es;
+    o.P = o.RF + mp * np * es;  // two tile-diagonals of two 32 x 32 parts per tile
     o.S = o.P + 2 * 2 * ST * ST * (Mt < Nt ? Mt : Nt) * es;
     o.C = o.S + mp * es;
     o.F = o.C + np * es;
@@ -98,7 +112,8 @@ __global__ void normalize_factor_kernel(const T* __restrict__ U, int64_t ldu, in
 template <typename T>
 __global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, int n, int mp, int np,
                                    const T* __restrict__ scales, int per_row, const T* __restrict__ col_scales,
-                                   T* __restrict__ X, T* __restrict__ S, T* __restrict__ C, T* __restrict__ R);
+                                   T* __restrict__ X, T* __restrict__ S, T* __restrict__ C, T* __restrict__ R,
+                                   T* __restrict__ D, T* __restrict__ RF);
 
 // Four consecutive elements (16-byte aligned), from global memory or LDS.
 template <typename T>
@@ -234,12 +249,14 @@ __global__ void normalize_factor_kernel(const T* __restrict__ U, int64_t ldu, in
 }
 
 // X = W zero-padded to mp x np; S = the scales, unit in the padding; with column
-// scales, C = them, unit in the padding; R (when given) = 0.  Rows as in normalize_factor_kernel,
+// scales, C = them, unit in the padding; R (when given) = 0; D and RF (when
+// given) = the unwritten pattern.  Rows as in normalize_factor_kernel,
 // four consecutive columns per thread.
 template <typename T>
 __global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, int n, int mp, int np,
                                    const T* __restrict__ scales, int per_row, const T* __restrict__ col_scales,
-                                   T* __restrict__ X, T* __restrict__ S, T* __restrict__ C, T* __restrict__ R) {
+                                   T* __restrict__ X, T* __restrict__ S, T* __restrict__ C, T* __restrict__ R,
+                                   T* __restrict__ D, T* __restrict__ RF) {
     const int c0 = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
     if (col_scales && blockIdx.y == 0 && c0 < np) {
 #pragma unroll
@@ -256,6 +273,12 @@ __global__ void init_solver_kernel(const T* __restrict__ W, int64_t ldw, int m, 
 #pragma unroll
             for (int u = 0; u < 4; ++u) v.set(u, T(0));
             v.store(R + int64_t(r) * np + c0);
+        }
+        if (D) {  // D and RF: not yet written (the persistent solver polls for them)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v.set(u, __builtin_bit_cast(T, unwritten_bits<T>()));
+            v.store(D + int64_t(r) * np + c0);
+            v.store(RF + int64_t(r) * np + c0);
         }
     }
 }
@@ -359,7 +382,16 @@ __device__ __forceinline__ void co_ld4(Vec4<T>& v, const T* base, int off) {
     }
 }
 
-// Bound on a chunk task's wait for one flag, in polls (each a device-coherent
+template <typename T>
+__device__ __forceinline__ bool unwritten(const Vec4<T>& v) {
+    using U = decltype(unwritten_bits<T>());
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) any |= __builtin_bit_cast(U, v[j]) == unwritten_bits<T>();
+    return any;
+}
+
+// Bound on a chunk task's wait for one value, in polls (each a device-coherent
 // load and a short sleep, about a microsecond): far beyond any wait of a
 // running chunk (a whole chunk takes a few hundred microseconds), so it only
 // ends a wait that could never be satisfied; the task then raises the abort
@@ -383,6 +415,7 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
     const int np = Nt * ST, mp = Mt * ST, pt = Mt < Nt ? Mt : Nt;
     T* const D = reinterpret_cast<T*>(ws + wo.D);
     T* const R = reinterpret_cast<T*>(ws + wo.R);
+    T* const RF = reinterpret_cast<T*>(ws + wo.RF);
     T* const P = reinterpret_cast<T*>(ws + wo.P);
     const T* const NA = reinterpret_cast<const T*>(ws + wo.NA);
     const T* const NB = reinterpret_cast<const T*>(ws + wo.NB);
@@ -443,46 +476,13 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
     // over all of that part's slices, so no partial sums cross waves
     const int part = wv >> 2, qd = wv & 3, qr = 16 * (qd >> 1), qc = 16 * (qd & 1);
     T* const Pt = P + (int64_t((Kt & 1) * pt + idx) * 2 + part) * ST * ST + qr * ST + qc;
-    // the chunk solver's flags (CHAINED)
-    int* const flags = reinterpret_cast<int*>(ws + wo.F);
-    int* const abort_word = flags + Mt * Nt + (Mt + Nt - 1 + CHUNK - 1) / CHUNK;
+    // the chunk solver's abort word (CHAINED); s_aborted: a wait of this task gave up
+    int* const abort_word = reinterpret_cast<int*>(ws + wo.F) + (Mt + Nt - 1 + CHUNK - 1) / CHUNK;
     __shared__ int s_aborted;
-    // wait until the tasks this one reads from have raised their flags (thread 0
-    // polls; the barrier and every thread's acquire fence then make their data
-    // visible here)
-    // (fresh: the tiles of the two freshest slices, else those two tiles back)
-    auto wait_deps = [&](bool fresh) {
-        if (t == 0) {
-            const ChunkDeps dp = chunk_deps(ChunkTask{Kt, idx}, c0, Nt);
-            const int w0 = fresh ? dp.f0 : dp.o0, w1 = fresh ? dp.f1 : dp.o1;
-            // both flags are polled together (two loads in flight per poll); a
-            // missing one counts as raised (its load reads word 0, unused)
-            const int* const p0 = flags + (w0 < 0 ? 0 : w0);
-            const int* const p1 = flags + (w1 < 0 ? 0 : w1);
-            bool r0 = w0 < 0, r1 = w1 < 0;
-            int ab = __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (uint32_t it = 0; !(r0 && r1) && !ab; ++it) {
-                const int v0 = __hip_atomic_load(p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const int v1 = __hip_atomic_load(p1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                r0 = r0 || v0 != 0;
-                r1 = r1 || v1 != 0;
-                if (it >= spin_limit) {
-                    __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    ab = 1;
-                } else if ((it & 63) == 63) {
-                    ab = __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-            s_aborted = ab;
-        }
+    if constexpr (CHAINED) {
+        if (t == 0) s_aborted = 0;
         __syncthreads();
-    };
-    // every thread's stores reach the device before thread 0 raises the tile's flag
-    auto raise_flag = [&]() {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
-        __syncthreads();
-        if (t == 0) __hip_atomic_store(flags + int64_t(I) * Nt + J, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
+    }
 
     // chunk sources of the tile: row tiles J' in [jl, J), column tiles I' in [il, I);
     // the freshest of each (J - 1, I - 1) lies on diagonal Kt - 1
@@ -514,7 +514,30 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
         } else {
             const int ip = ib + sl - n1;
             va.load(NB + int64_t(ip * ST + q8) * mp + I * ST + c4);  // A(r = c4 + j, k = q8)
-            co_ld4<CHAINED>(vb, R + int64_t(ip * ST) * np + J * ST, q8 * np + c4);  // B(k = q8, c = c4 + j)
+            co_ld4<CHAINED>(vb, RF + int64_t(ip * ST) * np + J * ST, q8 * np + c4);  // B(k = q8, c = c4 + j)
+        }
+    };
+    // chained: the handed-over operand of slice sl (the errors D of a row slice,
+    // RF of a column slice) is polled until every value is written (device-
+    // coherent loads; the writer stores each value once per call)
+    auto settle = [&](int sl, Vec4<T>& va, Vec4<T>& vb) {
+        if constexpr (CHAINED) {
+            const bool row = sl < n1;
+            Vec4<T>& v = row ? va : vb;
+            const T* const bp = row ? D + int64_t(I * ST) * np + (jb + sl) * ST
+                                    : RF + int64_t((ib + sl - n1) * ST) * np + J * ST;
+            for (uint32_t it = 0; unwritten(v); ++it) {
+                if (it >= spin_limit) {
+                    __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    atomicOr(&s_aborted, 1);
+                    break;
+                }
+                if ((it & 63) == 63 && __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                    atomicOr(&s_aborted, 1);
+                    break;
+                }
+                co_ld4<CHAINED>(v, bp, q8 * np + c4);
+            }
         }
     };
     // every load of the first batch is in flight before anything waits on one
@@ -526,7 +549,6 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
             if (u < BATCH && u < ns) fetch(u, pa[v], pb[v]);
         }
     };
-    if constexpr (CHAINED) wait_deps(false);
     first_batch();
     // operand op (0: A, 1: B) of staged slice u
     auto slot = [&](int u, int op) -> T* {
@@ -547,6 +569,7 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
             for (int v = 0; v < SLOTS; ++v) {
                 const int u = NFG * v + fgrp;
                 if (u < BATCH && sb + u < ns) {
+                    settle(sb + u, pa[v], pb[v]);
                     if (sb + u < n1) {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) slot(u, 0)[(c4 + j) * PK + q8] = pa[v][j];
@@ -674,10 +697,7 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
     for (int i = 0; i < 4; ++i) sblk[i] = ENTRY ? S[I * ST + r0 + i] * csb : S[I * ST + r0 + i];
     // chained: the tile's own data is on its way; now wait for the freshest
     // slices and the pre-accumulated products
-    if constexpr (CHAINED) {
-        wait_deps(true);
-        first_batch();
-    }
+    if constexpr (CHAINED) first_batch();
 
     // ---- prologue: rowpart (crow) and the chunk's column part (ccol), block layout.
     // X gets rowpart + the column part here; the in-tile column feedback of
@@ -863,13 +883,13 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
     // write R[I, J] = rowpart + Delta N_A[J, J] (read by the later leaves of the
     // chunk and by the band products of the later nodes), gathered from the
     // rounds that published it; waves 4..7 store Delta, the codes and V.
-    // (chained: the codes and V after the tile's flag, off the path of the tiles waiting on it)
+    // (the errors and RF first: the tiles waiting on them poll for them)
     T zv[4];
     if (blk) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int d = r0 + i + b;  // the entry's element diagonal
-            co_st<CHAINED>(R + int64_t(I * ST + r0 + i) * np + J * ST + b, xR[((d / RD) * ST + b) * RD + d % RD]);
+            co_st<CHAINED>(RF + int64_t(I * ST + r0 + i) * np + J * ST + b, xR[((d / RD) * ST + b) * RD + d % RD]);
         }
     } else {
 #pragma unroll
@@ -879,7 +899,6 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
             co_st<CHAINED>(D + gi * np + gj, bufB[b * PK + r0 + i]);
         }
     }
-    if constexpr (CHAINED) raise_flag();
     if (!blk) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -927,7 +946,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void chunk_kernel(int c0, int c1, int
                                                     CodeT<ENTRY>* __restrict__ Z, int64_t ldz, T* __restrict__ V,
                                                     int64_t ldv, uint32_t spin_limit) {
     const WsOffsets wo = ws_offsets(Mt, Nt, sizeof(T));
-    int* const counter = reinterpret_cast<int*>(ws + wo.F) + Mt * Nt + c0 / CHUNK;
+    int* const counter = reinterpret_cast<int*>(ws + wo.F) + c0 / CHUNK;
     __shared__ int s_ticket;
     for (;;) {
         __syncthreads();  // the previous task is done with the LDS and s_ticket
@@ -1061,6 +1080,7 @@ __device__ void band_stage2(const T* __restrict__ R, const T* __restrict__ NB, T
 template <typename T>
 __global__ __launch_bounds__(Band<T>::THREADS) void band_kernel(const T* __restrict__ D, const T* __restrict__ NA,
                                                                 const T* __restrict__ NB, T* __restrict__ R,
+                                                                const T* __restrict__ RF,
                                                                 T* __restrict__ X, int np, int mp, int Mt, int Nt,
                                                                 int K0, int mid, int K1, int P0, int nq, int n1,
                                                                 int sig0, int sig1) {
@@ -1069,7 +1089,7 @@ __global__ __launch_bounds__(Band<T>::THREADS) void band_kernel(const T* __restr
     if (b < n1)
         band_stage1<T, true>(D, NA, R, np, Nt, K0, mid, K1, P0 + b / nq, b % nq, sm);
     else
-        band_stage2<T, true>(R, NB, X, np, mp, Mt, Nt, K0, mid, K1, sig0, sig1, b - n1, sm);
+        band_stage2<T, true>(RF, NB, X, np, mp, Mt, Nt, K0, mid, K1, sig0, sig1, b - n1, sm);
 }
 
 // Stage 1 alone, one 256-thread workgroup per target block (the large nodes).
@@ -1171,7 +1191,7 @@ constexpr int CHUNK_GRID = 256;  // workgroups of a persistent chunk launch: one
 struct SolverLayout {
     int64_t mp, np, Mt, Nt;  // padded extents; tile counts in 32-tiles
     size_t bytes;
-    size_t off_NA, off_NB, off_X, off_D, off_R, off_P, off_S, off_C, off_F, off_L;
+    size_t off_NA, off_NB, off_X, off_D, off_R, off_RF, off_P, off_S, off_C, off_F, off_L;
 };
 
 SolverLayout solver_layout(kq_dtype dtype, int64_t m, int64_t n) {
@@ -1188,6 +1208,7 @@ SolverLayout solver_layout(kq_dtype dtype, int64_t m, int64_t n) {
     L.off_X = size_t(o.X);
     L.off_D = size_t(o.D);
     L.off_R = size_t(o.R);
+    L.off_RF = size_t(o.RF);
     L.off_P = size_t(o.P);
     L.off_S = size_t(o.S);
     L.off_C = size_t(o.C);
@@ -1201,7 +1222,7 @@ template <typename T>
 struct SolverRun {
     const SolverLayout& L;
     int m, n, qmin, qmax;
-    T *NA, *NB, *X, *D, *R, *P, *S;
+    T *NA, *NB, *X, *D, *R, *RF, *P, *S;
     T* C;     // column scales (WaterKron mode) or nullptr
     void* Z;  // int8 codes, or int32 in the WaterKron mode
     int64_t ldz;
@@ -1250,7 +1271,7 @@ struct SolverRun {
         }
         const bool fuse = n1 + n2 <= BAND_FUSE_MAX;
         if (fuse && n1 + n2 > 0) {
-            hipLaunchKernelGGL(band_kernel<T>, dim3(n1 + n2), dim3(Band<T>::THREADS), 0, st, D, NA, NB, R, X,
+            hipLaunchKernelGGL(band_kernel<T>, dim3(n1 + n2), dim3(Band<T>::THREADS), 0, st, D, NA, NB, R, RF, X,
                                int(L.np), int(L.mp), Mt, Nt, K0, mid, K1, P0, nq, n1, sig0, sig1);
             KQ_LAUNCHED("band_kernel");
         }
@@ -1260,7 +1281,7 @@ struct SolverRun {
             KQ_LAUNCHED("band_stage1_kernel");
         }
         if (!fuse && n2 > 0) {
-            hipLaunchKernelGGL(band_stage2_kernel<T>, dim3(n2), dim3(GEMM_THREADS), 0, st, R, NB, X, int(L.np),
+            hipLaunchKernelGGL(band_stage2_kernel<T>, dim3(n2), dim3(GEMM_THREADS), 0, st, RF, NB, X, int(L.np),
                                int(L.mp), Mt, Nt, K0, mid, K1, sig0, sig1);
             KQ_LAUNCHED("band_stage2_kernel");
         }
@@ -1329,7 +1350,8 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
     SolverRun<T> run{L, int(m), int(n), q.qmin, q.qmax,
                      reinterpret_cast<T*>(base + L.off_NA), reinterpret_cast<T*>(base + L.off_NB),
                      reinterpret_cast<T*>(base + L.off_X), reinterpret_cast<T*>(base + L.off_D),
-                     reinterpret_cast<T*>(base + L.off_R), reinterpret_cast<T*>(base + L.off_P),
+                     reinterpret_cast<T*>(base + L.off_R), reinterpret_cast<T*>(base + L.off_RF),
+                     reinterpret_cast<T*>(base + L.off_P),
                      reinterpret_cast<T*>(base + L.off_S),
                      q.col_scales ? reinterpret_cast<T*>(base + L.off_C) : nullptr, q.codes, q.ldc, V, ldv, st, base,
                      q.chained, chunk_spin_limit()};
@@ -1348,9 +1370,9 @@ kq_status quantize_typed(int64_t m, int64_t n, const T* W, int64_t ldw, const T*
     }
     hipLaunchKernelGGL(init_solver_kernel<T>, rows(L.np, L.mp), dim3(threads), 0, st, W, ldw, int(m), int(n),
                        int(L.mp), int(L.np), q.row_scales, q.per_row, q.col_scales, run.X, run.S, run.C,
-                       UB ? run.R : nullptr);
+                       UB ? run.R : nullptr, UB && run.chained ? run.D : nullptr, run.RF);
     KQ_LAUNCHED("init_solver_kernel");
-    if (UB && run.chained) {  // the chunk solver's flags, ticket counters and abort word start at zero
+    if (UB && run.chained) {  // the chunk solver's ticket counters and abort word start at zero
         const int64_t nw = flag_words(L.Mt, L.Nt);
         hipLaunchKernelGGL(zero_words_kernel, blocks(nw), dim3(threads), 0, st,
                            reinterpret_cast<int*>(base + L.off_F), nw);
