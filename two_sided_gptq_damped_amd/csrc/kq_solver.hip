@@ -31,8 +31,8 @@
 // feedback, one workgroup per tile, after pulling the feedback of the chunk's
 // earlier tiles.  One persistent launch runs a whole chunk (chunk_kernel): its
 // workgroups draw tile tasks in tile-diagonal order and a tile starts as soon as
-// the two tiles before it in its row and column are done (per-tile flags, see
-// kq_chunk_sched.hpp).
+// the outputs it reads of the tiles before it in its row and column have
+// arrived: it polls them (see kq_chunk_sched.hpp).
 //
 // Workspace layout (row-major, padded to multiples of 64 with zero weights,
 // unit scales and identity factors, so padding never reaches a real entry):
@@ -402,10 +402,10 @@ constexpr uint32_t CHUNK_SPIN_LIMIT = 1u << 18;  // the default; the environment
 // One leaf task on tile idx of tile-diagonal Kt of chunk [c0, c1): the sweep of
 // the tile, or (pre) the pre-accumulation of its chunk products over every
 // slice but its two freshest.  CHAINED: the task runs inside the persistent
-// chunk solver, sums the older slices' products itself (no pre tasks there),
-// waits for the tiles it reads through the flags (see kq_chunk_sched.hpp) and
-// raises its own when swept; otherwise the launch order provides the
-// dependencies (a launch per tile-diagonal, the pre role on its own workgroups).
+// chunk solver, sums the older slices' products itself (no pre tasks there) and
+// polls every handed-over value it reads until it is written (see
+// kq_chunk_sched.hpp); otherwise the launch order provides the dependencies (a
+// launch per tile-diagonal, the pre role on its own workgroups).
 template <typename T, bool ENTRY, bool CHAINED>
 __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int c1, int Mt, int Nt, int qmin,
                                           int qmax, char* __restrict__ ws, int m, int n,
