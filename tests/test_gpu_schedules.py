@@ -1,7 +1,7 @@
 """GPU parity of the two schedules of the two-sided solver.
 
 kron_quantize runs the recursion's leaves as one persistent launch per chunk of
-tile-diagonals (tiles handed over through device-coherent flags);
+tile-diagonals (each tile polls the outputs of its neighbours);
 kron_quantize_per_diagonal launches one kernel per tile-diagonal.  Both run the
 same operations in the same order, so codes, V and loss must be equal bit for
 bit, whatever order the workgroups run the tasks in (FastKron page, section
@@ -10,7 +10,7 @@ also checked against the oracle on the 32 x 32 fp64 problem (literal Kronecker
 GPTQ) and, in fp64, against the C left-looking loop up to the 1e-9 tie rule.
 Shapes span one tile, ragged edges, several chunks and recursion levels, n > m,
 and the 4096 x 4096 and 1024 x 4096 workloads; kron_quantize runs twice on one
-workspace (its flags are reset per call).
+workspace (its hand-over state is reset per call).
 """
 import numpy as np
 import pytest
@@ -125,7 +125,7 @@ def test_bounded_wait_ends_the_launch(monkeypatch):
     satisfied at its first poll gives up and raises the abort word: the launch
     must still drain (the call returns) and the tiles swept after the abort
     store NaN in V.  The next call, with the default bound, is exact again on the
-    same workspace (its flags are reset per call)."""
+    same workspace (its hand-over state is reset per call)."""
     m = n = 512
     c = synth.spectral(m, n, config=71)
     UA, UB, s = oracle_problem(c["W"], c["A"], c["B"], 3, True)
