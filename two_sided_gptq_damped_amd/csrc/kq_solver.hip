@@ -341,16 +341,9 @@ static_assert(SWEEP_THREADS == LEAF_THREADS, "every thread of the leaf takes par
 template <bool ENTRY>
 using CodeT = std::conditional_t<ENTRY, int32_t, int8_t>;
 
-// Device-coherent element access (agent-scope relaxed atomics): the data that
-// chunk tasks hand to one another goes through the device's coherence point,
-// so no cache needs a write-back or an invalidation at a hand-over.
-template <bool CO, typename T>
-__device__ __forceinline__ T co_ld(const T* p) {
-    if constexpr (CO)
-        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-        return *p;
-}
+// Device-coherent stores (agent-scope relaxed atomics) of the data that chunk
+// tasks hand to one another: it goes through the device's coherence point, so
+// no cache needs a write-back or an invalidation at a hand-over.
 template <bool CO, typename T>
 __device__ __forceinline__ void co_st(T* p, T v) {
     if constexpr (CO)
