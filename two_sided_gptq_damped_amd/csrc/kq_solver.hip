@@ -13,14 +13,14 @@
 // solve(K0, K1) over tile-diagonal ranges follows section 2.5's recursion:
 // solve(K0, mid); add the errors of the first half to the second half with two
 // batched products; solve(mid, K1).  The feedback is separable: the error
-// Delta[I', J'] reaches X[I, J] as N_B[I', I]^T Delta[I', J'] N_A[J', J].  R[I', J]
-// holds the row-propagated errors sum_{J' <= J} Delta[I', J'] N_A[J', J] of tile
-// (I', J): it is accumulated by the nodes before the tile's chunk and completed by
-// the tile's leaf.  At node [K0, K1) with split mid, for the targets of
-// diagonals [mid, K1):
+// Delta[I', J'] reaches X[I, J] as N_B[I', I]^T Delta[I', J'] N_A[J', J].  The
+// row-propagated errors sum_{J' <= J} Delta[I', J'] N_A[J', J] of tile (I', J) are
+// accumulated in R by the nodes before the tile's chunk; the tile's leaf
+// completes them and writes the complete tile to RF.  At node [K0, K1) with split
+// mid, for the targets of diagonals [mid, K1):
 //   stage 1  R[I', J] += sum_{J' : K0 <= I'+J' < mid} Delta[I', J'] N_A[J', J]
-//   stage 2  X[I, J] += sum_{I' : K0 <= I'+J < mid} N_B[I', I]^T R[I', J]
-// (stage 2 reads only left-half tiles, whose R is complete).  Each (source,
+//   stage 2  X[I, J] += sum_{I' : K0 <= I'+J < mid} N_B[I', I]^T RF[I', J]
+// (stage 2 reads only left-half tiles, whose RF is complete).  Each (source,
 // target) pair passes through one stage-1 or leaf row product and one stage-2
 // or leaf column product, so the band work is the method's own m n (m + n) up to
 // tile granularity.  Both stages run on 64 x 64 matrix-core output blocks
@@ -171,15 +171,17 @@ struct Vec4<double> {
 // (left-looking, the per-entry form of section 2.4 at tile granularity).  For
 // tile (I, J) on diagonal K of the chunk:
 //   rowpart = R[I, J] + sum_{c0 - I <= J' < J} Delta[I, J'] N_A[J', J]
-//   X[I, J] += N_B[I, I]^T rowpart + sum_{c0 - J <= I' < I} N_B[I', I]^T R[I', J]
-// (R[I', J] of the chunk's earlier tiles is complete), and after the sweep the
-// leaf writes R[I, J] = rowpart + Delta[I, J] N_A[J, J].  Both come out of the
+//   X[I, J] += N_B[I, I]^T rowpart + sum_{c0 - J <= I' < I} N_B[I', I]^T RF[I', J]
+// (RF[I', J] of the chunk's earlier tiles is complete), and after the sweep the
+// leaf writes RF[I, J] = rowpart + Delta[I, J] N_A[J, J].  Both come out of the
 // sweep: N_B[I, I]^T rowpart is rowpart plus the in-tile column feedback of
 // rowpart, and the sweep's row-accumulated errors start at rowpart, so its column
 // feedback carries that part and every entry's final row-accumulated value is
-// its entry of R[I, J].  The sums over the
+// its entry of RF[I, J].  The sums over the
 // slices before diagonal K - 1 are pre-accumulated by launch K - 1 (see the
-// kernel), so the leaf itself multiplies only the two freshest slices.  The
+// kernel), or in the persistent solver by the tile's own task while the
+// freshest slices are still being swept, so the leaf itself multiplies only the
+// two freshest slices after they arrive.  The
 // 32 x 32 x 32 products run on the matrix cores: their operands are staged
 // k-major in LDS and each wave owns one 16 x 16 quadrant of one of the two sums,
 // over all of its slices, so the sums need no reduction across waves.
@@ -874,7 +876,7 @@ __device__ __forceinline__ void leaf_task(bool pre, int Kt, int idx, int c0, int
     }
     // The last round's barrier made the errors and codes in bufB / bufA and every
     // entry's final row-accumulated value in xR complete.  Epilogue: waves 0..3
-    // write R[I, J] = rowpart + Delta N_A[J, J] (read by the later leaves of the
+    // write RF[I, J] = rowpart + Delta N_A[J, J] (read by the later leaves of the
     // chunk and by the band products of the later nodes), gathered from the
     // rounds that published it; waves 4..7 store Delta, the codes and V.
     // (the errors and RF first: the tiles waiting on them poll for them)
