@@ -9,8 +9,9 @@ bit, whatever order the workgroups run the tasks in (FastKron page, section
 also checked against the oracle on the 32 x 32 fp64 problem (literal Kronecker
 GPTQ) and, in fp64, against the C left-looking loop up to the 1e-9 tie rule.
 Shapes span one tile, ragged edges, several chunks and recursion levels, n > m,
-and the 4096 x 4096 and 1024 x 4096 workloads; kron_quantize runs twice on one
-workspace (its hand-over state is reset per call).
+and the 4096 x 4096, 1024 x 4096, 14336 x 4096 and 4096 x 14336 workloads;
+kron_quantize runs twice on one workspace (its hand-over state is reset per
+call).
 """
 import numpy as np
 import pytest
@@ -104,7 +105,7 @@ def test_per_tensor_scale_and_spectral_256():
         assert_same(both(up(c["W"], dtype), up(UA, dtype), up(UB, dtype), up(s, dtype), 4, False), "256")
 
 
-@pytest.mark.parametrize("m,n,bits", [(4096, 4096, 2), (1024, 4096, 3), (2048, 1536, 2)])
+@pytest.mark.parametrize("m,n,bits", [(4096, 4096, 2), (1024, 4096, 3), (2048, 1536, 2), (14336, 4096, 3), (4096, 14336, 2)])
 def test_llm_workloads_equal_launch_form(m, n, bits):
     c = synth.llm(m, n, bits, config=3)
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
