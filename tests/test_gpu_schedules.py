@@ -83,7 +83,7 @@ def test_tiny_fp64_matches_literal_kronecker_gptq():
     assert np.array_equal(outs[1][0], Z1)
 
 
-@pytest.mark.parametrize("m,n", [(1, 1), (32, 32), (33, 65), (100, 300), (300, 100), (520, 610)])
+@pytest.mark.parametrize("m,n", [(1, 1), (1, 200), (200, 1), (32, 32), (33, 65), (100, 300), (300, 100), (520, 610)])
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 def test_ragged_equals_launch_form(m, n, dtype):
     c = synth.spectral(m, n, config=60 + m % 7)
