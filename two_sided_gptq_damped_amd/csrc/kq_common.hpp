@@ -270,6 +270,14 @@ struct NoMask {
     __device__ __forceinline__ bool operator()(int, int) const { return true; }
 };
 
+// live(wy, wx, kt): whether the wave owning the 32 x 32 quadrant (wy, wx) of the
+// 64 x 64 output needs its product over the kt-th 32-deep tile of K.  A wave whose
+// operands are masked to zero over that tile, or whose output is discarded, skips
+// its matrix-core steps there (the sum is unchanged: it would add zeros).
+struct AllLive {
+    __device__ __forceinline__ bool operator()(int, int, int) const { return true; }
+};
+
 // K-slice depth as a parameter: KS = 16 R deep slices, each thread moving R
 // groups of the 16-deep loader pattern.  Deeper slices carry more matrix-core
 // work per global round trip, which matters when few blocks share a CU and the
@@ -330,16 +338,19 @@ struct GemmSmemK {
 // both outstanding (two register sets used in turn), so a block whose K loop is
 // bound by the latency of its own loads waits half as often.  K must be a
 // multiple of KS.
-template <typename T, int KS, bool A_KMAJ, bool B_KMAJ, typename MA, typename MB>
+template <typename T, int KS, bool A_KMAJ, bool B_KMAJ, typename MA, typename MB, typename LV = AllLive>
 __device__ void tile_gemm_masked_k2(const T* __restrict__ A, int64_t lda, const T* __restrict__ B, int64_t ldb, int K,
-                                    GemmSmemK<T, KS>& sm, WaveAcc<T>& acc, MA ma, MB mb) {
+                                    GemmSmemK<T, KS>& sm, WaveAcc<T>& acc, MA ma, MB mb, LV live = LV()) {
+    static_assert(KS <= 32 && 32 % KS == 0, "a slice lies in one 32-deep tile of K");
     constexpr int S = LdsStride<T>::value;
-    const int t = threadIdx.x & 255, lane = t & 63, w = t >> 6;
+    const int t = threadIdx.x & 255, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: scalar branches on live
     const int wy = w >> 1, wx = w & 1;
     LoaderK<T, A_KMAJ, B_KMAJ, KS> la, lb;
     const int nk = K / KS;
     if (nk == 0) return;
-    auto mma = [&](int buf) {
+    auto mma = [&](int buf, int s) {
+        if (!live(wy, wx, s * KS / 32)) return;
 #pragma unroll
         for (int q = 0; q < KS / KSTEP; ++q) acc.mma(sm.a[buf] + KSTEP * q * S, sm.b[buf] + KSTEP * q * S, wy, wx, lane);
     };
@@ -352,14 +363,14 @@ __device__ void tile_gemm_masked_k2(const T* __restrict__ A, int64_t lda, const 
     for (int s = 0; s < nk; s += 2) {
         // LDS stage 0 holds slice s, lb carries slice s + 1
         if (s + 2 < nk) la.fetch(A, lda, B, ldb, (s + 2) * KS, t);
-        mma(0);
+        mma(0, s);
         if (s + 1 < nk) {
             lb.apply((s + 1) * KS, t, ma, mb);
             lb.stash(sm.a[1], sm.b[1], t);
             __syncthreads();
             // LDS stage 1 holds slice s + 1, la carries slice s + 2
             if (s + 3 < nk) lb.fetch(A, lda, B, ldb, (s + 3) * KS, t);
-            mma(1);
+            mma(1, s + 1);
             if (s + 2 < nk) {
                 la.apply((s + 2) * KS, t, ma, mb);
                 la.stash(sm.a[0], sm.b[0], t);
@@ -381,10 +392,12 @@ struct SplitSmem {
     GemmSmem<T> st[G];
 };
 
-template <typename T, int G, bool A_KMAJ, bool B_KMAJ, typename MA, typename MB>
+template <typename T, int G, bool A_KMAJ, bool B_KMAJ, typename MA, typename MB, typename LV = AllLive>
 __device__ void tile_gemm_masked_splitk(const T* __restrict__ A, int64_t lda, const T* __restrict__ B,
-                                        int64_t ldb, int K, SplitSmem<T, G>& sm, WaveAcc<T>& acc, MA ma, MB mb) {
-    const int tg = threadIdx.x, grp = tg >> 8, t = tg & 255, lane = t & 63, w = t >> 6;
+                                        int64_t ldb, int K, SplitSmem<T, G>& sm, WaveAcc<T>& acc, MA ma, MB mb,
+                                        LV live = LV()) {
+    const int tg = threadIdx.x, grp = tg >> 8, t = tg & 255, lane = t & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: scalar branches on live
     const int wy = w >> 1, wx = w & 1;
     TileLoader<T, T, A_KMAJ, B_KMAJ, false> ld;
     GemmSmem<T>& my = sm.st[grp];
@@ -426,7 +439,7 @@ __device__ void tile_gemm_masked_splitk(const T* __restrict__ A, int64_t lda, co
             const int cur = it & 1;
             const int sn = s + G;  // this group's next slice
             if (sn < nk) ld.fetch(A, lda, B, ldb, sn * KSTEP, TILE, TILE, K, t);
-            if (s < nk) acc.mma(my.a[cur], my.b[cur], wy, wx, lane);
+            if (s < nk && live(wy, wx, s * KSTEP / 32)) acc.mma(my.a[cur], my.b[cur], wy, wx, lane);
             if (sn < nk) {
                 apply(sn * KSTEP);
                 ld.stash(my.a[cur ^ 1], my.b[cur ^ 1], t);

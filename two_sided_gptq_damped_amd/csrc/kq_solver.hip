@@ -1008,11 +1008,17 @@ __device__ void band_stage1(const T* __restrict__ D, const T* __restrict__ NA, T
         const int s = I0 + (r >> 5) + kl + (k >> 5);  // tile-diagonal of the source tile
         return s >= K0 && s < mid;
     };
+    // wave (wy, wx): sources (I0 + wy, kl + kt), target tile (I0 + wy, 2 Q + wx)
+    auto lv = [=](int wy, int wx, int kt) {
+        const int s = I0 + wy + kl + kt, k = I0 + wy + 2 * Q + wx;
+        return s >= K0 && s < mid && k >= mid && k < K1;
+    };
     if constexpr (SPLIT) {
-        tile_gemm_masked_splitk<T, Band<T>::G, false, false>(A, np, B, np, (kh - kl + 1) * ST, sm, acc, ma, NoMask());
+        tile_gemm_masked_splitk<T, Band<T>::G, false, false>(A, np, B, np, (kh - kl + 1) * ST, sm, acc, ma, NoMask(),
+                                                             lv);
         if (threadIdx.x >= 256) return;  // group 0 holds the product
     } else {
-        tile_gemm_masked_k2<T, 2 * KSTEP, false, false>(A, np, B, np, (kh - kl + 1) * ST, sm, acc, ma, NoMask());
+        tile_gemm_masked_k2<T, 2 * KSTEP, false, false>(A, np, B, np, (kh - kl + 1) * ST, sm, acc, ma, NoMask(), lv);
     }
     T* out = R + int64_t(I0) * ST * np + int64_t(Q) * TILE;
     for_each_acc(acc, [&](int r, int c, T v) {
@@ -1058,11 +1064,17 @@ __device__ void band_stage2(const T* __restrict__ R, const T* __restrict__ NB, T
     const T* A = NB + int64_t(kl) * ST * mp + int64_t(I0) * ST;  // A(r, k) = NB[k][r]
     const T* B = R + int64_t(kl) * ST * np + int64_t(J0) * ST;
     auto mb = [=](int k, int c) { return src_valid(kl + (k >> 5), J0 + (c >> 5)); };
+    // wave (wy, wx): sources R[kl + kt, J0 + wx], target tile (I0 + wy, J0 + wx)
+    auto lv = [=](int wy, int wx, int kt) {
+        const int k = I0 + wy + J0 + wx;
+        return src_valid(kl + kt, J0 + wx) && k >= mid && k < K1;
+    };
     if constexpr (SPLIT) {
-        tile_gemm_masked_splitk<T, Band<T>::G, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
+        tile_gemm_masked_splitk<T, Band<T>::G, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb,
+                                                            lv);
         if (threadIdx.x >= 256) return;  // group 0 holds the product
     } else {
-        tile_gemm_masked_k2<T, 2 * KSTEP, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb);
+        tile_gemm_masked_k2<T, 2 * KSTEP, true, false>(A, mp, B, np, (kh - kl + 1) * ST, sm, acc, NoMask(), mb, lv);
     }
     T* out = X + int64_t(I0) * ST * np + int64_t(J0) * ST;
     for_each_acc(acc, [&](int r, int c, T v) {
